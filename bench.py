@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA frozen-base hot path on one MI355X.
+
+One step = every row of the path over one batch of synthetic input, on the
+two Llama-7B-shaped weights (q 4096x4096 and up 11008x4096, bf16 ~N(0,0.02)):
+  1. quantize both weights (bf16 -> NF4 codes + 8-bit absmax codes + scales),
+  2. dequantize both to bf16,
+  3. decode forward (GEMV path) at M = 1, 4 and 16 tokens, each weight,
+  4. training forward at M = 4096 tokens (batch 4 x seq 1024), each weight,
+  5. backward dX, dA, dB at M = 4096, each weight (dY ~ N(0,1)),
+with LoRA r = 16, alpha = 32, A ~ N(0, 1/K), B ~ N(0, 0.01).
+`value` is the step's multiply-add work (2 flops per MAC; dequantization and
+quantization count no flops) over the measured step time, inputs resident in
+HBM. Per-call durations come from HIP events on the stream the library
+launches on; the roofline entry is the dominant call (the largest share of the
+step). The CPU baseline times the oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NF4 dequant-GEMM TFLOP/s & GEMV weight GB/s (fraction of roofline) per layer"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def nf4_bytes(N, K):
+    n = N * K
+    nb = n // 64
+    return n // 2 + nb + 4 * ((nb + 255) // 256)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the GEMV ring and bulk quantize/dequant bandwidth runs")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import qlora_fine_tuning_blockwise_amd as q
+    from qlora_fine_tuning_blockwise_amd import synthetic as syn
+
+    q._lib.load()  # fail loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = syn.LLAMA7B_TRAIN
+    r, alpha, Mt = cfg["r"], cfg["alpha"], cfg["M"]
+    Mdec = syn.LLAMA7B_DECODE["M"]
+    names = list(cfg["weights"])
+
+    # ------------------------------------------------------------ inputs (resident)
+    W, A, B, dY, nf4, deq, yb = {}, {}, {}, {}, {}, {}, {}
+    for i, name in enumerate(names):
+        N, K = cfg["weights"][name]
+        W[name] = syn.torch_normal_bf16((N, K), cfg["w_std"], syn.seed_of(3, i), dev)
+        A[name] = syn.torch_normal_bf16((K, r), 1.0 / K ** 0.5, syn.seed_of(3, 10 + i), dev)
+        B[name] = syn.torch_normal_bf16((r, N), 0.01, syn.seed_of(3, 20 + i), dev)
+        dY[name] = syn.torch_normal_bf16((Mt, N), 1.0, syn.seed_of(3, 30 + i), dev)
+        nf4[name] = q.qlora_quantize_nf4_dq(W[name])
+        deq[name] = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    K0 = cfg["weights"][names[0]][1]
+    x_train = syn.torch_normal_bf16((Mt, K0), 1.0, syn.seed_of(3, 40), dev)
+    x_dec = {M: syn.torch_normal_bf16((M, K0), 1.0, syn.seed_of(2, 40 + M), dev) for M in Mdec}
+    ws_bytes = max(max(q.qlora_workspace_bytes(0, M, *cfg["weights"][n], r) for M in Mdec + (Mt,))
+                   for n in names)
+    ws_bytes = max(ws_bytes, max(q.qlora_workspace_bytes(1, Mt, *cfg["weights"][n], r)
+                                 for n in names))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = {}
+    for name in names:
+        N, K = cfg["weights"][name]
+        out[name] = dict(
+            ydec={M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Mdec},
+            y=torch.empty((Mt, N), dtype=torch.float32, device=dev),
+            u=torch.empty((Mt, r), dtype=torch.float32, device=dev))
+
+    # ------------------------------------------------------------ flops per call
+    def fwd_flops(M, N, K):
+        return 2 * M * N * K + 2 * M * r * (K + N)
+
+    def bwd_flops(M, N, K):
+        return 2 * M * N * K + 2 * M * r * (N + K) + 2 * M * K * r + 2 * M * N * r
+
+    calls = []  # (label, fn, flops, bytes)
+    for name in names:
+        N, K = cfg["weights"][name]
+        w = nf4[name]
+        o = out[name]
+        calls.append((f"quantize_{name}", lambda w=w, name=name: q.qlora_quantize_nf4_dq(W[name], out=w),
+                      0, 2 * N * K + nf4_bytes(N, K)))
+        calls.append((f"dequant_{name}", lambda w=w, name=name: q.qlora_dequant_bf16(w, out=deq[name]),
+                      0, nf4_bytes(N, K) + 2 * N * K))
+    for name in names:
+        N, K = cfg["weights"][name]
+        w = nf4[name]
+        o = out[name]
+        for M in Mdec:
+            calls.append((f"fwd_decode_M{M}_{name}",
+                          lambda w=w, o=o, M=M, name=name: q.qlora_linear_fwd(
+                              w, x_dec[M], A[name], B[name], alpha, y=o["ydec"][M], workspace=ws),
+                          fwd_flops(M, N, K),
+                          nf4_bytes(N, K) + 2 * (M * K + K * r + r * N) + 4 * M * N))
+    for name in names:
+        N, K = cfg["weights"][name]
+        w = nf4[name]
+        o = out[name]
+        calls.append((f"fwd_train_{name}",
+                      lambda w=w, o=o, name=name: q.qlora_linear_fwd(
+                          w, x_train, A[name], B[name], alpha, y=o["y"], u_out=o["u"],
+                          workspace=ws),
+                      fwd_flops(Mt, N, K), 0))
+        calls.append((f"bwd_train_{name}",
+                      lambda w=w, o=o, name=name: q.qlora_linear_bwd(
+                          w, x_train, dY[name], A[name], B[name], alpha, u_saved=o["u"],
+                          workspace=ws),
+                      bwd_flops(Mt, N, K), 0))
+    step_flops = sum(c[2] for c in calls)
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in calls]
+
+    def step(record):
+        for (label, fn, _, _), (e0, e1) in zip(calls, ev):
+            if record:
+                e0.record(stream)
+            fn()
+            if record:
+                e1.record(stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    per_call = [0.0] * len(calls)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()  # read this step's events
+        for i, (e0, e1) in enumerate(ev):
+            per_call[i] += e0.elapsed_time(e1)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    # The step time is the sum of the event spans (device time, every call of
+    # the step in stream order); the host-clock time is reported beside it.
+    ms_step_dev = sum(per_call) / args.steps
+    ms_step_host = (t1 - t0) * 1e3 / args.steps
+    value = step_flops / (ms_step_dev * 1e-3) / 1e12
+
+    breakdown = {}
+    for (label, _, flops, nbytes), tot in zip(calls, per_call):
+        ms = tot / args.steps
+        e = {"ms": round(ms, 5)}
+        if flops:
+            e["tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+            e["frac_bf16_peak"] = round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if nbytes:
+            e["gbps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            e["frac_hbm_peak"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
+        breakdown[label] = e
+    # dominant call: the largest share of the step
+    dom = max(range(len(calls)), key=lambda i: per_call[i])
+    dl, _, dflops, _ = calls[dom]
+    dms = per_call[dom] / args.steps
+    achieved = dflops / (dms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel_call": dl, "flops_per_launch": dflops, "avg_ms": round(dms, 5)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step_dev, 4),
+        "ms_per_step_host": round(ms_step_host, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama7b_nf4_layer_pair: q 4096x4096 + up 11008x4096 bf16 "
+                               "N(0,0.02) -> NF4+DQ; decode M=1,4,16; train M=4096 fwd+bwd",
+                   "weights": {n: list(cfg["weights"][n]) for n in names},
+                   "M_decode": list(Mdec), "M_train": Mt, "r": r, "alpha": alpha},
+        "roofline": roofline, "breakdown": breakdown,
+    }
+
+    if not args.no_extras:
+        result["gemv_ring"] = gemv_ring(q, syn, torch, dev, r, alpha)
+        result["bulk_quantize"] = bulk_quantize(q, syn, torch, dev)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, syn, cfg, step_flops, ms_step_dev)
+    print(json.dumps(result), flush=True)
+
+
+def gemv_ring(q, syn, torch, dev, r, alpha):
+    """Decode GEMV weight bandwidth on a ring of distinct 11008x4096 weights
+    (> 512 MB of NF4, past the 256 MB Infinity Cache)."""
+    N, K = 11008, 4096
+    nw = 24
+    base = syn.torch_normal_bf16((N, K), 0.02, 777, dev)
+    ring = [q.qlora_quantize_nf4_dq(base) for _ in range(nw)]
+    for w in ring[1:]:  # distinct contents: perturb the codes bytes
+        w.codes.copy_(ring[0].codes.roll(1))
+    del base
+    A = syn.torch_normal_bf16((K, r), 1.0 / K ** 0.5, 778, dev)
+    B = syn.torch_normal_bf16((r, N), 0.01, 779, dev)
+    res = {"weight": [N, K], "ring_weights": nw, "ring_mb": round(nw * nf4_bytes(N, K) / 1e6, 1)}
+    for M in (1, 4, 16):
+        x = syn.torch_normal_bf16((M, K), 1.0, 780 + M, dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(q.qlora_workspace_bytes(0, M, N, K, r), dtype=torch.uint8, device=dev)
+        for w in ring:
+            q.qlora_linear_fwd(w, x, A, B, alpha, y=y, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 4
+        e0.record()
+        for _ in range(reps):
+            for w in ring:
+                q.qlora_linear_fwd(w, x, A, B, alpha, y=y, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (reps * nw)
+        wbytes = nf4_bytes(N, K) + 2 * (K * r + r * N)
+        gbps = wbytes / (ms * 1e-3) / 1e9
+        res[f"M{M}"] = {"us_per_call": round(ms * 1e3, 2), "weight_gbps": round(gbps, 1),
+                        "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                        "tokens_per_s": round(M / (ms * 1e-3), 1)}
+    del ring
+    torch.cuda.empty_cache()
+    return res
+
+
+def bulk_quantize(q, syn, torch, dev):
+    """Quantize and dequantize bandwidth on one 8192x28672 bf16 tensor (470 MB
+    in, past the Infinity Cache)."""
+    N, K = syn.BULK_65B["tensor"]
+    Wt = syn.torch_student_t_outliers_bf16((N, K), 4242, dev)
+    w = q.qlora_quantize_nf4_dq(Wt)
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    res = {"tensor": [N, K]}
+    for label, fn, nbytes in (("quantize", lambda: q.qlora_quantize_nf4_dq(Wt, out=w),
+                               2 * N * K + nf4_bytes(N, K)),
+                              ("dequant", lambda: q.qlora_dequant_bf16(w, out=out),
+                               nf4_bytes(N, K) + 2 * N * K)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        res[label] = {"ms": round(ms, 4), "gbps": round(gbps, 1),
+                      "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                      "params_per_s": round(N * K / (ms * 1e-3), 1)}
+    del Wt, w, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(np, syn, cfg, step_flops, ms_step):
+    """The oracle (single-threaded C) on a bounded sample of the step: quantize
+    and dequantize both weights in full, then forward and backward (dX, dA, dB)
+    on 32 of the 4096 token rows for both weights. Rate = sample flops / time."""
+    import oracle
+
+    r, alpha = cfg["r"], cfg["alpha"]
+    Ms = 32
+    flops = 0
+    t0 = time.perf_counter()
+    for i, (name, (N, K)) in enumerate(cfg["weights"].items()):
+        Wb = syn.normal_bf16((N, K), cfg["w_std"], syn.seed_of(3, i))
+        codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+        What = oracle.dequant_dq(codes, q8, s2)[1].reshape(N, K)
+        x = syn.normal_bf16((Ms, K), 1.0, syn.seed_of(3, 50))
+        A = syn.normal_bf16((K, r), 1.0 / K ** 0.5, syn.seed_of(3, 10 + i))
+        B = syn.normal_bf16((r, N), 0.01, syn.seed_of(3, 20 + i))
+        dY = syn.normal_bf16((Ms, N), 1.0, syn.seed_of(3, 30 + i))
+        oracle.linear_fwd(x, What, A, B, r, alpha)
+        oracle.linear_bwd(x, dY, What, A, B, r, alpha)
+        flops += 2 * Ms * N * K + 2 * Ms * r * (K + N)
+        flops += 2 * Ms * N * K + 2 * Ms * r * (N + K) + 2 * Ms * K * r + 2 * Ms * N * r
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"quantize+dequantize both weights in full, then fwd + bwd (dX, dA, dB) on "
+                      f"{Ms} of 4096 token rows per weight; {flops / 1e9:.2f} GFLOP in "
+                      f"{dt:.1f} s on one host core"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * qlora_amd.h - C ABI of the MI355X (gfx950) QLoRA frozen-base library.
+ *
+ * The library implements the frozen-base hot path of QLoRA as the pages on
+ * the method describe it:
+ *   [P1] "QLoRA", learning-llms.pages.dev/topics/qlora
+ *   [P2] "QLoRA", infra.bea.ai/guide/training/fine-tuning-adapters/qlora
+ *   [P3] "QLoRA", scalata.ai/resources/model-training/qlora
+ *   [P4] "What does QLoRA change about a LoRA run, and why does it fit on one
+ *        GPU?", katajob.com/questions/found-fine-tuning-peft-qlora-memory
+ *   [P5] "QLoRA viz", engineersofai.com/playground/qlora-viz
+ *
+ * STORAGE FORMAT (one format for every entry point)
+ *   A weight W is [N, K] row-major (N out-features, K in-features), flat
+ *   index e = n*K + k. K must be a multiple of 64 so that blocks never
+ *   straddle rows.
+ *   - block b = e / 64: 64 consecutive weights sharing one absmax ([P1]
+ *     bullets: small blocks of 64 weights, one scale per block);
+ *   - codes   uint8[N*K/2]: NF4 code of weight e in the low nibble of byte
+ *     e/2 when e is even, in the high nibble when e is odd;
+ *   - absmax_q int8[N*K/64]: the block absmax quantized to 8 bits
+ *     (0..127) - the double quantization of [P1] bullets, [P2] s1 "Double
+ *     Quantization", [P5] "Double Quantization";
+ *   - absmax_scale float[ceil(N*K/16384)]: one fp32 second-level scale per
+ *     group of 256 consecutive blocks.
+ *   Total 4 + 8/64 + 32/16384 = 4.126953125 bits per weight.
+ *
+ *   Dequantization ([P1] bullets: compute never happens in 4-bit; weights are
+ *   dequantized to bf16 just in time): with L the 16 NF4 levels,
+ *     c1_hat = fp32(absmax_q[b] * absmax_scale[b/256])
+ *     w_hat  = bf16_rne(fp32(L[code] * c1_hat)).
+ *
+ * CONVENTIONS
+ *   - Every pointer argument of a compute entry point is a DEVICE pointer
+ *     owned by the caller; the library allocates nothing and keeps no state
+ *     besides a constant codebook built on first use.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every compute
+ *     entry point only enqueues work on it and returns without synchronizing.
+ *   - Device pointers must be 16-byte aligned. Outputs must not alias inputs.
+ *   - Return value: QLORA_OK (0) or a status below. Argument errors are
+ *     detected on the host before anything is enqueued. No C++ exception
+ *     crosses the ABI.
+ *   - Concurrent calls on different streams are safe; calls sharing a
+ *     workspace buffer must be ordered by the caller.
+ */
+#ifndef QLORA_AMD_H
+#define QLORA_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define QLORA_OK 0
+#define QLORA_ERR_INVALID_ARG 1 /* NULL pointer, negative size, bad enum */
+#define QLORA_ERR_SHAPE 2       /* K % 64 != 0, N or K < 1 */
+#define QLORA_ERR_ALIGN 3       /* a device pointer is not 16-byte aligned */
+#define QLORA_ERR_DTYPE 4       /* unsupported dtype enum */
+#define QLORA_ERR_RANK 5        /* r not a positive multiple of 16, or r > 256 */
+#define QLORA_ERR_WORKSPACE 6   /* workspace smaller than qlora_workspace_bytes() */
+#define QLORA_ERR_LAUNCH 7      /* the HIP runtime reported an error on launch */
+#define QLORA_ERR_INTERNAL 8    /* codebook construction failed its self-check */
+
+/* Element types. */
+#define QLORA_DTYPE_F32 0
+#define QLORA_DTYPE_BF16 1
+
+/* Operations for qlora_workspace_bytes. */
+#define QLORA_OP_FWD 0
+#define QLORA_OP_BWD 1
+
+/* Format version of the storage layout above. */
+#define QLORA_FORMAT_VERSION 1u
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* qlora_strerror(int status);
+
+/* Byte sizes of the three quantized buffers of an [N,K] weight. Host only.
+ * Returns QLORA_ERR_SHAPE unless N >= 1, K >= 64 and K % 64 == 0. */
+int qlora_nf4_sizes(int64_t N, int64_t K, size_t* codes_bytes, size_t* absmax_q_bytes,
+                    size_t* absmax_scale_bytes);
+
+/* The library's NF4 codebook: 16 fp32 levels and the 15 fp32 decision
+ * thresholds used by the quantizer. Host only.
+ * Levels: quantiles of a standard normal distribution ([P1] bullets "NF4
+ * instead of a uniform grid"; [P2] s1 "Key Innovation: NF4") with equal
+ * probability steps, 8 positive and 7 negative levels, an exact 0, scaled so
+ * that the outermost levels are exactly -1 and +1. Threshold i is the
+ * midpoint of levels i and i+1 rounded toward -infinity to fp32, so that a
+ * normalised value x gets code #{i : x > threshold[i]}: the nearest level,
+ * ties to the lower code. */
+int qlora_codebook(float levels[16], float thresholds[15]);
+
+/* Identifier of the quantization setup (FNV-1a over the 16 level bit
+ * patterns, the block and group sizes, the nibble order and the form of the
+ * second level). [P4] "Operational coupling": the quantization setup belongs
+ * in the adapter's recorded metadata. Host only; 0 if the codebook failed. */
+uint32_t qlora_codebook_id(void);
+
+/* Device workspace, in bytes, that qlora_linear_fwd (op = QLORA_OP_FWD) or
+ * qlora_linear_bwd (op = QLORA_OP_BWD) needs for these sizes, assuming no
+ * saved u. Host only; 0 on invalid sizes. */
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
+
+/* Quantize once, at load time ([P4] "The mechanism": the pretrained weights
+ * are quantized once, at load time, and never updated; [P1] "controlled
+ * rounding" and its bullets; [P2] s1; [P3] "How it works").
+ *   W        [N,K] row-major, fp32 (w_dtype = QLORA_DTYPE_F32) or bf16
+ *            (QLORA_DTYPE_BF16). Values must be finite; a non-finite input
+ *            gives unspecified codes (no fault).
+ *   codes, absmax_q, absmax_scale  outputs, sizes from qlora_nf4_sizes.
+ * Per block: c1 = max|w|; x = w / c1 (correctly rounded fp32 division);
+ * code = #{i : x > threshold[i]}; an all-zero block gets code 7 (level 0).
+ * Per group of 256 blocks: c2 = max c1; s2 = c2 / 127; absmax_q =
+ * nearest integer to c1 / s2 (ties to the lower), clamped to [0,127], and 0
+ * for c1 == 0. The NF4 codes use the exact fp32 c1. */
+int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* codes,
+                          int8_t* absmax_q, float* absmax_scale, void* stream);
+
+/* Dequantize to bf16 ([P1] bullets "Compute never happens in 4-bit"; [P3]
+ * "How it works": each layer's 4-bit weights are unpacked into 16-bit).
+ *   W_out  [N,K] bf16, w_hat as in the format section. */
+int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
+                       int64_t N, int64_t K, uint16_t* W_out, void* stream);
+
+/* QLoRA linear forward ([P1] forward equation h = W_hat x + (alpha/r) B(Ax),
+ * here in row-major form):
+ *   u = x A                     (fp32 [M,r])
+ *   y = x W_hat^T + (alpha/r) u B
+ *   x  [M,K] bf16;  A [K,r] bf16;  B [r,N] bf16;  y [M,N] fp32 or bf16
+ *      (y_dtype; the bf16 output is the round-to-nearest-even of the fp32
+ *      result of the same computation).
+ *   u_out      fp32 [M,r] or NULL; when given it receives u (for the backward).
+ *   workspace  device buffer of at least qlora_workspace_bytes(FWD, M,N,K,r).
+ * The weight is read through its dequantized bf16 values, products are exact
+ * and accumulate in fp32. M == 0 is a successful no-op. r % 16 == 0. */
+int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
+                     int64_t N, int64_t K, const uint16_t* x, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int r, float alpha, void* y, int y_dtype, float* u_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* QLoRA linear backward ([P2] s3 "The Backward Pass Through Quantization":
+ * gradients flow through the dequantized frozen base, only the adapters get
+ * gradients; [P4] "The mechanism"):
+ *   v  = dY B^T                      (fp32 [M,r])
+ *   dX = dY W_hat + (alpha/r) v A^T  ([M,K], dx_dtype fp32 or bf16)
+ *   dA = (alpha/r) x^T v             ([K,r], grad_dtype fp32 or bf16)
+ *   dB = (alpha/r) u^T dY            ([r,N], grad_dtype), u = x A
+ *   dY [M,N] bf16; x, A, B as in the forward.
+ *   u_saved  fp32 [M,r] from qlora_linear_fwd's u_out, or NULL to recompute.
+ *   dX, dA, dB may each be NULL to skip that output (x may then be NULL if
+ *   both dA and dB are NULL).
+ * The frozen base is never written. M == 0 writes zero dA and dB. */
+int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
+                     int64_t N, int64_t K, const uint16_t* x, const uint16_t* dY, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int r, float alpha,
+                     const float* u_saved, void* dX, int dx_dtype, void* dA, void* dB,
+                     int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLORA_AMD_H */

@@ -1,0 +1,157 @@
+"""QLoRA frozen-base hot path for MI355X (gfx950): blockwise NF4 quantization
+with double quantization, dequantization to bf16, and the QLoRA linear layer
+(forward and backward), as hand-written HIP kernels behind a C ABI.
+
+The functions below carry the names of the C entry points
+(include/qlora_amd.h). They only marshal arguments: torch supplies device
+memory and the current stream, and every step of the computation runs in
+libqlora_amd.so. Tensors must be contiguous and on a ROCm device.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+
+__all__ = [
+    "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_id",
+    "qlora_workspace_bytes", "qlora_quantize_nf4_dq", "qlora_dequant_bf16",
+    "qlora_linear_fwd", "qlora_linear_bwd", "NF4Weight",
+]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.float32:
+        return _lib.DTYPE_F32
+    if dt == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+class NF4Weight:
+    """The three device buffers of one quantized [N, K] weight."""
+
+    def __init__(self, codes, absmax_q, absmax_scale, N: int, K: int):
+        self.codes, self.absmax_q, self.absmax_scale = codes, absmax_q, absmax_scale
+        self.N, self.K = int(N), int(K)
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.absmax_q.numel() + 4 * self.absmax_scale.numel()
+
+
+def qlora_strerror(status: int) -> str:
+    return _lib.strerror(status)
+
+
+def qlora_nf4_sizes(N: int, K: int):
+    cb, qb, sb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _lib.check(_lib.load().qlora_nf4_sizes(N, K, ctypes.byref(cb), ctypes.byref(qb),
+                                           ctypes.byref(sb)), "qlora_nf4_sizes")
+    return cb.value, qb.value, sb.value
+
+
+def qlora_codebook():
+    lv = np.zeros(16, np.float32)
+    th = np.zeros(15, np.float32)
+    _lib.check(_lib.load().qlora_codebook(lv.ctypes.data_as(ctypes.c_void_p),
+                                          th.ctypes.data_as(ctypes.c_void_p)), "qlora_codebook")
+    return lv, th
+
+
+def qlora_codebook_id() -> int:
+    return int(_lib.load().qlora_codebook_id())
+
+
+def qlora_workspace_bytes(op: int, M: int, N: int, K: int, r: int) -> int:
+    return int(_lib.load().qlora_workspace_bytes(op, M, N, K, r))
+
+
+def _alloc_nf4(N, K, device):
+    cb, qb, sb = qlora_nf4_sizes(N, K)
+    return (torch.empty(cb, dtype=torch.uint8, device=device),
+            torch.empty(qb, dtype=torch.int8, device=device),
+            torch.empty(sb // 4, dtype=torch.float32, device=device))
+
+
+def qlora_quantize_nf4_dq(W: torch.Tensor, out: NF4Weight | None = None, stream=None) -> NF4Weight:
+    """Quantize a [N, K] fp32 or bf16 device tensor to NF4 + double-quantized constants."""
+    N, K = W.shape
+    if out is None:
+        out = NF4Weight(*_alloc_nf4(N, K, W.device), N, K)
+    st = _lib.load().qlora_quantize_nf4_dq(_ptr(W), _dtype_code(W.dtype), N, K, _ptr(out.codes),
+                                           _ptr(out.absmax_q), _ptr(out.absmax_scale),
+                                           _stream(stream))
+    _lib.check(st, "qlora_quantize_nf4_dq")
+    return out
+
+
+def qlora_dequant_bf16(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=w.codes.device)
+    st = _lib.load().qlora_dequant_bf16(_ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale),
+                                        w.N, w.K, _ptr(out), _stream(stream))
+    _lib.check(st, "qlora_dequant_bf16")
+    return out
+
+
+def _workspace(op, M, N, K, r, device, workspace):
+    need = qlora_workspace_bytes(op, M, N, K, r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                     alpha: float, y: torch.Tensor | None = None, y_dtype=torch.float32,
+                     u_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """y = x W_hat^T + (alpha/r) (x A) B. x [M,K] bf16, A [K,r] bf16, B [r,N] bf16."""
+    M = x.shape[0]
+    r = A.shape[1]
+    if y is None:
+        y = torch.empty((M, w.N), dtype=y_dtype, device=x.device)
+    workspace = _workspace(_lib.OP_FWD, M, w.N, w.K, r, x.device, workspace)
+    st = _lib.load().qlora_linear_fwd(
+        _ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale), w.N, w.K, _ptr(x), M, _ptr(A),
+        _ptr(B), r, float(alpha), _ptr(y), _dtype_code(y.dtype), _ptr(u_out), _ptr(workspace),
+        workspace.numel(), _stream(stream))
+    _lib.check(st, "qlora_linear_fwd")
+    return y
+
+
+def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: torch.Tensor,
+                     B: torch.Tensor, alpha: float, u_saved: torch.Tensor | None = None,
+                     want_dx: bool = True, dx_dtype=torch.float32, grad_dtype=torch.float32,
+                     want_grads: bool = True, workspace: torch.Tensor | None = None,
+                     stream=None):
+    """Returns (dX or None, dA or None, dB or None)."""
+    M = dY.shape[0]
+    r = A.shape[1]
+    dev = dY.device
+    dX = torch.empty((M, w.K), dtype=dx_dtype, device=dev) if want_dx else None
+    dA = torch.empty((w.K, r), dtype=grad_dtype, device=dev) if want_grads else None
+    dB = torch.empty((r, w.N), dtype=grad_dtype, device=dev) if want_grads else None
+    workspace = _workspace(_lib.OP_BWD, M, w.N, w.K, r, dev, workspace)
+    st = _lib.load().qlora_linear_bwd(
+        _ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale), w.N, w.K, _ptr(x), _ptr(dY), M,
+        _ptr(A), _ptr(B), r, float(alpha), _ptr(u_saved), _ptr(dX), _dtype_code(dx_dtype),
+        _ptr(dA), _ptr(dB), _dtype_code(grad_dtype), _ptr(workspace), workspace.numel(),
+        _stream(stream))
+    _lib.check(st, "qlora_linear_bwd")
+    return dX, dA, dB

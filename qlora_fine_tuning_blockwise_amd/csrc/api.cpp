@@ -1,0 +1,275 @@
+// C ABI of the library: argument validation, workspace layout and the launch
+// sequence of each entry point. Every check runs on the host before anything
+// is enqueued; the compute entry points only enqueue kernels on the caller's
+// stream.
+#include <cstring>
+
+#include "../../include/qlora_amd.h"
+#include "internal.h"
+
+namespace qlora {
+namespace {
+
+constexpr int64_t kGemvMaxM = 16;  // decode sizes take the GEMV path
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool shape_ok(int64_t N, int64_t K) { return N >= 1 && K >= 64 && K % 64 == 0; }
+
+bool rank_ok(int r) { return r >= 16 && r <= 256 && r % 16 == 0; }
+
+size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace carve-up, shared by the size query and the entry points.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += round_up(bytes);
+    return o;
+  }
+};
+
+struct FwdLayout {
+  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, gemv = 0, total = 0;
+  bool gemv_path = false;
+};
+
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
+  FwdLayout L;
+  Carve c;
+  L.gemv_path = M <= kGemvMaxM;
+  L.At = c.take((size_t)r * K * 2);
+  L.u = need_u ? c.take((size_t)M * r * 4) : 0;
+  L.down = c.take((size_t)lora_down_slices(K) * M * r * 4);
+  if (L.gemv_path) {
+    L.gemv = c.take((size_t)gemv_splits(K) * M * N * 4);
+  } else {
+    L.Bt = c.take((size_t)N * r * 2);
+    L.ulr = c.take((size_t)M * 2 * r * 2);
+  }
+  L.total = c.off;
+  return L;
+}
+
+struct BwdLayout {
+  size_t At = 0, u = 0, down = 0, v = 0, svlr = 0, col = 0, total = 0;
+};
+
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
+  BwdLayout L;
+  Carve c;
+  if (need_u) {
+    L.At = c.take((size_t)r * K * 2);
+    L.u = c.take((size_t)M * r * 4);
+  }
+  const int64_t T = K > N ? K : N;
+  L.down = c.take((size_t)lora_down_slices(T) * M * r * 4);
+  L.v = c.take((size_t)M * r * 4);
+  L.svlr = c.take((size_t)M * 2 * r * 2);
+  L.col = c.take((size_t)colred_splits(M) * T * r * 4);
+  L.total = c.off;
+  return L;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
+
+}  // namespace
+}  // namespace qlora
+
+using namespace qlora;
+
+extern "C" {
+
+const char* qlora_strerror(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_INVALID_ARG: return "invalid argument (NULL pointer, negative size or bad enum)";
+    case QLORA_ERR_SHAPE: return "unsupported shape (need N >= 1, K >= 64, K % 64 == 0)";
+    case QLORA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case QLORA_ERR_DTYPE: return "unsupported dtype";
+    case QLORA_ERR_RANK: return "unsupported LoRA rank (need 16 <= r <= 256, r % 16 == 0)";
+    case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_LAUNCH: return "kernel launch failed";
+    case QLORA_ERR_INTERNAL: return "codebook self-check failed";
+    default: return "unknown status";
+  }
+}
+
+int qlora_nf4_sizes(int64_t N, int64_t K, size_t* codes_bytes, size_t* absmax_q_bytes,
+                    size_t* absmax_scale_bytes) {
+  if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
+  const int64_t n = N * K, nb = n / kBlock;
+  if (codes_bytes) *codes_bytes = (size_t)(n / 2);
+  if (absmax_q_bytes) *absmax_q_bytes = (size_t)nb;
+  if (absmax_scale_bytes) *absmax_scale_bytes = (size_t)((nb + kGroup - 1) / kGroup) * 4;
+  return QLORA_OK;
+}
+
+int qlora_codebook(float levels[16], float thresholds[15]) {
+  const Codebook* cb = nullptr;
+  const int st = get_codebook(&cb, nullptr);
+  if (st != QLORA_OK) return st;
+  if (levels) std::memcpy(levels, cb->level, sizeof cb->level);
+  if (thresholds) std::memcpy(thresholds, cb->thr, sizeof cb->thr);
+  return QLORA_OK;
+}
+
+uint32_t qlora_codebook_id(void) {
+  uint32_t id = 0;
+  return get_codebook(nullptr, &id) == QLORA_OK ? id : 0u;
+}
+
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
+  if (M < 0 || !shape_ok(N, K) || !rank_ok(r)) return 0;
+  if (op == QLORA_OP_FWD) return fwd_layout(M, N, K, r, true).total;
+  if (op == QLORA_OP_BWD) return bwd_layout(M, N, K, r, true).total;
+  return 0;
+}
+
+int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* codes,
+                          int8_t* absmax_q, float* absmax_scale, void* stream) {
+  const Codebook* cb = nullptr;
+  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+  if (!W || !codes || !absmax_q || !absmax_scale) return QLORA_ERR_INVALID_ARG;
+  if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
+  if (w_dtype != QLORA_DTYPE_F32 && w_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale))
+    return QLORA_ERR_ALIGN;
+  return launch_status(launch_quantize(W, w_dtype == QLORA_DTYPE_F32, N * K, codes, absmax_q,
+                                       absmax_scale, *cb, static_cast<hipStream_t>(stream)));
+}
+
+int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
+                       int64_t N, int64_t K, uint16_t* W_out, void* stream) {
+  const Codebook* cb = nullptr;
+  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+  if (!codes || !absmax_q || !absmax_scale || !W_out) return QLORA_ERR_INVALID_ARG;
+  if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale) || !aligned16(W_out))
+    return QLORA_ERR_ALIGN;
+  return launch_status(launch_dequant(codes, absmax_q, absmax_scale, N * K, W_out, *cb,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
+                     int64_t N, int64_t K, const uint16_t* x, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int r, float alpha, void* y, int y_dtype, float* u_out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const Codebook* cb = nullptr;
+  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+  if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
+  if (y_dtype != QLORA_DTYPE_F32 && y_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
+  if (!rank_ok(r)) return QLORA_ERR_RANK;
+  if (M == 0) return QLORA_OK;
+  if (!codes || !absmax_q || !absmax_scale || !x || !A || !B || !y) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale) || !aligned16(x) ||
+      !aligned16(A) || !aligned16(B) || !aligned16(y) || (u_out && !aligned16(u_out)) ||
+      (workspace && !aligned16(workspace)))
+    return QLORA_ERR_ALIGN;
+  const FwdLayout L = fwd_layout(M, N, K, r, u_out == nullptr);
+  if (!workspace || workspace_bytes < L.total) return QLORA_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float s = alpha / (float)r;
+  const bool ybf = y_dtype == QLORA_DTYPE_BF16;
+  uint16_t* At = at<uint16_t>(workspace, L.At);
+  float* u = u_out ? u_out : at<float>(workspace, L.u);
+  float* down = at<float>(workspace, L.down);
+  const int slices = lora_down_slices(K);
+  hipError_t e = launch_transpose_bf16(A, K, r, At, st);  // A^T [r,K]
+  if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
+  if (L.gemv_path) {
+    if (e == hipSuccess) e = launch_lora_down_finalize(down, slices, M, r, s, u, nullptr, st);
+    float* part = at<float>(workspace, L.gemv);
+    if (e == hipSuccess) e = launch_gemv_fwd(x, codes, absmax_q, absmax_scale, M, N, K, part, *cb, st);
+    if (e == hipSuccess)
+      e = launch_gemv_finalize(part, gemv_splits(K), u, B, M, N, r, s, y, ybf, st);
+  } else {
+    uint16_t* Bt = at<uint16_t>(workspace, L.Bt);
+    uint16_t* ulr = at<uint16_t>(workspace, L.ulr);
+    if (e == hipSuccess) e = launch_lora_down_finalize(down, slices, M, r, s, u, ulr, st);
+    if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
+    if (e == hipSuccess)
+      e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, *cb, st);
+  }
+  return launch_status(e);
+}
+
+int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
+                     int64_t N, int64_t K, const uint16_t* x, const uint16_t* dY, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int r, float alpha,
+                     const float* u_saved, void* dX, int dx_dtype, void* dA, void* dB,
+                     int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const Codebook* cb = nullptr;
+  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+  if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
+  if ((dx_dtype != QLORA_DTYPE_F32 && dx_dtype != QLORA_DTYPE_BF16) ||
+      (grad_dtype != QLORA_DTYPE_F32 && grad_dtype != QLORA_DTYPE_BF16))
+    return QLORA_ERR_DTYPE;
+  if (!rank_ok(r)) return QLORA_ERR_RANK;
+  if (!A || !B) return QLORA_ERR_INVALID_ARG;
+  if (M > 0 && !dY) return QLORA_ERR_INVALID_ARG;
+  if (dX && (!codes || !absmax_q || !absmax_scale)) return QLORA_ERR_INVALID_ARG;
+  if ((dA || dB) && M > 0 && !x) return QLORA_ERR_INVALID_ARG;
+  const void* ptrs[] = {codes, absmax_q, absmax_scale, x, dY, A, B, u_saved, dX, dA, dB, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool gbf = grad_dtype == QLORA_DTYPE_BF16;
+  const size_t gsz = gbf ? 2 : 4;
+  if (M == 0) {  // empty sums: zero adapter gradients, nothing else to do
+    hipError_t e = hipSuccess;
+    if (dA) e = launch_zero(dA, (size_t)K * r * gsz, st);
+    if (e == hipSuccess && dB) e = launch_zero(dB, (size_t)r * N * gsz, st);
+    return launch_status(e);
+  }
+  const bool need_u = dB && !u_saved;
+  const BwdLayout L = bwd_layout(M, N, K, r, need_u);
+  if (!workspace || workspace_bytes < L.total) return QLORA_ERR_WORKSPACE;
+
+  const float s = alpha / (float)r;
+  float* down = at<float>(workspace, L.down);
+  float* v = at<float>(workspace, L.v);
+  uint16_t* svlr = at<uint16_t>(workspace, L.svlr);
+  float* col = at<float>(workspace, L.col);
+  hipError_t e = hipSuccess;
+  // v = dY B^T (B [r,N] is already contiguous along N)
+  e = launch_lora_down_parts(dY, B, M, N, r, down, st);
+  if (e == hipSuccess)
+    e = launch_lora_down_finalize(down, lora_down_slices(N), M, r, s, v, svlr, st);
+  if (e == hipSuccess && dX)
+    e = launch_gemm_bwd(dY, codes, absmax_q, absmax_scale, svlr, A, M, N, K, r, dX,
+                        dx_dtype == QLORA_DTYPE_BF16, *cb, st);
+  if (e == hipSuccess && dA) {  // dA = s x^T v
+    e = launch_colred(x, v, M, K, r, col, st);
+    if (e == hipSuccess)
+      e = launch_colred_finalize(col, colred_splits(M), K, r, s, false, dA, gbf, st);
+  }
+  if (e == hipSuccess && dB) {  // dB = s u^T dY
+    const float* u = u_saved;
+    if (need_u) {
+      uint16_t* At = at<uint16_t>(workspace, L.At);
+      float* uw = at<float>(workspace, L.u);
+      e = launch_transpose_bf16(A, K, r, At, st);
+      if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
+      if (e == hipSuccess)
+        e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, uw, nullptr, st);
+      u = uw;
+    }
+    if (e == hipSuccess) e = launch_colred(dY, u, M, N, r, col, st);
+    if (e == hipSuccess)
+      e = launch_colred_finalize(col, colred_splits(M), N, r, s, true, dB, gbf, st);
+  }
+  return launch_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Device-side helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace qlora {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// Two fp32 values to a packed bf16 pair, round-to-nearest-even
+// (a single v_cvt_pk_bf16_f32 on gfx950). `a` goes to the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 ha = (__bf16)a;
+  const __bf16 hb = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// D = A(16x32) * B(32x16) + C with bf16 inputs and fp32 accumulation.
+// Lane l supplies row (l%16) of A and column (l%16) of B, each as the 8
+// consecutive reduction elements 8*(l/16)..8*(l/16)+7; it receives rows
+// 4*(l/16)..4*(l/16)+3 of column (l%16) of D.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t a, const u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Dequantized values of the 8 NF4 codes in one little-endian dword through a
+// 16-entry bf16 table in LDS (the table of one block: bf16(L[i] * c1_hat)).
+// Element i (nibble i) lands in bf16 slot i of the result.
+__device__ __forceinline__ u32x4_t lut8(uint32_t w, const uint16_t* tab) {
+  u32x4_t r;
+  r.x = (uint32_t)tab[w & 15u] | ((uint32_t)tab[(w >> 4) & 15u] << 16);
+  r.y = (uint32_t)tab[(w >> 8) & 15u] | ((uint32_t)tab[(w >> 12) & 15u] << 16);
+  r.z = (uint32_t)tab[(w >> 16) & 15u] | ((uint32_t)tab[(w >> 20) & 15u] << 16);
+  r.w = (uint32_t)tab[(w >> 24) & 15u] | ((uint32_t)tab[w >> 28] << 16);
+  return r;
+}
+
+// Build the 16-entry bf16 dequantization table of one block from its
+// 8-bit absmax code and the group scale: entry i = bf16(fp32(L[i] * c1_hat)),
+// c1_hat = fp32(q8 * s2). Writes 32 bytes at `dst` (16-byte aligned).
+__device__ __forceinline__ void build_table(const Codebook& cb, int q8, float s2, uint16_t* dst) {
+  const float ch = (float)q8 * s2;
+  u32x4_t t0, t1;
+  t0.x = pack_bf16x2(cb.level[0] * ch, cb.level[1] * ch);
+  t0.y = pack_bf16x2(cb.level[2] * ch, cb.level[3] * ch);
+  t0.z = pack_bf16x2(cb.level[4] * ch, cb.level[5] * ch);
+  t0.w = pack_bf16x2(cb.level[6] * ch, cb.level[7] * ch);
+  t1.x = pack_bf16x2(cb.level[8] * ch, cb.level[9] * ch);
+  t1.y = pack_bf16x2(cb.level[10] * ch, cb.level[11] * ch);
+  t1.z = pack_bf16x2(cb.level[12] * ch, cb.level[13] * ch);
+  t1.w = pack_bf16x2(cb.level[14] * ch, cb.level[15] * ch);
+  *reinterpret_cast<u32x4_t*>(dst) = t0;
+  *reinterpret_cast<u32x4_t*>(dst + 8) = t1;
+}
+
+__device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
+
+}  // namespace qlora

@@ -1,0 +1,77 @@
+// Internal declarations shared by the host API and the kernels of the library.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace qlora {
+
+constexpr int kBlock = 64;   // weights per first-level block
+constexpr int kGroup = 256;  // blocks per second-level group
+
+// NF4 codebook as the kernels receive it (by value, in kernel arguments).
+struct Codebook {
+  float level[16];
+  float thr[15];
+};
+
+// Builds the codebook once (thread safe). Returns QLORA_OK or
+// QLORA_ERR_INTERNAL; `cb` and `id` are valid only on QLORA_OK.
+int get_codebook(const Codebook** cb, uint32_t* id);
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error. Sizes are pre-validated.
+hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes, int8_t* q8,
+                           float* s2, const Codebook& cb, hipStream_t st);
+hipError_t launch_dequant(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t n,
+                          uint16_t* out, const Codebook& cb, hipStream_t st);
+
+// out[c][r'] = in[r'][c] for a bf16 [rows, cols] matrix.
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
+                                 hipStream_t st);
+
+// Rank-r down projection out[m][j] = sum_t X[m][t] * P[j][t] (X [M,T] bf16,
+// P [r,T] bf16, fp32 result) in t-slices: launch_lora_down_parts writes
+// part[slice][m][j]; launch_lora_down_finalize sums the slices into out and,
+// if lr != NULL, writes lr[m][0..r) = bf16(s*out), lr[m][r..2r) =
+// bf16(s*out - hi) (a two-term bf16 split of s*out).
+int lora_down_slices(int64_t T);
+hipError_t launch_lora_down_parts(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
+                                  int r, float* part, hipStream_t st);
+hipError_t launch_lora_down_finalize(const float* part, int slices, int64_t M, int r, float s,
+                                     float* out, uint16_t* lr, hipStream_t st);
+
+// y = x W_hat^T + [ulr-extended term], M > 16 path (MFMA tiles).
+hipError_t launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
+                           const float* s2, const uint16_t* ulr, const uint16_t* Bt, int64_t M,
+                           int64_t N, int64_t K, int r, void* y, bool y_bf16, const Codebook& cb,
+                           hipStream_t st);
+
+// Decode path (M <= 16): partial sums over K-slices, then a finalize kernel.
+int gemv_splits(int64_t K);
+hipError_t launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
+                           const float* s2, int64_t M, int64_t N, int64_t K, float* partial,
+                           const Codebook& cb, hipStream_t st);
+hipError_t launch_gemv_finalize(const float* partial, int splits, const float* u,
+                                const uint16_t* B, int64_t M, int64_t N, int r, float s, void* y,
+                                bool y_bf16, hipStream_t st);
+
+// dX = dY W_hat + [svlr-extended term with A].
+hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_t* q8,
+                           const float* s2, const uint16_t* svlr, const uint16_t* A, int64_t M,
+                           int64_t N, int64_t K, int r, void* dX, bool dx_bf16,
+                           const Codebook& cb, hipStream_t st);
+
+// Adapter gradients: part[split][c][j] = sum_{m in split} X[m][c] * P[m][j]
+// (X [M,C] bf16, P [M,r] fp32), then out = s * sum_split part, written as
+// [C,r] (transpose_out = false) or [r,C] (true), fp32 or bf16.
+int colred_splits(int64_t M);
+hipError_t launch_colred(const uint16_t* X, const float* P, int64_t M, int64_t C, int r,
+                         float* part, hipStream_t st);
+hipError_t launch_colred_finalize(const float* part, int splits, int64_t C, int r, float s,
+                                  bool transpose_out, void* out, bool out_bf16, hipStream_t st);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace qlora

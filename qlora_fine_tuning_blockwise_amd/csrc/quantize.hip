@@ -1,0 +1,240 @@
+// Blockwise NF4 quantization with double quantization, and dequantization to
+// bf16, for gfx950.
+//
+// [P1] "QLoRA", "controlled rounding": per block of weights find the absmax,
+// normalise, store the index of the nearest grid point plus one scale per
+// block; bullets: blocks of 64, NF4 levels, and the block constants quantized
+// again to 8 bits ("double quantization"). [P2] s1 "Double Quantization".
+//
+// Quantize: one workgroup per group of 256 blocks (16384 weights). Each thread
+// loads 8 consecutive weights per pass (a 16-byte bf16 load, coalesced across
+// the wave), 8 lanes cover one block; the block absmax is reduced across those
+// 8 lanes with DPP moves. Codes come from a 65-bucket table in LDS: the bucket
+// of x in [-1,1] (width 1/32) holds at most one decision threshold, so one
+// compare finishes the search. The 8 codes of a thread are packed into one
+// dword and stored. After all 8 passes the 256 block constants are in LDS and
+// the workgroup writes their 8-bit codes and the group's fp32 scale.
+#include "device.h"
+
+namespace qlora {
+namespace {
+
+constexpr int kLut = 128;  // 65 live buckets, padded so a masked index stays in bounds
+
+// Max of a non-negative value over each aligned group of 8 lanes.
+__device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t v) {
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+// Code of a normalised value x in [-1,1]: bucket b = floor(32x + 32), then
+// code = (#thresholds below the bucket) + (x > the bucket's threshold).
+// The index is masked, so a non-finite x still reads inside the table.
+__device__ __forceinline__ uint32_t nf4_code(float x, const u32x2_t* lut) {
+  const int b = ((int)__builtin_fmaf(x, 32.0f, 32.0f)) & (kLut - 1);
+  const u32x2_t e = lut[b];
+  return e.y + (x > __uint_as_float(e.x) ? 1u : 0u);
+}
+
+template <bool kF32In>
+__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ W, int64_t nblocks,
+                                                       uint8_t* __restrict__ codes,
+                                                       int8_t* __restrict__ q8,
+                                                       float* __restrict__ s2, Codebook cb) {
+  __shared__ u32x2_t lut[kLut];
+  __shared__ float c1s[kGroup];
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.x;
+  const int64_t b0 = g * kGroup;
+  const int nbg = (int)min((int64_t)kGroup, nblocks - b0);
+
+  if (tid < kLut) {
+    // bucket [lo, lo + 1/32); buckets past 64 repeat bucket 64
+    const float lo = -1.0f + (float)min(tid, 64) * 0.03125f;
+    const float hi = lo + 0.03125f;
+    uint32_t below = 0;
+    float inside = 2.0f;
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+      const float t = cb.thr[i];
+      below += (t < lo) ? 1u : 0u;
+      if (t >= lo && t < hi) inside = t;
+    }
+    lut[tid] = u32x2_t{__float_as_uint(inside), below};
+  }
+
+  // Issue every load of the group up front (8 passes x 8 weights).
+  constexpr int kWords = kF32In ? 8 : 4;  // dwords per 8 weights
+  uint32_t raw[8][kWords];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int bl = it * 32 + (tid >> 3);
+    const int64_t e0 = (b0 + bl) * kBlock + (tid & 7) * 8;
+    if (bl < nbg) {
+      if (kF32In) {
+        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(W) + e0);
+        const u32x4_t a = p[0], b = p[1];
+        raw[it][0] = a.x; raw[it][1] = a.y; raw[it][2] = a.z; raw[it][3] = a.w;
+        raw[it][4] = b.x; raw[it][5] = b.y; raw[it][6] = b.z; raw[it][7] = b.w;
+      } else {
+        const u32x4_t a =
+            *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(W) + e0);
+        raw[it][0] = a.x; raw[it][1] = a.y; raw[it][2] = a.z; raw[it][3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWords; ++j) raw[it][j] = 0u;
+    }
+  }
+  __syncthreads();  // lut ready
+
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int bl = it * 32 + (tid >> 3);
+    float w[8];
+    uint32_t amax = 0;
+    if (kF32In) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        w[j] = __uint_as_float(raw[it][j]);
+        amax = max(amax, raw[it][j] & 0x7FFFFFFFu);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t v = raw[it][j];
+        w[2 * j] = __uint_as_float(v << 16);
+        w[2 * j + 1] = __uint_as_float(v & 0xFFFF0000u);
+        amax = max(amax, max(v & 0x7FFFu, (v >> 16) & 0x7FFFu));
+      }
+      amax <<= 16;
+    }
+    amax = max_over_8_lanes(amax);
+    const float c1 = __uint_as_float(amax);
+    if (bl < nbg && (tid & 7) == 0) c1s[bl] = c1;
+
+    uint32_t word = 0;
+    if (c1 == 0.0f) {
+      word = 0x77777777u;  // all-zero block: every weight at the zero level
+    } else if (!kF32In && c1 >= 0x1p-60f && c1 <= 0x1p60f) {
+      // w / c1 from a correctly rounded reciprocal and one residual
+      // correction (Markstein's division step): x0 = w*r, e = w - x0*c1
+      // (one FMA), x = x0 + e*r. Checked exhaustively over every bf16 pair
+      // with c1 in this range and |w| <= c1: x equals the IEEE quotient
+      // whenever |w/c1| >= 2^-10, and always yields the same NF4 code (the
+      // smaller quotients that can differ in low bits sit far below every
+      // threshold).
+      const float rc = 1.0f / c1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x0 = w[j] * rc;
+        const float e = __builtin_fmaf(-x0, c1, w[j]);
+        const float x = __builtin_fmaf(e, rc, x0);
+        word |= nf4_code(x, lut) << (4 * j);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) word |= nf4_code(w[j] / c1, lut) << (4 * j);
+    }
+    if (bl < nbg) {
+      const int64_t e0 = (b0 + bl) * kBlock + (tid & 7) * 8;
+      *reinterpret_cast<uint32_t*>(codes + e0 / 2) = word;
+    }
+  }
+  __syncthreads();  // c1s complete
+
+  // Second level: c2 = max c1 over the group, s2 = c2/127,
+  // q8 = nearest integer of c1/s2 (ties to the lower), clamped to [0,127].
+  const float c1 = tid < nbg ? c1s[tid] : 0.0f;
+  float m = c1;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const float c2 = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = c2 / 127.0f;
+  if (tid < nbg) {
+    int q = 0;
+    if (c1 != 0.0f) {
+      const float v = c1 / sc;              // +inf when sc underflowed to 0
+      float t = ceilf(v - 0.5f);            // v - 0.5 is exact for v >= 0.5
+      t = fminf(fmaxf(t, 0.0f), 127.0f);
+      q = (int)t;
+    }
+    q8[b0 + tid] = (int8_t)q;
+  }
+  if (tid == 0) s2[g] = sc;
+}
+
+// Dequantize: a workgroup covers 128 blocks; two threads per block. Each
+// thread builds half of its block's 16-entry bf16 table in LDS, then expands
+// 32 codes (one 16-byte load) into 32 bf16 values (four 16-byte stores).
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const int8_t* __restrict__ q8,
+                                                      const float* __restrict__ s2,
+                                                      int64_t nblocks, uint16_t* __restrict__ out,
+                                                      Codebook cb) {
+  __shared__ __attribute__((aligned(16))) uint16_t tab[128 * 16];
+  const int tid = threadIdx.x;
+  const int lb = tid >> 1, half = tid & 1;
+  const int64_t b = (int64_t)blockIdx.x * 128 + lb;
+  const bool valid = b < nblocks;
+  u32x4_t c = zero4();
+  float ch = 0.0f;
+  if (valid) {
+    c = *reinterpret_cast<const u32x4_t*>(codes + b * 32 + half * 16);
+    ch = (float)q8[b] * s2[b >> 8];
+  }
+  {
+    float l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l[i] = half ? cb.level[8 + i] : cb.level[i];
+    u32x4_t t;
+    t.x = pack_bf16x2(l[0] * ch, l[1] * ch);
+    t.y = pack_bf16x2(l[2] * ch, l[3] * ch);
+    t.z = pack_bf16x2(l[4] * ch, l[5] * ch);
+    t.w = pack_bf16x2(l[6] * ch, l[7] * ch);
+    *reinterpret_cast<u32x4_t*>(&tab[lb * 16 + half * 8]) = t;
+  }
+  __syncthreads();
+  if (valid) {
+    const uint16_t* tb = &tab[lb * 16];
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + b * 64 + half * 32);
+    dst[0] = lut8(c.x, tb);
+    dst[1] = lut8(c.y, tb);
+    dst[2] = lut8(c.z, tb);
+    dst[3] = lut8(c.w, tb);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes, int8_t* q8,
+                           float* s2, const Codebook& cb, hipStream_t st) {
+  const int64_t nb = n / kBlock;
+  const int64_t ng = (nb + kGroup - 1) / kGroup;
+  if (ng == 0) return hipSuccess;
+  if (f32_in)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)ng), dim3(256), 0, st, W, nb, codes,
+                       q8, s2, cb);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)ng), dim3(256), 0, st, W, nb, codes,
+                       q8, s2, cb);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t n,
+                          uint16_t* out, const Codebook& cb, hipStream_t st) {
+  const int64_t nb = n / kBlock;
+  const int64_t grid = (nb + 127) / 128;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(256), 0, st, codes, q8, s2, nb,
+                     out, cb);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

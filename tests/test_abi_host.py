@@ -1,0 +1,160 @@
+"""CPU tests of the library boundary: it loads, exports what the header
+declares, agrees with the oracle's codebook, and rejects bad arguments on the
+host before touching the GPU. No compute call runs here."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from qlora_fine_tuning_blockwise_amd import _lib
+import qlora_fine_tuning_blockwise_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from qlora_fine_tuning_blockwise_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.header_functions()
+    assert {"qlora_quantize_nf4_dq", "qlora_dequant_bf16", "qlora_linear_fwd",
+            "qlora_linear_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_codebook_matches_oracle_bit_exact(lib, olib):
+    lv, th = q.qlora_codebook()
+    olv, oth = olib.nf4_codebook()
+    assert np.array_equal(lv.view(np.uint32), olv.view(np.uint32))
+    assert np.array_equal(th.view(np.uint32), oth.view(np.uint32))
+    cid = q.qlora_codebook_id()
+    assert cid != 0 and cid == q.qlora_codebook_id()
+
+
+def test_sizes_accounting(lib):
+    cb, qb, sb = q.qlora_nf4_sizes(4096, 4096)
+    assert (cb, qb, sb) == (4096 * 4096 // 2, 4096 * 4096 // 64, 4 * 4096 * 4096 // 16384)
+    assert 8 * (cb + qb + sb) / (4096 * 4096) == 4.126953125
+    cb, qb, sb = q.qlora_nf4_sizes(11008, 4096)  # 172 blocks per row: groups straddle rows
+    assert sb == 4 * ((11008 * 4096 // 64 + 255) // 256)
+    for N, K in ((0, 64), (4, 0), (4, 96), (4, 32)):
+        with pytest.raises(RuntimeError):
+            q.qlora_nf4_sizes(N, K)
+
+
+def test_strerror_covers_codes(lib):
+    texts = {q.qlora_strerror(s) for s in range(9)}
+    assert len(texts) == 9 and q.qlora_strerror(99) == "unknown status"
+
+
+FAKE = 1 << 20  # an aligned address never dereferenced: validation fails first
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+def test_quantize_validation(lib):
+    f = lib.qlora_quantize_nf4_dq
+    assert f(None, 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), None) == 1
+    assert f(_p(FAKE), 1, 4, 96, _p(FAKE), _p(FAKE), _p(FAKE), None) == 2
+    assert f(_p(FAKE), 1, 0, 64, _p(FAKE), _p(FAKE), _p(FAKE), None) == 2
+    assert f(_p(FAKE), 7, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), None) == 4
+    assert f(_p(FAKE + 2), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), None) == 3
+    d = lib.qlora_dequant_bf16
+    assert d(_p(FAKE), None, _p(FAKE), 4, 64, _p(FAKE), None) == 1
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 4, 65, _p(FAKE), None) == 2
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE + 4), 4, 64, _p(FAKE), None) == 3
+
+
+def _fwd(lib, **kw):
+    a = dict(codes=FAKE, q8=FAKE, s2=FAKE, N=64, K=128, x=FAKE, M=32, A=FAKE, B=FAKE, r=16,
+             alpha=32.0, y=FAKE, ydt=0, u=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    P = lambda v: None if v is None else _p(v)
+    return lib.qlora_linear_fwd(P(a["codes"]), P(a["q8"]), P(a["s2"]), a["N"], a["K"], P(a["x"]),
+                                a["M"], P(a["A"]), P(a["B"]), a["r"], a["alpha"], P(a["y"]),
+                                a["ydt"], P(a["u"]), P(a["ws"]), a["wsb"], None)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, x=None) == 1
+    assert _fwd(lib, M=-1) == 1
+    assert _fwd(lib, K=100) == 2
+    assert _fwd(lib, ydt=5) == 4
+    assert _fwd(lib, r=8) == 5
+    assert _fwd(lib, r=24) == 5
+    assert _fwd(lib, r=512) == 5
+    assert _fwd(lib, B=FAKE + 8) == 3
+    assert _fwd(lib, wsb=16) == 6
+    assert _fwd(lib, ws=None) == 6
+    assert _fwd(lib, M=0) == 0  # empty batch: a no-op that enqueues nothing
+
+
+def test_bwd_validation(lib):
+    f = lib.qlora_linear_bwd
+    base = [_p(FAKE)] * 3 + [64, 128, _p(FAKE), _p(FAKE), 32, _p(FAKE), _p(FAKE), 16, 32.0, None,
+                             _p(FAKE), 0, _p(FAKE), _p(FAKE), 0, _p(FAKE), 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(6, None) == 1          # dY missing
+    assert call(5, None) == 1          # x missing while dA/dB wanted
+    assert call(4, 96) == 2            # K % 64
+    assert call(14, 3) == 4            # dx dtype
+    assert call(17, 9) == 4            # grad dtype
+    assert call(10, 0) == 5            # r
+    assert call(8, _p(FAKE + 1)) == 3  # A misaligned
+    assert call(19, 64) == 6           # workspace too small
+
+
+def test_workspace_query(lib):
+    assert q.qlora_workspace_bytes(0, 16, 4096, 4096, 16) > 0
+    assert q.qlora_workspace_bytes(0, 4096, 4096, 4096, 16) > q.qlora_workspace_bytes(0, 1024, 4096, 4096, 16)
+    assert q.qlora_workspace_bytes(1, 4096, 11008, 4096, 16) > 0
+    assert q.qlora_workspace_bytes(0, 16, 4096, 4000, 16) == 0
+    assert q.qlora_workspace_bytes(2, 16, 4096, 4096, 16) == 0
+
+
+@pytest.fixture(scope="module")
+def arith(tmp_path_factory):
+    d = tmp_path_factory.mktemp("arith")
+    so = str(d / "arith.so")
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+                    os.path.join(ROOT, "tests", "csrc", "kernel_arith_check.c"), "-o", so, "-lm"],
+                   check=True)
+    L = ctypes.CDLL(so)
+    L.check_division.restype = ctypes.c_int64
+    L.check_division.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                 ctypes.POINTER(ctypes.c_int64)]
+    L.check_buckets.restype = ctypes.c_int64
+    L.check_buckets.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
+    return L
+
+
+def test_fast_division_exact_for_all_bf16_pairs(arith, lib):
+    _, th = q.qlora_codebook()
+    th = np.ascontiguousarray(th)
+    n, vbad = ctypes.c_int64(), ctypes.c_int64()
+    bad = arith.check_division(th.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n), ctypes.byref(vbad))
+    assert n.value > 4.9e8
+    assert bad == 0 and vbad.value == 0
+
+
+def test_bucket_code_search_exhaustive(arith, lib):
+    _, th = q.qlora_codebook()
+    th = np.ascontiguousarray(th)
+    n = ctypes.c_int64()
+    bad = arith.check_buckets(th.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n))
+    assert n.value == 2 * (0x3F800000 + 1) and bad == 0

@@ -1,0 +1,469 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: NF4 codes, 8-bit absmax codes, second-level scales, dequantized
+bf16. Tolerance (fp32 outputs): relative Frobenius error <= 2e-3 and max
+element error <= 1e-2 x RMS of the oracle output, for y, dX, dA, dB.
+"""
+import os
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qlora_fine_tuning_blockwise_amd as q
+from qlora_fine_tuning_blockwise_amd import synthetic as syn
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+REL_FROB = 2e-3
+MAX_REL_RMS = 1e-2
+POOL = cf.ThreadPoolExecutor(max_workers=8)  # oracle calls release the GIL
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def tol_check(got, ref, name):
+    got = got.astype(np.float64)
+    ref = ref.astype(np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), name
+    nref = np.linalg.norm(ref)
+    rf = np.linalg.norm(got - ref) / nref if nref > 0 else np.linalg.norm(got)
+    rms = np.sqrt(np.mean(ref ** 2)) if ref.size else 0.0
+    mx = np.max(np.abs(got - ref)) if ref.size else 0.0
+    assert rf <= REL_FROB, f"{name}: relative Frobenius error {rf:.3e}"
+    assert mx <= MAX_REL_RMS * rms + 1e-30, f"{name}: max error {mx:.3e} vs rms {rms:.3e}"
+    return rf
+
+
+def dev_bf16(bits):
+    return syn.bits_to_torch_bf16(bits).to(DEV)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def quantize_gpu(W):
+    w = q.qlora_quantize_nf4_dq(W)
+    torch.cuda.synchronize()
+    return w
+
+
+def assert_nf4_equal(w, codes, q8, s2, name):
+    gc, gq, gs = host(w.codes), host(w.absmax_q), host(w.absmax_scale)
+    if not np.array_equal(gc, codes):
+        i = int(np.argmax(gc != codes))
+        raise AssertionError(f"{name}: codes differ first at byte {i}: {gc[i]:#x} vs {codes[i]:#x}")
+    assert np.array_equal(gq, q8), f"{name}: absmax codes differ"
+    assert np.array_equal(gs.view(np.uint32), s2.view(np.uint32)), f"{name}: scales differ"
+
+
+# ------------------------------------------------------------------ quantize / dequant
+def _edge_weights():
+    """bf16 weights hitting the corners of the quantizer (64-aligned rows)."""
+    lv, _ = oracle.nf4_codebook()
+    rows = []
+    rng = np.random.default_rng(99)
+    for c in (1.0, 0.02, 3.0e38 / 2, 2.0 ** -70, 2.0 ** 70, 1e-39):
+        rows.append((lv.astype(np.float64) * c).astype(np.float32))
+        mids = ((lv[:-1].astype(np.float64) + lv[1:]) / 2 * c).astype(np.float32)
+        rows.append(np.concatenate([mids, np.array([c], np.float32)]))
+    rows.append(np.zeros(64, np.float32))
+    rows.append(np.full(64, -0.0, np.float32))
+    rows.append(np.array([1e-45, -1e-45, 1e-41, -2e-40, 0.0] * 13, np.float32)[:64])
+    rows.append(np.full(64, 0.125, np.float32))
+    rows.append(np.concatenate([rng.standard_normal(63).astype(np.float32) * 1e-3,
+                                np.array([-7.0], np.float32)]))
+    flat = np.concatenate([np.resize(r, 64) for r in rows])
+    flat = np.concatenate([flat, rng.standard_normal(64 * 300).astype(np.float32) * 0.02])
+    return syn.to_bf16_bits(flat).reshape(-1, 64)
+
+
+@pytest.mark.parametrize("shape", [(1, 64), (3, 192), (5, 4096), (257, 640)])
+def test_quantize_ragged_shapes_bit_exact(shape):
+    say("quantize ragged", shape)
+    Wb = syn.normal_bf16(shape, 0.02, 100 + shape[0])
+    w = quantize_gpu(dev_bf16(Wb))
+    assert_nf4_equal(w, *oracle.quantize_nf4_dq(Wb, "bf16"), f"ragged {shape}")
+
+
+def test_quantize_edge_values_bit_exact():
+    Wb = _edge_weights()
+    say("quantize edge values", Wb.shape)
+    w = quantize_gpu(dev_bf16(Wb))
+    codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+    assert_nf4_equal(w, codes, q8, s2, "edge")
+    deq = syn.torch_bf16_to_bits(q.qlora_dequant_bf16(w)).ravel()
+    _, wb = oracle.dequant_dq(codes, q8, s2)
+    assert np.array_equal(deq, wb)
+
+
+def test_quantize_f32_linear_1024_bit_exact():
+    cfg = syn.LINEAR_1024
+    W = syn.normal_f32(cfg["weights"]["w"], cfg["w_std"], syn.seed_of(1, 0))
+    say("quantize f32 1024x1024")
+    w = quantize_gpu(torch.from_numpy(W).to(DEV))
+    codes, q8, s2 = oracle.quantize_nf4_dq(W, "f32")
+    assert_nf4_equal(w, codes, q8, s2, "f32 1024")
+    deq = syn.torch_bf16_to_bits(q.qlora_dequant_bf16(w)).ravel()
+    assert np.array_equal(deq, oracle.dequant_dq(codes, q8, s2)[1])
+
+
+def test_quantize_f32_edge_values():
+    rng = np.random.default_rng(5)
+    W = np.concatenate([rng.standard_normal(64 * 40).astype(np.float32) * 0.02,
+                        np.array([1e-40, -3e-39, 0.0, 1e30] * 16, np.float32),
+                        np.zeros(64, np.float32)]).reshape(-1, 64)
+    w = quantize_gpu(torch.from_numpy(W).to(DEV))
+    assert_nf4_equal(w, *oracle.quantize_nf4_dq(W, "f32"), "f32 edge")
+
+
+@pytest.mark.parametrize("name", ["q", "up"])
+def test_quantize_dequant_llama7b_bit_exact(name):
+    shape = syn.LLAMA7B_TRAIN["weights"][name]
+    say("quantize llama7b", name, shape)
+    W = syn.torch_normal_bf16(shape, 0.02, syn.seed_of(2, 0 if name == "q" else 1), DEV)
+    w = quantize_gpu(W)
+    Wb = syn.torch_bf16_to_bits(W)
+    codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+    assert_nf4_equal(w, codes, q8, s2, name)
+    deq = syn.torch_bf16_to_bits(q.qlora_dequant_bf16(w)).ravel()
+    assert np.array_equal(deq, oracle.dequant_dq(codes, q8, s2)[1])
+
+
+def _sample_groups(ng, k, seed):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(ng, size=min(k, ng), replace=False).tolist()) | {0, ng - 1}
+    return sorted(pick)
+
+
+def test_quantize_70b_layer_sampled_groups():
+    """All 7 projections of the 70B-shaped layer; the oracle checks 48 sampled
+    16384-weight groups per projection (groups are independent)."""
+    cfg = syn.LAYER_70B
+    for i, (name, shape) in enumerate(cfg["weights"].items()):
+        say("quantize 70b", name, shape)
+        W = syn.torch_normal_bf16(shape, cfg["w_std"], syn.seed_of(4, i), DEV)
+        w = quantize_gpu(W)
+        flat = W.view(-1)
+        n = flat.numel()
+        ng = (n // 64 + 255) // 256
+        gc, gq, gs = host(w.codes), host(w.absmax_q), host(w.absmax_scale)
+        for gi in _sample_groups(ng, 48, i):
+            e0, e1 = gi * 16384, min(n, (gi + 1) * 16384)
+            seg = syn.torch_bf16_to_bits(flat[e0:e1])
+            codes, q8, s2 = oracle.quantize_nf4_dq(seg, "bf16")
+            assert np.array_equal(gc[e0 // 2:e1 // 2], codes), (name, gi)
+            assert np.array_equal(gq[e0 // 64:e1 // 64], q8), (name, gi)
+            assert gs[gi].view(np.uint32) == s2[0].view(np.uint32), (name, gi)
+        del W, w
+    torch.cuda.empty_cache()
+
+
+def test_bulk_65b_student_t_resident_and_roundtrip():
+    """277 heavy-tailed 8192x28672 tensors (65e9 weights) quantized on one GPU,
+    all NF4 buffers kept resident; tensors 0, 138, 276 bit-exact against the
+    oracle; every tensor's dequant round trip within the per-element bound."""
+    cfg = syn.BULK_65B
+    shape, T = cfg["tensor"], cfg["n_tensors"]
+    lv, _ = oracle.nf4_codebook()
+    halfgap = float(np.max(np.diff(lv.astype(np.float64))) / 2)
+    resident = []
+    checked = {0, 138, 276}
+    futures = {}
+    for t in range(T):
+        W = syn.torch_student_t_outliers_bf16(shape, syn.seed_of(5, t), DEV)
+        w = q.qlora_quantize_nf4_dq(W)
+        if t in checked:
+            torch.cuda.synchronize()
+            Wb = syn.torch_bf16_to_bits(W)
+            futures[t] = (POOL.submit(oracle.quantize_nf4_dq, Wb, "bf16"),
+                          host(w.codes), host(w.absmax_q), host(w.absmax_scale))
+        resident.append(w)
+        if t % 20 == 0:
+            say("bulk quantize", t, "of", T)
+        del W
+    torch.cuda.synchronize()
+    total = sum(w.nbytes() for w in resident)
+    n_params = T * shape[0] * shape[1]
+    assert total * 8 / n_params == 4.126953125
+    say("resident NF4 bytes", total)
+    # round trip: |w - w_hat| <= c1 * halfgap + |c1 - c1_hat| + small, per element
+    for t in range(T):
+        W = syn.torch_student_t_outliers_bf16(shape, syn.seed_of(5, t), DEV).float().view(-1, 64)
+        deq = q.qlora_dequant_bf16(resident[t]).float().view(-1, 64)
+        c1 = W.abs().amax(dim=1, keepdim=True)
+        qa = resident[t].absmax_q.float().view(-1, 1)
+        s2 = resident[t].absmax_scale.repeat_interleave(256)[: qa.shape[0]].view(-1, 1)
+        c1h = qa * s2
+        bound = c1 * (halfgap + 2.0 ** -22) + (c1 - c1h).abs() + c1h.abs() * 2.0 ** -7
+        assert bool(((W - deq).abs() <= bound).all()), f"round-trip bound, tensor {t}"
+        del W, deq
+    for t, (fut, gc, gq, gs) in futures.items():
+        codes, q8, s2 = fut.result()
+        assert np.array_equal(gc, codes), f"bulk tensor {t} codes"
+        assert np.array_equal(gq, q8), f"bulk tensor {t} absmax codes"
+        assert np.array_equal(gs.view(np.uint32), s2.view(np.uint32)), f"bulk tensor {t} scales"
+    del resident
+    torch.cuda.empty_cache()
+
+
+def test_quantize_deterministic():
+    W = syn.torch_normal_bf16((512, 4096), 0.02, 7, DEV)
+    a, b = quantize_gpu(W), quantize_gpu(W)
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.absmax_q, b.absmax_q)
+
+
+# ------------------------------------------------------------------ linear layer helpers
+class Problem:
+    """A seeded layer problem with both sides' inputs and the oracle's W_hat."""
+
+    def __init__(self, N, K, r, alpha, w_std=0.02, seed=0, w_dtype="bf16", zero_w=False):
+        self.N, self.K, self.r, self.alpha = N, K, r, alpha
+        if zero_w:
+            Wb = np.zeros((N, K), np.uint16)
+        else:
+            Wb = syn.normal_bf16((N, K), w_std, seed) if w_dtype == "bf16" else None
+        if w_dtype == "f32":
+            Wf = syn.normal_f32((N, K), w_std, seed)
+            self.w = quantize_gpu(torch.from_numpy(Wf).to(DEV))
+            codes, q8, s2 = oracle.quantize_nf4_dq(Wf, "f32")
+        else:
+            self.w = quantize_gpu(dev_bf16(Wb))
+            codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+        assert_nf4_equal(self.w, codes, q8, s2, "problem weight")
+        self.What = oracle.dequant_dq(codes, q8, s2)[1].reshape(N, K)
+        self.A = syn.normal_bf16((K, r), 1.0 / np.sqrt(K), seed + 1)
+        self.B = syn.normal_bf16((r, N), 0.01, seed + 2)
+        self.At, self.Bt = dev_bf16(self.A), dev_bf16(self.B)
+
+
+def run_fwd(P, x, **kw):
+    y = q.qlora_linear_fwd(P.w, dev_bf16(x), P.At, P.Bt, P.alpha, **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+# ------------------------------------------------------------------ forward
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("name", ["q", "up"])
+def test_fwd_decode_llama7b(M, name):
+    cfg = syn.LLAMA7B_DECODE
+    N, K = cfg["weights"][name]
+    say("fwd decode", name, M)
+    P = Problem(N, K, cfg["r"], cfg["alpha"], seed=syn.seed_of(2, 10 + (name == "up")))
+    x = syn.normal_bf16((M, K), 1.0, syn.seed_of(2, 20 + M))
+    y = host(run_fwd(P, x))
+    yo, _ = oracle.linear_fwd(x, P.What, P.A, P.B, P.r, P.alpha)
+    tol_check(y, yo, f"y decode {name} M={M}")
+
+
+@pytest.mark.parametrize("M,N,K,r", [(17, 320, 640, 16), (300, 100, 192, 32), (256, 512, 1024, 64),
+                                     (33, 1024, 128, 16), (8, 72, 64, 16)])
+def test_fwd_full_small(M, N, K, r):
+    say("fwd small", M, N, K, r)
+    P = Problem(N, K, r, 32.0, seed=M + N + K)
+    x = syn.normal_bf16((M, K), 1.0, 7 + M)
+    y = host(run_fwd(P, x))
+    yo, _ = oracle.linear_fwd(x, P.What, P.A, P.B, r, 32.0)
+    tol_check(y, yo, f"y {M}x{N}x{K}")
+    # bf16 output is the RNE rounding of the fp32 output of the same computation
+    yb = run_fwd(P, x, y_dtype=torch.bfloat16)
+    assert torch.equal(yb, torch.from_numpy(y).to(torch.bfloat16).to(DEV))
+
+
+def test_fwd_linear_1024_f32_weight():
+    cfg = syn.LINEAR_1024
+    N, K = cfg["weights"]["w"]
+    P = Problem(N, K, cfg["r"], cfg["alpha"], seed=syn.seed_of(1, 0), w_dtype="f32")
+    x = syn.normal_bf16((cfg["M"], K), 1.0, syn.seed_of(1, 3))
+    y = host(run_fwd(P, x))
+    yo, _ = oracle.linear_fwd(x, P.What, P.A, P.B, P.r, P.alpha)
+    tol_check(y, yo, "y 1024")
+
+
+@pytest.mark.parametrize("name", ["q", "up"])
+def test_fwd_train_llama7b_sampled_rows(name):
+    cfg = syn.LLAMA7B_TRAIN
+    N, K = cfg["weights"][name]
+    M = cfg["M"]
+    say("fwd train", name)
+    P = Problem(N, K, cfg["r"], cfg["alpha"], seed=syn.seed_of(3, 10 + (name == "up")))
+    x = syn.normal_bf16((M, K), 1.0, syn.seed_of(3, 20))
+    u = torch.empty((M, P.r), dtype=torch.float32, device=DEV)
+    y = run_fwd(P, x, u_out=u)
+    rows = np.array(sorted(set(np.random.default_rng(1).choice(M, 24, replace=False).tolist())
+                           | {0, 255, 256, M - 1}))
+    yo, uo = oracle.linear_fwd(x[rows], P.What, P.A, P.B, P.r, P.alpha)
+    tol_check(host(y)[rows], yo, f"y train {name}")
+    tol_check(host(u)[rows], uo, f"u train {name}")
+
+
+def test_fwd_one_hot_rows_exact_gemm_and_gemv():
+    """x rows one-hot, B = 0: y rows equal dequantized weight columns exactly,
+    which pins the in-kernel dequantization to the standalone one."""
+    N, K, r = 512, 1024, 16
+    P = Problem(N, K, r, 32.0, seed=5)
+    P.Bt = torch.zeros_like(P.Bt)
+    for M in (16, 64):
+        ks = np.random.default_rng(M).choice(K, M, replace=False)
+        x = np.zeros((M, K), np.uint16)
+        x[np.arange(M), ks] = 0x3F80
+        y = host(run_fwd(P, x))
+        Wf = oracle.bf16_to_f32(P.What)
+        assert np.array_equal(y, Wf[:, ks].T + 0.0), f"one-hot M={M}"
+
+
+def test_fwd_lora_only_isolated():
+    """All codes at the zero level: y is the adapter term alone."""
+    N, K, r = 384, 512, 16
+    P = Problem(N, K, r, 32.0, seed=9, zero_w=True)
+    assert int(host(P.w.codes).min()) == 0x77 == int(host(P.w.codes).max())
+    for M in (5, 100):
+        x = syn.normal_bf16((M, K), 1.0, 70 + M)
+        y = host(run_fwd(P, x))
+        yo, _ = oracle.linear_fwd(x, P.What, P.A, P.B, r, 32.0)
+        tol_check(y, yo, f"lora-only M={M}")
+
+
+def test_fwd_deterministic():
+    P = Problem(1024, 1024, 16, 32.0, seed=3)
+    x = syn.normal_bf16((300, 1024), 1.0, 4)
+    a, b = run_fwd(P, x), run_fwd(P, x)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ backward
+def run_bwd(P, x, dY, **kw):
+    out = q.qlora_linear_bwd(P.w, None if x is None else dev_bf16(x), dev_bf16(dY), P.At, P.Bt,
+                             P.alpha, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,r", [(16, 1024, 1024, 16), (300, 100, 192, 32), (64, 512, 640, 64),
+                                     (8, 72, 64, 16), (257, 256, 256, 16)])
+def test_bwd_full_small(M, N, K, r):
+    say("bwd small", M, N, K, r)
+    P = Problem(N, K, r, 24.0, seed=M + 2 * N + K)
+    x = syn.normal_bf16((M, K), 1.0, 3 + M)
+    dY = syn.normal_bf16((M, N), 1.0, 4 + M)
+    dX, dA, dB = run_bwd(P, x, dY)
+    go = oracle.linear_bwd(x, dY, P.What, P.A, P.B, r, 24.0)
+    tol_check(host(dX), go["dX"], "dX")
+    tol_check(host(dA), go["dA"], "dA")
+    tol_check(host(dB), go["dB"], "dB")
+    # bf16 outputs are the RNE of the fp32 ones
+    dXb, dAb, dBb = run_bwd(P, x, dY, dx_dtype=torch.bfloat16, grad_dtype=torch.bfloat16)
+    assert torch.equal(dXb, dX.to(torch.bfloat16))
+    assert torch.equal(dAb, dA.to(torch.bfloat16)) and torch.equal(dBb, dB.to(torch.bfloat16))
+
+
+def test_bwd_linear_1024_f32_weight():
+    cfg = syn.LINEAR_1024
+    N, K = cfg["weights"]["w"]
+    P = Problem(N, K, cfg["r"], cfg["alpha"], seed=syn.seed_of(1, 0), w_dtype="f32")
+    x = syn.normal_bf16((cfg["M"], K), 1.0, syn.seed_of(1, 3))
+    dY = syn.normal_bf16((cfg["M"], N), 1.0, syn.seed_of(1, 4))
+    u = torch.empty((cfg["M"], P.r), dtype=torch.float32, device=DEV)
+    run_fwd(P, x, u_out=u)
+    dX, dA, dB = run_bwd(P, x, dY, u_saved=u)
+    go = oracle.linear_bwd(x, dY, P.What, P.A, P.B, P.r, P.alpha)
+    for got, k in ((dX, "dX"), (dA, "dA"), (dB, "dB")):
+        tol_check(host(got), go[k], k + " 1024")
+    # saved u and recomputed u give the same dB bits
+    _, _, dB2 = run_bwd(P, x, dY)
+    assert torch.equal(dB, dB2)
+
+
+@pytest.mark.parametrize("name", ["q", "up"])
+def test_bwd_train_llama7b(name):
+    cfg = syn.LLAMA7B_TRAIN
+    N, K = cfg["weights"][name]
+    M = cfg["M"]
+    say("bwd train", name)
+    P = Problem(N, K, cfg["r"], cfg["alpha"], seed=syn.seed_of(3, 10 + (name == "up")))
+    x = syn.normal_bf16((M, K), 1.0, syn.seed_of(3, 20))
+    dY = syn.normal_bf16((M, N), 1.0, syn.seed_of(3, 30 + (name == "up")))
+    dX, dA, dB = run_bwd(P, x, dY)
+    rows = np.array(sorted(set(np.random.default_rng(2).choice(M, 24, replace=False).tolist())
+                           | {0, 255, 256, M - 1}))
+    f_dx = POOL.submit(oracle.linear_bwd, x[rows], dY[rows], P.What, P.A, P.B, P.r, P.alpha,
+                       ("dX",))
+    f_g = POOL.submit(oracle.linear_bwd, x, dY, P.What, P.A, P.B, P.r, P.alpha, ("dA", "dB"))
+    tol_check(host(dX)[rows], f_dx.result()["dX"], f"dX train {name}")
+    g = f_g.result()
+    tol_check(host(dA), g["dA"], f"dA train {name}")
+    tol_check(host(dB), g["dB"], f"dB train {name}")
+
+
+def test_bwd_one_hot_dy_rows_exact():
+    N, K, r = 320, 512, 16
+    P = Problem(N, K, r, 32.0, seed=11)
+    P.Bt = torch.zeros_like(P.Bt)
+    M = 40
+    ns = np.random.default_rng(4).choice(N, M, replace=False)
+    dY = np.zeros((M, N), np.uint16)
+    dY[np.arange(M), ns] = 0x3F80
+    dX, _, _ = run_bwd(P, None, dY, want_grads=False)
+    Wf = oracle.bf16_to_f32(P.What)
+    assert np.array_equal(host(dX), Wf[ns] + 0.0)
+
+
+def test_bwd_empty_batch_gives_zero_grads():
+    P = Problem(128, 256, 16, 32.0, seed=12)
+    x = np.zeros((0, 256), np.uint16)
+    dY = np.zeros((0, 128), np.uint16)
+    dX, dA, dB = run_bwd(P, x, dY)
+    assert dX.shape == (0, 256)
+    assert torch.count_nonzero(dA) == 0 and torch.count_nonzero(dB) == 0
+
+
+def test_layer_70b_fwd_bwd_sampled():
+    """All 7 projections of the 70B-shaped layer at M = 2048, r = 64, alpha = 16:
+    y and dX on 12 sampled rows, dA and dB in full."""
+    cfg = syn.LAYER_70B
+    M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
+    rows = np.array([0, 1, 255, 256, 511, 1000, 1023, 1024, 1500, 2046, 2047, 777])
+    x_shared = syn.normal_bf16((M, 8192), 1.0, syn.seed_of(4, 100))
+    jobs = []
+    for i, (name, (N, K)) in enumerate(cfg["weights"].items()):
+        say("70b layer", name, N, K)
+        Wd = syn.torch_normal_bf16((N, K), cfg["w_std"], syn.seed_of(4, i), DEV)
+        w = quantize_gpu(Wd)
+        Wb = syn.torch_bf16_to_bits(Wd)
+        del Wd
+        x = x_shared if name not in ("o", "down") else syn.normal_bf16((M, K), 1.0,
+                                                                       syn.seed_of(4, 110 + i))
+        A = syn.normal_bf16((K, r), 1.0 / np.sqrt(K), syn.seed_of(4, 20 + i))
+        B = syn.normal_bf16((r, N), 0.01, syn.seed_of(4, 30 + i))
+        dY = syn.normal_bf16((M, N), 1.0, syn.seed_of(4, 40 + i))
+        xt, At, Bt, dYt = dev_bf16(x), dev_bf16(A), dev_bf16(B), dev_bf16(dY)
+        u = torch.empty((M, r), dtype=torch.float32, device=DEV)
+        y = q.qlora_linear_fwd(w, xt, At, Bt, alpha, u_out=u)
+        dX, dA, dB = q.qlora_linear_bwd(w, xt, dYt, At, Bt, alpha, u_saved=u)
+        torch.cuda.synchronize()
+        got = (host(y)[rows], host(dX)[rows], host(dA), host(dB))
+        del w, y, dX, dA, dB, xt, dYt, u
+
+        def oracle_job(x=x, Wb=Wb, A=A, B=B, dY=dY):
+            codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+            What = oracle.dequant_dq(codes, q8, s2)[1].reshape(Wb.shape)
+            yo, _ = oracle.linear_fwd(x[rows], What, A, B, r, alpha)
+            gx = oracle.linear_bwd(x[rows], dY[rows], What, A, B, r, alpha, ("dX",))
+            gab = oracle.linear_bwd(x, dY, What, A, B, r, alpha, ("dA", "dB"))
+            return yo, gx["dX"], gab["dA"], gab["dB"]
+
+        jobs.append((name, got, POOL.submit(oracle_job)))
+        torch.cuda.empty_cache()
+    for name, got, fut in jobs:
+        ref = fut.result()
+        for g, rr, k in zip(got, ref, ("y", "dX", "dA", "dB")):
+            tol_check(g, rr, f"70b {name} {k}")
+        say("70b layer ok", name)
