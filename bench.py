@@ -33,6 +33,10 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
 def nf4_bytes(N, K):
     n = N * K
     nb = n // 64
@@ -150,6 +154,7 @@ def main():
             if record:
                 e1.record(stream)
 
+    log("inputs ready; warmup", args.warmup)
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -162,6 +167,7 @@ def main():
             per_call[i] += e0.elapsed_time(e1)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    log("timed", args.steps, "steps")
     # The step time is the sum of the event spans (device time, every call of
     # the step in stream order); the host-clock time is reported beside it.
     ms_step_dev = sum(per_call) / args.steps
@@ -201,9 +207,12 @@ def main():
     }
 
     if not args.no_extras:
+        log("gemv ring")
         result["gemv_ring"] = gemv_ring(q, syn, torch, dev, r, alpha)
+        log("bulk quantize/dequant")
         result["bulk_quantize"] = bulk_quantize(q, syn, torch, dev)
     if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(np, syn, cfg, step_flops, ms_step_dev)
     print(json.dumps(result), flush=True)
 

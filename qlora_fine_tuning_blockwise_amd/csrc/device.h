@@ -13,13 +13,13 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
 // Two fp32 values to a packed bf16 pair, round-to-nearest-even
-// (a single v_cvt_pk_bf16_f32 on gfx950). `a` goes to the low half.
+// (one v_cvt_pk_bf16_f32 on gfx950). `a` goes to the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 ha = (__bf16)a;
-  const __bf16 hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -31,6 +31,18 @@ __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v 
 // 4*(l/16)..4*(l/16)+3 of column (l%16) of D.
 __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t a, const u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// D = A(32x16) * B(16x32) + C with bf16 inputs and fp32 accumulation (the
+// full-rate bf16 MFMA of gfx950: 32K flops in 32 cycles). Lane l supplies row
+// (l%32) of A and column (l%32) of B as the 8 consecutive reduction elements
+// 8*(l/32)..8*(l/32)+7; its accumulator element e holds
+// D[8*(e/4) + 4*(l/32) + e%4][l%32].
+__device__ __forceinline__ f32x16_t mfma_32x32x16(const u32x4_t a, const u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
@@ -62,6 +74,23 @@ __device__ __forceinline__ void build_table(const Codebook& cb, int q8, float s2
   t1.w = pack_bf16x2(cb.level[14] * ch, cb.level[15] * ch);
   *reinterpret_cast<u32x4_t*>(dst) = t0;
   *reinterpret_cast<u32x4_t*>(dst + 8) = t1;
+}
+
+// Byte address of an LDS location (for explicit address arithmetic).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// Wait until at most `n` vector-memory operations of this wave are in flight
+// (loads, including direct-to-LDS loads, complete in issue order). Other
+// counters are left alone; the scheduler may not move instructions across
+// it. gfx9 s_waitcnt encoding: vmcnt in bits [3:0] and
+// [15:14], expcnt [6:4] (7 = no wait), lgkmcnt [11:8] (15 = no wait).
+template <int n>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_sched_barrier(0);  // nothing may be scheduled across the wait
 }
 
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }

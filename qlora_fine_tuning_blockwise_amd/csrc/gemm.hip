@@ -19,6 +19,8 @@
 //  - the LoRA term rides the same accumulators as extra reduction steps:
 //    [s*u_hi | s*u_lo] (bf16 split of the fp32 adapter product) times the
 //    matching adapter columns.
+#include <type_traits>
+
 #include "device.h"
 
 namespace qlora {
@@ -102,6 +104,20 @@ __device__ __forceinline__ void store4(void* out, int64_t ld, int64_t m, int64_t
 // row M-1 (their results are never stored).
 constexpr int kTileBytes = 256 * 128;
 
+// Static choice among three LDS buffers, so that every access names its
+// __shared__ array directly (keeps the buffers distinguishable to the
+// compiler's alias analysis, which decides where direct-to-LDS loads must be
+// waited for).
+template <int S, typename T>
+__device__ __forceinline__ T* pick3(T* a, T* b, T* c) {
+  if constexpr (S == 0)
+    return a;
+  else if constexpr (S == 1)
+    return b;
+  else
+    return c;
+}
+
 struct FwdArgs {
   const uint16_t* x;
   const uint8_t* codes;
@@ -114,20 +130,68 @@ struct FwdArgs {
   int r;
 };
 
+// Write 2 adjacent fp32 (or bf16) outputs of row m starting at column c.
+template <bool kBf16>
+__device__ __forceinline__ void store2(void* out, int64_t ld, int64_t m, int64_t c, int64_t cols,
+                                       float v0, float v1) {
+  if (kBf16) {
+    uint16_t* o = static_cast<uint16_t*>(out) + m * ld + c;
+    if (c + 2 <= cols && (ld & 1) == 0) {
+      *reinterpret_cast<uint32_t*>(o) = pack_bf16x2(v0, v1);
+    } else {
+      if (c < cols) o[0] = (uint16_t)(pack_bf16x2(v0, 0.0f) & 0xFFFFu);
+      if (c + 1 < cols) o[1] = (uint16_t)(pack_bf16x2(v1, 0.0f) & 0xFFFFu);
+    }
+  } else {
+    float* o = static_cast<float*>(out) + m * ld + c;
+    if (c + 2 <= cols && (ld & 1) == 0) {
+      *reinterpret_cast<f32x2_t*>(o) = f32x2_t{v0, v1};
+    } else {
+      if (c < cols) o[0] = v0;
+      if (c + 1 < cols) o[1] = v1;
+    }
+  }
+}
+
+// Tile mapping (v_mfma_f32_32x32x16_bf16). Lane l = 32h + c of wave w:
+//   MFMA (mt, nt) covers rows m0 + 32mt + (0..31) and output columns
+//   n0 + 64w + 2c + nt: lane column c holds the adjacent pair 2c, 2c+1.
+//   Step = 64 reduction elements = 4 substeps s of 16; in substep s lane
+//   group h supplies the 8 elements k0 + 32h + 8s + (0..7) of both operands,
+//   so a lane's 32 elements of a step are contiguous: one 16-byte code load
+//   per weight row, one 16-byte x chunk (4h+s) per row tile.
+//   Accumulator element e of lane l: row 32mt + 8(e/4) + 4h + e%4.
+//
+// Software pipeline of one step kb, three buffers of the x tile and tables:
+//   top:   DMA x(kb+2); load codes(kb+2) and the scales of kb+3 (12 vector
+//          memory instructions); build this wave's tables of step kb+1 from
+//          scales loaded two steps earlier.
+//   body:  32 groups (s, mt): 2 MFMAs each on the B fragments of substep s,
+//          while the fragments of substep s+1 (or of step kb+1, substep 0)
+//          are looked up, 2 LUT reads per group.
+//   end:   wait until only this step's loads are in flight (x(kb+1) has
+//          landed), then barrier.
+// All waits are explicit counts of younger loads. The only ordering relied
+// on is that every load of a step is younger than every load of the steps
+// before it (loads within a step's issue block may be reordered). A wave only
+// reads tables its own threads build (rows 64w..64w+63), and LDS operations
+// of one wave complete in order, so tables need no barrier.
 template <bool kOutBf16>
 __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb) {
   __shared__ __attribute__((aligned(1024))) uint16_t xs0[kTileBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t xs1[kTileBytes / 2];
-  __shared__ __attribute__((aligned(16))) uint16_t tab0[256 * 16];
-  __shared__ __attribute__((aligned(16))) uint16_t tab1[256 * 16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t xs2[kTileBytes / 2];
+  __shared__ __attribute__((aligned(32))) uint16_t tab0[256 * 16];
+  __shared__ __attribute__((aligned(32))) uint16_t tab1[256 * 16];
+  __shared__ __attribute__((aligned(32))) uint16_t tab2[256 * 16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
   const int64_t KB = K / 64;
 
-  // DMA source offsets (elements, from the tile's first row) of the 8
-  // instructions of this lane: slot (w*8+j)*64 + lane -> row (w*8+j)*8 + lane/8,
-  // stored chunk lane%8, holding global chunk (lane%8) ^ ((lane/8)%8).
+  // x DMA: instruction j of wave w, lane l -> slot (w*8+j)*64 + l -> row
+  // (w*8+j)*8 + l/8, stored chunk slot l%8 holding global chunk
+  // (l%8) ^ ((l/8)%8) (row & 7 == (l/8)%8).
   const uint16_t* xrow0 = p.x + m0 * K;
   uint32_t xoff[8];
   {
@@ -140,131 +204,188 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
       xoff[j] = (uint32_t)(row * K + chunk * 8);
     }
   }
-  // Codes of the 4 weight rows of this lane (clamped into the matrix; rows
-  // past N get an all-zero table below).
+  // Code rows of this lane: n0 + 64w + 2c + nt (clamped; rows past N get an
+  // all-zero table), 16-byte segment at byte k0/2 + 16h.
   const uint8_t* crow0 = p.codes + ((n0 * K) >> 1);
-  uint32_t coff[4];
+  uint32_t coff[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    int64_t row = 64 * w + 4 * c + t;
+  for (int nt = 0; nt < 2; ++nt) {
+    int64_t row = 64 * w + 2 * c + nt;
     row = n0 + row < N ? row : N - 1 - n0;
-    coff[t] = (uint32_t)((row * K) >> 1) + 8 * g;
+    coff[nt] = (uint32_t)((row * K) >> 1) + 16 * h;
   }
-  // Table row of this thread.
   const int64_t trow = n0 + tid;
   const bool trow_ok = trow < N;
   const int64_t tbase = (trow_ok ? trow : N - 1) * KB;
 
+  // 8 vector-memory instructions
   auto issue_x = [&](int64_t kb, uint16_t* dst) {
     const uint16_t* src = xrow0 + kb * 64;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       __builtin_amdgcn_global_load_lds(src + xoff[j], dst + (w * 8 + j) * 512, 16, 0, 0);
   };
-  auto load_codes = [&](int64_t kb, u32x2_t (&cr)[4]) {
+  // 2 vector-memory instructions
+  auto load_codes = [&](int64_t kb, u32x4_t (&cr)[2]) {
     const uint8_t* src = crow0 + kb * 32;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) cr[t] = *reinterpret_cast<const u32x2_t*>(src + coff[t]);
+    for (int nt = 0; nt < 2; ++nt) cr[nt] = *reinterpret_cast<const u32x4_t*>(src + coff[nt]);
   };
+  // 2 vector-memory instructions (unconditional; rows past N are zeroed when
+  // the table is built)
   auto load_scale = [&](int64_t kb, int& qv, float& sv) {
     const int64_t bi = tbase + kb;
-    qv = trow_ok ? (int)p.q8[bi] : 0;
+    qv = (int)p.q8[bi];
     sv = p.s2[bi >> 8];
   };
 
-  f32x4_t acc[16][4];
+  f32x16_t acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][nt][e] = 0.0f;
 
-  // Lane-constant LDS offsets (elements).
-  const int a_off0 = c * 64 + (((2 * g) ^ (c & 7)) << 3);
-  const int a_off1 = c * 64 + (((2 * g + 1) ^ (c & 7)) << 3);
-  const int t_off = (64 * w + 4 * c) * 16;
+  // Lane-constant byte offsets: A fragment of substep s (row tile 0), and the
+  // table of this lane's weight row nt = 0 (row nt = 1 is 32 bytes further).
+  int a_off[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) a_off[s] = c * 128 + (((4 * h + s) ^ (c & 7)) << 4);
+  const uint32_t t_byte = (uint32_t)(64 * w + 2 * c) * 32;
 
-  auto compute = [&](const uint16_t* xb, const uint16_t* tb, const u32x2_t (&cc)[4]) {
+  // One substep: 8 groups of (A fragment of row tile mt, 2 MFMAs) with B
+  // fragments bc, while fragments bn are looked up from code words wn (the
+  // dword of each weight row holding the next substep's 8 codes) in table
+  // array tarr: group mt looks up dword mt%4 of fragment mt/4 (2 LUT reads).
+  // A fragments are read two groups ahead; LUT results are packed two groups
+  // after they are issued.
+  auto substep = [&](const char* xa, const u32x4_t (&bc)[2], u32x4_t (&bn)[2],
+                     const uint32_t (&wn)[2], const uint16_t* tarr) {
+    const char* tb = reinterpret_cast<const char*>(tarr);
+    u32x4_t a[3];
+    a[0] = *reinterpret_cast<const u32x4_t*>(xa);
+    a[1] = *reinterpret_cast<const u32x4_t*>(xa + 4096);
+    uint32_t lo[8], hi[8];
 #pragma unroll
-    for (int kf = 0; kf < 2; ++kf) {
-      u32x4_t bfr[4];
+    for (int mt = 0; mt < 8; ++mt) {
+      if (mt + 2 < 8) a[(mt + 2) % 3] = *reinterpret_cast<const u32x4_t*>(xa + (mt + 2) * 4096);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bfr[t] = lut8(kf ? cc[t].y : cc[t].x, tb + t_off + t * 16);
-      const uint16_t* xa = xb + (kf ? a_off1 : a_off0);
-#pragma unroll
-      for (int mt = 0; mt < 16; ++mt) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(xa + mt * 1024);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_16x16x32(a, bfr[t], acc[mt][t]);
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_32x32x16(a[mt % 3], bc[nt], acc[mt][nt]);
+      {
+        const int f = mt >> 2, q = mt & 3;
+        const uint32_t base = t_byte + f * 32;  // 32-byte aligned: OR-ing the offset adds
+        const uint32_t wd = wn[f];
+        const uint32_t olo = q == 0 ? (((wd << 1) & 30u) | base) : (((wd >> (8 * q - 1)) & 30u) | base);
+        const uint32_t ohi = ((wd >> (8 * q + 3)) & 30u) | base;
+        lo[mt] = *reinterpret_cast<const uint16_t*>(tb + olo);
+        hi[mt] = *reinterpret_cast<const uint16_t*>(tb + ohi);
       }
+      if (mt >= 2) bn[(mt - 2) >> 2][(mt - 2) & 3] = lo[mt - 2] | (hi[mt - 2] << 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // A fragment read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LUT reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // address / pack VALU
     }
+    bn[1][2] = lo[6] | (hi[6] << 16);
+    bn[1][3] = lo[7] | (hi[7] << 16);
   };
 
-  // Prologue: tile 0 in flight, table 0 built, codes 0 and scales 1 loaded.
-  u32x2_t cc[4], cn[4];
-  int qv, qn;
-  float sv, sn;
+  // Prologue: x(0), x(1) in flight; codes 0, 1; scales 0, 1, 2; table 0
+  // built; B fragments of (step 0, substep 0) looked up. Per-step state lives
+  // in three slots indexed by (step mod 3) so no loaded register is copied.
+  u32x4_t cw[3][2];
+  int qs[3] = {0, 0, 0};
+  float ss[3] = {0.0f, 0.0f, 0.0f};
+  const int64_t kb1 = KB > 1 ? 1 : 0, kb2 = KB > 2 ? 2 : KB - 1;
   issue_x(0, xs0);
-  load_codes(0, cc);
-  load_scale(0, qv, sv);
-  build_table(cb, qv, sv, tab0 + tid * 16);
-  if (KB > 1) load_scale(1, qn, sn);
-  __syncthreads();
-
-  // Steady state, two steps per trip so every LDS address is static.
-  // Step kb computes from buffer kb&1 while the DMA for kb+1 fills the other
-  // buffer and the loads for kb+1 / kb+2 land; one barrier per step.
-  auto step = [&](int64_t kb, uint16_t* xcur, uint16_t* tcur, uint16_t* xnext, uint16_t* tnext) {
-    const bool more = kb + 1 < KB;
-    if (more) {
-      issue_x(kb + 1, xnext);
-      load_codes(kb + 1, cn);
-    }
-    int q2 = 0;
-    float s2v = 0.0f;
-    if (kb + 2 < KB) load_scale(kb + 2, q2, s2v);
-    compute(xcur, tcur, cc);
-    if (more) build_table(cb, qn, sn, tnext + tid * 16);
-    __syncthreads();
+  issue_x(kb1, xs1);
+  load_codes(0, cw[0]);
+  load_codes(kb1, cw[1]);
+  load_scale(0, qs[0], ss[0]);
+  load_scale(kb1, qs[1], ss[1]);
+  load_scale(kb2, qs[2], ss[2]);
+  wait_vmem<0>();
+  build_table(cb, trow_ok ? qs[0] : 0, ss[0], tab0 + tid * 16);
+  u32x4_t bf0[2], bf1[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) cc[t] = cn[t];
-    qn = q2;
-    sn = s2v;
+  for (int nt = 0; nt < 2; ++nt) bf0[nt] = lut8(cw[0][nt].x, tab0 + (64 * w + 2 * c + nt) * 16);
+  __syncthreads();  // x(0) and x(1) visible in every wave
+
+  // Every step issues the same 12 vector-memory instructions (indices past
+  // the last step are clamped to it: those loads land in buffers never read),
+  // so the wait counts are exact on every path.
+  auto step = [&](int64_t kb, auto slot) {
+    constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+    const int64_t k2 = kb + 2 < KB ? kb + 2 : KB - 1;
+    const int64_t k3 = kb + 3 < KB ? kb + 3 : KB - 1;
+    const char* x0 = reinterpret_cast<const char*>(pick3<S0>(xs0, xs1, xs2));
+    uint16_t* const x2 = pick3<S2>(xs0, xs1, xs2);
+    uint16_t* const t0 = pick3<S0>(tab0, tab1, tab2);
+    uint16_t* const t1 = pick3<S1>(tab0, tab1, tab2);
+    issue_x(k2, x2);
+    load_codes(k2, cw[S2]);
+    load_scale(k3, qs[S0], ss[S0]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
+    // scales(kb+1) came two steps ago: 24 younger loads at most
+    wait_vmem<24>();
+    build_table(cb, trow_ok ? qs[S1] : 0, ss[S1], t1 + tid * 16);
+    const uint32_t w1[2] = {cw[S0][0].y, cw[S0][1].y};
+    const uint32_t w2[2] = {cw[S0][0].z, cw[S0][1].z};
+    const uint32_t w3[2] = {cw[S0][0].w, cw[S0][1].w};
+    substep(x0 + a_off[0], bf0, bf1, w1, t0);
+    substep(x0 + a_off[1], bf1, bf0, w2, t0);
+    substep(x0 + a_off[2], bf0, bf1, w3, t0);
+    // codes(kb+1) were issued in the previous step; the scheduler may order
+    // loads freely within a step, so only "all of this step's 12 loads are
+    // younger" is certain
+    wait_vmem<12>();
+    const uint32_t wn[2] = {cw[S1][0].x, cw[S1][1].x};
+    substep(x0 + a_off[3], bf1, bf0, wn, t1);
+    // only this step's 12 loads may be in flight: x(kb+1) has landed
+    wait_vmem<12>();
+    __builtin_amdgcn_s_barrier();
   };
-  for (int64_t kb = 0; kb < KB; kb += 2) {
-    step(kb, xs0, tab0, xs1, tab1);
-    if (kb + 1 < KB) step(kb + 1, xs1, tab1, xs0, tab0);
+  // Three unconditional steps per trip (so every path into a step has the
+  // same loads in flight), then the remaining one or two steps.
+  int64_t kb = 0;
+  for (; kb + 3 <= KB; kb += 3) {
+    step(kb, std::integral_constant<int, 0>());
+    step(kb + 1, std::integral_constant<int, 1>());
+    step(kb + 2, std::integral_constant<int, 2>());
   }
+  if (kb < KB) step(kb, std::integral_constant<int, 0>());
+  if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>());
 
-  // Adapter term as 2r extra reduction elements.
+  // Adapter term as 2r extra reduction elements, 16 per MFMA: lane group h
+  // supplies elements 16q + 8h + (0..7).
   const int r = p.r, r2 = 2 * r;
-  for (int q = 0; q < r2 / 32; ++q) {
-    const int jj = 32 * q + 8 * g;
+  for (int q = 0; q < r2 / 16; ++q) {
+    const int jj = 16 * q + 8 * h;
     const int jb = jj % r;
-    u32x4_t bfr[4];
+    u32x4_t bfr[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t n = n0 + 64 * w + 4 * c + t;
-      bfr[t] = n < N ? *reinterpret_cast<const u32x4_t*>(p.Bt + n * r + jb) : zero4();
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t n = n0 + 64 * w + 2 * c + nt;
+      bfr[nt] = n < N ? *reinterpret_cast<const u32x4_t*>(p.Bt + n * r + jb) : zero4();
     }
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt) {
-      const int64_t m = m0 + 16 * mt + c;
+    for (int mt = 0; mt < 8; ++mt) {
+      const int64_t m = m0 + 32 * mt + c;
       const u32x4_t a = m < M ? *reinterpret_cast<const u32x4_t*>(p.ulr + m * r2 + jj) : zero4();
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_16x16x32(a, bfr[t], acc[mt][t]);
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_32x32x16(a, bfr[nt], acc[mt][nt]);
     }
   }
 
-  const int64_t ncol = n0 + 64 * w + 4 * c;
+  const int64_t ncol = n0 + 64 * w + 2 * c;
   if (ncol < N) {
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = m0 + 16 * mt + 4 * g + v;
-        if (m < M)
-          store4<kOutBf16>(p.y, N, m, ncol, N, acc[mt][0][v], acc[mt][1][v], acc[mt][2][v],
-                           acc[mt][3][v]);
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) store2<kOutBf16>(p.y, N, m, ncol, N, acc[mt][0][e], acc[mt][1][e]);
       }
   }
 }
@@ -419,15 +540,37 @@ struct BwdArgs {
   int r;
 };
 
+// Tile mapping (v_mfma_f32_32x32x16_bf16). Lane l = 32h + c of wave w:
+//   MFMA (mt, nt) covers rows m0 + 32mt + (0..31) and output columns
+//   kbase + 2c + nt (kbase = first column of wave w, a block boundary).
+//   Step = 64 weight rows (the reduction) = 4 substeps s of 16; in substep s
+//   lane group h supplies rows n0 + 32h + 8s + (0..7) of both operands. The
+//   B fragment of (nt, s) holds, for each of those 8 rows, nibble nt of the
+//   code byte of columns kbase + 2c, kbase + 2c + 1.
+//
+// Pipeline of one step ns, three buffers of dY, code blocks and tables:
+//   top:   DMA dY(ns+2); DMA this wave's code block (64 rows x its 32 bytes)
+//          of step ns+2; load the scales of ns+3 (12 vector-memory
+//          instructions); build this wave's tables of step ns+1.
+//   body:  32 groups (s, mt) of 2 MFMAs on the fragments of substep s while
+//          the fragments of substep s+1 (or of step ns+1, substep 0) are
+//          looked up, 2 LUT reads per group; the 8 code bytes of the next
+//          substep are read at the start of each substep.
+//   end:   wait until only this step's loads are in flight, then barrier.
+// Wave w only reads the code bytes and tables of its own 64 columns, which
+// its own lanes fetch and build, so those need only this wave's waits.
 template <bool kOutBf16>
 __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb) {
   __shared__ __attribute__((aligned(1024))) uint16_t ys0[kTileBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t ys1[kTileBytes / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t ys2[kTileBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint8_t cs0[64 * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t cs1[64 * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t tab0[256 * 16];
-  __shared__ __attribute__((aligned(16))) uint16_t tab1[256 * 16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t cs2[64 * 128];
+  __shared__ __attribute__((aligned(32))) uint16_t tab0[256 * 16];
+  __shared__ __attribute__((aligned(32))) uint16_t tab1[256 * 16];
+  __shared__ __attribute__((aligned(32))) uint16_t tab2[256 * 16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m0 = (int64_t)blockIdx.y * kBM;
   const int64_t kt0 = (int64_t)blockIdx.x * kBN;
@@ -436,8 +579,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
   const int64_t kbase = kt0 + 64 * w;
   const bool wave_live = kbase < K;
 
-  // dY DMA: slot (w*8+j)*64 + lane -> row (w*8+j)*8 + lane/8, chunk slot lane%8
-  // holding global chunk (lane%8) ^ ((lane/8)%8) of that row.
+  // dY DMA: instruction j of wave w, lane l -> slot (w*8+j)*64 + l -> row
+  // (w*8+j)*8 + l/8, chunk slot l%8 holding global chunk (l%8) ^ ((l/8)%8).
   const uint16_t* yrow0 = p.dY + m0 * N;
   uint32_t yoff[8];
   const int ychunk = (lane & 7) ^ ((lane >> 3) & 7);
@@ -450,141 +593,204 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
       yoff[j] = (uint32_t)(row * N);
     }
   }
-  // Code DMA: 512 chunks of 16 B per step; wave w moves chunks [128w, 128w+128):
-  // instruction j, lane l -> chunk 128w + 64j + l -> row (128w+64j+l)/8, byte
-  // column 16*((128w+64j+l)%8) of the workgroup's 128-byte span. Columns past
-  // K are clamped to the last in-range chunk of the row (never used).
-  uint32_t ccol[2];
-  int crow[2];
+  // Code DMA of this wave: 64 rows x 32 bytes (columns kbase..kbase+63) =
+  // 128 chunks of 16 B: instruction j, lane l -> chunk 64j + l -> row
+  // (64j+l)/2, half (64j+l)%2, stored at byte (64j+l)*16 of the wave's 2 KB.
+  const int64_t ccol = (wave_live ? kbase : K - 64) / 2;
+  int crow[2], chalf[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int ch = 128 * w + 64 * j + lane;
-    crow[j] = ch >> 3;
-    int64_t col = kt0 / 2 + 16 * (ch & 7);
-    if (col + 16 > K / 2) col = K / 2 - 16;
-    ccol[j] = (uint32_t)col;
+    crow[j] = (64 * j + lane) >> 1;
+    chalf[j] = (64 * j + lane) & 1;
   }
-  // Table of this thread: weight row nb0 + (tid & 63), block kt0/64 + (tid >> 6).
   const int64_t tblk = kt0 / 64 + (tid >> 6);
   const bool tblk_ok = tblk < KB;
 
-  auto issue = [&](int64_t ns, uint16_t* ydst, uint8_t* cdst) {
-    const int64_t nb0 = ns * 64;
-    int64_t ccl = nb0 + ychunk * 8;
+  // 8 vector-memory instructions
+  auto issue_y = [&](int64_t ns, uint16_t* ydst) {
+    int64_t ccl = ns * 64 + ychunk * 8;
     if (ccl + 8 > N) ccl = N - 8;
     const uint16_t* ysrc = yrow0 + ccl;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       __builtin_amdgcn_global_load_lds(ysrc + yoff[j], ydst + (w * 8 + j) * 512, 16, 0, 0);
+  };
+  // 2 vector-memory instructions
+  auto issue_codes = [&](int64_t ns, uint8_t* cdst) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      int64_t row = nb0 + crow[j];
+      int64_t row = ns * 64 + crow[j];
       row = row < N ? row : N - 1;
-      __builtin_amdgcn_global_load_lds(p.codes + row * (K / 2) + ccol[j],
-                                       cdst + (128 * w + 64 * j) * 16, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(p.codes + row * (K / 2) + ccol + 16 * chalf[j],
+                                       cdst + w * 2048 + 64 * j * 16, 16, 0, 0);
     }
   };
+  // 2 vector-memory instructions (unconditional; masked when the table is built)
   auto load_scale = [&](int64_t ns, int& qv, float& sv) {
     const int64_t nn = ns * 64 + (tid & 63);
-    const bool ok = nn < N && tblk_ok;
     const int64_t bi = (nn < N ? nn : N - 1) * KB + (tblk_ok ? tblk : KB - 1);
-    qv = ok ? (int)p.q8[bi] : 0;
+    qv = (int)p.q8[bi];
     sv = p.s2[bi >> 8];
   };
+  auto scale_ok = [&](int64_t ns) { return ns * 64 + (tid & 63) < N && tblk_ok; };
 
-  f32x4_t acc[16][4];
+  f32x16_t acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][nt][e] = 0.0f;
 
-  const int a_off0 = c * 64 + (((2 * g) ^ (c & 7)) << 3);
-  const int a_off1 = c * 64 + (((2 * g + 1) ^ (c & 7)) << 3);
-  const int tb_off = (w * 64 + 16 * g) * 16;       // table of this lane's first row
-  const int cb_off = (16 * g) * 128 + w * 32 + 2 * c;  // code bytes of this lane's first row
-
-  auto compute = [&](const uint16_t* yb, const uint8_t* cbuf, const uint16_t* tb) {
+  int a_off[4];
 #pragma unroll
-    for (int kf = 0; kf < 2; ++kf) {
-      uint32_t cw[8];
+  for (int s = 0; s < 4; ++s) a_off[s] = c * 128 + (((4 * h + s) ^ (c & 7)) << 4);
+  const uint32_t t_byte = (uint32_t)((w * 64 + 32 * h) * 32);  // table of this lane's row 0
+  const int cb_off = w * 2048 + (32 * h) * 32 + c;             // its code byte of row 0
+
+  // The 8 code bytes (rows 8s..8s+7 of this lane's half) of substep s.
+  auto code_bytes = [&](const uint8_t* cbuf, int s, uint32_t (&b)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = cbuf[cb_off + (8 * s + i) * 32];
+  };
+  // One substep: 8 groups (A fragment of row tile mt, 2 MFMAs) on fragments
+  // bc, while fragments bn of substep sn (code bytes b, table array tarr) are
+  // looked up: group mt looks up dword mt%4 (rows 2(mt%4), 2(mt%4)+1) of
+  // fragment mt/4.
+  auto substep = [&](const char* ya, const u32x4_t (&bc)[2], u32x4_t (&bn)[2],
+                     const uint32_t (&b)[8], const uint16_t* tarr, int sn) {
+    const char* tb = reinterpret_cast<const char*>(tarr);
+    u32x4_t a[3];
+    a[0] = *reinterpret_cast<const u32x4_t*>(ya);
+    a[1] = *reinterpret_cast<const u32x4_t*>(ya + 4096);
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      if (mt + 2 < 8) a[(mt + 2) % 3] = *reinterpret_cast<const u32x4_t*>(ya + (mt + 2) * 4096);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_32x32x16(a[mt % 3], bc[nt], acc[mt][nt]);
+      {
+        const int f = mt >> 2, q = mt & 3;
+        const uint32_t r0 = t_byte + (uint32_t)(8 * sn + 2 * q) * 32;
+        const uint32_t b0 = b[2 * q], b1 = b[2 * q + 1];
+        const uint32_t o0 = f == 0 ? ((b0 << 1) & 30u) : ((b0 >> 3) & 30u);
+        const uint32_t o1 = f == 0 ? ((b1 << 1) & 30u) : ((b1 >> 3) & 30u);
+        lo[mt] = *reinterpret_cast<const uint16_t*>(tb + (r0 | o0));
+        hi[mt] = *reinterpret_cast<const uint16_t*>(tb + ((r0 + 32) | o1));
+      }
+      if (mt >= 2) bn[(mt - 2) >> 2][(mt - 2) & 3] = lo[mt - 2] | (hi[mt - 2] << 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    bn[1][2] = lo[6] | (hi[6] << 16);
+    bn[1][3] = lo[7] | (hi[7] << 16);
+  };
+
+  // Prologue: dY(0), dY(1), code blocks 0 and 1, scales 0..2; table 0 built;
+  // fragments of (step 0, substep 0) looked up.
+  int qs[3] = {0, 0, 0};
+  float ss[3] = {0.0f, 0.0f, 0.0f};
+  const int64_t ns1 = NS > 1 ? 1 : 0, ns2 = NS > 2 ? 2 : NS - 1;
+  issue_y(0, ys0);
+  issue_y(ns1, ys1);
+  issue_codes(0, cs0);
+  issue_codes(ns1, cs1);
+  load_scale(0, qs[0], ss[0]);
+  load_scale(ns1, qs[1], ss[1]);
+  load_scale(ns2, qs[2], ss[2]);
+  wait_vmem<0>();
+  build_table(cb, scale_ok(0) ? qs[0] : 0, ss[0], tab0 + tid * 16);
+  u32x4_t bf0[2], bf1[2];
+  {
+    uint32_t b[8];
+    code_bytes(cs0, 0, b);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      uint32_t v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        cw[i] = *reinterpret_cast<const uint16_t*>(cbuf + cb_off + (8 * kf + i) * 128);
-      u32x4_t bfr[4];
-      const uint16_t* trow = tb + tb_off + kf * 8 * 16;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = trow[i * 16 + ((cw[i] >> (4 * t)) & 15u)];
-        bfr[t] = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                         h[6] | (h[7] << 16)};
-      }
-      const uint16_t* ya = yb + (kf ? a_off1 : a_off0);
-#pragma unroll
-      for (int mt = 0; mt < 16; ++mt) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ya + mt * 1024);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_16x16x32(a, bfr[t], acc[mt][t]);
-      }
+        v[i] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(tab0) + t_byte +
+                                                  i * 32 + 2 * ((b[i] >> (4 * nt)) & 15u));
+      bf0[nt] = u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                        v[6] | (v[7] << 16)};
     }
-  };
-
-  int qv, qn;
-  float sv, sn;
-  issue(0, ys0, cs0);
-  load_scale(0, qv, sv);
-  build_table(cb, qv, sv, tab0 + tid * 16);
-  if (NS > 1) load_scale(1, qn, sn);
-  __syncthreads();
-
-  auto step = [&](int64_t ns, uint16_t* ycur, uint8_t* ccur, uint16_t* tcur, uint16_t* ynext,
-                  uint8_t* cnext, uint16_t* tnext) {
-    const bool more = ns + 1 < NS;
-    if (more) issue(ns + 1, ynext, cnext);
-    int q2 = 0;
-    float s2v = 0.0f;
-    if (ns + 2 < NS) load_scale(ns + 2, q2, s2v);
-    compute(ycur, ccur, tcur);
-    if (more) build_table(cb, qn, sn, tnext + tid * 16);
-    __syncthreads();
-    qn = q2;
-    sn = s2v;
-  };
-  for (int64_t ns = 0; ns < NS; ns += 2) {
-    step(ns, ys0, cs0, tab0, ys1, cs1, tab1);
-    if (ns + 1 < NS) step(ns + 1, ys1, cs1, tab1, ys0, cs0, tab0);
   }
+  __syncthreads();  // dY(0), dY(1) visible everywhere
 
+  // Every step issues the same 12 vector-memory instructions (indices past
+  // the last step are clamped), so the wait counts are exact on every path.
+  auto step = [&](int64_t ns, auto slot) {
+    constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+    const int64_t n2 = ns + 2 < NS ? ns + 2 : NS - 1;
+    const int64_t n3 = ns + 3 < NS ? ns + 3 : NS - 1;
+    const char* y0 = reinterpret_cast<const char*>(pick3<S0>(ys0, ys1, ys2));
+    uint16_t* const y2 = pick3<S2>(ys0, ys1, ys2);
+    const uint8_t* c0 = pick3<S0>(cs0, cs1, cs2);
+    const uint8_t* c1 = pick3<S1>(cs0, cs1, cs2);
+    uint8_t* const c2 = pick3<S2>(cs0, cs1, cs2);
+    uint16_t* const t0 = pick3<S0>(tab0, tab1, tab2);
+    uint16_t* const t1 = pick3<S1>(tab0, tab1, tab2);
+    issue_y(n2, y2);
+    issue_codes(n2, c2);
+    load_scale(n3, qs[S0], ss[S0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // scales(ns+1) came two steps ago: at least 24 younger loads
+    wait_vmem<24>();
+    build_table(cb, scale_ok(ns + 1) ? qs[S1] : 0, ss[S1], t1 + tid * 16);
+    uint32_t b1[8], b2[8], b3[8], bn[8];
+    code_bytes(c0, 1, b1);
+    substep(y0 + a_off[0], bf0, bf1, b1, t0, 1);
+    code_bytes(c0, 2, b2);
+    substep(y0 + a_off[1], bf1, bf0, b2, t0, 2);
+    code_bytes(c0, 3, b3);
+    substep(y0 + a_off[2], bf0, bf1, b3, t0, 3);
+    // this wave's code block of ns+1 came in the previous step
+    wait_vmem<12>();
+    code_bytes(c1, 0, bn);
+    substep(y0 + a_off[3], bf1, bf0, bn, t1, 0);
+    // only this step's 12 loads may be in flight: dY(ns+1) has landed
+    wait_vmem<12>();
+    __builtin_amdgcn_s_barrier();
+  };
+  int64_t ns = 0;
+  for (; ns + 3 <= NS; ns += 3) {
+    step(ns, std::integral_constant<int, 0>());
+    step(ns + 1, std::integral_constant<int, 1>());
+    step(ns + 2, std::integral_constant<int, 2>());
+  }
+  if (ns < NS) step(ns, std::integral_constant<int, 0>());
+  if (ns + 1 < NS) step(ns + 1, std::integral_constant<int, 1>());
+
+  // Adapter term as 2r extra reduction elements, 16 per MFMA.
   const int r = p.r, r2 = 2 * r;
-  for (int q = 0; q < r2 / 32; ++q) {
-    const int jj = 32 * q + 8 * g;
+  for (int q = 0; q < r2 / 16; ++q) {
+    const int jj = 16 * q + 8 * h;
     const int jb = jj % r;
-    u32x4_t bfr[4];
+    u32x4_t bfr[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t kc = kbase + 4 * c + t;
-      bfr[t] = kc < K ? *reinterpret_cast<const u32x4_t*>(p.A + kc * r + jb) : zero4();
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t kc = kbase + 2 * c + nt;
+      bfr[nt] = kc < K ? *reinterpret_cast<const u32x4_t*>(p.A + kc * r + jb) : zero4();
     }
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt) {
-      const int64_t m = m0 + 16 * mt + c;
+    for (int mt = 0; mt < 8; ++mt) {
+      const int64_t m = m0 + 32 * mt + c;
       const u32x4_t a = m < M ? *reinterpret_cast<const u32x4_t*>(p.svlr + m * r2 + jj) : zero4();
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_16x16x32(a, bfr[t], acc[mt][t]);
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_32x32x16(a, bfr[nt], acc[mt][nt]);
     }
   }
 
-  const int64_t kcol = kbase + 4 * c;
+  const int64_t kcol = kbase + 2 * c;
   if (wave_live) {
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = m0 + 16 * mt + 4 * g + v;
-        if (m < M)
-          store4<kOutBf16>(p.dX, K, m, kcol, K, acc[mt][0][v], acc[mt][1][v], acc[mt][2][v],
-                           acc[mt][3][v]);
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) store2<kOutBf16>(p.dX, K, m, kcol, K, acc[mt][0][e], acc[mt][1][e]);
       }
   }
 }
