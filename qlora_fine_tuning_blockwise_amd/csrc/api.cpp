@@ -53,20 +53,20 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
 }
 
 struct BwdLayout {
-  size_t At = 0, u = 0, down = 0, v = 0, svlr = 0, col = 0, total = 0;
+  size_t At = 0, down = 0, v = 0, svlr = 0, vT = 0, uT = 0, col = 0, total = 0;
 };
 
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   BwdLayout L;
   Carve c;
-  if (need_u) {
-    L.At = c.take((size_t)r * K * 2);
-    L.u = c.take((size_t)M * r * 4);
-  }
+  if (need_u) L.At = c.take((size_t)r * K * 2);
   const int64_t T = K > N ? K : N;
   L.down = c.take((size_t)lora_down_slices(T) * M * r * 4);
   L.v = c.take((size_t)M * r * 4);
   L.svlr = c.take((size_t)M * 2 * r * 2);
+  const size_t Mp = (size_t)((M + 7) & ~(int64_t)7);
+  L.vT = c.take(2 * (size_t)r * Mp * 2);
+  L.uT = c.take(2 * (size_t)r * Mp * 2);
   L.col = c.take((size_t)colred_splits(M) * T * r * 4);
   L.total = c.off;
   return L;
@@ -186,7 +186,8 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
   hipError_t e = launch_transpose_bf16(A, K, r, At, st);  // A^T [r,K]
   if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
   if (L.gemv_path) {
-    if (e == hipSuccess) e = launch_lora_down_finalize(down, slices, M, r, s, u, nullptr, st);
+    if (e == hipSuccess)
+      e = launch_lora_down_finalize(down, slices, M, r, s, u, nullptr, nullptr, st);
     float* part = at<float>(workspace, L.gemv);
     if (e == hipSuccess) e = launch_gemv_fwd(x, codes, absmax_q, absmax_scale, M, N, K, part, *cb, st);
     if (e == hipSuccess)
@@ -194,7 +195,7 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
   } else {
     uint16_t* Bt = at<uint16_t>(workspace, L.Bt);
     uint16_t* ulr = at<uint16_t>(workspace, L.ulr);
-    if (e == hipSuccess) e = launch_lora_down_finalize(down, slices, M, r, s, u, ulr, st);
+    if (e == hipSuccess) e = launch_lora_down_finalize(down, slices, M, r, s, u, ulr, nullptr, st);
     if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
     if (e == hipSuccess)
       e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, *cb, st);
@@ -240,34 +241,38 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
   float* down = at<float>(workspace, L.down);
   float* v = at<float>(workspace, L.v);
   uint16_t* svlr = at<uint16_t>(workspace, L.svlr);
+  uint16_t* vT = at<uint16_t>(workspace, L.vT);
+  uint16_t* uT = at<uint16_t>(workspace, L.uT);
   float* col = at<float>(workspace, L.col);
   hipError_t e = hipSuccess;
-  // v = dY B^T (B [r,N] is already contiguous along N)
+  // v = dY B^T (B [r,N] is already contiguous along N); the finalize writes
+  // the split of s*v both row-major (dX tiles) and transposed (dA).
   e = launch_lora_down_parts(dY, B, M, N, r, down, st);
   if (e == hipSuccess)
-    e = launch_lora_down_finalize(down, lora_down_slices(N), M, r, s, v, svlr, st);
+    e = launch_lora_down_finalize(down, lora_down_slices(N), M, r, s, v, svlr, dA ? vT : nullptr,
+                                  st);
   if (e == hipSuccess && dX)
     e = launch_gemm_bwd(dY, codes, absmax_q, absmax_scale, svlr, A, M, N, K, r, dX,
                         dx_dtype == QLORA_DTYPE_BF16, *cb, st);
-  if (e == hipSuccess && dA) {  // dA = s x^T v
-    e = launch_colred(x, v, M, K, r, col, st);
+  if (e == hipSuccess && dA) {  // dA = x^T (s v)
+    e = launch_colred(x, vT, M, K, r, col, st);
     if (e == hipSuccess)
-      e = launch_colred_finalize(col, colred_splits(M), K, r, s, false, dA, gbf, st);
+      e = launch_colred_finalize(col, colred_splits(M), K, r, 1.0f, false, dA, gbf, st);
   }
-  if (e == hipSuccess && dB) {  // dB = s u^T dY
-    const float* u = u_saved;
+  if (e == hipSuccess && dB) {  // dB = (s u)^T dY
     if (need_u) {
       uint16_t* At = at<uint16_t>(workspace, L.At);
-      float* uw = at<float>(workspace, L.u);
       e = launch_transpose_bf16(A, K, r, At, st);
       if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
       if (e == hipSuccess)
-        e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, uw, nullptr, st);
-      u = uw;
+        e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, nullptr, nullptr, uT,
+                                      st);
+    } else {
+      e = launch_lora_down_finalize(u_saved, 1, M, r, s, nullptr, nullptr, uT, st);
     }
-    if (e == hipSuccess) e = launch_colred(dY, u, M, N, r, col, st);
+    if (e == hipSuccess) e = launch_colred(dY, uT, M, N, r, col, st);
     if (e == hipSuccess)
-      e = launch_colred_finalize(col, colred_splits(M), N, r, s, true, dB, gbf, st);
+      e = launch_colred_finalize(col, colred_splits(M), N, r, 1.0f, true, dB, gbf, st);
   }
   return launch_status(e);
 }

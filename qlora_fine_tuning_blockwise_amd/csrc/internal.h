@@ -34,14 +34,16 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
 
 // Rank-r down projection out[m][j] = sum_t X[m][t] * P[j][t] (X [M,T] bf16,
 // P [r,T] bf16, fp32 result) in t-slices: launch_lora_down_parts writes
-// part[slice][m][j]; launch_lora_down_finalize sums the slices into out and,
-// if lr != NULL, writes lr[m][0..r) = bf16(s*out), lr[m][r..2r) =
-// bf16(s*out - hi) (a two-term bf16 split of s*out).
+// part[slice][m][j]; launch_lora_down_finalize sums the slices into out (if
+// out != NULL) and writes a two-term bf16 split of s*out: if lr != NULL as
+// lr[m][0..r) = bf16(s*out), lr[m][r..2r) = bf16(s*out - hi); if lrT != NULL
+// transposed as lrT[j][m] (hi) and lrT[r+j][m] (lo), row stride
+// Mp = round_up(M, 8), zero for m >= M.
 int lora_down_slices(int64_t T);
 hipError_t launch_lora_down_parts(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
                                   int r, float* part, hipStream_t st);
 hipError_t launch_lora_down_finalize(const float* part, int slices, int64_t M, int r, float s,
-                                     float* out, uint16_t* lr, hipStream_t st);
+                                     float* out, uint16_t* lr, uint16_t* lrT, hipStream_t st);
 
 // y = x W_hat^T + [ulr-extended term], M > 16 path (MFMA tiles).
 hipError_t launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
@@ -65,10 +67,11 @@ hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_
                            const Codebook& cb, hipStream_t st);
 
 // Adapter gradients: part[split][c][j] = sum_{m in split} X[m][c] * P[m][j]
-// (X [M,C] bf16, P [M,r] fp32), then out = s * sum_split part, written as
-// [C,r] (transpose_out = false) or [r,C] (true), fp32 or bf16.
+// (X [M,C] bf16; P given as the transposed two-term bf16 split PT [2r, Mp]
+// written by launch_lora_down_finalize), then out = s * sum_split part,
+// written as [C,r] (transpose_out = false) or [r,C] (true), fp32 or bf16.
 int colred_splits(int64_t M);
-hipError_t launch_colred(const uint16_t* X, const float* P, int64_t M, int64_t C, int r,
+hipError_t launch_colred(const uint16_t* X, const uint16_t* PT, int64_t M, int64_t C, int r,
                          float* part, hipStream_t st);
 hipError_t launch_colred_finalize(const float* part, int splits, int64_t C, int r, float s,
                                   bool transpose_out, void* out, bool out_bf16, hipStream_t st);

@@ -11,9 +11,9 @@
 //    a finalize kernel sums the slices in a fixed order and also emits the
 //    two-term bf16 split of s*out used by the tile kernels.
 //  - colred: the adapter gradients dA = s x^T v and dB = s u^T dY reduce over
-//    the token dimension M; each thread owns one column of X and accumulates
-//    r fp32 products per element against rows of P staged in LDS. Slices of M
-//    go to separate partial buffers, summed in a fixed order by a finalize.
+//    the token dimension M, on MFMA with a transposed read of x from LDS and
+//    the fp32 rank-side operand split into two bf16 terms. Slices of M go to
+//    separate partial buffers, summed in a fixed order by a finalize.
 #include "device.h"
 
 namespace qlora {
@@ -102,75 +102,166 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
   }
 }
 
-// out[m][j] = sum over slices; lr[m][j] = bf16(s*out), lr[m][r+j] = bf16(s*out - hi).
-__global__ __launch_bounds__(256) void lora_down_finalize_kernel(const float* __restrict__ part,
-                                                                 int slices, int64_t M, int r,
-                                                                 float s, float* __restrict__ out,
-                                                                 uint16_t* __restrict__ lr) {
+// out[m][j] = sum over slices (skipped if out == NULL); with sv = s*out:
+// lr[m][j] = bf16(sv), lr[m][r+j] = bf16(sv - hi) (row-major two-term split),
+// lrT[j][m] = bf16(sv), lrT[r+j][m] = bf16(sv - hi) (transposed, row stride
+// Mp, zero for M <= m < Mp). Either split output may be NULL. The grid
+// covers Mp * r elements.
+__global__ __launch_bounds__(256) void lora_down_finalize_kernel(
+    const float* __restrict__ part, int slices, int64_t M, int64_t Mp, int r, float s,
+    float* __restrict__ out, uint16_t* __restrict__ lr, uint16_t* __restrict__ lrT) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= M * r) return;
+  if (i >= Mp * r) return;
+  const int64_t m = i / r;
+  const int j = (int)(i % r);
+  if (m >= M) {
+    if (lrT) {
+      lrT[(int64_t)j * Mp + m] = 0;
+      lrT[(int64_t)(r + j) * Mp + m] = 0;
+    }
+    return;
+  }
   float v = 0.0f;
   for (int sl = 0; sl < slices; ++sl) v += part[(int64_t)sl * M * r + i];
-  out[i] = v;
+  if (out) out[i] = v;
+  const float sv = s * v;
+  const uint32_t hi = pack_bf16x2(sv, 0.0f) & 0xFFFFu;
+  const float rem = sv - __uint_as_float(hi << 16);
+  const uint32_t lo = pack_bf16x2(rem, 0.0f) & 0xFFFFu;
   if (lr) {
-    const int64_t m = i / r;
-    const int j = (int)(i % r);
-    const float sv = s * v;
-    const uint32_t hi = pack_bf16x2(sv, 0.0f) & 0xFFFFu;
-    const float rem = sv - __uint_as_float(hi << 16);
-    const uint32_t lo = pack_bf16x2(rem, 0.0f) & 0xFFFFu;
     lr[m * 2 * r + j] = (uint16_t)hi;
     lr[m * 2 * r + r + j] = (uint16_t)lo;
+  }
+  if (lrT) {
+    lrT[(int64_t)j * Mp + m] = (uint16_t)hi;
+    lrT[(int64_t)(r + j) * Mp + m] = (uint16_t)lo;
   }
 }
 
 // ----------------------------------------------------------------- colred
-constexpr int kColMS = 256;  // rows of M per slice
-constexpr int kColStage = 64;  // rows of P staged in LDS at a time
+constexpr int kColMS = 512;   // rows of M per workgroup slice
+constexpr int kColStep = 64;  // rows of M staged in LDS per step
+constexpr int kColLdX = 66;   // x tile row stride in bf16 (132 B)
+constexpr int kColLdP = 72;   // P tile row stride in bf16 (144 B)
 
-// part[slice][c][j0 + j] = sum_{m in slice} X[m][c] * P[m][j0 + j], j < RW.
-// grid: (ceil(C/256), slices, r/RW).
-template <int RW>
+// part[slice][c][j] = sum_{m in slice} X[m][c] * (PT[j][m] + PT[r + j][m]).
+// X [M, C] bf16; PT [2r, Mp] bf16 holds a two-term split of the rank-side
+// operand, transposed, zero for m >= M (Mp = M rounded up to 8).
+// MFMA 16x16x32 with the reduction over m: the x operand needs 8 consecutive
+// rows of one column per lane, read from an LDS tile with one 16-bit read per
+// element (row stride 132 B puts the four 8-row groups of a read in distinct
+// banks); the P operand is one 16-byte LDS read per lane.
+// grid: (ceil(C/64), slices, ceil(r/64)); wave w owns columns 16w..16w+15.
+template <bool kVec>
 __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict__ X,
-                                                     const float* __restrict__ P, int64_t M,
-                                                     int64_t C, int r, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) float ps[kColStage][RW];
-  const int tid = threadIdx.x;
-  const int64_t col = (int64_t)blockIdx.x * 256 + tid;
+                                                     const uint16_t* __restrict__ PT, int64_t M,
+                                                     int64_t Mp, int64_t C, int r,
+                                                     float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kColStep][kColLdX];
+  __shared__ __attribute__((aligned(16))) uint16_t ps[2][64][kColLdP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
   const int slice = blockIdx.y;
-  const int j0 = blockIdx.z * RW;
+  const int jt0 = blockIdx.z * 4;
+  const int ntile = min(4, r / 16 - jt0);
   const int64_t ms0 = (int64_t)slice * kColMS;
   const int64_t ms1 = min(M, ms0 + kColMS);
-  float acc[RW];
+  const int nsteps = (int)((ms1 - ms0 + kColStep - 1) / kColStep);
+
+  // Staging roles: x rows (tid >> 3) and (tid >> 3) + 32, columns 8*(tid & 7);
+  // P chunk q = tid + 256*t (t < ntile): tile row jr = q >> 3 of 16*ntile
+  // hi rows then 16*ntile lo rows, m chunk 8*(q & 7).
+  const int xr = tid >> 3, xq = tid & 7;
+  const int64_t xc = c0 + 8 * xq;
+  u32x4_t xv[2], pv[4];
+
+  auto load_step = [&](int st) {
+    const int64_t mb = ms0 + (int64_t)st * kColStep;
 #pragma unroll
-  for (int j = 0; j < RW; ++j) acc[j] = 0.0f;
-  for (int64_t mb = ms0; mb < ms1; mb += kColStage) {
-    const int rows = (int)min((int64_t)kColStage, ms1 - mb);
-    __syncthreads();
-    for (int i = tid; i < kColStage * RW; i += 256) {
-      const int rr = i / RW, jj = i % RW;
-      ps[rr][jj] = rr < rows ? P[(mb + rr) * r + j0 + jj] : 0.0f;
+    for (int h = 0; h < 2; ++h) {
+      const int64_t m = mb + xr + 32 * h;
+      if (kVec) {
+        xv[h] = (m < ms1 && xc < C) ? *reinterpret_cast<const u32x4_t*>(X + m * C + xc) : zero4();
+      } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          e[k] = (m < ms1 && xc + k < C) ? X[m * C + xc + k] : (uint16_t)0;
+        xv[h] = u32x4_t{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
+                        e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)};
+      }
     }
-    __syncthreads();
-    if (col < C) {
-      for (int rr = 0; rr < rows; ++rr) {
-        const float xv = bf16_lo(X[(mb + rr) * C + col]);
 #pragma unroll
-        for (int j = 0; j < RW; j += 4) {
-          const f32x4_t p = *reinterpret_cast<const f32x4_t*>(&ps[rr][j]);
-          acc[j] = __builtin_fmaf(xv, p.x, acc[j]);
-          acc[j + 1] = __builtin_fmaf(xv, p.y, acc[j + 1]);
-          acc[j + 2] = __builtin_fmaf(xv, p.z, acc[j + 2]);
-          acc[j + 3] = __builtin_fmaf(xv, p.w, acc[j + 3]);
+    for (int t = 0; t < 4; ++t) {
+      if (t < ntile) {
+        const int q = tid + 256 * t;
+        const int jr = q >> 3;  // 0 .. 32*ntile-1
+        const int hl = jr >= 16 * ntile;
+        const int j = 16 * jt0 + jr - hl * 16 * ntile;
+        const int64_t m = mb + 8 * (q & 7);
+        pv[t] = m < Mp ? *reinterpret_cast<const u32x4_t*>(PT + ((int64_t)hl * r + j) * Mp + m)
+                       : zero4();
+      }
+    }
+  };
+  auto store_step = [&]() {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t* d = reinterpret_cast<uint32_t*>(&xs[xr + 32 * h][8 * xq]);
+      d[0] = xv[h].x;
+      d[1] = xv[h].y;
+      d[2] = xv[h].z;
+      d[3] = xv[h].w;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < ntile) {
+        const int q = tid + 256 * t;
+        const int jr = q >> 3;
+        const int hl = jr >= 16 * ntile;
+        *reinterpret_cast<u32x4_t*>(&ps[hl][jr - hl * 16 * ntile][8 * (q & 7)]) = pv[t];
+      }
+    }
+  };
+
+  f32x4_t acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (nsteps > 0) load_step(0);
+  for (int st = 0; st < nsteps; ++st) {
+    __syncthreads();  // previous step's reads are done
+    store_step();
+    if (st + 1 < nsteps) load_step(st + 1);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint16_t* xb = &xs[32 * ks + 8 * g][16 * w + i];
+      u32x4_t a;
+      a.x = (uint32_t)xb[0 * kColLdX] | ((uint32_t)xb[1 * kColLdX] << 16);
+      a.y = (uint32_t)xb[2 * kColLdX] | ((uint32_t)xb[3 * kColLdX] << 16);
+      a.z = (uint32_t)xb[4 * kColLdX] | ((uint32_t)xb[5 * kColLdX] << 16);
+      a.w = (uint32_t)xb[6 * kColLdX] | ((uint32_t)xb[7 * kColLdX] << 16);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < ntile) {
+          const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(&ps[0][16 * t + i][32 * ks + 8 * g]);
+          const u32x4_t bl = *reinterpret_cast<const u32x4_t*>(&ps[1][16 * t + i][32 * ks + 8 * g]);
+          acc[t] = mfma_16x16x32(a, bh, acc[t]);
+          acc[t] = mfma_16x16x32(a, bl, acc[t]);
         }
       }
     }
   }
-  if (col < C) {
-    float* o = part + ((int64_t)slice * C + col) * r + j0;
+  // acc[t][v] = sum for column c0 + 16w + 4g + v and rank index 16(jt0 + t) + i.
 #pragma unroll
-    for (int j = 0; j < RW; j += 4)
-      *reinterpret_cast<f32x4_t*>(o + j) = f32x4_t{acc[j], acc[j + 1], acc[j + 2], acc[j + 3]};
+  for (int v = 0; v < 4; ++v) {
+    const int64_t c = c0 + 16 * w + 4 * g + v;
+    if (c < C) {
+      float* o = part + ((int64_t)slice * C + c) * r + 16 * jt0 + i;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t < ntile) o[16 * t] = acc[t][v];
+    }
   }
 }
 
@@ -219,25 +310,25 @@ hipError_t launch_lora_down_parts(const uint16_t* X, const uint16_t* P, int64_t 
 }
 
 hipError_t launch_lora_down_finalize(const float* part, int slices, int64_t M, int r, float s,
-                                     float* out, uint16_t* lr, hipStream_t st) {
-  const dim3 grid((unsigned)((M * r + 255) / 256));
-  hipLaunchKernelGGL(lora_down_finalize_kernel, grid, dim3(256), 0, st, part, slices, M, r, s, out,
-                     lr);
+                                     float* out, uint16_t* lr, uint16_t* lrT, hipStream_t st) {
+  const int64_t Mp = (M + 7) & ~(int64_t)7;
+  const dim3 grid((unsigned)((Mp * r + 255) / 256));
+  hipLaunchKernelGGL(lora_down_finalize_kernel, grid, dim3(256), 0, st, part, slices, M, Mp, r, s,
+                     out, lr, lrT);
   return hipGetLastError();
 }
 
 int colred_splits(int64_t M) { return (int)((M + kColMS - 1) / kColMS); }
 
-hipError_t launch_colred(const uint16_t* X, const float* P, int64_t M, int64_t C, int r,
+hipError_t launch_colred(const uint16_t* X, const uint16_t* PT, int64_t M, int64_t C, int r,
                          float* part, hipStream_t st) {
-  const int slices = colred_splits(M);
-  if (r % 64 == 0) {
-    const dim3 grid((unsigned)((C + 255) / 256), (unsigned)slices, (unsigned)(r / 64));
-    hipLaunchKernelGGL(colred_kernel<64>, grid, dim3(256), 0, st, X, P, M, C, r, part);
-  } else {
-    const dim3 grid((unsigned)((C + 255) / 256), (unsigned)slices, (unsigned)(r / 16));
-    hipLaunchKernelGGL(colred_kernel<16>, grid, dim3(256), 0, st, X, P, M, C, r, part);
-  }
+  const int64_t Mp = (M + 7) & ~(int64_t)7;
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)colred_splits(M),
+                  (unsigned)((r / 16 + 3) / 4));
+  if (C % 8 == 0)
+    hipLaunchKernelGGL(colred_kernel<true>, grid, dim3(256), 0, st, X, PT, M, Mp, C, r, part);
+  else
+    hipLaunchKernelGGL(colred_kernel<false>, grid, dim3(256), 0, st, X, PT, M, Mp, C, r, part);
   return hipGetLastError();
 }
 
