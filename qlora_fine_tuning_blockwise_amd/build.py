@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqlora_amd.so")
-SOURCES = ["codebook.cpp", "api.cpp", "quantize.hip", "gemm.hip", "lora.hip"]
+SOURCES = ["codebook.cpp", "api.cpp", "quantize.hip", "gemm.hip", "lora.hip", "decode.hip"]
 
 # Bit-exact arithmetic: no fast-math, no FP contraction, IEEE fp32 division,
 # denormals kept. Packed-fp32 VALU forms are switched off for the device.
@@ -16,6 +16,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # LDS tiles are written and read through different integer types by the
+    # same wave without a barrier in between; program order must hold.
+    "-fno-strict-aliasing",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

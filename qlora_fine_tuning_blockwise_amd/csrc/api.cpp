@@ -31,7 +31,7 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, gemv = 0, total = 0;
+  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, total = 0;
   bool gemv_path = false;
 };
 
@@ -39,12 +39,12 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   FwdLayout L;
   Carve c;
   L.gemv_path = M <= kGemvMaxM;
-  L.At = c.take((size_t)r * K * 2);
-  L.u = need_u ? c.take((size_t)M * r * 4) : 0;
-  L.down = c.take((size_t)lora_down_slices(K) * M * r * 4);
   if (L.gemv_path) {
-    L.gemv = c.take((size_t)gemv_splits(K) * M * N * 4);
+    L.down = c.take((size_t)decode_down_slices(K) * M * r * 4);
   } else {
+    L.At = c.take((size_t)r * K * 2);
+    L.u = need_u ? c.take((size_t)M * r * 4) : 0;
+    L.down = c.take((size_t)lora_down_slices(K) * M * r * 4);
     L.Bt = c.take((size_t)N * r * 2);
     L.ulr = c.take((size_t)M * 2 * r * 2);
   }
@@ -59,9 +59,13 @@ struct BwdLayout {
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   BwdLayout L;
   Carve c;
-  if (need_u) L.At = c.take((size_t)r * K * 2);
+  // u is recomputed with the kernels of the forward pass for this M, so that
+  // it has the same bits as the u the forward pass returns.
+  if (need_u && M > kGemvMaxM) L.At = c.take((size_t)r * K * 2);
   const int64_t T = K > N ? K : N;
-  L.down = c.take((size_t)lora_down_slices(T) * M * r * 4);
+  const int down_slices = lora_down_slices(T) > decode_down_slices(K) ? lora_down_slices(T)
+                                                                      : decode_down_slices(K);
+  L.down = c.take((size_t)down_slices * M * r * 4);
   L.v = c.take((size_t)M * r * 4);
   L.svlr = c.take((size_t)M * 2 * r * 2);
   const size_t Mp = (size_t)((M + 7) & ~(int64_t)7);
@@ -179,23 +183,22 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float s = alpha / (float)r;
   const bool ybf = y_dtype == QLORA_DTYPE_BF16;
-  uint16_t* At = at<uint16_t>(workspace, L.At);
-  float* u = u_out ? u_out : at<float>(workspace, L.u);
   float* down = at<float>(workspace, L.down);
-  const int slices = lora_down_slices(K);
-  hipError_t e = launch_transpose_bf16(A, K, r, At, st);  // A^T [r,K]
-  if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
+  hipError_t e = hipSuccess;
   if (L.gemv_path) {
+    e = launch_lora_down_decode(x, A, M, K, r, down, st);
     if (e == hipSuccess)
-      e = launch_lora_down_finalize(down, slices, M, r, s, u, nullptr, nullptr, st);
-    float* part = at<float>(workspace, L.gemv);
-    if (e == hipSuccess) e = launch_gemv_fwd(x, codes, absmax_q, absmax_scale, M, N, K, part, *cb, st);
-    if (e == hipSuccess)
-      e = launch_gemv_finalize(part, gemv_splits(K), u, B, M, N, r, s, y, ybf, st);
+      e = launch_gemv(x, codes, absmax_q, absmax_scale, down, decode_down_slices(K), B, M, N, K, r,
+                      s, u_out, y, ybf, *cb, st);
   } else {
+    uint16_t* At = at<uint16_t>(workspace, L.At);
+    float* u = u_out ? u_out : at<float>(workspace, L.u);
     uint16_t* Bt = at<uint16_t>(workspace, L.Bt);
     uint16_t* ulr = at<uint16_t>(workspace, L.ulr);
-    if (e == hipSuccess) e = launch_lora_down_finalize(down, slices, M, r, s, u, ulr, nullptr, st);
+    e = launch_transpose_bf16(A, K, r, At, st);  // A^T [r,K]
+    if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
+    if (e == hipSuccess)
+      e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, u, ulr, nullptr, st);
     if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
     if (e == hipSuccess)
       e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, *cb, st);
@@ -260,7 +263,12 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
       e = launch_colred_finalize(col, colred_splits(M), K, r, 1.0f, false, dA, gbf, st);
   }
   if (e == hipSuccess && dB) {  // dB = (s u)^T dY
-    if (need_u) {
+    if (need_u && M <= kGemvMaxM) {
+      e = launch_lora_down_decode(x, A, M, K, r, down, st);
+      if (e == hipSuccess)
+        e = launch_lora_down_finalize(down, decode_down_slices(K), M, r, s, nullptr, nullptr, uT,
+                                      st);
+    } else if (need_u) {
       uint16_t* At = at<uint16_t>(workspace, L.At);
       e = launch_transpose_bf16(A, K, r, At, st);
       if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);

@@ -1,0 +1,336 @@
+// Decode path of the QLoRA layer (M <= 16 tokens) on gfx950: two launches.
+//
+// [P1] "QLoRA" forward equation: y = x doubleDequant(c1, c2, W) + s (x A) B
+// with s = alpha / r; [P2] s2 (4-bit NormalFloat, Double Quantization).
+//
+//  1. lora_down_decode: per K slice (at most 16), part[slice][m][j] =
+//     sum_k x[m,k] A[k,j] on MFMA (A read transposed from an LDS panel).
+//  2. gemv: the frozen-weight product streams the NF4 codes once from HBM
+//     and finishes the layer in its epilogue: the adapter term s (sum of the
+//     slices) B is added before y is written.
+//
+// The weight stream is the roofline: per weight, 0.5 byte of code plus 1/64
+// byte of block scale. Dequantization runs beside the loads: each lane owns a
+// full 64-weight block of one row in each of two chunks of K and looks its
+// codes up in a 16-entry table of its own. The tables live in LDS as one
+// 4-byte column per lane (entry e of lane t at 256*e + 4*t inside the wave's
+// 4 KB region), so a lookup instruction touches 64 distinct banks whatever
+// the codes are; the two halves of an entry hold the bf16 values of the
+// lane's two blocks. The lookup address is assembled with one byte permute
+// per code.
+#include "device.h"
+
+namespace qlora {
+namespace {
+
+// ------------------------------------------------------ adapter down, decode
+constexpr int kDecMaxSlices = 16;  // K slices (partial sums) of the down projection
+constexpr int kDecLd = 18;         // panel row stride in bf16 (36 B)
+
+// grid: (slices, r / 16). Workgroup `slice` reduces k in [slice*L, (slice+1)*L)
+// in 256-wide pieces (wave w: the piece's k 64w .. 64w+63) for the 16 adapter
+// columns j0..j0+15; the four waves are summed in order. part[slice][m][j].
+__global__ __launch_bounds__(256) void lora_down_decode_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ A,
+                                                               int64_t M, int64_t K, int r,
+                                                               int64_t L,
+                                                               float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t as[4][64][kDecLd];
+  __shared__ float red[4][16][17];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int slice = blockIdx.x;
+  const int j0 = blockIdx.y * 16;
+  const int64_t k0 = (int64_t)slice * L, k1 = min(K, k0 + L);
+  // x rows >= M are read from row M-1: they only feed output rows that are
+  // never stored.
+  const int64_t mrow = min((int64_t)i, M - 1);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t kp = k0; kp < k1; kp += 256) {
+    const int64_t kw = kp + 64 * w;
+    // Panel A[kw .. kw+63][j0 .. j0+15]: 128 chunks of 16 bytes, 2 per lane.
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int q = lane + 64 * it, row = q >> 1, half = q & 1;
+      const int64_t k = kw + row;
+      const u32x4_t v =
+          k < k1 ? *reinterpret_cast<const u32x4_t*>(A + k * r + j0 + 8 * half) : zero4();
+      uint32_t* d = reinterpret_cast<uint32_t*>(&as[w][row][8 * half]);
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int64_t k = kw + 32 * s + 8 * g;
+      const u32x4_t a = k < k1 ? *reinterpret_cast<const u32x4_t*>(x + mrow * K + k) : zero4();
+      const uint16_t* pa = &as[w][32 * s + 8 * g][i];
+      u32x4_t b;
+      b.x = (uint32_t)pa[0 * kDecLd] | ((uint32_t)pa[1 * kDecLd] << 16);
+      b.y = (uint32_t)pa[2 * kDecLd] | ((uint32_t)pa[3 * kDecLd] << 16);
+      b.z = (uint32_t)pa[4 * kDecLd] | ((uint32_t)pa[5 * kDecLd] << 16);
+      b.w = (uint32_t)pa[6 * kDecLd] | ((uint32_t)pa[7 * kDecLd] << 16);
+      acc = mfma_16x16x32(a, b, acc);
+    }
+  }
+  // acc[v] = partial sum for m = 4g + v, j = j0 + i.
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[w][4 * g + v][i] = acc[v];
+  __syncthreads();
+  const int m = tid >> 4, j = tid & 15;
+  if (m < M)
+    part[((int64_t)slice * M + m) * r + j0 + j] =
+        ((red[0][m][j] + red[1][m][j]) + red[2][m][j]) + red[3][m][j];
+}
+
+// Slice length of the down projection: whole 256-wide pieces.
+int64_t decode_down_len(int64_t K, int slices) {
+  const int64_t pieces = (K + 255) / 256;
+  return ((pieces + slices - 1) / slices) * 256;
+}
+
+// ----------------------------------------------------------------- GEMV
+constexpr int kGvWaves = 8;  // waves per workgroup; 256-wide K chunks go round-robin to them
+
+struct GemvArgs {
+  const uint16_t* x;      // [M, K] bf16
+  const uint8_t* codes;   // [N, K/2]
+  const int8_t* q8;       // [N*K/64]
+  const float* s2;        // [ceil(N*K/64/256)]
+  const float* upart;     // [slices, M, r] from lora_down_decode
+  const uint16_t* B;      // [r, N] bf16
+  float* u_out;           // [M, r] fp32 or NULL
+  void* y;                // [M, N] fp32 or bf16
+  int64_t M, N, K;
+  int r, slices;
+  float s;
+};
+
+// Byte selectors of v_perm_b32 building a lookup address: byte 0 from the
+// lane's column offset (src1 byte 0), byte 1 from byte b of the code word
+// (src0 byte b), bytes 2 and 3 zero.
+__device__ __forceinline__ uint32_t lut_addr(uint32_t codebytes, uint32_t colbase, int b) {
+  return __builtin_amdgcn_perm(codebytes, colbase, 0x0C0C0000u | ((uint32_t)(4 + b) << 8));
+}
+
+// Issue the eight table reads for code word `cw` (element e = nibble e) from
+// half `half` of the lane's table entries. `region` carries the wave's
+// region bits in the high nibble of every byte.
+__device__ __forceinline__ void lookup_issue(const char* tab, uint32_t cw, uint32_t region,
+                                             uint32_t colbase, int half, uint32_t v[8]) {
+  const uint32_t lo = (cw & 0x0F0F0F0Fu) | region;
+  const uint32_t hi = ((cw >> 4) & 0x0F0F0F0Fu) | region;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    v[2 * b] = *reinterpret_cast<const uint16_t*>(tab + lut_addr(lo, colbase, b) + 2 * half);
+    v[2 * b + 1] = *reinterpret_cast<const uint16_t*>(tab + lut_addr(hi, colbase, b) + 2 * half);
+  }
+}
+
+// Pack eight 16-bit table values into an MFMA operand (value e to bf16 slot e).
+__device__ __forceinline__ u32x4_t lookup_pack(const uint32_t v[8]) {
+  return u32x4_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
+                 __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                 __builtin_amdgcn_perm(v[5], v[4], 0x05040100u),
+                 __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)};
+}
+
+// grid: ceil(N / 16), 512 threads, two workgroups per CU. Workgroup rows
+// n0 .. n0+15 form one 16-row MFMA tile; 256-wide chunk G of K goes to wave
+// G % 8, and a wave takes its chunks in pairs. Within a chunk, lane group
+// g = lane / 16 owns block 4G + g of row n0 + i (i = lane % 16); the two
+// halves of a table entry hold the lane's blocks of the two chunks of a
+// pair. MFMA rows are the tokens (rows >= M are zero and never stored).
+// Dynamic LDS: s*u [M][r] fp32, then the B columns of the workgroup [r][16]
+// bf16.
+template <bool kOutBf16>
+__global__ __launch_bounds__(512, 4) void gemv_kernel(GemvArgs p, Codebook cb) {
+  __shared__ __attribute__((aligned(16))) uint32_t tabs[kGvWaves][16][64];
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int r = p.r;
+  const int mr = (int)M * r;
+  float* us = dyn;
+  uint16_t* bs = reinterpret_cast<uint16_t*>(dyn + mr);
+  const int64_t KB = K / 64;                                  // blocks per row
+  const int64_t nchunk = (KB + 3) / 4;                        // 256-wide chunks
+  const int64_t nch = (nchunk - w + kGvWaves - 1) / kGvWaves; // chunks of this wave
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t nrow = min(n0 + i, N - 1);
+
+  u32x4_t cw[2][2];  // [chunk of the pair][half of the 32-byte block]
+  int qv[2];
+  float sv[2];
+  u32x4_t xa[2][4];  // [buffer][k-step within a half chunk]
+
+  auto block_of = [&](int64_t ci) { return 4 * (kGvWaves * ci + w) + g; };
+  auto load_codes = [&](int slot, int64_t ci) {
+    const int64_t b = min(block_of(ci), KB - 1);
+    const uint8_t* cp = p.codes + nrow * (K / 2) + 32 * b;
+    cw[slot][0] = *reinterpret_cast<const u32x4_t*>(cp);
+    cw[slot][1] = *reinterpret_cast<const u32x4_t*>(cp + 16);
+    const int64_t bi = nrow * KB + b;
+    qv[slot] = p.q8[bi];
+    sv[slot] = p.s2[bi >> 8];
+  };
+  // x through a buffer resource: lanes of tokens >= M and blocks past the
+  // row end (or past the wave's last chunk) use an out-of-range offset and
+  // read zeros without a memory access.
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.x, (short)0, (int)(M * K * 2), 0x00020000);
+  auto load_x = [&](int buf, int64_t ci, int hh) {  // k-steps 4hh .. 4hh+3 of chunk ci
+    const int64_t blk = block_of(ci);
+    const uint32_t off = (i < M && blk < KB) ? (uint32_t)((i * K + 64 * blk + 32 * hh) * 2)
+                                             : 0x80000000u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      xa[buf][s] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xres, (int)(off + 16 * s), 0, 0));
+  };
+
+  // Region bits of this wave's tables (address bits 12..14 = wave), or-ed
+  // into the high nibble of each code byte.
+  const uint32_t region = 0x10101010u * (uint32_t)w;
+  const uint32_t colbase = 4u * (uint32_t)lane;
+  const char* tab = reinterpret_cast<const char*>(&tabs[0][0][0]);
+
+  // One pair of chunks, straight-line: every load is issued unconditionally
+  // (code indices clamped to the wave's last chunk) so that the wait counts
+  // stay exact; a chunk past the wave's end gets a zero table.
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto pair = [&](int64_t c0, bool reload) {
+    // Entry e = {bf16(L[e] c1_hat(block of chunk c0)), bf16(L[e] c1_hat(block of chunk c0+1))};
+    // a block past the end of the row gets zeros.
+    const float ch0 = c0 < nch && block_of(c0) < KB ? (float)qv[0] * sv[0] : 0.0f;
+    const float ch1 = c0 + 1 < nch && block_of(c0 + 1) < KB ? (float)qv[1] * sv[1] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      tabs[w][e][lane] = pack_bf16x2(cb.level[e] * ch0, cb.level[e] * ch1);
+    const uint32_t cwd[2][8] = {{cw[0][0].x, cw[0][0].y, cw[0][0].z, cw[0][0].w, cw[0][1].x,
+                                 cw[0][1].y, cw[0][1].z, cw[0][1].w},
+                                {cw[1][0].x, cw[1][0].y, cw[1][0].z, cw[1][0].w, cw[1][1].x,
+                                 cw[1][1].y, cw[1][1].z, cw[1][1].w}};
+    // 16 lookup groups j = (chunk j/8 of the pair, k-step j%8), software
+    // pipelined: the reads of group j+1 are in flight while group j is packed
+    // and fed to the MFMA. x streams in half chunks (four groups each), one
+    // half chunk ahead.
+    uint32_t v[2][8];
+    lookup_issue(tab, cwd[0][0], region, colbase, 0, v[0]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if ((j & 3) == 0) {
+        const int q = (j >> 2) + 1;  // next half chunk
+        if (q < 4)
+          load_x(q & 1, c0 + (q >> 1), q & 1);
+        else
+          load_x(0, c0 + 2, 0);
+      }
+      if (j + 1 < 16)
+        lookup_issue(tab, cwd[(j + 1) >> 3][(j + 1) & 7], region, colbase, (j + 1) >> 3,
+                     v[(j + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4_t bop = lookup_pack(v[j & 1]);
+      acc = mfma_16x16x32(xa[(j >> 2) & 1][j & 3], bop, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (reload) {
+      load_codes(0, min(c0 + 2, nch - 1));
+      load_codes(1, min(c0 + 3, nch - 1));
+    }
+  };
+
+  // The weight stream is issued first; the adapter operands (read only in
+  // the epilogue) load behind it.
+  if (nch > 0) {
+    load_codes(0, 0);
+    load_codes(1, min((int64_t)1, nch - 1));
+    load_x(0, 0, 0);
+  }
+  // u = sum of the slices in order (same bits as the finalize kernel's sum);
+  // the loads use clamped slice indices so that they are issued
+  // unconditionally, the padding terms are +0.
+  auto usum = [&](int idx) {
+    float t[kDecMaxSlices];
+#pragma unroll
+    for (int k = 0; k < kDecMaxSlices; ++k) t[k] = p.upart[(int64_t)min(k, p.slices - 1) * mr + idx];
+    float u = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kDecMaxSlices; ++k) u += k < p.slices ? t[k] : 0.0f;
+    us[idx] = p.s * u;
+    if (p.u_out && blockIdx.x == 0) p.u_out[idx] = u;
+  };
+  auto bload = [&](int idx) {
+    const int j = idx >> 4, nl = idx & 15;
+    bs[idx] = p.B[(int64_t)j * N + min(n0 + nl, N - 1)];
+  };
+  if (tid < mr) usum(tid);
+  if (tid < r * 16) bload(tid);
+  for (int idx = tid + 512; idx < mr; idx += 512) usum(idx);       // M * r > 512
+  for (int idx = tid + 512; idx < r * 16; idx += 512) bload(idx);  // r > 32
+  if (nch > 0) {
+    if (nch <= 2) {
+      pair(0, false);
+    } else {
+      for (int64_t c0 = 0; c0 < nch; c0 += 2) pair(c0, true);
+    }
+  }
+
+  // Cross-wave sum (each wave's partial tile goes to its own table region,
+  // which only it reads), adapter term, store. acc[v] = y partial for token
+  // m = 4g + v and row n0 + i.
+  float* red = reinterpret_cast<float*>(&tabs[w][0][0]);  // [16][17] per wave
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[(4 * g + v) * 17 + i] = acc[v];
+  __syncthreads();
+  if (tid < 256) {
+    const int m = tid >> 4, nl = tid & 15;
+    const int64_t n = n0 + nl;
+    if (m < M && n < N) {
+      const int o = m * 17 + nl;
+      float v = reinterpret_cast<const float*>(&tabs[0][0][0])[o];
+#pragma unroll
+      for (int ww = 1; ww < kGvWaves; ++ww) v += reinterpret_cast<const float*>(&tabs[ww][0][0])[o];
+      float lo = 0.0f;
+      for (int j = 0; j < r; ++j) lo = __builtin_fmaf(us[m * r + j], bf16_lo(bs[j * 16 + nl]), lo);
+      v += lo;
+      if (kOutBf16)
+        static_cast<uint16_t*>(p.y)[m * N + n] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+      else
+        static_cast<float*>(p.y)[m * N + n] = v;
+    }
+  }
+}
+
+}  // namespace
+
+int decode_down_slices(int64_t K) {
+  const int64_t pieces = (K + 255) / 256;
+  const int64_t per = (pieces + kDecMaxSlices - 1) / kDecMaxSlices;
+  return (int)((pieces + per - 1) / per);
+}
+
+hipError_t launch_lora_down_decode(const uint16_t* x, const uint16_t* A, int64_t M, int64_t K,
+                                   int r, float* part, hipStream_t st) {
+  const int slices = decode_down_slices(K);
+  const dim3 grid((unsigned)slices, (unsigned)(r / 16));
+  hipLaunchKernelGGL(lora_down_decode_kernel, grid, dim3(256), 0, st, x, A, M, K, r,
+                     decode_down_len(K, slices), part);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
+                       const float* s2, const float* upart, int slices, const uint16_t* B,
+                       int64_t M, int64_t N, int64_t K, int r, float s, float* u_out, void* y,
+                       bool y_bf16, const Codebook& cb, hipStream_t st) {
+  const GemvArgs a{x, codes, q8, s2, upart, B, u_out, y, M, N, K, r, slices, s};
+  const dim3 grid((unsigned)((N + 15) / 16));
+  const size_t dyn = (size_t)M * r * 4 + (size_t)r * 16 * 2;  // s*u and the B columns
+  if (y_bf16)
+    hipLaunchKernelGGL(gemv_kernel<true>, grid, dim3(64 * kGvWaves), dyn, st, a, cb);
+  else
+    hipLaunchKernelGGL(gemv_kernel<false>, grid, dim3(64 * kGvWaves), dyn, st, a, cb);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -95,4 +95,21 @@ __device__ __forceinline__ void wait_vmem() {
 
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
+// sum_{k < n} p[k * stride], added in order k = 0, 1, ... starting from +0.
+// The loads of U consecutive terms are issued together (a plain loop with a
+// run-time trip count waits for each load in turn); the padding terms are +0
+// and leave the sum unchanged, so every U gives the same bits.
+template <int U>
+__device__ __forceinline__ float sum_strided(const float* __restrict__ p, int64_t stride, int n) {
+  float v = 0.0f;
+  for (int k0 = 0; k0 < n; k0 += U) {
+    float t[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) t[k] = k0 + k < n ? p[(int64_t)(k0 + k) * stride] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < U; ++k) v += t[k];
+  }
+  return v;
+}
+
 }  // namespace qlora

@@ -795,109 +795,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
   }
 }
 
-// ----------------------------------------------------------------- decode GEMV
-// M <= 16. A workgroup covers 64 weight rows and a 512-wide slice of K; wave w
-// owns rows n0 + 16w + c. The x slice [16 x 512] and the slice's 512 block
-// tables live in LDS; the codes stream from HBM with 16-byte loads, all
-// issued before any compute. MFMA rows are the (zero-padded) tokens.
-constexpr int kGemvKC = 512;
-constexpr int kGemvXS = kGemvKC + 8;
-
-__global__ __launch_bounds__(256) void gemv_fwd_kernel(const uint16_t* __restrict__ x,
-                                                       const uint8_t* __restrict__ codes,
-                                                       const int8_t* __restrict__ q8,
-                                                       const float* __restrict__ s2, int64_t M,
-                                                       int64_t N, int64_t K,
-                                                       float* __restrict__ partial, Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[16 * kGemvXS];
-  __shared__ __attribute__((aligned(16))) uint16_t tabs[64 * (kGemvKC / 64) * 16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 64;
-  const int split = blockIdx.y;
-  const int64_t ks0 = (int64_t)split * kGemvKC;
-  const int kc = (int)min((int64_t)kGemvKC, K - ks0);  // multiple of 64
-  const int nblk = kc / 64;
-  const int64_t KB = K / 64;
-  const int64_t n = n0 + 16 * w + c;
-
-  // Codes of this lane: row n, 4 x 32 nibbles at k = ks0 + 128*it + 32g.
-  u32x4_t cw[kGemvKC / 128];
-#pragma unroll
-  for (int it = 0; it < kGemvKC / 128; ++it) {
-    const int kk = 128 * it + 32 * g;
-    cw[it] = (n < N && kk < kc)
-                 ? *reinterpret_cast<const u32x4_t*>(codes + ((n * K + ks0 + kk) >> 1))
-                 : zero4();
-  }
-  // x slice into LDS: 16 rows x kc columns; rows >= M are zero.
-  for (int i = tid; i < 16 * (kGemvKC / 8); i += 256) {
-    const int row = i / (kGemvKC / 8), col = (i % (kGemvKC / 8)) * 8;
-    u32x4_t v = zero4();
-    if (row < M && col < kc) v = *reinterpret_cast<const u32x4_t*>(x + row * K + ks0 + col);
-    *reinterpret_cast<u32x4_t*>(&xs[row * kGemvXS + col]) = v;
-  }
-  // Tables: 64 rows x nblk blocks.
-  for (int i = tid; i < 64 * (kGemvKC / 64); i += 256) {
-    const int row = i & 63, blk = i >> 6;
-    const int64_t nn = n0 + row;
-    int qv = 0;
-    float sv = 0.0f;
-    if (nn < N && blk < nblk) {
-      const int64_t bi = nn * KB + ks0 / 64 + blk;
-      qv = q8[bi];
-      sv = s2[bi >> 8];
-    }
-    build_table(cb, qv, sv, &tabs[(row * (kGemvKC / 64) + blk) * 16]);
-  }
-  __syncthreads();
-
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t* trow = &tabs[(16 * w + c) * (kGemvKC / 64) * 16];
-#pragma unroll
-  for (int it = 0; it < kGemvKC / 128; ++it) {
-    const int kk = 128 * it + 32 * g;  // this lane's 32 k, all in one block
-    if (128 * it < kc) {
-      const uint16_t* tb = trow + (kk / 64) * 16;
-      const uint32_t wd[4] = {cw[it].x, cw[it].y, cw[it].z, cw[it].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4_t b = lut8(wd[q], tb);
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[c * kGemvXS + kk + 8 * q]);
-        acc = mfma_16x16x32(a, b, acc);
-      }
-    }
-  }
-  if (n < N) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * g + v;
-      if (m < M) partial[((int64_t)split * M + m) * N + n] = acc[v];
-    }
-  }
-}
-
-// y[m,n] = sum_split partial + s * sum_j u[m,j] B[j,n]
-template <bool kOutBf16>
-__global__ __launch_bounds__(256) void gemv_finalize_kernel(const float* __restrict__ partial,
-                                                            int splits,
-                                                            const float* __restrict__ u,
-                                                            const uint16_t* __restrict__ B,
-                                                            int64_t M, int64_t N, int r, float s,
-                                                            void* __restrict__ y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= M * N) return;
-  const int64_t m = i / N, n = i % N;
-  float acc = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) acc += partial[((int64_t)sp * M + m) * N + n];
-  float lo = 0.0f;
-  for (int j = 0; j < r; ++j) lo = __builtin_fmaf(u[m * r + j], bf16_lo(B[(int64_t)j * N + n]), lo);
-  const float v = __builtin_fmaf(s, lo, acc);
-  if (kOutBf16)
-    static_cast<uint16_t*>(y)[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
-  else
-    static_cast<float*>(y)[i] = v;
-}
-
 }  // namespace
 
 hipError_t launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
@@ -931,31 +828,6 @@ hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_
     hipLaunchKernelGGL(gemm_bwd_general_kernel<false>, grid, dim3(256), 0, st, dY, codes, q8, s2,
                        svlr, A, M, N, K, r, dX, cb);
   }
-  return hipGetLastError();
-}
-
-int gemv_splits(int64_t K) { return (int)((K + kGemvKC - 1) / kGemvKC); }
-
-hipError_t launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
-                           const float* s2, int64_t M, int64_t N, int64_t K, float* partial,
-                           const Codebook& cb, hipStream_t st) {
-  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)gemv_splits(K));
-  hipLaunchKernelGGL(gemv_fwd_kernel, grid, dim3(256), 0, st, x, codes, q8, s2, M, N, K, partial,
-                     cb);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv_finalize(const float* partial, int splits, const float* u,
-                                const uint16_t* B, int64_t M, int64_t N, int r, float s, void* y,
-                                bool y_bf16, hipStream_t st) {
-  const int64_t total = M * N;
-  const dim3 grid((unsigned)((total + 255) / 256));
-  if (y_bf16)
-    hipLaunchKernelGGL(gemv_finalize_kernel<true>, grid, dim3(256), 0, st, partial, splits, u, B,
-                       M, N, r, s, y);
-  else
-    hipLaunchKernelGGL(gemv_finalize_kernel<false>, grid, dim3(256), 0, st, partial, splits, u, B,
-                       M, N, r, s, y);
   return hipGetLastError();
 }
 

@@ -51,14 +51,17 @@ hipError_t launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const int8_t
                            int64_t N, int64_t K, int r, void* y, bool y_bf16, const Codebook& cb,
                            hipStream_t st);
 
-// Decode path (M <= 16): partial sums over K-slices, then a finalize kernel.
-int gemv_splits(int64_t K);
-hipError_t launch_gemv_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
-                           const float* s2, int64_t M, int64_t N, int64_t K, float* partial,
-                           const Codebook& cb, hipStream_t st);
-hipError_t launch_gemv_finalize(const float* partial, int splits, const float* u,
-                                const uint16_t* B, int64_t M, int64_t N, int r, float s, void* y,
-                                bool y_bf16, hipStream_t st);
+// Decode path (M <= 16), two launches: part[slice][m][j] = sum over one of
+// decode_down_slices(K) slices of K of x[m,k] A[k,j] (A [K,r] as given), then the GEMV with
+// y = x W_hat^T + s * (sum_slice part) B in its epilogue; u_out (if not NULL)
+// receives u = sum_slice part.
+int decode_down_slices(int64_t K);
+hipError_t launch_lora_down_decode(const uint16_t* x, const uint16_t* A, int64_t M, int64_t K,
+                                   int r, float* part, hipStream_t st);
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
+                       const float* s2, const float* upart, int slices, const uint16_t* B,
+                       int64_t M, int64_t N, int64_t K, int r, float s, float* u_out, void* y,
+                       bool y_bf16, const Codebook& cb, hipStream_t st);
 
 // dX = dY W_hat + [svlr-extended term with A].
 hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_t* q8,

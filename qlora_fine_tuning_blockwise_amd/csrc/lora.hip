@@ -121,8 +121,7 @@ __global__ __launch_bounds__(256) void lora_down_finalize_kernel(
     }
     return;
   }
-  float v = 0.0f;
-  for (int sl = 0; sl < slices; ++sl) v += part[(int64_t)sl * M * r + i];
+  const float v = sum_strided<8>(part + i, M * r, slices);
   if (out) out[i] = v;
   const float sv = s * v;
   const uint32_t hi = pack_bf16x2(sv, 0.0f) & 0xFFFFu;
@@ -273,9 +272,7 @@ __global__ __launch_bounds__(256) void colred_finalize_kernel(const float* __res
                                                               void* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index in [C, r] order
   if (i >= C * r) return;
-  float v = 0.0f;
-  for (int sl = 0; sl < slices; ++sl) v += part[(int64_t)sl * C * r + i];
-  v *= s;
+  const float v = s * sum_strided<8>(part + i, C * r, slices);
   const int64_t c = i / r;
   const int j = (int)(i % r);
   const int64_t o = transpose_out ? (int64_t)j * C + c : i;
