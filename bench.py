@@ -12,9 +12,18 @@ with LoRA r = 16, alpha = 32, A ~ N(0, 1/K), B ~ N(0, 0.01).
 `value` is the step's multiply-add work (2 flops per MAC; dequantization and
 quantization count no flops) over the measured step time, inputs resident in
 HBM. Per-call durations come from HIP events on the stream the library
-launches on; the roofline entry is the dominant call (the largest share of the
-step). The CPU baseline times the oracle on a bounded sample of the same
-workload.
+launches on. The roofline entry is the dominant kernel, the forward tile GEMM
+on the 11008x4096 weight (gemm_fwd_kernel, the longest single dispatch of the
+step), timed by the events around its call; `traffic` is that kernel's HBM
+bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters scaled by the
+same counters' reading for a copy of known size, and null when the kernel
+source no longer matches the one the counters were taken on. The CPU baseline
+times the oracle on a bounded sample of the same workload.
+
+Counter helpers: `--only CALL` runs one call of the step (e.g. fwd_train_up)
+for the timed iterations and prints its mean time; `--copy-calibration BYTES`
+runs a device-to-device copy of BYTES bytes (the reference reading for the
+counter scale).
 """
 from __future__ import annotations
 
@@ -31,6 +40,15 @@ if ROOT not in sys.path:
 METRIC = "NF4 dequant-GEMM TFLOP/s & GEMV weight GB/s (fraction of roofline) per layer"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+# HBM traffic of gemm_fwd_kernel per launch at x [4096,4096], W [11008,4096],
+# y fp32, from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled
+# by the counters' reading for a copy of known size. Valid while the tile
+# kernel source hashes to `src_sha256`.
+TRAFFIC = {"kernel": "gemm_fwd_kernel", "call": "fwd_train_up", "src": "gemm.hip",
+           "src_sha256": "5f9bf031da12838418fe315e1d3188fc07aec07147685ab53763fb51d6001baf",
+           "fetch_bytes": 662728704,   # 323598 KiB x 2.000 (copy reference)
+           "write_bytes": 225443840}   # 220160 KiB x 1.000 (copy reference)
 
 
 def log(*a):
@@ -51,7 +69,38 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the GEMV ring and bulk quantize/dequant bandwidth runs")
+    ap.add_argument("--only", default=None, help="run only this call of the step (counter runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="time a device copy of BYTES bytes and exit (counter scale reference)")
     return ap.parse_args()
+
+
+def kernel_src_sha(name):
+    import hashlib
+    path = os.path.join(ROOT, "qlora_fine_tuning_blockwise_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def copy_calibration(nbytes, steps):
+    import torch
+    dev = torch.device("cuda:0")
+    # an elementwise kernel (not a DMA copy) so that the L2 counters see it
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.bitwise_xor(src, 0, out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.bitwise_xor(src, 0, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "steps": steps,
+                      "ms": round(ms, 5), "gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
 
 
 def main():
@@ -60,6 +109,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     import numpy as np
     import torch
 
@@ -141,6 +193,25 @@ def main():
                           workspace=ws),
                       bwd_flops(Mt, N, K), 0))
     step_flops = sum(c[2] for c in calls)
+    if args.only:
+        sel = [c for c in calls if c[0] == args.only]
+        if not sel:
+            sys.exit(f"--only: no call named {args.only}; calls: {[c[0] for c in calls]}")
+        label, fn, flops, _ = sel[0]
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"call": label, "steps": args.steps, "ms": round(ms, 5),
+                          "tflops": round(flops / (ms * 1e-3) / 1e12, 2) if flops else None}),
+              flush=True)
+        return
 
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -185,14 +256,18 @@ def main():
             e["gbps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
             e["frac_hbm_peak"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
         breakdown[label] = e
-    # dominant call: the largest share of the step
-    dom = max(range(len(calls)), key=lambda i: per_call[i])
+    # dominant kernel: the forward tile GEMM on the larger weight
+    dom = [c[0] for c in calls].index(TRAFFIC["call"])
     dl, _, dflops, _ = calls[dom]
     dms = per_call[dom] / args.steps
     achieved = dflops / (dms * 1e-3) / 1e12
+    traffic = None
+    if TRAFFIC["src_sha256"] and TRAFFIC["src_sha256"] == kernel_src_sha(TRAFFIC["src"]):
+        traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel_call": dl, "flops_per_launch": dflops, "avg_ms": round(dms, 5)}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": TRAFFIC["kernel"], "kernel_call": dl,
+                "flops_per_launch": dflops, "avg_ms": round(dms, 5)}
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -297,20 +372,21 @@ def cpu_baseline(np, syn, cfg, step_flops, ms_step):
     r, alpha = cfg["r"], cfg["alpha"]
     Ms = 32
     flops = 0
-    t0 = time.perf_counter()
+    dt = 0.0
     for i, (name, (N, K)) in enumerate(cfg["weights"].items()):
         Wb = syn.normal_bf16((N, K), cfg["w_std"], syn.seed_of(3, i))
-        codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
-        What = oracle.dequant_dq(codes, q8, s2)[1].reshape(N, K)
         x = syn.normal_bf16((Ms, K), 1.0, syn.seed_of(3, 50))
         A = syn.normal_bf16((K, r), 1.0 / K ** 0.5, syn.seed_of(3, 10 + i))
         B = syn.normal_bf16((r, N), 0.01, syn.seed_of(3, 20 + i))
         dY = syn.normal_bf16((Ms, N), 1.0, syn.seed_of(3, 30 + i))
+        t0 = time.perf_counter()
+        codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+        What = oracle.dequant_dq(codes, q8, s2)[1].reshape(N, K)
         oracle.linear_fwd(x, What, A, B, r, alpha)
         oracle.linear_bwd(x, dY, What, A, B, r, alpha)
+        dt += time.perf_counter() - t0
         flops += 2 * Ms * N * K + 2 * Ms * r * (K + N)
         flops += 2 * Ms * N * K + 2 * Ms * r * (N + K) + 2 * Ms * K * r + 2 * Ms * N * r
-    dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"quantize+dequantize both weights in full, then fwd + bwd (dX, dA, dB) on "
                       f"{Ms} of 4096 token rows per weight; {flops / 1e9:.2f} GFLOP in "
