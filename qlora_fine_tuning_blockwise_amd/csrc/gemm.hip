@@ -163,30 +163,33 @@ __device__ __forceinline__ void store2(void* out, int64_t ld, int64_t m, int64_t
 //   Accumulator element e of lane l: row 32mt + 8(e/4) + 4h + e%4.
 //
 // Software pipeline of one step kb, three buffers of the x tile and tables:
-//   top:   DMA x(kb+2); load codes(kb+2) and the scales of kb+3 (12 vector
-//          memory instructions); build this wave's tables of step kb+1 from
-//          scales loaded two steps earlier.
+//   top:   wait for the previous step's loads; build this wave's tables of
+//          step kb+1 from scales loaded two steps earlier; DMA x(kb+2), load
+//          codes(kb+2) and the scales of kb+3 (14 vector memory instructions).
 //   body:  32 groups (s, mt): 2 MFMAs each on the B fragments of substep s,
 //          while the fragments of substep s+1 (or of step kb+1, substep 0)
 //          are looked up, 2 LUT reads per group.
-//   end:   wait until only this step's loads are in flight (x(kb+1) has
-//          landed), then barrier.
-// All waits are explicit counts of younger loads. The only ordering relied
-// on is that every load of a step is younger than every load of the steps
-// before it (loads within a step's issue block may be reordered). A wave only
-// reads tables its own threads build (rows 64w..64w+63), and LDS operations
-// of one wave complete in order, so tables need no barrier.
+//   end:   barrier (x(kb+1) landed at the top of the step).
+// Loads of a step have the whole next step to land. A wave only
+// reads tables its own threads build (its 4 KB region per buffer), and LDS
+// operations of one wave complete in order, so tables need no barrier.
+// Table layout: one 4-byte column per lane, 16 entries 256 bytes apart, so a
+// lookup instruction reads 64 distinct banks whatever the codes; the lookup
+// address is one byte permute of the code word (column offset in byte 0, code
+// and region bits in byte 1).
 template <bool kOutBf16>
 __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb) {
   __shared__ __attribute__((aligned(1024))) uint16_t xs0[kTileBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t xs1[kTileBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t xs2[kTileBytes / 2];
-  __shared__ __attribute__((aligned(32))) uint16_t tab0[256 * 16];
-  __shared__ __attribute__((aligned(32))) uint16_t tab1[256 * 16];
-  __shared__ __attribute__((aligned(32))) uint16_t tab2[256 * 16];
+  // The tables come first in LDS (largest alignment): lookup addresses then
+  // need no base added, it would not fit the 16-bit DS offset field.
+  __shared__ __attribute__((aligned(4096))) uint32_t tabs[3][4][16][64];  // [buffer][wave][entry][column]
+  __shared__ __attribute__((aligned(16))) float levels[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  if (tid < 16) levels[tid] = cb.level[tid];
   const int64_t KB = K / 64;
 
   // x DMA: instruction j of wave w, lane l -> slot (w*8+j)*64 + l -> row
@@ -214,9 +217,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
     row = n0 + row < N ? row : N - 1 - n0;
     coff[nt] = (uint32_t)((row * K) >> 1) + 16 * h;
   }
-  const int64_t trow = n0 + tid;
-  const bool trow_ok = trow < N;
-  const int64_t tbase = (trow_ok ? trow : N - 1) * KB;
+  // Scales of the lane's two weight rows (clamped; rows past N get zeros).
+  int64_t sbase[2];
+  bool srow_ok[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t row = n0 + 64 * w + 2 * c + nt;
+    srow_ok[nt] = row < N;
+    sbase[nt] = (row < N ? row : N - 1) * KB;
+  }
 
   // 8 vector-memory instructions
   auto issue_x = [&](int64_t kb, uint16_t* dst) {
@@ -231,12 +240,34 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) cr[nt] = *reinterpret_cast<const u32x4_t*>(src + coff[nt]);
   };
-  // 2 vector-memory instructions (unconditional; rows past N are zeroed when
+  // 4 vector-memory instructions (unconditional; rows past N are zeroed when
   // the table is built)
-  auto load_scale = [&](int64_t kb, int& qv, float& sv) {
-    const int64_t bi = tbase + kb;
-    qv = (int)p.q8[bi];
-    sv = p.s2[bi >> 8];
+  auto load_scale = [&](int64_t kb, int (&qv)[2], float (&sv)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t bi = sbase[nt] + kb;
+      qv[nt] = (int)p.q8[bi];
+      sv[nt] = p.s2[bi >> 8];
+    }
+  };
+  // Tables of one step: column t = lane of this wave holds entry e =
+  // {bf16(L[e] c1_hat(row 2c)), bf16(L[e] c1_hat(row 2c+1))} at byte
+  // 256 e + 4 t of the wave's 4 KB region; the two lanes of a column pair
+  // (c, c+32) hold the same rows, so lane (c, h) computes entries 8h..8h+7 and
+  // writes them to both columns.
+  auto build_cols = [&](const int (&qv)[2], const float (&sv)[2], uint32_t* region) {
+    const float ch0 = srow_ok[0] ? (float)qv[0] * sv[0] : 0.0f;
+    const float ch1 = srow_ok[1] ? (float)qv[1] * sv[1] : 0.0f;
+    const f32x4_t la = *reinterpret_cast<const f32x4_t*>(&levels[8 * h]);
+    const f32x4_t lb = *reinterpret_cast<const f32x4_t*>(&levels[8 * h + 4]);
+    const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+    uint32_t* col = region + 8 * h * 64 + c;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t v = pack_bf16x2(lv[j] * ch0, lv[j] * ch1);
+      col[j * 64] = v;
+      col[j * 64 + 32] = v;
+    }
   };
 
   f32x16_t acc[8][2];
@@ -247,12 +278,16 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][nt][e] = 0.0f;
 
-  // Lane-constant byte offsets: A fragment of substep s (row tile 0), and the
-  // table of this lane's weight row nt = 0 (row nt = 1 is 32 bytes further).
+  // Lane-constant byte offsets: A fragment of substep s (row tile 0); the
+  // lane's table column. Region bits of (buffer S, wave w): address bits
+  // 12..15 = 4S + w, or-ed into the high nibble of every code byte.
   int a_off[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) a_off[s] = c * 128 + (((4 * h + s) ^ (c & 7)) << 4);
-  const uint32_t t_byte = (uint32_t)(64 * w + 2 * c) * 32;
+  const uint32_t colbase = 4u * (uint32_t)lane;
+  const uint32_t region[3] = {0x10101010u * (uint32_t)w, 0x10101010u * (uint32_t)(4 + w),
+                              0x10101010u * (uint32_t)(8 + w)};
+  const char* tb = reinterpret_cast<const char*>(&tabs[0][0][0][0]);
 
   // One substep: 8 groups of (A fragment of row tile mt, 2 MFMAs) with B
   // fragments bc, while fragments bn are looked up from code words wn (the
@@ -261,42 +296,46 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
   // A fragments are read two groups ahead; LUT results are packed two groups
   // after they are issued.
   auto substep = [&](const char* xa, const u32x4_t (&bc)[2], u32x4_t (&bn)[2],
-                     const uint32_t (&wn)[2], const uint16_t* tarr) {
-    const char* tb = reinterpret_cast<const char*>(tarr);
+                     const uint32_t (&wn)[2], uint32_t rg) {
     u32x4_t a[3];
     a[0] = *reinterpret_cast<const u32x4_t*>(xa);
     a[1] = *reinterpret_cast<const u32x4_t*>(xa + 4096);
-    uint32_t lo[8], hi[8];
+    uint32_t lo[8], hi[8], clo = 0, chi = 0;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       if (mt + 2 < 8) a[(mt + 2) % 3] = *reinterpret_cast<const u32x4_t*>(xa + (mt + 2) * 4096);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_32x32x16(a[mt % 3], bc[nt], acc[mt][nt]);
       {
+        // group mt: byte q of the next code word of row f; its low nibble is
+        // element 2q, its high nibble element 2q+1; row f's value is the
+        // half f of the table entry
         const int f = mt >> 2, q = mt & 3;
-        const uint32_t base = t_byte + f * 32;  // 32-byte aligned: OR-ing the offset adds
-        const uint32_t wd = wn[f];
-        const uint32_t olo = q == 0 ? (((wd << 1) & 30u) | base) : (((wd >> (8 * q - 1)) & 30u) | base);
-        const uint32_t ohi = ((wd >> (8 * q + 3)) & 30u) | base;
-        lo[mt] = *reinterpret_cast<const uint16_t*>(tb + olo);
-        hi[mt] = *reinterpret_cast<const uint16_t*>(tb + ohi);
+        if (q == 0) {
+          clo = (wn[f] & 0x0F0F0F0Fu) | rg;
+          chi = ((wn[f] >> 4) & 0x0F0F0F0Fu) | rg;
+        }
+        const uint32_t sel = 0x0C0C0000u | ((uint32_t)(4 + q) << 8);
+        lo[mt] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(clo, colbase, sel) + 2 * f);
+        hi[mt] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(chi, colbase, sel) + 2 * f);
       }
-      if (mt >= 2) bn[(mt - 2) >> 2][(mt - 2) & 3] = lo[mt - 2] | (hi[mt - 2] << 16);
+      if (mt >= 2)
+        bn[(mt - 2) >> 2][(mt - 2) & 3] = __builtin_amdgcn_perm(hi[mt - 2], lo[mt - 2], 0x05040100u);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // A fragment read
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LUT reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // address / pack VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // address / pack VALU
     }
-    bn[1][2] = lo[6] | (hi[6] << 16);
-    bn[1][3] = lo[7] | (hi[7] << 16);
+    bn[1][2] = __builtin_amdgcn_perm(hi[6], lo[6], 0x05040100u);
+    bn[1][3] = __builtin_amdgcn_perm(hi[7], lo[7], 0x05040100u);
   };
 
   // Prologue: x(0), x(1) in flight; codes 0, 1; scales 0, 1, 2; table 0
   // built; B fragments of (step 0, substep 0) looked up. Per-step state lives
   // in three slots indexed by (step mod 3) so no loaded register is copied.
   u32x4_t cw[3][2];
-  int qs[3] = {0, 0, 0};
-  float ss[3] = {0.0f, 0.0f, 0.0f};
+  int qs[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+  float ss[3][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
   const int64_t kb1 = KB > 1 ? 1 : 0, kb2 = KB > 2 ? 2 : KB - 1;
   issue_x(0, xs0);
   issue_x(kb1, xs1);
@@ -306,11 +345,29 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
   load_scale(kb1, qs[1], ss[1]);
   load_scale(kb2, qs[2], ss[2]);
   wait_vmem<0>();
-  build_table(cb, trow_ok ? qs[0] : 0, ss[0], tab0 + tid * 16);
+  __syncthreads();  // codebook levels, x(0) and x(1) visible in every wave
+  build_cols(qs[0], ss[0], &tabs[0][w][0][0]);
   u32x4_t bf0[2], bf1[2];
+  {
+    // B fragments of (step 0, substep 0): the same lookups as a substep's
+    uint32_t v[2][8];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) bf0[nt] = lut8(cw[0][nt].x, tab0 + (64 * w + 2 * c + nt) * 16);
-  __syncthreads();  // x(0) and x(1) visible in every wave
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint32_t wd = cw[0][nt].x;
+      const uint32_t clo = (wd & 0x0F0F0F0Fu) | region[0];
+      const uint32_t chi = ((wd >> 4) & 0x0F0F0F0Fu) | region[0];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t sel = 0x0C0C0000u | ((uint32_t)(4 + q) << 8);
+        v[nt][2 * q] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(clo, colbase, sel) + 2 * nt);
+        v[nt][2 * q + 1] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(chi, colbase, sel) + 2 * nt);
+      }
+      bf0[nt] = u32x4_t{__builtin_amdgcn_perm(v[nt][1], v[nt][0], 0x05040100u),
+                        __builtin_amdgcn_perm(v[nt][3], v[nt][2], 0x05040100u),
+                        __builtin_amdgcn_perm(v[nt][5], v[nt][4], 0x05040100u),
+                        __builtin_amdgcn_perm(v[nt][7], v[nt][6], 0x05040100u)};
+    }
+  }
 
   // Every step issues the same 12 vector-memory instructions (indices past
   // the last step are clamped to it: those loads land in buffers never read),
@@ -321,29 +378,27 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
     const int64_t k3 = kb + 3 < KB ? kb + 3 : KB - 1;
     const char* x0 = reinterpret_cast<const char*>(pick3<S0>(xs0, xs1, xs2));
     uint16_t* const x2 = pick3<S2>(xs0, xs1, xs2);
-    uint16_t* const t0 = pick3<S0>(tab0, tab1, tab2);
-    uint16_t* const t1 = pick3<S1>(tab0, tab1, tab2);
+    // Tables of step kb+1 first, while nothing younger than the previous
+    // step's loads is in flight: the table stores (merged into write2) carry
+    // no alias scope, so they wait for every outstanding load, which here are
+    // loads issued a whole step earlier.
+    wait_vmem<0>();
+    build_cols(qs[S1], ss[S1], &tabs[S1][w][0][0]);
+    __builtin_amdgcn_sched_barrier(0);  // the table stores stay ahead of the new loads
     issue_x(k2, x2);
     load_codes(k2, cw[S2]);
     load_scale(k3, qs[S0], ss[S0]);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
-    // scales(kb+1) came two steps ago: 24 younger loads at most
-    wait_vmem<24>();
-    build_table(cb, trow_ok ? qs[S1] : 0, ss[S1], t1 + tid * 16);
     const uint32_t w1[2] = {cw[S0][0].y, cw[S0][1].y};
     const uint32_t w2[2] = {cw[S0][0].z, cw[S0][1].z};
     const uint32_t w3[2] = {cw[S0][0].w, cw[S0][1].w};
-    substep(x0 + a_off[0], bf0, bf1, w1, t0);
-    substep(x0 + a_off[1], bf1, bf0, w2, t0);
-    substep(x0 + a_off[2], bf0, bf1, w3, t0);
-    // codes(kb+1) were issued in the previous step; the scheduler may order
-    // loads freely within a step, so only "all of this step's 12 loads are
-    // younger" is certain
-    wait_vmem<12>();
+    substep(x0 + a_off[0], bf0, bf1, w1, region[S0]);
+    substep(x0 + a_off[1], bf1, bf0, w2, region[S0]);
+    substep(x0 + a_off[2], bf0, bf1, w3, region[S0]);
+    // codes(kb+1) and x(kb+1) were issued in the previous step and have
+    // landed (the wait at the top of this step)
     const uint32_t wn[2] = {cw[S1][0].x, cw[S1][1].x};
-    substep(x0 + a_off[3], bf1, bf0, wn, t1);
-    // only this step's 12 loads may be in flight: x(kb+1) has landed
-    wait_vmem<12>();
+    substep(x0 + a_off[3], bf1, bf0, wn, region[S1]);
     __builtin_amdgcn_s_barrier();
   };
   // Three unconditional steps per trip (so every path into a step has the
