@@ -46,9 +46,9 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # by the counters' reading for a copy of known size. Valid while the tile
 # kernel source hashes to `src_sha256`.
 TRAFFIC = {"kernel": "gemm_fwd_kernel", "call": "fwd_train_up", "src": "gemm.hip",
-           "src_sha256": "5f9bf031da12838418fe315e1d3188fc07aec07147685ab53763fb51d6001baf",
-           "fetch_bytes": 662728704,   # 323598 KiB x 2.000 (copy reference)
-           "write_bytes": 225443840}   # 220160 KiB x 1.000 (copy reference)
+           "src_sha256": "3000446b4d58e86e455debadfbf3cc250401c5ae1206664391741e999c28403b",
+           "fetch_bytes": 485529600,   # 237075 KiB x 2.000 (copy reference)
+           "write_bytes": 180355072}   # 176128 KiB x 1.000 (copy reference)
 
 
 def log(*a):

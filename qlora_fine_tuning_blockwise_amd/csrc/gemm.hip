@@ -5,18 +5,19 @@
 // time for the matmul); [P2] s3 "The Backward Pass Through Quantization"
 // (dequantize on the fly, compute in bf16, only adapter gradients).
 //
-// Structure shared by the forward and backward tile kernels:
-//  - a workgroup of 4 waves owns a 256 (M) x 256 (output columns) tile; each
-//    wave owns all 256 rows of its 64 columns, so every weight element of the
-//    tile is dequantized exactly once per workgroup, in registers, straight
-//    into the MFMA B operand - no bf16 copy of the weight goes through LDS;
-//  - the activation tile (x or dY, 256 x 64 bf16) is staged through LDS,
-//    double buffered, padded rows, and read as MFMA A operands;
-//  - per 64-wide reduction step each thread builds one 16-entry bf16 table
-//    (bf16(L[i] * c1_hat)) for one (weight row, block) into LDS; a code is
-//    dequantized by one LDS lookup, exactly as the standalone dequant kernel;
-//  - v_mfma_f32_16x16x32_bf16 with fp32 accumulators (256 per lane);
-//  - the LoRA term rides the same accumulators as extra reduction steps:
+//  - Forward (gemm_fwd_kernel): 512 x 128 output tiles; the NF4 weight tile
+//    is dequantized once per workgroup into a bf16 LDS tile shared by the four
+//    waves; x is staged through LDS with coalesced loads.
+//  - Backward dX (gemm_bwd_kernel): 256 x 256 output tiles; each wave owns
+//    all 256 rows of its 64 output columns and dequantizes its weight
+//    fragments in registers, straight into the MFMA B operand; the dY tile
+//    arrives by direct-to-LDS loads. gemm_bwd_general_kernel covers N not a
+//    multiple of 8.
+//  - All use v_mfma_f32_32x32x16_bf16 (16x16x32 in the general kernel) with
+//    fp32 accumulators. A code is dequantized by one LDS lookup in a 16-entry
+//    bf16 table (bf16(L[i] * c1_hat)) of its (row, block), exactly as the
+//    standalone dequant kernel.
+//  - The LoRA term rides the same accumulators as extra reduction steps:
 //    [s*u_hi | s*u_lo] (bf16 split of the fp32 adapter product) times the
 //    matching adapter columns.
 #include <type_traits>
@@ -87,20 +88,11 @@ __device__ __forceinline__ void store4(void* out, int64_t ld, int64_t m, int64_t
   }
 }
 
-// ----------------------------------------------------------------- forward
-// y[m,n] = sum_k x[m,k] w_hat[n,k] + sum_j ulr[m,j] Bt[n, j mod r]
-//
-// Workgroup tile 256 (M) x 256 (N), 4 waves; wave w owns output columns
-// n0 + 64w + 4c + t (c = lane%16, t = 0..3): MFMA t of a row tile holds column
-// 4c + t at lane column c, so each lane ends with 4 adjacent columns.
-// Reduction chunk for lane group g = lane/16 in half kf of a 64-wide step:
-// k = k0 + 16g + 8kf + (0..7), for both operands.
-//
-// The x tile (256 x 64 bf16 = 32 KB) arrives by direct-to-LDS DMA
+// Bytes of a 256 x 64 bf16 activation tile staged by direct-to-LDS loads
 // (global_load_lds_dwordx4: lane l of an instruction writes LDS bytes
-// [16l, 16l+16) of that instruction's 1 KB window), two buffers. Rows are 128 B;
-// 16-byte chunk c of row r sits at chunk slot c ^ (r & 7), so the 16 rows one
-// A-fragment read touches spread over all 32 banks. Rows past M are clamped to
+// [16l, 16l+16) of that instruction's 1 KB window). Rows are 128 B; 16-byte
+// chunk c of row r sits at chunk slot c ^ (r & 7), so the 16 rows one
+// A-fragment read touches spread over all banks. Rows past M are clamped to
 // row M-1 (their results are never stored).
 constexpr int kTileBytes = 256 * 128;
 
@@ -153,264 +145,277 @@ __device__ __forceinline__ void store2(void* out, int64_t ld, int64_t m, int64_t
   }
 }
 
-// Tile mapping (v_mfma_f32_32x32x16_bf16). Lane l = 32h + c of wave w:
-//   MFMA (mt, nt) covers rows m0 + 32mt + (0..31) and output columns
-//   n0 + 64w + 2c + nt: lane column c holds the adjacent pair 2c, 2c+1.
-//   Step = 64 reduction elements = 4 substeps s of 16; in substep s lane
-//   group h supplies the 8 elements k0 + 32h + 8s + (0..7) of both operands,
-//   so a lane's 32 elements of a step are contiguous: one 16-byte code load
-//   per weight row, one 16-byte x chunk (4h+s) per row tile.
-//   Accumulator element e of lane l: row 32mt + 8(e/4) + 4h + e%4.
+// ----------------------------------------------------------------- forward
+// y[m,n] = sum_k x[m,k] w_hat[n,k] + sum_j ulr[m,j] Bt[n, j mod r]
 //
-// Software pipeline of one step kb, three buffers of the x tile and tables:
-//   top:   wait for the previous step's loads; build this wave's tables of
-//          step kb+1 from scales loaded two steps earlier; DMA x(kb+2), load
-//          codes(kb+2) and the scales of kb+3 (14 vector memory instructions).
-//   body:  32 groups (s, mt): 2 MFMAs each on the B fragments of substep s,
-//          while the fragments of substep s+1 (or of step kb+1, substep 0)
-//          are looked up, 2 LUT reads per group.
-//   end:   barrier (x(kb+1) landed at the top of the step).
-// Loads of a step have the whole next step to land. A wave only
-// reads tables its own threads build (its 4 KB region per buffer), and LDS
-// operations of one wave complete in order, so tables need no barrier.
-// Table layout: one 4-byte column per lane, 16 entries 256 bytes apart, so a
-// lookup instruction reads 64 distinct banks whatever the codes; the lookup
-// address is one byte permute of the code word (column offset in byte 0, code
-// and region bits in byte 1).
+// Workgroup tile 512 (M) x 128 (N), reduction steps of 32; wave w owns rows
+// m0 + 128w .. +127 and all 128 columns (4 x 4 v_mfma_f32_32x32x16_bf16
+// tiles). Every weight element of the tile is dequantized once per
+// workgroup into a bf16 tile in LDS that all four waves read, so each
+// dequantized element feeds 512 rows of x.
+//
+// x tile (512 x 32 bf16 = 32 KB per step): coalesced 16-byte loads (four
+// lanes cover a row's 64 bytes) into registers one step ahead, stored to a
+// three-buffer LDS ring the step after; 16-byte chunk c of row r sits at
+// chunk slot c ^ ((r / 4) % 4), so the 16 rows of one fragment read fall in
+// distinct banks. Reduction order inside a step: lane group h = lane / 32
+// supplies elements k0 + 16h + 8s + (0..7) in substep s, for both operands.
+//
+// Dequantization role of a thread: tile row dr = 32w + lane/2, half
+// hb = lane % 2 of a step's 32 elements (16 codes = 8 bytes). The lane's
+// 16-entry table (bf16(L[e] c1_hat) of the row's current block) is a 4-byte
+// column of its wave's 4 KB LDS region: entry e at 256 e + 4 lane, the value
+// in the low half. A lookup instruction touches 64 distinct banks; its
+// address is one byte permute of the code word. The two lanes of a row build
+// 8 entries each and write both columns.
+//
+// Step kb reads x tile kb % 3 and bf16 tile kb % 3; it stores x(kb+2) (loaded
+// last step) and dequantizes step kb+2 into the rings, and prefetches the
+// fragments of (kb+1, substep 0), whose tiles were completed before the
+// previous barrier:
+//   issue x(kb+3) loads, codes(kb+3), (odd steps) scales of step kb+3; wait
+//   for the previous step's loads; store x(kb+2); on even steps build the
+//   tables of the block starting at step kb+2; substep 0: read the fragments
+//   of substep 1, issue the lookups of code word 0 of step kb+2, 16 MFMAs,
+//   pack and store; substep 1: read the fragments of (kb+1, 0), lookups of
+//   code word 1, 16 MFMAs, pack and store; barrier.
+constexpr int kF2BM = 512;
+constexpr int kF2BN = 128;
+constexpr int kF2Ld = 40;  // bf16 weight tile row stride (80 B): B reads of one instruction hit distinct banks
+constexpr int kF2Tile = kF2BN * kF2Ld;
+constexpr int kF2XTile = kF2BM * 32;  // x tile, bf16 elements
+
 template <bool kOutBf16>
 __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb) {
-  __shared__ __attribute__((aligned(1024))) uint16_t xs0[kTileBytes / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t xs1[kTileBytes / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t xs2[kTileBytes / 2];
   // The tables come first in LDS (largest alignment): lookup addresses then
-  // need no base added, it would not fit the 16-bit DS offset field.
-  __shared__ __attribute__((aligned(4096))) uint32_t tabs[3][4][16][64];  // [buffer][wave][entry][column]
+  // need no base added.
+  __shared__ __attribute__((aligned(16384))) uint32_t tabs[4][16][64];
+  __shared__ __attribute__((aligned(1024))) uint16_t xs[3 * kF2XTile];
+  __shared__ __attribute__((aligned(16))) uint16_t wt[3 * kF2Tile];
   __shared__ __attribute__((aligned(16))) float levels[16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 31, h = lane >> 5;
   const int64_t M = p.M, N = p.N, K = p.K;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
-  if (tid < 16) levels[tid] = cb.level[tid];
+  const int64_t m0 = (int64_t)blockIdx.y * kF2BM, n0 = (int64_t)blockIdx.x * kF2BN;
   const int64_t KB = K / 64;
+  const int nsteps = (int)(K / 32);
+  if (tid < 16) levels[tid] = cb.level[tid];
+  auto clamp = [&](int kb) { return kb < nsteps ? kb : nsteps - 1; };
 
-  // x DMA: instruction j of wave w, lane l -> slot (w*8+j)*64 + l -> row
-  // (w*8+j)*8 + l/8, stored chunk slot l%8 holding global chunk
-  // (l%8) ^ ((l/8)%8) (row & 7 == (l/8)%8).
-  const uint16_t* xrow0 = p.x + m0 * K;
-  uint32_t xoff[8];
-  {
-    const int chunk = (lane & 7) ^ ((lane >> 3) & 7);
-    const int64_t last = M - 1 - m0;
+  // x staging role: chunk q = tid + 256 j (j < 8) of the tile -> row q / 4,
+  // 16-byte chunk q % 4; rows past M read row M-1 (never stored).
+  const uint16_t* xsrc[8];
+  int xdst[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int64_t row = (w * 8 + j) * 8 + (lane >> 3);
-      row = row < last ? row : last;
-      xoff[j] = (uint32_t)(row * K + chunk * 8);
-    }
+  for (int j = 0; j < 8; ++j) {
+    const int q = tid + 256 * j, row = q >> 2, c = q & 3;
+    const int64_t grow = m0 + row < M ? m0 + row : M - 1;
+    xsrc[j] = p.x + grow * K + 8 * c;
+    xdst[j] = row * 32 + 8 * (c ^ ((row >> 2) & 3));
   }
-  // Code rows of this lane: n0 + 64w + 2c + nt (clamped; rows past N get an
-  // all-zero table), 16-byte segment at byte k0/2 + 16h.
-  const uint8_t* crow0 = p.codes + ((n0 * K) >> 1);
-  uint32_t coff[2];
+  u32x4_t xr[8];
+  auto load_x = [&](int kb) {
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    int64_t row = 64 * w + 2 * c + nt;
-    row = n0 + row < N ? row : N - 1 - n0;
-    coff[nt] = (uint32_t)((row * K) >> 1) + 16 * h;
-  }
-  // Scales of the lane's two weight rows (clamped; rows past N get zeros).
-  int64_t sbase[2];
-  bool srow_ok[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int64_t row = n0 + 64 * w + 2 * c + nt;
-    srow_ok[nt] = row < N;
-    sbase[nt] = (row < N ? row : N - 1) * KB;
-  }
-
-  // 8 vector-memory instructions
-  auto issue_x = [&](int64_t kb, uint16_t* dst) {
-    const uint16_t* src = xrow0 + kb * 64;
+    for (int j = 0; j < 8; ++j) xr[j] = *reinterpret_cast<const u32x4_t*>(xsrc[j] + 32 * kb);
+  };
+  auto store_x = [&](int tile) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_global_load_lds(src + xoff[j], dst + (w * 8 + j) * 512, 16, 0, 0);
+      *reinterpret_cast<u32x4_t*>(&xs[tile * kF2XTile + xdst[j]]) = xr[j];
   };
-  // 2 vector-memory instructions
-  auto load_codes = [&](int64_t kb, u32x4_t (&cr)[2]) {
-    const uint8_t* src = crow0 + kb * 32;
+  // A fragment of row tile mt, substep s: row 128w + 32mt + i, chunk 2h + s.
+  const int arow0 = 128 * w + i;
+  auto read_afrag = [&](int tile, int s, u32x4_t (&af)[4]) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) cr[nt] = *reinterpret_cast<const u32x4_t*>(src + coff[nt]);
-  };
-  // 4 vector-memory instructions (unconditional; rows past N are zeroed when
-  // the table is built)
-  auto load_scale = [&](int64_t kb, int (&qv)[2], float (&sv)[2]) {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t bi = sbase[nt] + kb;
-      qv[nt] = (int)p.q8[bi];
-      sv[nt] = p.s2[bi >> 8];
+    for (int mt = 0; mt < 4; ++mt) {
+      const int row = arow0 + 32 * mt;
+      af[mt] = *reinterpret_cast<const u32x4_t*>(
+          &xs[tile * kF2XTile + row * 32 + 8 * ((2 * h + s) ^ ((row >> 2) & 3))]);
     }
   };
-  // Tables of one step: column t = lane of this wave holds entry e =
-  // {bf16(L[e] c1_hat(row 2c)), bf16(L[e] c1_hat(row 2c+1))} at byte
-  // 256 e + 4 t of the wave's 4 KB region; the two lanes of a column pair
-  // (c, c+32) hold the same rows, so lane (c, h) computes entries 8h..8h+7 and
-  // writes them to both columns.
-  auto build_cols = [&](const int (&qv)[2], const float (&sv)[2], uint32_t* region) {
-    const float ch0 = srow_ok[0] ? (float)qv[0] * sv[0] : 0.0f;
-    const float ch1 = srow_ok[1] ? (float)qv[1] * sv[1] : 0.0f;
-    const f32x4_t la = *reinterpret_cast<const f32x4_t*>(&levels[8 * h]);
-    const f32x4_t lb = *reinterpret_cast<const f32x4_t*>(&levels[8 * h + 4]);
+
+  // dequantization role
+  const int dr = 32 * w + (lane >> 1), hb = lane & 1;
+  const bool drow_ok = n0 + dr < N;
+  const int64_t drow = drow_ok ? n0 + dr : N - 1;
+  const uint8_t* dcode = p.codes + drow * (K / 2) + 8 * hb;
+  const int64_t dblk = drow * KB;
+  u32x2_t cr[2];  // codes of step j in cr[j % 2]
+  int qv = 0;
+  float sv = 0.0f;
+  auto load_c = [&](int par, int kb) {
+    cr[par] = *reinterpret_cast<const u32x2_t*>(dcode + 16 * kb);
+  };
+  auto load_s = [&](int kb) {
+    const int64_t bi = dblk + kb / 2;
+    qv = (int)p.q8[bi];
+    sv = p.s2[bi >> 8];
+  };
+  const uint32_t colbase = 4u * (uint32_t)lane;
+  const uint32_t region = 0x10101010u * (uint32_t)w;
+  const char* tb = reinterpret_cast<const char*>(&tabs[0][0][0]);
+  auto build = [&]() {
+    const float ch = drow_ok ? (float)qv * sv : 0.0f;
+    const f32x4_t la = *reinterpret_cast<const f32x4_t*>(&levels[8 * hb]);
+    const f32x4_t lb = *reinterpret_cast<const f32x4_t*>(&levels[8 * hb + 4]);
     const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-    uint32_t* col = region + 8 * h * 64 + c;
+    uint32_t* col = &tabs[w][8 * hb][lane & ~1];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t v = pack_bf16x2(lv[j] * ch0, lv[j] * ch1);
-      col[j * 64] = v;
-      col[j * 64 + 32] = v;
+      const uint32_t v = pack_bf16x2(lv[j] * ch, 0.0f);
+      *reinterpret_cast<u32x2_t*>(col + j * 64) = u32x2_t{v, v};
     }
   };
-
-  f32x16_t acc[8][2];
+  // Lookups of the eight codes of code word cw (element e = nibble e).
+  auto lookup_issue = [&](uint32_t cw, uint32_t (&v)[8]) {
+    const uint32_t lo = (cw & 0x0F0F0F0Fu) | region;
+    const uint32_t hi = ((cw >> 4) & 0x0F0F0F0Fu) | region;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][nt][e] = 0.0f;
-
-  // Lane-constant byte offsets: A fragment of substep s (row tile 0); the
-  // lane's table column. Region bits of (buffer S, wave w): address bits
-  // 12..15 = 4S + w, or-ed into the high nibble of every code byte.
-  int a_off[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) a_off[s] = c * 128 + (((4 * h + s) ^ (c & 7)) << 4);
-  const uint32_t colbase = 4u * (uint32_t)lane;
-  const uint32_t region[3] = {0x10101010u * (uint32_t)w, 0x10101010u * (uint32_t)(4 + w),
-                              0x10101010u * (uint32_t)(8 + w)};
-  const char* tb = reinterpret_cast<const char*>(&tabs[0][0][0][0]);
-
-  // One substep: 8 groups of (A fragment of row tile mt, 2 MFMAs) with B
-  // fragments bc, while fragments bn are looked up from code words wn (the
-  // dword of each weight row holding the next substep's 8 codes) in table
-  // array tarr: group mt looks up dword mt%4 of fragment mt/4 (2 LUT reads).
-  // A fragments are read two groups ahead; LUT results are packed two groups
-  // after they are issued.
-  auto substep = [&](const char* xa, const u32x4_t (&bc)[2], u32x4_t (&bn)[2],
-                     const uint32_t (&wn)[2], uint32_t rg) {
-    u32x4_t a[3];
-    a[0] = *reinterpret_cast<const u32x4_t*>(xa);
-    a[1] = *reinterpret_cast<const u32x4_t*>(xa + 4096);
-    uint32_t lo[8], hi[8], clo = 0, chi = 0;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      if (mt + 2 < 8) a[(mt + 2) % 3] = *reinterpret_cast<const u32x4_t*>(xa + (mt + 2) * 4096);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_32x32x16(a[mt % 3], bc[nt], acc[mt][nt]);
-      {
-        // group mt: byte q of the next code word of row f; its low nibble is
-        // element 2q, its high nibble element 2q+1; row f's value is the
-        // half f of the table entry
-        const int f = mt >> 2, q = mt & 3;
-        if (q == 0) {
-          clo = (wn[f] & 0x0F0F0F0Fu) | rg;
-          chi = ((wn[f] >> 4) & 0x0F0F0F0Fu) | rg;
-        }
-        const uint32_t sel = 0x0C0C0000u | ((uint32_t)(4 + q) << 8);
-        lo[mt] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(clo, colbase, sel) + 2 * f);
-        hi[mt] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(chi, colbase, sel) + 2 * f);
-      }
-      if (mt >= 2)
-        bn[(mt - 2) >> 2][(mt - 2) & 3] = __builtin_amdgcn_perm(hi[mt - 2], lo[mt - 2], 0x05040100u);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // A fragment read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LUT reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // address / pack VALU
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t sel = 0x0C0C0000u | ((uint32_t)(4 + b) << 8);
+      v[2 * b] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(lo, colbase, sel));
+      v[2 * b + 1] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(hi, colbase, sel));
     }
-    bn[1][2] = __builtin_amdgcn_perm(hi[6], lo[6], 0x05040100u);
-    bn[1][3] = __builtin_amdgcn_perm(hi[7], lo[7], 0x05040100u);
+  };
+  auto pack = [&](const uint32_t (&v)[8]) {
+    return u32x4_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
+                   __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                   __builtin_amdgcn_perm(v[5], v[4], 0x05040100u),
+                   __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)};
+  };
+  const int wt_off = dr * kF2Ld + 16 * hb;  // this thread's 16 elements of a bf16 tile
+  const int fr_off = i * kF2Ld + 16 * h;    // this lane's B fragment of column tile 0
+  auto read_bfrag = [&](int tile, int s, u32x4_t (&bf)[4]) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      bf[nt] = *reinterpret_cast<const u32x4_t*>(&wt[tile * kF2Tile + fr_off + 32 * nt * kF2Ld + 8 * s]);
   };
 
-  // Prologue: x(0), x(1) in flight; codes 0, 1; scales 0, 1, 2; table 0
-  // built; B fragments of (step 0, substep 0) looked up. Per-step state lives
-  // in three slots indexed by (step mod 3) so no loaded register is copied.
-  u32x4_t cw[3][2];
-  int qs[3][2] = {{0, 0}, {0, 0}, {0, 0}};
-  float ss[3][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
-  const int64_t kb1 = KB > 1 ? 1 : 0, kb2 = KB > 2 ? 2 : KB - 1;
-  issue_x(0, xs0);
-  issue_x(kb1, xs1);
-  load_codes(0, cw[0]);
-  load_codes(kb1, cw[1]);
-  load_scale(0, qs[0], ss[0]);
-  load_scale(kb1, qs[1], ss[1]);
-  load_scale(kb2, qs[2], ss[2]);
-  wait_vmem<0>();
-  __syncthreads();  // codebook levels, x(0) and x(1) visible in every wave
-  build_cols(qs[0], ss[0], &tabs[0][w][0][0]);
-  u32x4_t bf0[2], bf1[2];
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.0f;
+
+  // Prologue: x tiles 0, 1 and bf16 tiles 0, 1 (block 0) in LDS; x(2) in
+  // registers; codes of step 2, scales of block 1; fragments of (0, 0).
   {
-    // B fragments of (step 0, substep 0): the same lookups as a substep's
-    uint32_t v[2][8];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const uint32_t wd = cw[0][nt].x;
-      const uint32_t clo = (wd & 0x0F0F0F0Fu) | region[0];
-      const uint32_t chi = ((wd >> 4) & 0x0F0F0F0Fu) | region[0];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t sel = 0x0C0C0000u | ((uint32_t)(4 + q) << 8);
-        v[nt][2 * q] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(clo, colbase, sel) + 2 * nt);
-        v[nt][2 * q + 1] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(chi, colbase, sel) + 2 * nt);
-      }
-      bf0[nt] = u32x4_t{__builtin_amdgcn_perm(v[nt][1], v[nt][0], 0x05040100u),
-                        __builtin_amdgcn_perm(v[nt][3], v[nt][2], 0x05040100u),
-                        __builtin_amdgcn_perm(v[nt][5], v[nt][4], 0x05040100u),
-                        __builtin_amdgcn_perm(v[nt][7], v[nt][6], 0x05040100u)};
-    }
-  }
-
-  // Every step issues the same 12 vector-memory instructions (indices past
-  // the last step are clamped to it: those loads land in buffers never read),
-  // so the wait counts are exact on every path.
-  auto step = [&](int64_t kb, auto slot) {
-    constexpr int S0 = decltype(slot)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
-    const int64_t k2 = kb + 2 < KB ? kb + 2 : KB - 1;
-    const int64_t k3 = kb + 3 < KB ? kb + 3 : KB - 1;
-    const char* x0 = reinterpret_cast<const char*>(pick3<S0>(xs0, xs1, xs2));
-    uint16_t* const x2 = pick3<S2>(xs0, xs1, xs2);
-    // Tables of step kb+1 first, while nothing younger than the previous
-    // step's loads is in flight: the table stores (merged into write2) carry
-    // no alias scope, so they wait for every outstanding load, which here are
-    // loads issued a whole step earlier.
+    load_c(0, 0);
+    load_c(1, clamp(1));
+    load_s(0);
+    load_x(0);
     wait_vmem<0>();
-    build_cols(qs[S1], ss[S1], &tabs[S1][w][0][0]);
-    __builtin_amdgcn_sched_barrier(0);  // the table stores stay ahead of the new loads
-    issue_x(k2, x2);
-    load_codes(k2, cw[S2]);
-    load_scale(k3, qs[S0], ss[S0]);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
-    const uint32_t w1[2] = {cw[S0][0].y, cw[S0][1].y};
-    const uint32_t w2[2] = {cw[S0][0].z, cw[S0][1].z};
-    const uint32_t w3[2] = {cw[S0][0].w, cw[S0][1].w};
-    substep(x0 + a_off[0], bf0, bf1, w1, region[S0]);
-    substep(x0 + a_off[1], bf1, bf0, w2, region[S0]);
-    substep(x0 + a_off[2], bf0, bf1, w3, region[S0]);
-    // codes(kb+1) and x(kb+1) were issued in the previous step and have
-    // landed (the wait at the top of this step)
-    const uint32_t wn[2] = {cw[S1][0].x, cw[S1][1].x};
-    substep(x0 + a_off[3], bf1, bf0, wn, region[S1]);
-    __builtin_amdgcn_s_barrier();
+    store_x(0);
+    load_x(clamp(1));
+    wait_vmem<0>();
+    store_x(1);
+    load_x(clamp(2));
+    __syncthreads();  // codebook levels
+    build();
+    uint32_t v0[8], v1[8], v2[8], v3[8];
+    lookup_issue(cr[0].x, v0);
+    lookup_issue(cr[0].y, v1);
+    lookup_issue(cr[1].x, v2);
+    lookup_issue(cr[1].y, v3);
+    *reinterpret_cast<u32x4_t*>(&wt[0 * kF2Tile + wt_off]) = pack(v0);
+    *reinterpret_cast<u32x4_t*>(&wt[0 * kF2Tile + wt_off + 8]) = pack(v1);
+    *reinterpret_cast<u32x4_t*>(&wt[1 * kF2Tile + wt_off]) = pack(v2);
+    *reinterpret_cast<u32x4_t*>(&wt[1 * kF2Tile + wt_off + 8]) = pack(v3);
+    load_c(0, clamp(2));
+    load_s(clamp(2));
+    wait_vmem<0>();
+    __syncthreads();
+  }
+  u32x4_t afa[4], afb[4], bfa[4], bfb[4];
+  read_afrag(0, 0, afa);
+  read_bfrag(0, 0, bfa);
+
+  // One substep: 16 MFMAs on fragments (ac, bc) while the fragments of the
+  // next substep (tile ntile, substep ns) are read into (an, bn) and the eight
+  // codes of word cw are looked up, packed and stored at wdst. Issue order
+  // (pinned with scheduling groups): eight times {MFMA, fragment read,
+  // address permute, lookup}, then four MFMAs, then four times {MFMA, pack},
+  // so no LDS result is waited for while MFMAs remain to be issued.
+  auto substep = [&](int ntile, int ns, uint32_t cw, const u32x4_t (&ac)[4], const u32x4_t (&bc)[4],
+                     u32x4_t (&an)[4], u32x4_t (&bn)[4], uint16_t* wdst) {
+    const uint32_t lo = (cw & 0x0F0F0F0Fu) | region;
+    const uint32_t hi = ((cw >> 4) & 0x0F0F0F0Fu) | region;
+    uint32_t v[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int mt = g >> 2, nt = g & 3;
+      acc[mt][nt] = mfma_32x32x16(ac[mt], bc[nt], acc[mt][nt]);
+      if (g < 4) {
+        const int row = arow0 + 32 * g;
+        an[g] = *reinterpret_cast<const u32x4_t*>(
+            &xs[ntile * kF2XTile + row * 32 + 8 * ((2 * h + ns) ^ ((row >> 2) & 3))]);
+      } else {
+        bn[g - 4] = *reinterpret_cast<const u32x4_t*>(
+            &wt[ntile * kF2Tile + fr_off + 32 * (g - 4) * kF2Ld + 8 * ns]);
+      }
+      const uint32_t sel = 0x0C0C0000u | ((uint32_t)(4 + (g >> 1)) << 8);
+      v[g] = *reinterpret_cast<const uint16_t*>(
+          tb + __builtin_amdgcn_perm((g & 1) ? hi : lo, colbase, sel));
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // fragment read
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // address permute
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // lookup
+    }
+#pragma unroll
+    for (int g = 8; g < 12; ++g) {
+      acc[g >> 2][g & 3] = mfma_32x32x16(ac[g >> 2], bc[g & 3], acc[g >> 2][g & 3]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    uint32_t pk[4];
+#pragma unroll
+    for (int g = 12; g < 16; ++g) {
+      acc[g >> 2][g & 3] = mfma_32x32x16(ac[g >> 2], bc[g & 3], acc[g >> 2][g & 3]);
+      const int b = g - 12;
+      pk[b] = __builtin_amdgcn_perm(v[2 * b + 1], v[2 * b], 0x05040100u);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // pack
+    }
+    *reinterpret_cast<u32x4_t*>(wdst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // Three unconditional steps per trip (so every path into a step has the
-  // same loads in flight), then the remaining one or two steps.
-  int64_t kb = 0;
-  for (; kb + 3 <= KB; kb += 3) {
+  auto step = [&](int kb, auto q6) {
+    constexpr int Q = decltype(q6)::value;  // kb % 6
+    constexpr int P2 = Q % 2, P3 = Q % 3;
+    constexpr int T1 = (P3 + 1) % 3, T2 = (P3 + 2) % 3;
+    // x(kb+2) is in registers (loaded last step): store it, then load x(kb+3)
+    wait_vmem<0>();
+    store_x(T2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(clamp(kb + 3));
+    load_c(P2 ^ 1, clamp(kb + 3));
+    if (P2 == 1) load_s(clamp(kb + 3));
+    __builtin_amdgcn_sched_barrier(0);
+    if (P2 == 0) build();  // step kb+2 starts a block
+    __builtin_amdgcn_sched_barrier(0);
+    const u32x2_t cn = cr[P2];
+    uint16_t* const wd = &wt[T2 * kF2Tile + wt_off];
+    substep(P3, 1, cn.x, afa, bfa, afb, bfb, wd);   // substep 0: prefetch (kb, 1)
+    substep(T1, 0, cn.y, afb, bfb, afa, bfa, wd + 8);  // substep 1: prefetch (kb+1, 0)
+    __syncthreads();
+  };
+  int kb = 0;
+  for (; kb + 6 <= nsteps; kb += 6) {
     step(kb, std::integral_constant<int, 0>());
     step(kb + 1, std::integral_constant<int, 1>());
     step(kb + 2, std::integral_constant<int, 2>());
+    step(kb + 3, std::integral_constant<int, 3>());
+    step(kb + 4, std::integral_constant<int, 4>());
+    step(kb + 5, std::integral_constant<int, 5>());
   }
-  if (kb < KB) step(kb, std::integral_constant<int, 0>());
-  if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>());
+  if (kb < nsteps) {
+    step(kb, std::integral_constant<int, 0>());
+    step(kb + 1, std::integral_constant<int, 1>());
+  }
+  if (kb + 2 < nsteps) {
+    step(kb + 2, std::integral_constant<int, 2>());
+    step(kb + 3, std::integral_constant<int, 3>());
+  }
 
   // Adapter term as 2r extra reduction elements, 16 per MFMA: lane group h
   // supplies elements 16q + 8h + (0..7).
@@ -418,30 +423,39 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
   for (int q = 0; q < r2 / 16; ++q) {
     const int jj = 16 * q + 8 * h;
     const int jb = jj % r;
-    u32x4_t bfr[2];
+    u32x4_t bfr[4];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t n = n0 + 64 * w + 2 * c + nt;
+    for (int nt = 0; nt < 4; ++nt) {
+      const int64_t n = n0 + 32 * nt + i;
       bfr[nt] = n < N ? *reinterpret_cast<const u32x4_t*>(p.Bt + n * r + jb) : zero4();
     }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const int64_t m = m0 + 32 * mt + c;
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t m = m0 + 128 * w + 32 * mt + i;
       const u32x4_t a = m < M ? *reinterpret_cast<const u32x4_t*>(p.ulr + m * r2 + jj) : zero4();
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_32x32x16(a, bfr[nt], acc[mt][nt]);
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_32x32x16(a, bfr[nt], acc[mt][nt]);
     }
   }
 
-  const int64_t ncol = n0 + 64 * w + 2 * c;
-  if (ncol < N) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+  for (int nt = 0; nt < 4; ++nt) {
+    const int64_t n = n0 + 32 * nt + i;
+    if (n < N) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m < M) store2<kOutBf16>(p.y, N, m, ncol, N, acc[mt][0][e], acc[mt][1][e]);
-      }
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t m = m0 + 128 * w + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (m < M) {
+            if (kOutBf16)
+              static_cast<uint16_t*>(p.y)[m * N + n] =
+                  (uint16_t)(pack_bf16x2(acc[mt][nt][e], 0.0f) & 0xFFFFu);
+            else
+              static_cast<float*>(p.y)[m * N + n] = acc[mt][nt][e];
+          }
+        }
+    }
   }
 }
 
@@ -856,8 +870,8 @@ hipError_t launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const int8_t
                            const float* s2, const uint16_t* ulr, const uint16_t* Bt, int64_t M,
                            int64_t N, int64_t K, int r, void* y, bool y_bf16, const Codebook& cb,
                            hipStream_t st) {
-  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
   const FwdArgs a{x, codes, q8, s2, ulr, Bt, y, M, N, K, r};
+  const dim3 grid((unsigned)((N + kF2BN - 1) / kF2BN), (unsigned)((M + kF2BM - 1) / kF2BM));
   if (y_bf16)
     hipLaunchKernelGGL(gemm_fwd_kernel<true>, grid, dim3(256), 0, st, a, cb);
   else
