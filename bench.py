@@ -12,18 +12,20 @@ with LoRA r = 16, alpha = 32, A ~ N(0, 1/K), B ~ N(0, 0.01).
 `value` is the step's multiply-add work (2 flops per MAC; dequantization and
 quantization count no flops) over the measured step time, inputs resident in
 HBM. Per-call durations come from HIP events on the stream the library
-launches on. The roofline entry is the dominant kernel, the forward tile GEMM
-on the 11008x4096 weight (gemm_fwd_kernel, the longest single dispatch of the
-step), timed by the events around its call; `traffic` is that kernel's HBM
-bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters scaled by the
-same counters' reading for a copy of known size, and null when the kernel
-source no longer matches the one the counters were taken on. The CPU baseline
-times the oracle on a bounded sample of the same workload.
+launches on. The roofline entry is the dominant kernel: the bf16 MFMA GEMM of
+the training forward on the 11008x4096 weight (gemm_nt_kernel, the longest
+single dispatch of the step), launched alone through qlora_gemm_bf16_nt on the
+same operands (x, the dequantized weight, the rank-r extension) and timed by
+HIP events around back-to-back launches; `traffic` is that kernel's HBM bytes per
+launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters scaled by the same
+counters' reading for a copy of known size, and null when the kernel source no
+longer matches the one the counters were taken on. The CPU baseline times the
+oracle on a bounded sample of the same workload.
 
 Counter helpers: `--only CALL` runs one call of the step (e.g. fwd_train_up)
-for the timed iterations and prints its mean time; `--copy-calibration BYTES`
-runs a device-to-device copy of BYTES bytes (the reference reading for the
-counter scale).
+or the roofline launch (gemm_nt_up) for the timed iterations and prints its
+mean time; `--copy-calibration BYTES` runs a device-to-device copy of BYTES
+bytes (the reference reading for the counter scale).
 """
 from __future__ import annotations
 
@@ -41,13 +43,13 @@ METRIC = "NF4 dequant-GEMM TFLOP/s & GEMV weight GB/s (fraction of roofline) per
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
-# HBM traffic of gemm_fwd_kernel per launch at x [4096,4096], W [11008,4096],
-# y fp32, from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled
-# by the counters' reading for a copy of known size. Valid while the tile
-# kernel source hashes to `src_sha256`.
-TRAFFIC = {"kernel": "gemm_fwd_kernel", "call": "fwd_train_up", "src": "gemm.hip",
-           "src_sha256": "3000446b4d58e86e455debadfbf3cc250401c5ae1206664391741e999c28403b",
-           "fetch_bytes": 485529600,   # 237075 KiB x 2.000 (copy reference)
+# HBM traffic of gemm_nt_kernel per launch at x [4096,4096], W [11008,4096]
+# bf16, y fp32, from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+# scaled by the counters' reading for a copy of known size. Valid while the
+# kernel source hashes to `src_sha256` (None: not measured for this source).
+TRAFFIC = {"kernel": "gemm_nt_kernel", "call": "gemm_nt_up", "src": "gemm_nt.hip",
+           "src_sha256": "76fd80344b6119f40b3a1a11f3e7741eb375c728c2c9be2d4de7cfb2f816a8c5",
+           "fetch_bytes": 593145856,   # 289622 KiB x 2.000 (copy reference)
            "write_bytes": 180355072}   # 176128 KiB x 1.000 (copy reference)
 
 
@@ -193,10 +195,21 @@ def main():
                           workspace=ws),
                       bwd_flops(Mt, N, K), 0))
     step_flops = sum(c[2] for c in calls)
+
+    # The roofline launch: the forward's dense stage on the up weight alone.
+    Nu, Ku = cfg["weights"]["up"]
+    q.qlora_dequant_bf16(nf4["up"], out=deq["up"])
+    e_up = syn.torch_normal_bf16((Mt, 2 * r), 0.01, syn.seed_of(3, 50), dev)
+    f_up = B["up"].t().contiguous()
+    y_up = torch.empty((Mt, Nu), dtype=torch.float32, device=dev)
+    roof = ("gemm_nt_up",
+            lambda: q.qlora_gemm_bf16_nt(x_train, deq["up"], e_up, f_up, y=y_up),
+            2 * Mt * Nu * Ku + 2 * Mt * (2 * r) * Nu, 0)
     if args.only:
-        sel = [c for c in calls if c[0] == args.only]
+        sel = [c for c in calls + [roof] if c[0] == args.only]
         if not sel:
-            sys.exit(f"--only: no call named {args.only}; calls: {[c[0] for c in calls]}")
+            sys.exit(f"--only: no call named {args.only}; "
+                     f"calls: {[c[0] for c in calls + [roof]]}")
         label, fn, flops, _ = sel[0]
         for _ in range(args.warmup):
             fn()
@@ -256,18 +269,27 @@ def main():
             e["gbps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
             e["frac_hbm_peak"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
         breakdown[label] = e
-    # dominant kernel: the forward tile GEMM on the larger weight
-    dom = [c[0] for c in calls].index(TRAFFIC["call"])
-    dl, _, dflops, _ = calls[dom]
-    dms = per_call[dom] / args.steps
+    # dominant kernel: the forward GEMM on the larger weight, launched alone
+    _, rfn, dflops, _ = roof
+    for _ in range(args.warmup):
+        rfn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        rfn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / args.steps
     achieved = dflops / (dms * 1e-3) / 1e12
     traffic = None
     if TRAFFIC["src_sha256"] and TRAFFIC["src_sha256"] == kernel_src_sha(TRAFFIC["src"]):
         traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": TRAFFIC["kernel"], "kernel_call": dl,
-                "flops_per_launch": dflops, "avg_ms": round(dms, 5)}
+                "traffic": traffic, "kernel": TRAFFIC["kernel"], "kernel_call": roof[0],
+                "shape": {"M": Mt, "N": Nu, "K": Ku, "r": r}, "flops_per_launch": dflops,
+                "avg_ms": round(dms, 5)}
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,

@@ -103,7 +103,8 @@ uint32_t qlora_codebook_id(void);
 
 /* Device workspace, in bytes, that qlora_linear_fwd (op = QLORA_OP_FWD) or
  * qlora_linear_bwd (op = QLORA_OP_BWD) needs for these sizes, assuming no
- * saved u. Host only; 0 on invalid sizes. */
+ * saved u. From M = 512 rows on it includes N*K*2 bytes for the dequantized
+ * weight (see qlora_gemm_bf16_nt). Host only; 0 on invalid sizes. */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
 
 /* Quantize once, at load time ([P4] "The mechanism": the pretrained weights
@@ -160,6 +161,27 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
                      const uint16_t* A, const uint16_t* B, int r, float alpha,
                      const float* u_saved, void* dX, int dx_dtype, void* dA, void* dB,
                      int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dense stage of the large-batch path: the product with a weight that is
+ * already dequantized ([P1] bullets: the 4-bit weight is expanded to bf16
+ * just in time, then multiplied in bf16 with fp32 accumulation; [P3] "How it
+ * works"), plus a rank extension:
+ *   y = a b^T + e [f | f]^T
+ *   a  [M,K] bf16, row stride lda elements;  b [N,K] bf16, row stride ldb
+ *      (for instance W_out of qlora_dequant_bf16);  e [M,2r] bf16;
+ *   f  [N,r] bf16;  y [M,N] fp32 or bf16 (y_dtype; bf16 is the
+ *      round-to-nearest-even of the fp32 result).
+ * From M = 512 rows on, qlora_linear_fwd dequantizes the weight once into
+ * its workspace and runs this stage with a = x, b = w_hat, f = B^T and e the
+ * two-term split [hi | lo] of (alpha/r) u (hi = bf16(v), lo = bf16(v - hi)),
+ * so that e [f|f]^T adds (hi + lo) B; qlora_linear_bwd does the same for dX
+ * with a = dY, b = w_hat^T, f = A. Requires K >= 32 and K % 32 == 0, lda and
+ * ldb multiples of 8 with 512*lda + 2*K < 2^31 (likewise ldb), lda, ldb >= K,
+ * r as for the linear entry points (QLORA_ERR_SHAPE / QLORA_ERR_RANK
+ * otherwise). M == 0 is a successful no-op. */
+int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
+                       const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t K,
+                       int r, void* y, int y_dtype, void* stream);
 
 #ifdef __cplusplus
 }

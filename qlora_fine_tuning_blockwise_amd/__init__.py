@@ -19,7 +19,7 @@ from . import _lib
 __all__ = [
     "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_id",
     "qlora_workspace_bytes", "qlora_quantize_nf4_dq", "qlora_dequant_bf16",
-    "qlora_linear_fwd", "qlora_linear_bwd", "NF4Weight",
+    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "NF4Weight",
 ]
 
 
@@ -155,3 +155,21 @@ def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: 
         _stream(stream))
     _lib.check(st, "qlora_linear_bwd")
     return dX, dA, dB
+
+
+def qlora_gemm_bf16_nt(a: torch.Tensor, b: torch.Tensor, e: torch.Tensor, f: torch.Tensor,
+                       y: torch.Tensor | None = None, y_dtype=torch.float32,
+                       stream=None) -> torch.Tensor:
+    """y = a b^T + e [f|f]^T. a [M,K], b [N,K], e [M,2r], f [N,r], all bf16."""
+    M, K = a.shape
+    N = b.shape[0]
+    r = f.shape[1]
+    if b.shape[1] != K or e.shape != (M, 2 * r) or f.shape[0] != N:
+        raise ValueError("qlora_gemm_bf16_nt: inconsistent shapes")
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=a.device)
+    st = _lib.load().qlora_gemm_bf16_nt(_ptr(a), K, _ptr(b), K, _ptr(e), _ptr(f), M, N, K, r,
+                                        _ptr(y), _dtype_code(y.dtype), _stream(stream))
+    _lib.check(st, "qlora_gemm_bf16_nt")
+    return y
+

@@ -36,6 +36,7 @@ SIGNATURES = {
     "qlora_linear_fwd": (INT, [P, P, P, I64, I64, P, I64, P, P, INT, FLT, P, INT, P, P, SZ, P]),
     "qlora_linear_bwd": (INT, [P, P, P, I64, I64, P, P, I64, P, P, INT, FLT, P, P, INT, P, P, INT,
                                P, SZ, P]),
+    "qlora_gemm_bf16_nt": (INT, [P, I64, P, I64, P, P, I64, I64, I64, INT, P, INT, P]),
 }
 
 _lib = None

@@ -11,6 +11,13 @@ namespace qlora {
 namespace {
 
 constexpr int64_t kGemvMaxM = 16;  // decode sizes take the GEMV path
+// From this many rows on, the weight is dequantized once into the workspace
+// and the product runs as a plain bf16 GEMM (the dequantization is then a
+// small share of the call); below it the tile kernels dequantize in place.
+constexpr int64_t kPlainMinM = 512;
+
+bool fwd_plain(int64_t M, int64_t K) { return M >= kPlainMinM && gemm_nt_supported(K, K, K); }
+bool bwd_plain(int64_t M, int64_t N) { return M >= kPlainMinM && gemm_nt_supported(N, N, N); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -31,8 +38,8 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, total = 0;
-  bool gemv_path = false;
+  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, W = 0, total = 0;
+  bool gemv_path = false, plain = false;
 };
 
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
@@ -47,13 +54,16 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
     L.down = c.take((size_t)lora_down_slices(K) * M * r * 4);
     L.Bt = c.take((size_t)N * r * 2);
     L.ulr = c.take((size_t)M * 2 * r * 2);
+    L.plain = fwd_plain(M, K);
+    if (L.plain) L.W = c.take((size_t)N * K * 2);
   }
   L.total = c.off;
   return L;
 }
 
 struct BwdLayout {
-  size_t At = 0, down = 0, v = 0, svlr = 0, vT = 0, uT = 0, col = 0, total = 0;
+  size_t At = 0, down = 0, v = 0, svlr = 0, vT = 0, uT = 0, col = 0, Wt = 0, total = 0;
+  bool plain = false;
 };
 
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
@@ -72,6 +82,8 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   L.vT = c.take(2 * (size_t)r * Mp * 2);
   L.uT = c.take(2 * (size_t)r * Mp * 2);
   L.col = c.take((size_t)colred_splits(M) * T * r * 4);
+  L.plain = bwd_plain(M, N);
+  if (L.plain) L.Wt = c.take((size_t)K * N * 2);
   L.total = c.off;
   return L;
 }
@@ -200,8 +212,13 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
     if (e == hipSuccess)
       e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, u, ulr, nullptr, st);
     if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
-    if (e == hipSuccess)
+    if (e == hipSuccess && L.plain) {
+      uint16_t* W = at<uint16_t>(workspace, L.W);
+      e = launch_dequant(codes, absmax_q, absmax_scale, N * K, W, *cb, st);
+      if (e == hipSuccess) e = launch_gemm_nt(x, K, W, K, ulr, Bt, M, N, K, r, y, ybf, st);
+    } else if (e == hipSuccess) {
       e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, *cb, st);
+    }
   }
   return launch_status(e);
 }
@@ -254,9 +271,15 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
   if (e == hipSuccess)
     e = launch_lora_down_finalize(down, lora_down_slices(N), M, r, s, v, svlr, dA ? vT : nullptr,
                                   st);
-  if (e == hipSuccess && dX)
+  if (e == hipSuccess && dX && L.plain) {  // dX = dY w_hat through w_hat^T [K,N]
+    uint16_t* Wt = at<uint16_t>(workspace, L.Wt);
+    e = launch_dequant_t(codes, absmax_q, absmax_scale, N, K, Wt, *cb, st);
+    if (e == hipSuccess)
+      e = launch_gemm_nt(dY, N, Wt, N, svlr, A, M, K, N, r, dX, dx_dtype == QLORA_DTYPE_BF16, st);
+  } else if (e == hipSuccess && dX) {
     e = launch_gemm_bwd(dY, codes, absmax_q, absmax_scale, svlr, A, M, N, K, r, dX,
                         dx_dtype == QLORA_DTYPE_BF16, *cb, st);
+  }
   if (e == hipSuccess && dA) {  // dA = x^T (s v)
     e = launch_colred(x, vT, M, K, r, col, st);
     if (e == hipSuccess)
@@ -283,6 +306,22 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
       e = launch_colred_finalize(col, colred_splits(M), N, r, 1.0f, true, dB, gbf, st);
   }
   return launch_status(e);
+}
+
+int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
+                       const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t K,
+                       int r, void* y, int y_dtype, void* stream) {
+  if (M < 0 || N < 1 || K < 1) return M < 0 ? QLORA_ERR_INVALID_ARG : QLORA_ERR_SHAPE;
+  if (lda < K || ldb < K || !gemm_nt_supported(K, lda, ldb)) return QLORA_ERR_SHAPE;
+  if (y_dtype != QLORA_DTYPE_F32 && y_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
+  if (!rank_ok(r)) return QLORA_ERR_RANK;
+  if (M == 0) return QLORA_OK;
+  if (!a || !b || !e || !f || !y) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(e) || !aligned16(f) || !aligned16(y))
+    return QLORA_ERR_ALIGN;
+  return launch_status(launch_gemm_nt(a, lda, b, ldb, e, f, M, N, K, r, y,
+                                      y_dtype == QLORA_DTYPE_BF16,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,4 +1,6 @@
-// Dequantize-into-MFMA kernels of the QLoRA linear layer on gfx950.
+// Dequantize-into-MFMA kernels of the QLoRA linear layer on gfx950, used for
+// 16 < M < 512 rows (from 512 rows on the weight is dequantized once and the
+// plain GEMM of gemm_nt.hip runs instead).
 //
 // [P1] "QLoRA" forward equation h = W_hat x + (alpha/r) B(Ax) and bullets
 // ("Compute never happens in 4-bit": the weight is dequantized to bf16 just in

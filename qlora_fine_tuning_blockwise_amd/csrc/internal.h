@@ -69,6 +69,18 @@ hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_
                            int64_t N, int64_t K, int r, void* dX, bool dx_bf16,
                            const Codebook& cb, hipStream_t st);
 
+// Large-M path: plain bf16 GEMM y[M,N] = a[M,Kr] b[N,Kr]^T + e[M,2r] [f|f][N,2r]^T
+// (a, b row-major with row strides lda, ldb; e the two-term split written by
+// launch_lora_down_finalize; f [N,r]). gemm_nt_supported says whether the
+// shape fits the kernel (Kr a multiple of 32, 16-byte aligned rows).
+bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb);
+hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
+                          const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t Kr,
+                          int r, void* y, bool y_bf16, hipStream_t st);
+// out[k][n] = w_hat[n][k] as bf16 ([K, N], the transpose of launch_dequant's output).
+hipError_t launch_dequant_t(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t N,
+                            int64_t K, uint16_t* out, const Codebook& cb, hipStream_t st);
+
 // Adapter gradients: part[split][c][j] = sum_{m in split} X[m][c] * P[m][j]
 // (X [M,C] bf16; P given as the transposed two-term bf16 split PT [2r, Mp]
 // written by launch_lora_down_finalize), then out = s * sum_split part,

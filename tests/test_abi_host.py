@@ -119,12 +119,38 @@ def test_bwd_validation(lib):
     assert call(19, 64) == 6           # workspace too small
 
 
+def test_gemm_nt_validation(lib):
+    f = lib.qlora_gemm_bf16_nt
+    base = [_p(FAKE), 64, _p(FAKE), 64, _p(FAKE), _p(FAKE), 8, 128, 64, 16, _p(FAKE), 0, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(6, -1) == 1            # M < 0
+    assert call(7, 0) == 2             # N < 1
+    assert call(8, 48) == 2            # K % 32
+    assert call(1, 32) == 2            # lda < K
+    assert call(3, 68) == 2            # ldb % 8
+    assert call(1, 1 << 22) == 2       # tile row offsets past 2^31 bytes
+    assert call(11, 3) == 4            # y dtype
+    assert call(9, 8) == 5             # r
+    assert call(0, None) == 1          # a missing
+    assert call(4, _p(FAKE + 8)) == 3  # e misaligned
+    assert call(6, 0) == 0             # empty: a no-op
+
+
 def test_workspace_query(lib):
     assert q.qlora_workspace_bytes(0, 16, 4096, 4096, 16) > 0
     assert q.qlora_workspace_bytes(0, 4096, 4096, 4096, 16) > q.qlora_workspace_bytes(0, 1024, 4096, 4096, 16)
     assert q.qlora_workspace_bytes(1, 4096, 11008, 4096, 16) > 0
     assert q.qlora_workspace_bytes(0, 16, 4096, 4000, 16) == 0
     assert q.qlora_workspace_bytes(2, 16, 4096, 4096, 16) == 0
+    # from 512 rows on the dequantized weight lives in the workspace
+    for op in (0, 1):
+        big = q.qlora_workspace_bytes(op, 512, 4096, 1024, 16)
+        small = q.qlora_workspace_bytes(op, 511, 4096, 1024, 16)
+        assert big - small >= 4096 * 1024 * 2
 
 
 @pytest.fixture(scope="module")

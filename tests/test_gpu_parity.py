@@ -4,8 +4,9 @@ Bit-exact: NF4 codes, 8-bit absmax codes, second-level scales, dequantized
 bf16. Tolerance (fp32 outputs): relative Frobenius error <= 2e-3 and max
 element error <= 1e-2 x RMS of the oracle output, for y, dX, dA, dB.
 """
-import os
 import concurrent.futures as cf
+import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -265,7 +266,9 @@ def test_fwd_decode_llama7b(M, name):
 
 
 @pytest.mark.parametrize("M,N,K,r", [(17, 320, 640, 16), (300, 100, 192, 32), (256, 512, 1024, 64),
-                                     (33, 1024, 128, 16), (8, 72, 64, 16)])
+                                     (33, 1024, 128, 16), (8, 72, 64, 16),
+                                     # large-M path: ragged tile rows and columns, step tails
+                                     (600, 520, 192, 16), (512, 256, 64, 32), (700, 300, 1024, 64)])
 def test_fwd_full_small(M, N, K, r):
     say("fwd small", M, N, K, r)
     P = Problem(N, K, r, 32.0, seed=M + N + K)
@@ -311,7 +314,7 @@ def test_fwd_one_hot_rows_exact_gemm_and_gemv():
     N, K, r = 512, 1024, 16
     P = Problem(N, K, r, 32.0, seed=5)
     P.Bt = torch.zeros_like(P.Bt)
-    for M in (16, 64):
+    for M in (16, 64, 600):
         ks = np.random.default_rng(M).choice(K, M, replace=False)
         x = np.zeros((M, K), np.uint16)
         x[np.arange(M), ks] = 0x3F80
@@ -332,11 +335,39 @@ def test_fwd_lora_only_isolated():
         tol_check(y, yo, f"lora-only M={M}")
 
 
-def test_fwd_deterministic():
+@pytest.mark.parametrize("M", [300, 600])
+def test_fwd_deterministic(M):
     P = Problem(1024, 1024, 16, 32.0, seed=3)
-    x = syn.normal_bf16((300, 1024), 1.0, 4)
+    x = syn.normal_bf16((M, 1024), 1.0, 4)
     a, b = run_fwd(P, x), run_fwd(P, x)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("M,N,K,r,pad", [(300, 520, 96, 16, 0), (513, 256, 64, 32, 24),
+                                         (256, 256, 32, 16, 0), (40, 1030, 320, 64, 8)])
+def test_gemm_bf16_nt_dense_stage(M, N, K, r, pad):
+    """The dense stage on its own: y = a b^T + e [f|f]^T against the fp64
+    product of the same bf16 inputs; a given with a row stride K + pad."""
+    say("gemm nt", M, N, K, r, pad)
+    a_full = syn.normal_bf16((M, K + pad), 1.0, 50 + M)
+    b = syn.normal_bf16((N, K), 0.05, 51 + N)
+    e = syn.normal_bf16((M, 2 * r), 1.0, 52 + r)
+    f = syn.normal_bf16((N, r), 0.1, 53 + K)
+    at, bt, et, ft = dev_bf16(a_full), dev_bf16(b), dev_bf16(e), dev_bf16(f)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    L = q._lib.load()
+    P_ = ctypes.c_void_p
+    st = L.qlora_gemm_bf16_nt(P_(at.data_ptr()), K + pad, P_(bt.data_ptr()), K, P_(et.data_ptr()),
+                              P_(ft.data_ptr()), M, N, K, r, P_(y.data_ptr()), 0,
+                              P_(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    f64 = lambda v: oracle.bf16_to_f32(v).astype(np.float64)
+    ref = f64(a_full[:, :K]) @ f64(b).T + f64(e) @ np.concatenate([f64(f), f64(f)], 1).T
+    tol_check(host(y), ref, f"gemm nt {M}x{N}x{K}")
+    if pad == 0:
+        yb = q.qlora_gemm_bf16_nt(at, bt, et, ft, y_dtype=torch.bfloat16)
+        assert torch.equal(yb, y.to(torch.bfloat16))
 
 
 # ------------------------------------------------------------------ backward
@@ -348,7 +379,9 @@ def run_bwd(P, x, dY, **kw):
 
 
 @pytest.mark.parametrize("M,N,K,r", [(16, 1024, 1024, 16), (300, 100, 192, 32), (64, 512, 640, 64),
-                                     (8, 72, 64, 16), (257, 256, 256, 16)])
+                                     (8, 72, 64, 16), (257, 256, 256, 16),
+                                     # large-M path (reduction over N = 544, 320)
+                                     (600, 544, 192, 16), (520, 320, 640, 32)])
 def test_bwd_full_small(M, N, K, r):
     say("bwd small", M, N, K, r)
     P = Problem(N, K, r, 24.0, seed=M + 2 * N + K)
@@ -403,11 +436,11 @@ def test_bwd_train_llama7b(name):
     tol_check(host(dB), g["dB"], f"dB train {name}")
 
 
-def test_bwd_one_hot_dy_rows_exact():
-    N, K, r = 320, 512, 16
+@pytest.mark.parametrize("M,N", [(40, 320), (600, 640)])
+def test_bwd_one_hot_dy_rows_exact(M, N):
+    K, r = 512, 16
     P = Problem(N, K, r, 32.0, seed=11)
     P.Bt = torch.zeros_like(P.Bt)
-    M = 40
     ns = np.random.default_rng(4).choice(N, M, replace=False)
     dY = np.zeros((M, N), np.uint16)
     dY[np.arange(M), ns] = 0x3F80
