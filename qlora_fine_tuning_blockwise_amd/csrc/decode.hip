@@ -241,7 +241,8 @@ __global__ __launch_bounds__(512, 4) void gemv_kernel(GemvArgs p, Codebook cb) {
   };
 
   // The weight stream is issued first; the adapter operands (read only in
-  // the epilogue) load behind it.
+  // the epilogue) load behind it into registers and are consumed after the
+  // weight work, so their latency overlaps it.
   if (nch > 0) {
     load_codes(0, 0);
     load_codes(1, min((int64_t)1, nch - 1));
@@ -250,24 +251,25 @@ __global__ __launch_bounds__(512, 4) void gemv_kernel(GemvArgs p, Codebook cb) {
   // u = sum of the slices in order (same bits as the finalize kernel's sum);
   // the loads use clamped slice indices so that they are issued
   // unconditionally, the padding terms are +0.
-  auto usum = [&](int idx) {
-    float t[kDecMaxSlices];
+  auto uload = [&](int idx, float (&t)[kDecMaxSlices]) {
 #pragma unroll
     for (int k = 0; k < kDecMaxSlices; ++k) t[k] = p.upart[(int64_t)min(k, p.slices - 1) * mr + idx];
+  };
+  auto ustore = [&](int idx, const float (&t)[kDecMaxSlices]) {
     float u = 0.0f;
 #pragma unroll
     for (int k = 0; k < kDecMaxSlices; ++k) u += k < p.slices ? t[k] : 0.0f;
     us[idx] = p.s * u;
     if (p.u_out && blockIdx.x == 0) p.u_out[idx] = u;
   };
-  auto bload = [&](int idx) {
+  auto bval = [&](int idx) {
     const int j = idx >> 4, nl = idx & 15;
-    bs[idx] = p.B[(int64_t)j * N + min(n0 + nl, N - 1)];
+    return p.B[(int64_t)j * N + min(n0 + nl, N - 1)];
   };
-  if (tid < mr) usum(tid);
-  if (tid < r * 16) bload(tid);
-  for (int idx = tid + 512; idx < mr; idx += 512) usum(idx);       // M * r > 512
-  for (int idx = tid + 512; idx < r * 16; idx += 512) bload(idx);  // r > 32
+  float ut[kDecMaxSlices];
+  uint16_t bv = 0;
+  if (tid < mr) uload(tid, ut);
+  if (tid < r * 16) bv = bval(tid);
   if (nch > 0) {
     if (nch <= 2) {
       pair(0, false);
@@ -275,6 +277,13 @@ __global__ __launch_bounds__(512, 4) void gemv_kernel(GemvArgs p, Codebook cb) {
       for (int64_t c0 = 0; c0 < nch; c0 += 2) pair(c0, true);
     }
   }
+  if (tid < mr) ustore(tid, ut);
+  if (tid < r * 16) bs[tid] = bv;
+  for (int idx = tid + 512; idx < mr; idx += 512) {  // M * r > 512
+    uload(idx, ut);
+    ustore(idx, ut);
+  }
+  for (int idx = tid + 512; idx < r * 16; idx += 512) bs[idx] = bval(idx);  // r > 32
 
   // Cross-wave sum (each wave's partial tile goes to its own table region,
   // which only it reads), adapter term, store. acc[v] = y partial for token

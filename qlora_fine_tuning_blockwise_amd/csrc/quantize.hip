@@ -170,44 +170,68 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   if (tid == 0) s2[g] = sc;
 }
 
-// Dequantize: a workgroup covers 128 blocks; two threads per block. Each
-// thread builds half of its block's 16-entry bf16 table in LDS, then expands
-// 32 codes (one 16-byte load) into 32 bf16 values (four 16-byte stores).
+// Dequantize. Lane j (0..7) of an 8-lane group takes code word j (codes
+// 8j..8j+7) of one block, so a wave covers 8 consecutive blocks per pass:
+// 256 bytes of codes in and 1 KB of bf16 out, both contiguous. Each block's
+// 16-entry bf16 table (bf16(L[i] * c1_hat)) sits at bytes 32g of the pass's
+// 256-byte LDS region (g = block within the pass): the 8 tables fill one row
+// of the 64 LDS banks, and a group only reads its own table, so every lookup
+// instruction is free of bank conflicts. Lane j writes entries 2j and 2j+1;
+// its group reads them back in the same wave (LDS keeps a wave's order). A
+// lookup address is one v_perm: byte 0 = 32g + 2*code (computed four codes
+// at a time), bytes 1..3 = the region's offset. Each wave runs kDqPasses
+// passes with every load issued first. Lanes past the last block redo the
+// last block (same values to the same place), so no lane branches.
+constexpr int kDqPasses = 4;
+
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const int8_t* __restrict__ q8,
                                                       const float* __restrict__ s2,
                                                       int64_t nblocks, uint16_t* __restrict__ out,
                                                       Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint16_t tab[128 * 16];
-  const int tid = threadIdx.x;
-  const int lb = tid >> 1, half = tid & 1;
-  const int64_t b = (int64_t)blockIdx.x * 128 + lb;
-  const bool valid = b < nblocks;
-  u32x4_t c = zero4();
-  float ch = 0.0f;
-  if (valid) {
-    c = *reinterpret_cast<const u32x4_t*>(codes + b * 32 + half * 16);
-    ch = (float)q8[b] * s2[b >> 8];
-  }
-  {
-    float l[8];
+  __shared__ __attribute__((aligned(1024))) uint32_t tab[4 * kDqPasses * 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 3, j = lane & 7;
+  const int64_t b0 = ((int64_t)blockIdx.x * 4 + w) * (8 * kDqPasses) + g;
+  int64_t bk[kDqPasses];
+  uint32_t cw[kDqPasses];
+  float ch[kDqPasses];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) l[i] = half ? cb.level[8 + i] : cb.level[i];
-    u32x4_t t;
-    t.x = pack_bf16x2(l[0] * ch, l[1] * ch);
-    t.y = pack_bf16x2(l[2] * ch, l[3] * ch);
-    t.z = pack_bf16x2(l[4] * ch, l[5] * ch);
-    t.w = pack_bf16x2(l[6] * ch, l[7] * ch);
-    *reinterpret_cast<u32x4_t*>(&tab[lb * 16 + half * 8]) = t;
+  for (int p = 0; p < kDqPasses; ++p) {
+    bk[p] = b0 + 8 * p < nblocks ? b0 + 8 * p : nblocks - 1;
+    cw[p] = reinterpret_cast<const uint32_t*>(codes)[bk[p] * 8 + j];
+    ch[p] = (float)q8[bk[p]] * s2[bk[p] >> 8];
   }
-  __syncthreads();
-  if (valid) {
-    const uint16_t* tb = &tab[lb * 16];
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + b * 64 + half * 32);
-    dst[0] = lut8(c.x, tb);
-    dst[1] = lut8(c.y, tb);
-    dst[2] = lut8(c.z, tb);
-    dst[3] = lut8(c.w, tb);
+  // levels 2j and 2j+1 of this lane (uniform values, selected per lane)
+  float l0 = cb.level[0], l1 = cb.level[1];
+#pragma unroll
+  for (int jj = 1; jj < 8; ++jj)
+    if (j == jj) {
+      l0 = cb.level[2 * jj];
+      l1 = cb.level[2 * jj + 1];
+    }
+  const char* tb = reinterpret_cast<const char*>(tab);
+  const uint32_t gb = 0x01010101u * (uint32_t)(32 * g);
+#pragma unroll
+  for (int p = 0; p < kDqPasses; ++p)
+    tab[(w * kDqPasses + p) * 64 + 8 * g + j] = pack_bf16x2(l0 * ch[p], l1 * ch[p]);
+#pragma unroll
+  for (int p = 0; p < kDqPasses; ++p) {
+    const uint32_t region = (uint32_t)(w * kDqPasses + p) * 256u;  // low byte 0
+    const uint32_t tl = ((cw[p] & 0x0F0F0F0Fu) << 1) + gb;        // 32g + 2*code, per byte
+    const uint32_t th = (((cw[p] >> 4) & 0x0F0F0F0Fu) << 1) + gb;
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t sel = 0x03020104u + (uint32_t)k;
+      v[2 * k] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(tl, region, sel));
+      v[2 * k + 1] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(th, region, sel));
+    }
+    *reinterpret_cast<u32x4_t*>(out + bk[p] * 64 + 8 * j) =
+        u32x4_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
+                __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                __builtin_amdgcn_perm(v[5], v[4], 0x05040100u),
+                __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)};
   }
 }
 
@@ -230,7 +254,8 @@ hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes
 hipError_t launch_dequant(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t n,
                           uint16_t* out, const Codebook& cb, hipStream_t st) {
   const int64_t nb = n / kBlock;
-  const int64_t grid = (nb + 127) / 128;
+  const int64_t per_wg = 4 * 8 * kDqPasses;  // blocks per workgroup
+  const int64_t grid = (nb + per_wg - 1) / per_wg;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(256), 0, st, codes, q8, s2, nb,
                      out, cb);
