@@ -49,8 +49,8 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # scaled by the counters' reading for a copy of known size. Valid while the
 # kernel source hashes to `src_sha256` (None: not measured for this source).
 TRAFFIC = {"kernel": "gemm_nt_kernel", "call": "gemm_nt_up", "src": "gemm_nt.hip",
-           "src_sha256": "76fd80344b6119f40b3a1a11f3e7741eb375c728c2c9be2d4de7cfb2f816a8c5",
-           "fetch_bytes": 593145856,   # 289622 KiB x 2.000 (copy reference)
+           "src_sha256": "b36c2bdf943ce58df831ff2e73a783d235f443292e92ac9fed406942e3963d99",
+           "fetch_bytes": 593584128,   # 289836 KiB x 2.000 (copy reference)
            "write_bytes": 180355072}   # 176128 KiB x 1.000 (copy reference)
 
 

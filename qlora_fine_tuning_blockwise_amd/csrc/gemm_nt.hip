@@ -7,9 +7,10 @@
 // matmul); [P2] s3 "The Backward Pass Through Quantization" (the input
 // gradient goes through the dequantized weight, in the compute type).
 //
-//  - dequant_t_kernel writes w_hat^T ([K, N] bf16), so that the input
-//    gradient dX = dY w_hat reduces over contiguous rows like the forward.
-//    (The forward uses the row-major dequantization of quantize.hip.)
+//  - The weight operand comes from quantize.hip: the row-major
+//    dequantization for the forward, the transposed one (w_hat^T, [K, N]) for
+//    the input gradient, so that dX = dY w_hat reduces over contiguous rows
+//    like the forward.
 //  - gemm_nt_kernel: y[M,N] = a[M,Kr] b[N,Kr]^T + e[M,2r] f'[N,2r]^T where
 //    f' repeats the r columns of f twice (e holds the two-term bf16 split of
 //    the scaled adapter product, so the extension adds s*u B exactly as the
@@ -319,76 +320,6 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
   }
 }
 
-// w_hat^T: out[k][n] = bf16(L[code(n,k)] * c1_hat(n, k/64)), c1_hat =
-// fp32(q8 * s2) (the same roundings as the row-major dequantization).
-// Workgroup tile: 128 weight rows x 256 columns. Lane p of wave w owns rows
-// n0 + 2p, n0 + 2p + 1 and column ranges [32(w + 4j), +32) (j = 0, 1); it
-// packs the pair (row 2p, row 2p+1) of each column into one dword of the
-// transposed LDS tile (row k: 64 dwords, so a wave's 64 stores of one k hit
-// 64 consecutive dwords), then the workgroup writes 256-byte rows of out.
-__global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
-                                                        const int8_t* __restrict__ q8,
-                                                        const float* __restrict__ s2, int64_t N,
-                                                        int64_t K, uint16_t* __restrict__ out,
-                                                        Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint32_t tile[256 * 64];
-  __shared__ float levels[16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * 128, k0 = (int64_t)blockIdx.y * 256;
-  const int64_t KB = K / 64;
-  if (tid < 16) levels[tid] = cb.level[tid];
-  __syncthreads();
-  const int64_t na = n0 + 2 * lane, nb = na + 1;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int kq = w + 4 * j;
-    const int64_t kk = k0 + 32 * kq;
-    u32x4_t ca = zero4(), cbv = zero4();
-    float cha = 0.0f, chb = 0.0f;
-    if (kk < K) {
-      const int64_t blk = kk / 64;
-      if (na < N) {
-        ca = *reinterpret_cast<const u32x4_t*>(codes + na * (K / 2) + kk / 2);
-        cha = (float)q8[na * KB + blk] * s2[(na * KB + blk) >> 8];
-      }
-      if (nb < N) {
-        cbv = *reinterpret_cast<const u32x4_t*>(codes + nb * (K / 2) + kk / 2);
-        chb = (float)q8[nb * KB + blk] * s2[(nb * KB + blk) >> 8];
-      }
-    }
-    const uint32_t wa[4] = {ca.x, ca.y, ca.z, ca.w};
-    const uint32_t wb[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float va = levels[(wa[d] >> (4 * s)) & 15u] * cha;
-        const float vb = levels[(wb[d] >> (4 * s)) & 15u] * chb;
-        tile[(32 * kq + 8 * d + s) * 64 + lane] = pack_bf16x2(va, vb);
-      }
-  }
-  __syncthreads();
-  // 256 rows x 256 bytes: 16 lanes per row, 16 rows per pass.
-  const int col = tid & 15, rsub = tid >> 4;
-  const int64_t nc = n0 + 8 * col;
-#pragma unroll 4
-  for (int pass = 0; pass < 16; ++pass) {
-    const int kr = 16 * pass + rsub;
-    const int64_t k = k0 + kr;
-    if (k >= K) break;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&tile[kr * 64 + 4 * col]);
-    uint16_t* dst = out + k * N + nc;
-    if (nc + 8 <= N && (N & 7) == 0) {
-      *reinterpret_cast<u32x4_t*>(dst) = v;
-    } else {
-      const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        if (nc + t < N) dst[t] = (uint16_t)(vv[t >> 1] >> (16 * (t & 1)));
-    }
-  }
-}
-
 }  // namespace
 
 bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb) {
@@ -411,11 +342,5 @@ hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_t(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t N,
-                            int64_t K, uint16_t* out, const Codebook& cb, hipStream_t st) {
-  const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((K + 255) / 256));
-  hipLaunchKernelGGL(dequant_t_kernel, grid, dim3(256), 0, st, codes, q8, s2, N, K, out, cb);
-  return hipGetLastError();
-}
 
 }  // namespace qlora

@@ -73,13 +73,46 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
   f32x4_t acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int64_t t = tw0; t < tw1; t += 32) {
-    const u32x4_t a = load8(X, M, T, m0 + c, t + 8 * g, vec_ok);
+  if (vec_ok && (T & 31) == 0) {
+    // Fixed trip count with every load issued first: indices are clamped into
+    // the matrix and the steps past this wave's range (or rows past M) are
+    // zeroed, which adds +0 to the same accumulation order.
+    constexpr int kSteps = kDownTC / 4 / 32;
+    const bool rok = m0 + c < M;
+    const int64_t xrow = rok ? m0 + c : M - 1;
+    u32x4_t av[kSteps];
+#pragma unroll
+    for (int it = 0; it < kSteps; ++it) {
+      const int64_t t = tw0 + 32 * it;
+      const int64_t tc = t + 32 <= T ? t : T - 32;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(X + xrow * T + tc + 8 * g);
+      av[it] = (rok && t < tw1) ? v : zero4();
+    }
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
       if (jt < ntile) {
-        const u32x4_t b = load8(P, r, T, j0 + 16 * jt + c, t + 8 * g, vec_ok);
-        acc[jt] = mfma_16x16x32(a, b, acc[jt]);
+        u32x4_t bv[kSteps];
+#pragma unroll
+        for (int it = 0; it < kSteps; ++it) {
+          const int64_t t = tw0 + 32 * it;
+          const int64_t tc = t + 32 <= T ? t : T - 32;
+          const u32x4_t v =
+              *reinterpret_cast<const u32x4_t*>(P + (int64_t)(j0 + 16 * jt + c) * T + tc + 8 * g);
+          bv[it] = t < tw1 ? v : zero4();
+        }
+#pragma unroll
+        for (int it = 0; it < kSteps; ++it) acc[jt] = mfma_16x16x32(av[it], bv[it], acc[jt]);
+      }
+    }
+  } else {
+    for (int64_t t = tw0; t < tw1; t += 32) {
+      const u32x4_t a = load8(X, M, T, m0 + c, t + 8 * g, vec_ok);
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        if (jt < ntile) {
+          const u32x4_t b = load8(P, r, T, j0 + 16 * jt + c, t + 8 * g, vec_ok);
+          acc[jt] = mfma_16x16x32(a, b, acc[jt]);
+        }
       }
     }
   }

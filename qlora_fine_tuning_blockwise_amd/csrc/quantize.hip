@@ -1,5 +1,5 @@
 // Blockwise NF4 quantization with double quantization, and dequantization to
-// bf16, for gfx950.
+// bf16 (row-major, and transposed for the input gradient), for gfx950.
 //
 // [P1] "QLoRA", "controlled rounding": per block of weights find the absmax,
 // normalise, store the index of the nearest grid point plus one scale per
@@ -235,6 +235,77 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   }
 }
 
+// w_hat^T: out[k][n] = bf16(L[code(n,k)] * c1_hat(n, k/64)), c1_hat =
+// fp32(q8 * s2) (the same roundings as the row-major dequantization).
+// Workgroup tile: 128 weight rows x 128 columns (32 KB of LDS, so four
+// workgroups share a CU). Lane p of wave w owns rows n0 + 2p, n0 + 2p + 1 and
+// columns [32w, 32w + 32) of the tile; it packs the pair (row 2p, row 2p+1)
+// of each column into one dword of the transposed LDS tile (row k: 64 dwords,
+// so a wave's 64 stores of one k hit 64 consecutive dwords), then the
+// workgroup writes 256-byte rows of out.
+constexpr int kDtCols = 128;  // tile columns (k)
+
+__global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
+                                                        const int8_t* __restrict__ q8,
+                                                        const float* __restrict__ s2, int64_t N,
+                                                        int64_t K, uint16_t* __restrict__ out,
+                                                        Codebook cb) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile[kDtCols * 64];
+  __shared__ float levels[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 128, k0 = (int64_t)blockIdx.y * kDtCols;
+  const int64_t KB = K / 64;
+  const int64_t na = n0 + 2 * lane, nb = na + 1;
+  const int64_t kk = k0 + 32 * w;
+  u32x4_t ca = zero4(), cbv = zero4();
+  float cha = 0.0f, chb = 0.0f;
+  if (kk < K) {
+    const int64_t blk = kk / 64;
+    if (na < N) {
+      ca = *reinterpret_cast<const u32x4_t*>(codes + na * (K / 2) + kk / 2);
+      cha = (float)q8[na * KB + blk] * s2[(na * KB + blk) >> 8];
+    }
+    if (nb < N) {
+      cbv = *reinterpret_cast<const u32x4_t*>(codes + nb * (K / 2) + kk / 2);
+      chb = (float)q8[nb * KB + blk] * s2[(nb * KB + blk) >> 8];
+    }
+  }
+  if (tid < 16) levels[tid] = cb.level[tid];
+  __syncthreads();
+  {
+    const uint32_t wa[4] = {ca.x, ca.y, ca.z, ca.w};
+    const uint32_t wb[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float va = levels[(wa[d] >> (4 * s)) & 15u] * cha;
+        const float vb = levels[(wb[d] >> (4 * s)) & 15u] * chb;
+        tile[(32 * w + 8 * d + s) * 64 + lane] = pack_bf16x2(va, vb);
+      }
+  }
+  __syncthreads();
+  // kDtCols rows x 256 bytes: 16 lanes per row, 16 rows per pass.
+  const int col = tid & 15, rsub = tid >> 4;
+  const int64_t nc = n0 + 8 * col;
+#pragma unroll
+  for (int pass = 0; pass < kDtCols / 16; ++pass) {
+    const int kr = 16 * pass + rsub;
+    const int64_t k = k0 + kr;
+    if (k >= K) break;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&tile[kr * 64 + 4 * col]);
+    uint16_t* dst = out + k * N + nc;
+    if (nc + 8 <= N && (N & 7) == 0) {
+      *reinterpret_cast<u32x4_t*>(dst) = v;
+    } else {
+      const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (nc + t < N) dst[t] = (uint16_t)(vv[t >> 1] >> (16 * (t & 1)));
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes, int8_t* q8,
@@ -259,6 +330,14 @@ hipError_t launch_dequant(const uint8_t* codes, const int8_t* q8, const float* s
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(256), 0, st, codes, q8, s2, nb,
                      out, cb);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_dequant_t(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t N,
+                            int64_t K, uint16_t* out, const Codebook& cb, hipStream_t st) {
+  const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((K + kDtCols - 1) / kDtCols));
+  hipLaunchKernelGGL(dequant_t_kernel, grid, dim3(256), 0, st, codes, q8, s2, N, K, out, cb);
   return hipGetLastError();
 }
 
