@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "oracle_linear_fwd": (ctypes.c_int, [P, I64, I64, P, I64, P, P, ctypes.c_int, D, P, P]),
             "oracle_linear_bwd": (ctypes.c_int,
                                   [P, P, I64, I64, P, I64, P, P, ctypes.c_int, D, P, P, P]),
+            "oracle_merge_lora": (ctypes.c_int, [P, P, P, P, I64, I64, P, P, ctypes.c_int,
+                                                 ctypes.c_float, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -264,3 +266,25 @@ def linear_bwd(x, dY, What, A, B, r: int, alpha: float, want=("dX", "dA", "dB"))
     if dB is not None:
         out["dB"] = dB
     return out
+
+
+# ------------------------------------------------------------------ merge
+def merge_lora(A, B, r: int, alpha: float, nf4=None, W=None):
+    """[P1] bullets (merging forces a re-quantization); [P4] "Merge friction".
+    out = base + (alpha/r) (A B)^T in binary32 with the adapter sum in order
+    j = 0..r-1; base = dequantized NF4 (nf4 = (codes, q8, s2, N, K)) or the
+    bf16 weight W [N, K] (uint16 bits). Returns fp32 [N, K]."""
+    A = _c(A, np.uint16)
+    B = _c(B, np.uint16)
+    if W is not None:
+        W = _c(W, np.uint16)
+        N, K = W.shape
+        codes = q8 = s2 = None
+    else:
+        codes, q8, s2, N, K = nf4
+        codes, q8, s2 = _c(codes, np.uint8), _c(q8, np.int8), _c(s2, np.float32)
+    out = np.empty((N, K), np.float32)
+    _check(lib().oracle_merge_lora(_p(codes), _p(q8), _p(s2), _p(W), N, K, _p(A), _p(B), r,
+                                   float(alpha), _p(out)), "merge_lora")
+    return out
+

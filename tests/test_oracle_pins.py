@@ -449,3 +449,87 @@ def test_alpha_scales_only_the_adapter_term(olib):
     y2, _ = olib.linear_fwd(x, What, A, B, r, 48.0)
     y0, _ = olib.linear_fwd(x, What, A, B, r, 0.0)
     assert np.allclose(y2 - y0, 3.0 * (y1 - y0), rtol=1e-12, atol=1e-15)
+
+
+# -------------------------------------------------------------------- merge
+def _exact_adapter_sum(A, B):
+    """sum_j A[k,j] B[j,n] for every (n, k) in exact rational arithmetic (the
+    bf16 values are dyadic rationals), returned as float64 with one rounding."""
+    from fractions import Fraction
+    Af = [[Fraction(float(v)) for v in row] for row in A]
+    Bf = [[Fraction(float(v)) for v in row] for row in B]
+    K, r = len(Af), len(Af[0])
+    N = len(Bf[0])
+    out = np.empty((N, K))
+    for n in range(N):
+        for k in range(K):
+            out[n, k] = float(sum(Af[k][j] * Bf[j][n] for j in range(r)))
+    return out
+
+
+def test_merge_zero_adapter_returns_the_base(olib):
+    """B = 0: nothing is added, the base comes back exactly (both base kinds)."""
+    N, K, r = 64, 128, 16
+    W = syn.normal_bf16((N, K), 0.02, 31)
+    A = syn.normal_bf16((K, r), 0.1, 32)
+    B = np.zeros((r, N), np.uint16)
+    assert np.array_equal(olib.merge_lora(A, B, r, 32.0, W=W), olib.bf16_to_f32(W))
+    codes, q8, s2 = olib.quantize_nf4_dq(W, "bf16")
+    what = olib.dequant_dq(codes, q8, s2)[1]
+    got = olib.merge_lora(A, B, r, 32.0, nf4=(codes, q8, s2, N, K))
+    assert np.array_equal(got, olib.bf16_to_f32(what).reshape(N, K))
+
+
+def test_merge_adapter_sum_within_the_sequential_rounding_bound(olib):
+    """Zero base and alpha = r (s = 1): the output is the binary32 adapter sum.
+    It must lie within the error bound of r-1 sequential roundings of the exact
+    sum, (r-1) 2^-24 sum_j |A[k,j] B[j,n]| (plus one half-ulp for the final
+    additions), for a non-square shape, so a transposed A or B fails."""
+    N, K, r = 24, 64, 16
+    A = syn.normal_bf16((K, r), 0.5, 33)
+    B = syn.normal_bf16((r, N), 0.5, 34)
+    W = np.zeros((N, K), np.uint16)
+    got = olib.merge_lora(A, B, r, float(r), W=W).astype(np.float64)
+    Af, Bf = olib.bf16_to_f32(A).astype(np.float64), olib.bf16_to_f32(B).astype(np.float64)
+    exact = _exact_adapter_sum(Af, Bf)
+    mag = (np.abs(Bf).T @ np.abs(Af).T)  # [N, K] sum of |terms|
+    bound = (r - 1) * 2.0 ** -24 * mag + 2.0 ** -24 * np.abs(exact)
+    assert np.all(np.abs(got - exact) <= bound + 1e-300)
+
+
+def test_merge_scales_by_alpha_over_r(olib):
+    """Zero base: doubling alpha doubles every output exactly (scaling by a
+    power of two is exact in binary32)."""
+    N, K, r = 16, 64, 32
+    A = syn.normal_bf16((K, r), 0.1, 35)
+    B = syn.normal_bf16((r, N), 0.1, 36)
+    W = np.zeros((N, K), np.uint16)
+    a = olib.merge_lora(A, B, r, 8.0, W=W)
+    b = olib.merge_lora(A, B, r, 16.0, W=W)
+    assert np.array_equal(b, 2.0 * a)
+
+
+def test_merge_into_4bit_base_adds_a_second_rounding(olib):
+    """[P1]/[P4]: requantizing after merging into the 4-bit base layers a
+    second rounding on top of the first, while merging into the 16-bit weight
+    and quantizing once does not. Against the exact 16-bit merge W + s (AB)^T,
+    the 4-bit path's error after requantization is clearly larger, and the
+    clean path's error matches plain one-shot quantization of that merge."""
+    N, K, r = 256, 1024, 16
+    W = syn.normal_bf16((N, K), 0.02, 37)
+    A = syn.normal_bf16((K, r), 1.0 / np.sqrt(K), 38)
+    B = syn.normal_bf16((r, N), 0.01, 39)
+    exact = olib.merge_lora(A, B, r, 32.0, W=W).astype(np.float64)
+    codes, q8, s2 = olib.quantize_nf4_dq(W, "bf16")
+    m4 = olib.merge_lora(A, B, r, 32.0, nf4=(codes, q8, s2, N, K))
+
+    def requant_err(merged):
+        c, q, s = olib.quantize_nf4_dq(merged, "f32")
+        back = olib.bf16_to_f32(olib.dequant_dq(c, q, s)[1]).reshape(N, K).astype(np.float64)
+        return np.linalg.norm(back - exact) / np.linalg.norm(exact)
+
+    e_clean = requant_err(exact.astype(np.float32))
+    e_4bit = requant_err(m4)
+    print(f"requantization error vs the exact merge: clean {e_clean:.4f}, 4-bit {e_4bit:.4f}")
+    assert e_4bit > 1.2 * e_clean, (e_4bit, e_clean)
+    assert 0.02 < e_clean < 0.2
