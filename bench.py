@@ -310,10 +310,59 @@ def main():
         result["gemv_ring"] = gemv_ring(q, syn, torch, dev, r, alpha)
         log("bulk quantize/dequant")
         result["bulk_quantize"] = bulk_quantize(q, syn, torch, dev)
+        log("merge + requantize")
+        result["merge"] = merge_section(q, syn, torch, dev, cfg, nf4, W, A, B, r, alpha)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(np, syn, cfg, step_flops, ms_step_host)
     print(json.dumps(result), flush=True)
+
+
+def merge_section(q, syn, torch, dev, cfg, nf4, W, A, B, r, alpha, iters=10):
+    """Adapter merge on the up weight: the merge into the 4-bit base
+    (dequantize + s (AB)^T in binary32, fp32 out) and its requantization, each
+    timed with HIP events; plus the relative Frobenius error of the
+    requantized weight against the exact 16-bit merge W + s (AB)^T, for the
+    4-bit path and for the clean path (merge into the bf16 weight, quantize
+    once) that the pages recommend."""
+    N, K = cfg["weights"]["up"]
+    w = nf4["up"]
+    merged = torch.empty((N, K), dtype=torch.float32, device=dev)
+    ws = torch.empty(q.qlora_workspace_bytes(2, 0, N, K, r), dtype=torch.uint8, device=dev)
+    wq = q.qlora_quantize_nf4_dq(merged)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    ms_m = timed(lambda: q.qlora_merge_lora(A["up"], B["up"], alpha, w=w, out=merged, workspace=ws))
+    ms_q = timed(lambda: q.qlora_quantize_nf4_dq(merged, out=wq))
+    m_bytes = nf4_bytes(N, K) + 2 * r * (N + K) + 4 * N * K
+    q_bytes = 4 * N * K + nf4_bytes(N, K)
+    # errors against the exact 16-bit merge (measurement only)
+    q.qlora_merge_lora(A["up"], B["up"], alpha, w=w, out=merged, workspace=ws)
+    q.qlora_quantize_nf4_dq(merged, out=wq)
+    back4 = q.qlora_dequant_bf16(wq).float()
+    exact = q.qlora_merge_lora(A["up"], B["up"], alpha, W=W["up"], workspace=ws)
+    wc = q.qlora_quantize_nf4_dq(exact)
+    backc = q.qlora_dequant_bf16(wc).float()
+    nrm = torch.linalg.norm(exact)
+    e4 = float(torch.linalg.norm(back4 - exact) / nrm)
+    ec = float(torch.linalg.norm(backc - exact) / nrm)
+    return {"weight": [N, K], "r": r,
+            "merge_4bit_base": {"ms": round(ms_m, 5), "gbps": round(m_bytes / (ms_m * 1e-3) / 1e9, 1),
+                                "frac_hbm_peak": round(m_bytes / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+            "requantize_f32": {"ms": round(ms_q, 5), "gbps": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
+                               "frac_hbm_peak": round(q_bytes / (ms_q * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+            "rel_err_vs_16bit_merge": {"merge_into_4bit_then_requantize": round(e4, 5),
+                                       "merge_into_bf16_then_quantize": round(ec, 5)}}
 
 
 def gemv_ring(q, syn, torch, dev, r, alpha):

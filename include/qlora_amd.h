@@ -72,6 +72,7 @@ extern "C" {
 /* Operations for qlora_workspace_bytes. */
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1
+#define QLORA_OP_MERGE 2
 
 /* Format version of the storage layout above. */
 #define QLORA_FORMAT_VERSION 1u
@@ -101,9 +102,9 @@ int qlora_codebook(float levels[16], float thresholds[15]);
  * in the adapter's recorded metadata. Host only; 0 if the codebook failed. */
 uint32_t qlora_codebook_id(void);
 
-/* Device workspace, in bytes, that qlora_linear_fwd (op = QLORA_OP_FWD) or
- * qlora_linear_bwd (op = QLORA_OP_BWD) needs for these sizes, assuming no
- * saved u. From M = 512 rows on it includes N*K*2 bytes for the dequantized
+/* Device workspace, in bytes, that qlora_linear_fwd (op = QLORA_OP_FWD),
+ * qlora_linear_bwd (op = QLORA_OP_BWD) or qlora_merge_lora (op =
+ * QLORA_OP_MERGE, M ignored) needs for these sizes, assuming no saved u. From M = 512 rows on it includes N*K*2 bytes for the dequantized
  * weight (see qlora_gemm_bf16_nt). Host only; 0 on invalid sizes. */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
 
@@ -161,6 +162,26 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
                      const uint16_t* A, const uint16_t* B, int r, float alpha,
                      const float* u_saved, void* dX, int dx_dtype, void* dA, void* dB,
                      int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Merge the trained adapter into the base, in binary32 ([P1] bullets:
+ * folding BA into a 4-bit W forces a re-quantization, a second rounding;
+ * [P4] "What it costs", "Merge friction": the clean path merges into the
+ * 16-bit weights and quantizes once afterwards):
+ *   merged[n][k] = base[n][k] + s * d[n][k],  s = alpha / r (binary32),
+ *   d[n][k] = sum_j A[k][j] B[j][n], starting from +0 and taking the terms
+ *   j = 0..r-1 in order, each as one fused multiply-add (one rounding per
+ *   term); then s*d rounds, then the final sum rounds (nearest-even).
+ *   base = w_hat (the dequantized NF4 weight: codes, absmax_q, absmax_scale)
+ *          when W is NULL, else the bf16 weight W [N,K].
+ *   A [K,r] bf16; B [r,N] bf16; merged fp32 [N,K] (caller-owned output).
+ *   workspace  at least qlora_workspace_bytes(QLORA_OP_MERGE, 0, N, K, r).
+ * Requantizing the merged weight is qlora_quantize_nf4_dq with
+ * QLORA_DTYPE_F32 input. Same shape and rank rules as the linear entry
+ * points; QLORA_ERR_INVALID_ARG when neither base is given. */
+int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
+                     const uint16_t* W, int64_t N, int64_t K, const uint16_t* A,
+                     const uint16_t* B, int r, float alpha, float* merged, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* Dense stage of the large-batch path: the product with a weight that is
  * already dequantized ([P1] bullets: the 4-bit weight is expanded to bf16

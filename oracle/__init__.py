@@ -272,7 +272,7 @@ def linear_bwd(x, dY, What, A, B, r: int, alpha: float, want=("dX", "dA", "dB"))
 def merge_lora(A, B, r: int, alpha: float, nf4=None, W=None):
     """[P1] bullets (merging forces a re-quantization); [P4] "Merge friction".
     out = base + (alpha/r) (A B)^T in binary32 with the adapter sum in order
-    j = 0..r-1; base = dequantized NF4 (nf4 = (codes, q8, s2, N, K)) or the
+    j = 0..r-1, one fused multiply-add per term; base = dequantized NF4 (nf4 = (codes, q8, s2, N, K)) or the
     bf16 weight W [N, K] (uint16 bits). Returns fp32 [N, K]."""
     A = _c(A, np.uint16)
     B = _c(B, np.uint16)

@@ -19,7 +19,7 @@ from . import _lib
 __all__ = [
     "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_id",
     "qlora_workspace_bytes", "qlora_quantize_nf4_dq", "qlora_dequant_bf16",
-    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "NF4Weight",
+    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "qlora_merge_lora", "NF4Weight",
 ]
 
 
@@ -172,4 +172,27 @@ def qlora_gemm_bf16_nt(a: torch.Tensor, b: torch.Tensor, e: torch.Tensor, f: tor
                                         _ptr(y), _dtype_code(y.dtype), _stream(stream))
     _lib.check(st, "qlora_gemm_bf16_nt")
     return y
+
+
+def qlora_merge_lora(A: torch.Tensor, B: torch.Tensor, alpha: float, w: NF4Weight | None = None,
+                     W: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """merged = base + (alpha/r) (A B)^T as fp32 [N, K]; base = the dequantized
+    NF4 weight w, or the bf16 weight W. Requantize with qlora_quantize_nf4_dq."""
+    if (w is None) == (W is None):
+        raise ValueError("qlora_merge_lora: give exactly one of w (NF4) and W (bf16)")
+    N, K = (w.N, w.K) if w is not None else W.shape
+    r = A.shape[1]
+    dev = A.device
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=dev)
+    need = qlora_workspace_bytes(_lib.OP_MERGE, 0, N, K, r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    nf = (w.codes, w.absmax_q, w.absmax_scale) if w is not None else (None, None, None)
+    st = _lib.load().qlora_merge_lora(_ptr(nf[0]), _ptr(nf[1]), _ptr(nf[2]), _ptr(W), N, K,
+                                      _ptr(A), _ptr(B), r, float(alpha), _ptr(out),
+                                      _ptr(workspace), workspace.numel(), _stream(stream))
+    _lib.check(st, "qlora_merge_lora")
+    return out
 

@@ -18,6 +18,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 OP_FWD = 0
 OP_BWD = 1
+OP_MERGE = 2
 
 P = ctypes.c_void_p
 I64 = ctypes.c_int64
@@ -37,6 +38,7 @@ SIGNATURES = {
     "qlora_linear_bwd": (INT, [P, P, P, I64, I64, P, P, I64, P, P, INT, FLT, P, P, INT, P, P, INT,
                                P, SZ, P]),
     "qlora_gemm_bf16_nt": (INT, [P, I64, P, I64, P, P, I64, I64, I64, INT, P, INT, P]),
+    "qlora_merge_lora": (INT, [P, P, P, P, I64, I64, P, P, INT, FLT, P, P, SZ, P]),
 }
 
 _lib = None

@@ -88,6 +88,19 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   return L;
 }
 
+struct MergeLayout {
+  size_t At = 0, Bt = 0, total = 0;
+};
+
+MergeLayout merge_layout(int64_t N, int64_t K, int r) {
+  MergeLayout L;
+  Carve c;
+  L.At = c.take((size_t)r * K * 2);
+  L.Bt = c.take((size_t)N * r * 2);
+  L.total = c.off;
+  return L;
+}
+
 template <typename T>
 T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
@@ -145,6 +158,7 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
   if (M < 0 || !shape_ok(N, K) || !rank_ok(r)) return 0;
   if (op == QLORA_OP_FWD) return fwd_layout(M, N, K, r, true).total;
   if (op == QLORA_OP_BWD) return bwd_layout(M, N, K, r, true).total;
+  if (op == QLORA_OP_MERGE) return merge_layout(N, K, r).total;
   return 0;
 }
 
@@ -322,6 +336,32 @@ int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_
   return launch_status(launch_gemm_nt(a, lda, b, ldb, e, f, M, N, K, r, y,
                                       y_dtype == QLORA_DTYPE_BF16,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
+                     const uint16_t* W, int64_t N, int64_t K, const uint16_t* A,
+                     const uint16_t* B, int r, float alpha, float* merged, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const Codebook* cb = nullptr;
+  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+  if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
+  if (!rank_ok(r)) return QLORA_ERR_RANK;
+  if (!A || !B || !merged) return QLORA_ERR_INVALID_ARG;
+  if (!W && (!codes || !absmax_q || !absmax_scale)) return QLORA_ERR_INVALID_ARG;
+  const void* ptrs[] = {codes, absmax_q, absmax_scale, W, A, B, merged, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
+  const MergeLayout L = merge_layout(N, K, r);
+  if (!workspace || workspace_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* At = at<uint16_t>(workspace, L.At);
+  uint16_t* Bt = at<uint16_t>(workspace, L.Bt);
+  hipError_t e = launch_transpose_bf16(A, K, r, At, st);      // A^T [r,K]
+  if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
+  if (e == hipSuccess)
+    e = launch_merge(W ? nullptr : codes, absmax_q, absmax_scale, W, N, K, At, Bt, r,
+                     alpha / (float)r, merged, *cb, st);
+  return launch_status(e);
 }
 
 }  // extern "C"

@@ -81,6 +81,14 @@ hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int
 hipError_t launch_dequant_t(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t N,
                             int64_t K, uint16_t* out, const Codebook& cb, hipStream_t st);
 
+// merged = base + s (A B)^T in binary32 (adapter sum in order j = 0..r-1);
+// base = the dequantized NF4 weight (W == NULL) or the bf16 weight W.
+// At = A^T [r,K], Bt = B^T [N,r].
+hipError_t launch_merge(const uint8_t* codes, const int8_t* q8, const float* s2,
+                        const uint16_t* W, int64_t N, int64_t K, const uint16_t* At,
+                        const uint16_t* Bt, int r, float s, float* out, const Codebook& cb,
+                        hipStream_t st);
+
 // Adapter gradients: part[split][c][j] = sum_{m in split} X[m][c] * P[m][j]
 // (X [M,C] bf16; P given as the transposed two-term bf16 split PT [2r, Mp]
 // written by launch_lora_down_finalize), then out = s * sum_split part,

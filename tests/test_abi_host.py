@@ -140,12 +140,30 @@ def test_gemm_nt_validation(lib):
     assert call(6, 0) == 0             # empty: a no-op
 
 
+def test_merge_validation(lib):
+    f = lib.qlora_merge_lora
+    base = [_p(FAKE), _p(FAKE), _p(FAKE), None, 64, 128, _p(FAKE), _p(FAKE), 16, 32.0, _p(FAKE),
+            _p(FAKE), 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(5, 100) == 2            # K % 64
+    assert call(8, 8) == 5              # r
+    assert call(10, None) == 1          # merged missing
+    assert call(0, None) == 1           # neither NF4 base nor bf16 base
+    assert call(6, _p(FAKE + 4)) == 3   # A misaligned
+    assert call(12, 64) == 6            # workspace too small
+    assert lib.qlora_workspace_bytes(2, 0, 64, 128, 16) >= 2 * 16 * (64 + 128)
+
+
 def test_workspace_query(lib):
     assert q.qlora_workspace_bytes(0, 16, 4096, 4096, 16) > 0
     assert q.qlora_workspace_bytes(0, 4096, 4096, 4096, 16) > q.qlora_workspace_bytes(0, 1024, 4096, 4096, 16)
     assert q.qlora_workspace_bytes(1, 4096, 11008, 4096, 16) > 0
     assert q.qlora_workspace_bytes(0, 16, 4096, 4000, 16) == 0
-    assert q.qlora_workspace_bytes(2, 16, 4096, 4096, 16) == 0
+    assert q.qlora_workspace_bytes(3, 16, 4096, 4096, 16) == 0  # no such op
     # from 512 rows on the dequantized weight lives in the workspace
     for op in (0, 1):
         big = q.qlora_workspace_bytes(op, 512, 4096, 1024, 16)

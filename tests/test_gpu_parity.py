@@ -500,3 +500,43 @@ def test_layer_70b_fwd_bwd_sampled():
         for g, rr, k in zip(got, ref, ("y", "dX", "dA", "dB")):
             tol_check(g, rr, f"70b {name} {k}")
         say("70b layer ok", name)
+
+
+# ------------------------------------------------------------------- merge
+@pytest.mark.parametrize("N,K,r,base", [(1024, 1024, 16, "nf4"), (1024, 1024, 16, "bf16"),
+                                        (257, 640, 32, "nf4"), (72, 64, 64, "bf16"),
+                                        (11008, 4096, 16, "nf4")])
+def test_merge_and_requantize_bit_exact(N, K, r, base):
+    """merged = base + s (A B)^T bit for bit against the oracle, then the
+    requantized codes, 8-bit scale codes and second-level scales bit for bit."""
+    say("merge", N, K, r, base)
+    Wb = syn.normal_bf16((N, K), 0.02, 60 + r)
+    A = syn.normal_bf16((K, r), 1.0 / np.sqrt(K), 61 + r)
+    B = syn.normal_bf16((r, N), 0.01, 62 + r)
+    At, Bt = dev_bf16(A), dev_bf16(B)
+    if base == "nf4":
+        w = quantize_gpu(dev_bf16(Wb))
+        codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+        merged = q.qlora_merge_lora(At, Bt, 32.0, w=w)
+        ref = oracle.merge_lora(A, B, r, 32.0, nf4=(codes, q8, s2, N, K))
+    else:
+        merged = q.qlora_merge_lora(At, Bt, 32.0, W=dev_bf16(Wb))
+        ref = oracle.merge_lora(A, B, r, 32.0, W=Wb)
+    torch.cuda.synchronize()
+    got = host(merged)
+    assert got.dtype == np.float32
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), "merged weight bits"
+    wq = q.qlora_quantize_nf4_dq(merged)
+    assert_nf4_equal(wq, *oracle.quantize_nf4_dq(ref, "f32"), f"requantized {base}")
+
+
+def test_merge_zero_adapter_gives_the_dequantized_base():
+    N, K, r = 320, 512, 16
+    Wb = syn.normal_bf16((N, K), 0.02, 70)
+    w = quantize_gpu(dev_bf16(Wb))
+    A = dev_bf16(syn.normal_bf16((K, r), 0.1, 71))
+    merged = q.qlora_merge_lora(A, torch.zeros((r, N), dtype=torch.bfloat16, device=DEV), 32.0, w=w)
+    deq = q.qlora_dequant_bf16(w)
+    torch.cuda.synchronize()
+    assert torch.equal(merged, deq.float())
+

@@ -482,8 +482,8 @@ def test_merge_zero_adapter_returns_the_base(olib):
 
 def test_merge_adapter_sum_within_the_sequential_rounding_bound(olib):
     """Zero base and alpha = r (s = 1): the output is the binary32 adapter sum.
-    It must lie within the error bound of r-1 sequential roundings of the exact
-    sum, (r-1) 2^-24 sum_j |A[k,j] B[j,n]| (plus one half-ulp for the final
+    It must lie within the error bound of r sequential roundings of the exact
+    sum, r 2^-24 sum_j |A[k,j] B[j,n]| (plus one half-ulp for the final
     additions), for a non-square shape, so a transposed A or B fails."""
     N, K, r = 24, 64, 16
     A = syn.normal_bf16((K, r), 0.5, 33)
@@ -493,7 +493,7 @@ def test_merge_adapter_sum_within_the_sequential_rounding_bound(olib):
     Af, Bf = olib.bf16_to_f32(A).astype(np.float64), olib.bf16_to_f32(B).astype(np.float64)
     exact = _exact_adapter_sum(Af, Bf)
     mag = (np.abs(Bf).T @ np.abs(Af).T)  # [N, K] sum of |terms|
-    bound = (r - 1) * 2.0 ** -24 * mag + 2.0 ** -24 * np.abs(exact)
+    bound = r * 2.0 ** -24 * mag + 2.0 ** -24 * np.abs(exact)
     assert np.all(np.abs(got - exact) <= bound + 1e-300)
 
 
