@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
                                   [P, P, I64, I64, P, I64, P, P, ctypes.c_int, D, P, P, P]),
             "oracle_merge_lora": (ctypes.c_int, [P, P, P, P, I64, I64, P, P, ctypes.c_int,
                                                  ctypes.c_float, P]),
+            "oracle_adamw_step": (ctypes.c_int, [P, P, ctypes.c_int, P, P, I64] +
+                                  [D] * 5 + [I64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -288,3 +290,25 @@ def merge_lora(A, B, r: int, alpha: float, nf4=None, W=None):
                                    float(alpha), _p(out)), "merge_lora")
     return out
 
+
+
+# ------------------------------------------------------------------ AdamW
+def adamw_step(p, g, m, v, lr: float, beta1: float, beta2: float, eps: float, wd: float,
+               t: int):
+    """[P2] precision table (fp32 Adam state, 12 bytes per adapter parameter:
+    master value and two moments); [P4] "The memory term LoRA does not
+    remove". One AdamW step in binary32 on copies of p, m, v (fp32 arrays of
+    one shape); g is fp32 or bf16 bits (uint16). Returns (p, m, v, p_bf16)."""
+    p = np.array(p, np.float32, copy=True, order="C")
+    m = np.array(m, np.float32, copy=True, order="C")
+    v = np.array(v, np.float32, copy=True, order="C")
+    g = np.ascontiguousarray(g)
+    if g.dtype not in (np.float32, np.uint16) or g.shape != p.shape:
+        raise ValueError("g must be fp32 or bf16 bits of the parameters' shape")
+    if m.shape != p.shape or v.shape != p.shape:
+        raise ValueError("m and v must have the parameters' shape")
+    pb = np.empty(p.shape, np.uint16)
+    _check(lib().oracle_adamw_step(_p(p), _p(g), int(g.dtype == np.uint16), _p(m), _p(v),
+                                   p.size, float(lr), float(beta1), float(beta2), float(eps),
+                                   float(wd), int(t), _p(pb)), "adamw_step")
+    return p, m, v, pb

@@ -479,3 +479,72 @@ int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2,
     free(base);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* AdamW step on the adapter parameters                                     */
+/* [P2] precision table (the Adam state of an adapter parameter is fp32,    */
+/* 12 bytes); [P4] "The memory term LoRA does not remove" (what a trained   */
+/* parameter carries: optimizer moments and a master copy). The 12 bytes   */
+/* are read as the fp32 master value p and the two fp32 moments m and v;    */
+/* the bf16 adapter the layer reads is the master value rounded to bf16.    */
+/* [P1] paragraph on paged optimizers, [P3] "How it works": the state may   */
+/* sit in host memory; that changes where it lives, not what is computed.  */
+/*                                                                          */
+/* Decoupled weight decay (AdamW). Step t >= 1. The hyper-parameters are    */
+/* given in double; every scalar below is computed in double from them and  */
+/* rounded once to binary32:                                                */
+/*   b1 = beta1, b2 = beta2, e = eps, decay = 1 - lr*wd, c1 = 1 - beta1,    */
+/*   c2 = 1 - beta2, step_size = lr / (1 - beta1^t),                        */
+/*   bc2_sqrt = sqrt(1 - beta2^t).                                          */
+/* Per element in binary32, every operation rounded, no fused operations:   */
+/*   p <- p*decay                                                           */
+/*   m <- b1*m + c1*g                                                       */
+/*   v <- b2*v + c2*(g*g)                                                   */
+/*   p <- p - step_size * (m / (sqrt(v)/bc2_sqrt + e))                      */
+/* g is the gradient (bf16 widened, or fp32).                               */
+/* ------------------------------------------------------------------------ */
+static void adamw_scalars(double lr, double beta1, double beta2, double eps, double wd,
+                          int64_t t, float sc[8]) {
+    const double b1t = pow(beta1, (double)t), b2t = pow(beta2, (double)t);
+    sc[0] = (float)beta1;
+    sc[1] = (float)beta2;
+    sc[2] = (float)eps;
+    sc[3] = (float)(1.0 - lr * wd);
+    sc[4] = (float)(1.0 - beta1);
+    sc[5] = (float)(1.0 - beta2);
+    sc[6] = (float)(lr / (1.0 - b1t));
+    sc[7] = (float)sqrt(1.0 - b2t);
+}
+
+int oracle_adamw_step(float* p, const void* g, int g_is_bf16, float* m, float* v, int64_t n,
+                      double lr, double beta1, double beta2, double eps, double wd, int64_t t,
+                      uint16_t* p_bf16) {
+    if (n < 0 || t < 1 || (n > 0 && (!p || !g || !m || !v))) return 1;
+    if (!(beta1 >= 0.0 && beta1 < 1.0 && beta2 >= 0.0 && beta2 < 1.0)) return 1;
+    float sc[8];
+    adamw_scalars(lr, beta1, beta2, eps, wd, t, sc);
+    const float b1 = sc[0], b2 = sc[1], e = sc[2], decay = sc[3], c1 = sc[4], c2 = sc[5];
+    const float step_size = sc[6], bc2_sqrt = sc[7];
+    for (int64_t i = 0; i < n; ++i) {
+        const float gi = g_is_bf16 ? oracle_bf16_to_f32(((const uint16_t*)g)[i])
+                                   : ((const float*)g)[i];
+        const float pd = p[i] * decay;
+        const float mb = b1 * m[i];
+        const float mg = c1 * gi;
+        const float mi = mb + mg;
+        const float vb = b2 * v[i];
+        const float gg = gi * gi;
+        const float vg = c2 * gg;
+        const float vi = vb + vg;
+        const float sq = sqrtf(vi);
+        const float dn = sq / bc2_sqrt;
+        const float de = dn + e;
+        const float q = mi / de;
+        const float up = step_size * q;
+        p[i] = pd - up;
+        m[i] = mi;
+        v[i] = vi;
+        if (p_bf16) p_bf16[i] = oracle_f32_to_bf16(p[i]);
+    }
+    return 0;
+}

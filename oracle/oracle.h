@@ -1,7 +1,8 @@
 /*
  * CPU oracle for the QLoRA frozen-base path: blockwise NF4 quantization with
- * double quantization of the block constants, dequantization to bf16, and the
- * QLoRA linear layer (forward and backward) in double precision.
+ * double quantization of the block constants, dequantization to bf16, the
+ * QLoRA linear layer (forward and backward) in double precision, the merge of
+ * the adapter into the base and the AdamW step on the adapter (binary32).
  *
  * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
  * this code: only the test suite, the smoke check and the benchmark's CPU
@@ -102,6 +103,15 @@ int oracle_linear_bwd(const uint16_t* x, const uint16_t* dY, int64_t M, int64_t 
 int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2,
                       const uint16_t* wbf16, int64_t N, int64_t K, const uint16_t* A,
                       const uint16_t* B, int r, float alpha, float* out);
+
+/* AdamW step in binary32 on n adapter parameters (see oracle.c): fp32
+ * master values p, fp32 moments m and v updated in place; g is bf16
+ * (g_is_bf16 != 0) or fp32; t >= 1 is the step number; p_bf16 (may be NULL)
+ * receives the master values rounded to bf16. The hyper-parameters are
+ * double; the per-element arithmetic is binary32. */
+int oracle_adamw_step(float* p, const void* g, int g_is_bf16, float* m, float* v, int64_t n,
+                      double lr, double beta1, double beta2, double eps, double wd, int64_t t,
+                      uint16_t* p_bf16);
 
 #ifdef __cplusplus
 }

@@ -533,3 +533,142 @@ def test_merge_into_4bit_base_adds_a_second_rounding(olib):
     print(f"requantization error vs the exact merge: clean {e_clean:.4f}, 4-bit {e_4bit:.4f}")
     assert e_4bit > 1.2 * e_clean, (e_4bit, e_clean)
     assert 0.02 < e_clean < 0.2
+
+
+# ------------------------------------------------------------------- AdamW
+_HP = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.01)
+
+
+def _rne_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even) by integer arithmetic."""
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_adamw_tracks_torch_adamw_in_double(olib):
+    """[P2] precision table: Adam with fp32 state. torch.optim.AdamW run in
+    float64 on the same gradients (a library routine of the textbook AdamW,
+    decoupled decay, bias-corrected moments) agrees with the binary32 oracle
+    over ten steps to within its rounding: a wrong decay, bias correction,
+    moment index or sign moves the result by far more."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    n = 4096
+    p0 = rng.normal(0, 0.02, n).astype(np.float32)
+    grads = [rng.normal(0, 1e-2, n).astype(np.float32) * rng.lognormal(0, 1, n).astype(np.float32)
+             for _ in range(10)]
+    pt = torch.nn.Parameter(torch.tensor(p0, dtype=torch.float64))
+    opt = torch.optim.AdamW([pt], lr=_HP["lr"], betas=(_HP["beta1"], _HP["beta2"]),
+                            eps=_HP["eps"], weight_decay=_HP["wd"])
+    p, m, v = p0, np.zeros(n, np.float32), np.zeros(n, np.float32)
+    u = 2.0 ** -24
+    b1, b2 = _HP["beta1"], _HP["beta2"]
+    bm = np.zeros(n)  # running bounds on the moments' rounding error
+    bv = np.zeros(n)
+    for t, g in enumerate(grads, 1):
+        pt.grad = torch.tensor(g, dtype=torch.float64)
+        m_prev, v_prev = m.astype(np.float64), v.astype(np.float64)
+        opt.step()
+        p, m, v, _ = olib.adamw_step(p, g, m, v, t=t, **_HP)
+        st = opt.state[pt]
+        m_ref, v_ref = st["exp_avg"].numpy(), st["exp_avg_sq"].numpy()
+        g64 = g.astype(np.float64)
+        # each moment update: two scalar roundings, two products, one sum
+        bm = b1 * bm + 4 * u * (b1 * np.abs(m_prev) + (1 - b1) * np.abs(g64))
+        bv = b2 * bv + 5 * u * (b2 * v_prev + (1 - b2) * g64 * g64)
+        assert np.all(np.abs(m - m_ref) <= bm), t
+        assert np.all(np.abs(v - v_ref) <= bv), t
+        # per step: the decay and the subtraction each round p (one ulp
+        # together), and the update (a few lr at most) carries the moments'
+        # relative error, a few dozen ulps (more where m nearly cancels, still
+        # well under 1e-5 of lr)
+        err = np.abs(p - pt.detach().numpy())
+        assert np.all(err <= t * (_HP["lr"] * 1e-5 + 2 * u * np.abs(p))), (t, err.max())
+
+
+def test_adamw_first_step_closed_form(olib):
+    """At t = 1 the bias corrections make m^ = g and v^ = g^2 exactly, so the
+    step without decay is p - lr g / (|g| + eps): about lr against the
+    gradient's sign."""
+    rng = np.random.default_rng(6)
+    g = (rng.choice([-1.0, 1.0], 2000) * 10.0 ** rng.uniform(-4, 0, 2000)).astype(np.float32)
+    p0 = rng.normal(0, 0.02, 2000).astype(np.float32)
+    z = np.zeros_like(p0)
+    hp = dict(_HP, wd=0.0)
+    p, m, v, _ = olib.adamw_step(p0, g, z, z, t=1, **hp)
+    g64 = g.astype(np.float64)
+    want = p0 - hp["lr"] * g64 / (np.abs(g64) + hp["eps"])
+    assert np.allclose(p, want, rtol=0, atol=4 * 2.0 ** -24 * np.abs(p0).max() + 1e-10)
+    assert np.all(np.sign(p - p0) == -np.sign(g))
+
+
+def test_adamw_constant_gradient_keeps_the_step_size(olib):
+    """A gradient held constant for t steps gives m^_t = g and v^_t = g^2 at
+    every t (the bias corrections divide out 1 - beta^t exactly), so each
+    step moves p by lr g / (|g| + eps). An off-by-one in the step count of
+    either correction breaks this from the first steps on."""
+    rng = np.random.default_rng(7)
+    g = (rng.choice([-1.0, 1.0], 512) * 10.0 ** rng.uniform(-3, 0, 512)).astype(np.float32)
+    hp = dict(_HP, wd=0.0, lr=1e-3)
+    p = np.zeros(512, np.float32)
+    m = np.zeros(512, np.float32)
+    v = np.zeros(512, np.float32)
+    step = hp["lr"] * g.astype(np.float64) / (np.abs(g.astype(np.float64)) + hp["eps"])
+    for t in range(1, 21):
+        before = p.astype(np.float64)
+        p, m, v, _ = olib.adamw_step(p, g, m, v, t=t, **hp)
+        moved = before - p.astype(np.float64)
+        assert np.allclose(moved, step, rtol=2e-4, atol=0), t
+
+
+def test_adamw_decay_only_is_exact(olib):
+    """With g = 0 and zero moments the update term is 0 / eps = 0, so the step
+    is the decoupled decay alone: p * RN32(1 - lr*wd), one rounding."""
+    rng = np.random.default_rng(8)
+    p0 = rng.normal(0, 0.02, 1000).astype(np.float32)
+    z = np.zeros_like(p0)
+    hp = dict(_HP, wd=0.1, lr=1e-2)
+    p, m, v, pb = olib.adamw_step(p0, z, z, z, t=3, **hp)
+    decay = np.float32(1.0 - hp["lr"] * hp["wd"])
+    assert np.array_equal(p, p0 * decay)
+    assert not m.any() and not v.any()
+    assert np.array_equal(pb, _rne_bf16(p))
+
+
+def test_adamw_gradient_scale_invariance_without_eps(olib):
+    """With eps = 0 the Adam step is invariant to scaling every gradient by a
+    power of two: m scales by 2^k, v by 2^2k, sqrt(v) by 2^k, all exactly, so
+    the quotient and the parameters come out bit for bit the same. A step that
+    divides by v instead of sqrt(v), or mixes the moments, is not invariant."""
+    rng = np.random.default_rng(9)
+    n = 777
+    p = [rng.normal(0, 0.02, n).astype(np.float32)] * 2
+    m = [np.zeros(n, np.float32)] * 2
+    v = [np.zeros(n, np.float32)] * 2
+    hp = dict(_HP, eps=0.0)
+    for t in range(1, 6):
+        g = rng.normal(0, 1e-3, n).astype(np.float32)
+        out = [olib.adamw_step(p[i], g * np.float32(2.0 ** (6 * i)), m[i], v[i], t=t, **hp)
+               for i in range(2)]
+        p = [o[0] for o in out]
+        m = [o[1] for o in out]
+        v = [o[2] for o in out]
+        assert np.array_equal(p[0], p[1]), t
+        assert np.array_equal(m[0] * np.float32(64.0), m[1]), t
+
+
+def test_adamw_bf16_gradient_and_bf16_copy(olib):
+    """A bf16 gradient acts as its exact fp32 widening; the bf16 adapter copy
+    is the fp32 master rounded to nearest-even."""
+    rng = np.random.default_rng(10)
+    n = 3000
+    gb = syn.normal_bf16((n,), 1e-2, 11)
+    g32 = (gb.astype(np.uint32) << 16).view(np.float32)
+    p0 = rng.normal(0, 0.02, n).astype(np.float32)
+    m0 = rng.normal(0, 1e-3, n).astype(np.float32)
+    v0 = (rng.normal(0, 1e-3, n) ** 2).astype(np.float32)
+    a = olib.adamw_step(p0, gb, m0, v0, t=4, **_HP)
+    b = olib.adamw_step(p0, g32, m0, v0, t=4, **_HP)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    assert np.array_equal(a[3], _rne_bf16(a[0]))
