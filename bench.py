@@ -312,6 +312,8 @@ def main():
         result["bulk_quantize"] = bulk_quantize(q, syn, torch, dev)
         log("merge + requantize")
         result["merge"] = merge_section(q, syn, torch, dev, cfg, nf4, W, A, B, r, alpha)
+        log("adamw step on the adapter arena")
+        result["adamw"] = adamw_section(q, syn, torch, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(np, syn, cfg, step_flops, ms_step_host)
@@ -363,6 +365,50 @@ def merge_section(q, syn, torch, dev, cfg, nf4, W, A, B, r, alpha, iters=10):
                                "frac_hbm_peak": round(q_bytes / (ms_q * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
             "rel_err_vs_16bit_merge": {"merge_into_4bit_then_requantize": round(e4, 5),
                                        "merge_into_bf16_then_quantize": round(ec, 5)}}
+
+
+def adamw_section(q, syn, torch, dev, iters=10):
+    """AdamW on every adapter of a Llama-7B decoder at rank 16 (one flat
+    arena, bf16 gradients, bf16 copy written): 28 bytes per parameter. Timed
+    with HIP events with the state in HBM, then with the master values and
+    moments in pinned host memory (the paged state; 24 of the 28 bytes cross
+    the host link)."""
+    n = syn.adapter_arena_params()
+    g = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_(0.0, 1e-2)
+    pb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    res = {"params": n, "bytes_per_param": 28}
+
+    def run(where, P, M, V):
+        step = [0]
+
+        def one():
+            step[0] += 1
+            q.qlora_adamw_step(P, g, M, V, step=step[0], lr=2e-4, weight_decay=0.01,
+                               param_bf16=pb)
+        for _ in range(2):
+            one()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k = iters if where == "hbm" else 3
+        e0.record()
+        for _ in range(k):
+            one()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / k
+        gbps = 28 * n / (ms * 1e-3) / 1e9
+        res[where] = {"ms": round(ms, 4), "gbps": round(gbps, 1),
+                      "params_per_s": round(n / (ms * 1e-3), 1)}
+        if where == "hbm":
+            res[where]["frac_hbm_peak"] = round(gbps / PEAK_HBM_GBPS, 4)
+
+    P = torch.empty(n, dtype=torch.float32, device=dev).normal_(0.0, 0.02)
+    M = torch.zeros(n, dtype=torch.float32, device=dev)
+    V = torch.zeros(n, dtype=torch.float32, device=dev)
+    run("hbm", P, M, V)
+    Ph, Mh, Vh = (t.cpu().pin_memory() for t in (P, M, V))
+    del P, M, V
+    run("pinned_host", Ph, Mh, Vh)
+    return res
 
 
 def gemv_ring(q, syn, torch, dev, r, alpha):

@@ -183,6 +183,40 @@ int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* 
                      const uint16_t* B, int r, float alpha, float* merged, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* AdamW step on the adapter parameters, in place ([P2] precision table: the
+ * Adam state of an adapter parameter is fp32, 12 bytes - read as the fp32
+ * master value and two fp32 moments; [P4] "The memory term LoRA does not
+ * remove": master copies and optimizer moments are the trained parameters'
+ * state). n parameters as flat arrays, typically every adapter of a model
+ * laid out in one buffer so that one call steps them all:
+ *   param       fp32[n]  master values, updated in place;
+ *   grad        [n]      QLORA_DTYPE_BF16 (the pages' adapter gradients) or
+ *                        QLORA_DTYPE_F32, read only;
+ *   exp_avg     fp32[n]  first moment m, updated in place;
+ *   exp_avg_sq  fp32[n]  second moment v, updated in place;
+ *   param_bf16  bf16[n]  receives RNbf16 of the new master values (the
+ *                        adapter the linear layer reads), or NULL.
+ *   step        the 1-based step number t.
+ * Scalars, each computed on the host in double and rounded once to fp32:
+ *   decay = 1 - lr*weight_decay, c1 = 1 - beta1, c2 = 1 - beta2,
+ *   step_size = lr / (1 - beta1^t), bc2_sqrt = sqrt(1 - beta2^t), and
+ *   beta1, beta2, eps themselves. Per element in fp32, every operation
+ *   rounded to nearest-even and none fused:
+ *   p = p*decay;  m = beta1*m + c1*g;  v = beta2*v + c2*(g*g);
+ *   p = p - step_size * (m / (sqrt(v)/bc2_sqrt + eps)).
+ * Paged state ([P1] paragraph on paged optimizers; [P3] "How it works": the
+ * optimizer state moves to CPU memory instead of the run failing): every
+ * array may live in device memory or in pinned, mapped host memory
+ * (hipHostMalloc); the kernel then streams that array across the host link.
+ * Pageable host memory is rejected with QLORA_ERR_INVALID_ARG. The arrays
+ * must not overlap. n == 0 is a no-op. QLORA_ERR_INVALID_ARG for n < 0,
+ * step < 1, beta outside [0, 1), non-finite lr, eps or weight_decay, or a
+ * NULL array (param_bf16 aside); QLORA_ERR_DTYPE for another grad_dtype;
+ * QLORA_ERR_ALIGN for an array not 16-byte aligned. */
+int qlora_adamw_step(float* param, const void* grad, int grad_dtype, float* exp_avg,
+                     float* exp_avg_sq, uint16_t* param_bf16, int64_t n, double lr, double beta1,
+                     double beta2, double eps, double weight_decay, int64_t step, void* stream);
+
 /* Dense stage of the large-batch path: the product with a weight that is
  * already dequantized ([P1] bullets: the 4-bit weight is expanded to bf16
  * just in time, then multiplied in bf16 with fp32 accumulation; [P3] "How it

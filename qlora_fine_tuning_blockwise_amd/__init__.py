@@ -19,7 +19,8 @@ from . import _lib
 __all__ = [
     "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_id",
     "qlora_workspace_bytes", "qlora_quantize_nf4_dq", "qlora_dequant_bf16",
-    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "qlora_merge_lora", "NF4Weight",
+    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "qlora_merge_lora", "qlora_adamw_step",
+    "NF4Weight",
 ]
 
 
@@ -196,3 +197,25 @@ def qlora_merge_lora(A: torch.Tensor, B: torch.Tensor, alpha: float, w: NF4Weigh
     _lib.check(st, "qlora_merge_lora")
     return out
 
+
+
+def qlora_adamw_step(param: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor,
+                     exp_avg_sq: torch.Tensor, step: int, lr: float, beta1: float = 0.9,
+                     beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+                     param_bf16: torch.Tensor | None = None, stream=None) -> None:
+    """One AdamW step in place on flat fp32 master values, moments and an
+    optional bf16 copy; grad is bf16 or fp32. The arrays may be device tensors
+    or pinned host tensors (the paged state); the step runs on the GPU."""
+    n = param.numel()
+    for name, t, dt in (("param", param, torch.float32), ("exp_avg", exp_avg, torch.float32),
+                        ("exp_avg_sq", exp_avg_sq, torch.float32),
+                        ("param_bf16", param_bf16, torch.bfloat16)):
+        if t is not None and (t.dtype != dt or t.numel() != n):
+            raise ValueError(f"qlora_adamw_step: {name} must be {dt} with {n} elements")
+    if grad.numel() != n:
+        raise ValueError("qlora_adamw_step: grad must have as many elements as param")
+    st = _lib.load().qlora_adamw_step(_ptr(param), _ptr(grad), _dtype_code(grad.dtype),
+                                      _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(param_bf16), n,
+                                      float(lr), float(beta1), float(beta2), float(eps),
+                                      float(weight_decay), int(step), _stream(stream))
+    _lib.check(st, "qlora_adamw_step")

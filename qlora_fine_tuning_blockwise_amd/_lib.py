@@ -25,6 +25,7 @@ I64 = ctypes.c_int64
 INT = ctypes.c_int
 SZ = ctypes.c_size_t
 FLT = ctypes.c_float
+DBL = ctypes.c_double
 
 SIGNATURES = {
     "qlora_strerror": (ctypes.c_char_p, [INT]),
@@ -39,6 +40,7 @@ SIGNATURES = {
                                P, SZ, P]),
     "qlora_gemm_bf16_nt": (INT, [P, I64, P, I64, P, P, I64, I64, I64, INT, P, INT, P]),
     "qlora_merge_lora": (INT, [P, P, P, P, I64, I64, P, P, INT, FLT, P, P, SZ, P]),
+    "qlora_adamw_step": (INT, [P, P, INT, P, P, P, I64, DBL, DBL, DBL, DBL, DBL, I64, P]),
 }
 
 _lib = None

@@ -2,6 +2,7 @@
 // sequence of each entry point. Every check runs on the host before anything
 // is enqueued; the compute entry points only enqueue kernels on the caller's
 // stream.
+#include <cmath>
 #include <cstring>
 
 #include "../../include/qlora_amd.h"
@@ -107,6 +108,24 @@ T* at(void* base, size_t off) {
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
+
+// The address a kernel uses for p: device memory as it is; host memory only
+// if the runtime has pinned it and mapped it for the device (hipHostMalloc),
+// translated to its device-side address; managed memory as it is. Returns
+// NULL for anything else (pageable host memory is not reachable).
+void* device_view(void* p) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the lookup failure; it is not a launch error
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged || a.isManaged)
+    return p;
+  if (a.type == hipMemoryTypeHost && a.devicePointer && a.hostPointer)
+    return static_cast<char*>(a.devicePointer) +
+           (static_cast<char*>(p) - static_cast<char*>(a.hostPointer));
+  return nullptr;
+}
 
 }  // namespace
 }  // namespace qlora
@@ -362,6 +381,40 @@ int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* 
     e = launch_merge(W ? nullptr : codes, absmax_q, absmax_scale, W, N, K, At, Bt, r,
                      alpha / (float)r, merged, *cb, st);
   return launch_status(e);
+}
+
+int qlora_adamw_step(float* param, const void* grad, int grad_dtype, float* exp_avg,
+                     float* exp_avg_sq, uint16_t* param_bf16, int64_t n, double lr, double beta1,
+                     double beta2, double eps, double weight_decay, int64_t step, void* stream) {
+  if (n < 0 || step < 1) return QLORA_ERR_INVALID_ARG;
+  if (grad_dtype != QLORA_DTYPE_F32 && grad_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
+  if (!(beta1 >= 0.0 && beta1 < 1.0 && beta2 >= 0.0 && beta2 < 1.0)) return QLORA_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(weight_decay))
+    return QLORA_ERR_INVALID_ARG;
+  if (n == 0) return QLORA_OK;
+  if (!param || !grad || !exp_avg || !exp_avg_sq) return QLORA_ERR_INVALID_ARG;
+  const void* ptrs[] = {param, grad, exp_avg, exp_avg_sq, param_bf16};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
+  void* view[5] = {param, const_cast<void*>(grad), exp_avg, exp_avg_sq, param_bf16};
+  for (void*& p : view) {
+    if (p && !(p = device_view(p))) return QLORA_ERR_INVALID_ARG;
+    if (p && !aligned16(p)) return QLORA_ERR_ALIGN;  // the mapped address, too
+  }
+  const double b1t = std::pow(beta1, (double)step), b2t = std::pow(beta2, (double)step);
+  AdamScalars s;
+  s.b1 = (float)beta1;
+  s.b2 = (float)beta2;
+  s.eps = (float)eps;
+  s.decay = (float)(1.0 - lr * weight_decay);
+  s.c1 = (float)(1.0 - beta1);
+  s.c2 = (float)(1.0 - beta2);
+  s.step_size = (float)(lr / (1.0 - b1t));
+  s.bc2_sqrt = (float)std::sqrt(1.0 - b2t);
+  return launch_status(launch_adamw(static_cast<float*>(view[0]), view[1],
+                                    grad_dtype == QLORA_DTYPE_BF16, static_cast<float*>(view[2]),
+                                    static_cast<float*>(view[3]), static_cast<uint16_t*>(view[4]),
+                                    n, s, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -89,6 +89,21 @@ hipError_t launch_merge(const uint8_t* codes, const int8_t* q8, const float* s2,
                         const uint16_t* Bt, int r, float s, float* out, const Codebook& cb,
                         hipStream_t st);
 
+// AdamW step scalars, each computed on the host in double from the
+// hyper-parameters and rounded once to binary32.
+struct AdamScalars {
+  float b1, b2, eps;  // beta1, beta2, eps
+  float decay;        // 1 - lr*wd
+  float c1, c2;       // 1 - beta1, 1 - beta2
+  float step_size;    // lr / (1 - beta1^t)
+  float bc2_sqrt;     // sqrt(1 - beta2^t)
+};
+
+// AdamW on n parameters in place (p, m, v fp32; g bf16 or fp32; pb the bf16
+// copy of p, may be NULL). Pointers may be device or mapped host memory.
+hipError_t launch_adamw(float* p, const void* g, bool g_bf16, float* m, float* v, uint16_t* pb,
+                        int64_t n, const AdamScalars& s, hipStream_t st);
+
 // Adapter gradients: part[split][c][j] = sum_{m in split} X[m][c] * P[m][j]
 // (X [M,C] bf16; P given as the transposed two-term bf16 split PT [2r, Mp]
 // written by launch_lora_down_finalize), then out = s * sum_split part,

@@ -30,6 +30,35 @@ LAYER_70B = dict(name="llama70b_layer",
 BULK_65B = dict(name="bulk_quantize_65b", tensor=(8192, 28672), n_tensors=277,
                 w_dtype="bf16")
 
+# Adapters of every linear layer of a Llama-7B decoder (32 layers; q, k, v, o
+# 4096x4096; gate, up 11008x4096; down 4096x11008) at rank 16, laid out
+# back to back in one flat arena: A [K, r] then B [r, N] per projection.
+LLAMA7B_PROJECTIONS = {"q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096),
+                       "o": (4096, 4096), "gate": (11008, 4096), "up": (11008, 4096),
+                       "down": (4096, 11008)}
+
+
+def adapter_arena_params(projections=LLAMA7B_PROJECTIONS, layers: int = 32, r: int = 16) -> int:
+    """Trainable parameters of the adapters: r (K + N) per projection."""
+    return layers * sum(r * (K + N) for N, K in projections.values())
+
+
+def adam_state(n: int, seed: int):
+    """A mid-training optimizer state: fp32 master values N(0, 0.02), first
+    moments N(0, 1e-3), second moments (N(0, 1e-3))^2."""
+    g = np.random.default_rng(seed)
+    p = (g.standard_normal(n, dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    m = (g.standard_normal(n, dtype=np.float32) * np.float32(1e-3)).astype(np.float32)
+    v = np.square(g.standard_normal(n, dtype=np.float32) * np.float32(1e-3)).astype(np.float32)
+    return p, m, v
+
+
+def adapter_grad_f32(n: int, seed: int) -> np.ndarray:
+    """Heavy-tailed adapter gradients: N(0, 1e-2) times a log-normal(0, 1) scale."""
+    g = np.random.default_rng(seed)
+    z = g.standard_normal(n, dtype=np.float32) * np.float32(1e-2)
+    return (z * g.lognormal(0.0, 1.0, n).astype(np.float32)).astype(np.float32)
+
 
 def seed_of(workload: int, index: int) -> int:
     return 1000 * workload + index

@@ -202,3 +202,26 @@ def test_bucket_code_search_exhaustive(arith, lib):
     n = ctypes.c_int64()
     bad = arith.check_buckets(th.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n))
     assert n.value == 2 * (0x3F800000 + 1) and bad == 0
+
+
+def test_adamw_validation(lib):
+    f = lib.qlora_adamw_step
+    base = [_p(FAKE), _p(FAKE), 1, _p(FAKE), _p(FAKE), None, 1000, 1e-4, 0.9, 0.999, 1e-8, 0.0,
+            1, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+    assert call(6, -1) == 1             # n < 0
+    assert call(12, 0) == 1             # step < 1
+    assert call(2, 7) == 4              # grad dtype
+    assert call(8, 1.0) == 1            # beta1 outside [0, 1)
+    assert call(9, -0.1) == 1           # beta2 outside [0, 1)
+    assert call(7, float("nan")) == 1   # lr not finite
+    assert call(10, float("inf")) == 1  # eps not finite
+    assert call(3, None) == 1           # exp_avg missing
+    assert call(1, None) == 1           # grad missing
+    assert call(0, _p(FAKE + 4)) == 3   # param misaligned
+    assert call(5, _p(FAKE + 8)) == 3   # bf16 copy misaligned
+    assert call(6, 0) == 0              # empty: nothing to do

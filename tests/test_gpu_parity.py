@@ -540,3 +540,100 @@ def test_merge_zero_adapter_gives_the_dequantized_base():
     torch.cuda.synchronize()
     assert torch.equal(merged, deq.float())
 
+
+
+# ------------------------------------------------------------------- AdamW
+_ADAM = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.01)
+
+
+def _adam_gpu_steps(p, m, v, grads, gbf16, want_copy, pinned=False, t0=1):
+    """Runs the steps through the C ABI; state on the device, or in pinned
+    host memory when `pinned` (the paged optimizer state)."""
+    def put(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return t.pin_memory() if pinned else t.to(DEV)
+    P, Mm, V = put(p), put(m), put(v)
+    pb = torch.empty(p.size, dtype=torch.bfloat16, device=DEV) if want_copy else None
+    for i, g in enumerate(grads):
+        G = dev_bf16(syn.to_bf16_bits(g)) if gbf16 else torch.from_numpy(g).to(DEV)
+        q.qlora_adamw_step(P, G, Mm, V, step=t0 + i, lr=_ADAM["lr"], beta1=_ADAM["beta1"],
+                           beta2=_ADAM["beta2"], eps=_ADAM["eps"], weight_decay=_ADAM["wd"],
+                           param_bf16=pb)
+    torch.cuda.synchronize()
+    out = [host(P), host(Mm), host(V)]
+    out.append(syn.torch_bf16_to_bits(pb) if want_copy else None)
+    return out
+
+
+def _adam_oracle_steps(p, m, v, grads, gbf16, t0=1):
+    pb = None
+    for i, g in enumerate(grads):
+        gi = syn.to_bf16_bits(g) if gbf16 else g
+        p, m, v, pb = oracle.adamw_step(p, gi, m, v, _ADAM["lr"], _ADAM["beta1"], _ADAM["beta2"],
+                                        _ADAM["eps"], _ADAM["wd"], t0 + i)
+    return p, m, v, pb
+
+
+def _assert_bits(got, ref, name):
+    g = np.ascontiguousarray(got).view(np.uint32 if got.dtype == np.float32 else np.uint16)
+    r = np.ascontiguousarray(ref).view(np.uint32 if ref.dtype == np.float32 else np.uint16)
+    if not np.array_equal(g, r):
+        i = int(np.argmax(g != r))
+        raise AssertionError(f"{name}: first difference at {i}: {got[i]!r} vs {ref[i]!r}")
+
+
+@pytest.mark.parametrize("n,gbf16,copy,steps,t0", [(8, True, True, 1, 1), (1003, True, True, 3, 1),
+                                                   (4096 + 5, False, True, 2, 7),
+                                                   (777777, True, False, 2, 100),
+                                                   (1, False, True, 1, 1)])
+def test_adamw_bit_exact(n, gbf16, copy, steps, t0):
+    """p, m, v and the bf16 copy bit for bit against the oracle over several
+    steps; ragged n (the tail thread's scalar path), both gradient types."""
+    say("adamw", n, gbf16, copy, steps, t0)
+    p, m, v = syn.adam_state(n, 70 + n % 97)
+    grads = [syn.adapter_grad_f32(n, 80 + i) for i in range(steps)]
+    got = _adam_gpu_steps(p, m, v, grads, gbf16, copy, t0=t0)
+    ref = _adam_oracle_steps(p, m, v, grads, gbf16, t0=t0)
+    for k, (a, b) in enumerate(zip(got[:3], ref[:3])):
+        _assert_bits(a, b, "pmv"[k])
+    if copy:
+        _assert_bits(got[3], ref[3], "bf16 copy")
+
+
+def test_adamw_full_adapter_arena_bit_exact():
+    """Every adapter of a Llama-7B decoder at rank 16 (39,976,960 parameters
+    in one arena), one step with bf16 gradients, against the oracle."""
+    n = syn.adapter_arena_params()
+    say("adamw arena", n)
+    p, m, v = syn.adam_state(n, 71)
+    grads = [syn.adapter_grad_f32(n, 81)]
+    got = _adam_gpu_steps(p, m, v, grads, True, True, t0=5)
+    ref = _adam_oracle_steps(p, m, v, grads, True, t0=5)
+    for k, (a, b) in enumerate(zip(got, ref)):
+        _assert_bits(a, b, "pmvb"[k])
+
+
+def test_adamw_paged_state_in_host_memory():
+    """The paged state: master values and moments in pinned host memory,
+    stepped by the GPU kernel across the host link, give the same bits."""
+    n = 100003
+    say("adamw paged", n)
+    p, m, v = syn.adam_state(n, 72)
+    grads = [syn.adapter_grad_f32(n, 90 + i) for i in range(2)]
+    got = _adam_gpu_steps(p, m, v, grads, True, True, pinned=True)
+    ref = _adam_oracle_steps(p, m, v, grads, True)
+    for k, (a, b) in enumerate(zip(got, ref)):
+        _assert_bits(a, b, "pmvb"[k])
+
+
+def test_adamw_rejects_pageable_host_memory():
+    """Memory the device cannot reach is refused before any launch."""
+    n = 64
+    P = torch.zeros(n, dtype=torch.float32)  # plain pageable host tensor
+    G = torch.zeros(n, dtype=torch.float32, device=DEV)
+    Mm = torch.zeros(n, dtype=torch.float32, device=DEV)
+    V = torch.zeros(n, dtype=torch.float32, device=DEV)
+    with pytest.raises(RuntimeError):
+        q.qlora_adamw_step(P, G, Mm, V, step=1, lr=1e-3)
+    torch.cuda.synchronize()
+    assert not P.any()
