@@ -68,8 +68,15 @@ def lib() -> ctypes.CDLL:
             "oracle_linear_fwd": (ctypes.c_int, [P, I64, I64, P, I64, P, P, ctypes.c_int, D, P, P]),
             "oracle_linear_bwd": (ctypes.c_int,
                                   [P, P, I64, I64, P, I64, P, P, ctypes.c_int, D, P, P, P]),
-            "oracle_merge_lora": (ctypes.c_int, [P, P, P, P, I64, I64, P, P, ctypes.c_int,
-                                                 ctypes.c_float, P]),
+            "oracle_merge_lora": (ctypes.c_int, [P, P, P, ctypes.c_int, P, I64, I64, P, P,
+                                                 ctypes.c_int, ctypes.c_float, P]),
+            "oracle_e4m3_to_f32": (ctypes.c_float, [ctypes.c_uint8]),
+            "oracle_f32_to_e4m3": (ctypes.c_uint8, [ctypes.c_float]),
+            "oracle_q8_value": (ctypes.c_float, [ctypes.c_uint8, ctypes.c_int]),
+            "oracle_double_quant_fmt": (ctypes.c_int, [P, I64, ctypes.c_int, P, P]),
+            "oracle_quantize_nf4_dq_fmt": (ctypes.c_int, [P, ctypes.c_int, I64, ctypes.c_int, P,
+                                                          P, P]),
+            "oracle_dequant_dq_fmt": (ctypes.c_int, [P, P, P, I64, ctypes.c_int, P, P]),
             "oracle_adamw_step": (ctypes.c_int, [P, P, ctypes.c_int, P, P, I64] +
                                   [D] * 5 + [I64, P]),
         }
@@ -141,45 +148,63 @@ def quantize_nf4_first(w) -> tuple[np.ndarray, np.ndarray]:
     return codes, c1
 
 
-def double_quant(c1):
+# Second-level formats of the 8-bit absmax code (the q8 arrays below are
+# byte containers of dtype int8 in every format).
+DQ_INT8, DQ_UINT8, DQ_E4M3 = 0, 1, 2
+
+
+def e4m3_to_f32(b) -> np.ndarray:
+    """Values of FP8 E4M3 codes (uint8 array)."""
+    b = _c(b, np.uint8).ravel()
+    return np.array([lib().oracle_e4m3_to_f32(int(x)) for x in b], np.float32)
+
+
+def f32_to_e4m3(x) -> np.ndarray:
+    """Nearest E4M3 codes of non-negative fp32 values (ties to even, saturating)."""
+    x = _c(x, np.float32).ravel()
+    return np.array([lib().oracle_f32_to_e4m3(float(v)) for v in x], np.uint8)
+
+
+def double_quant(c1, fmt: int = DQ_INT8):
     c1 = _c(c1, np.float32).ravel()
     nb = c1.size
     q8 = np.zeros(nb, np.int8)
     s2 = np.zeros((nb + GROUP - 1) // GROUP, np.float32)
-    _check(lib().oracle_double_quant(_p(c1), nb, _p(q8), _p(s2)), "double_quant")
+    _check(lib().oracle_double_quant_fmt(_p(c1), nb, int(fmt), _p(q8), _p(s2)), "double_quant")
     return q8, s2
 
 
-def quantize_nf4_dq(w, dtype: str):
-    """Both levels. ``dtype`` is 'f32' (fp32 values) or 'bf16' (uint16 bit patterns).
+def quantize_nf4_dq(w, dtype: str, fmt: int = DQ_INT8):
+    """Both levels. ``dtype`` is 'f32' (fp32 values) or 'bf16' (uint16 bit
+    patterns); ``fmt`` the second-level format.
 
-    Returns (codes uint8[n/2], q8 int8[n/64], s2 fp32[ceil(n/16384)]).
+    Returns (codes uint8[n/2], q8 int8[n/64] (bytes), s2 fp32[ceil(n/16384)]).
     """
     if dtype == "f32":
         w = _c(w, np.float32).ravel()
-        fn = lib().oracle_quantize_nf4_dq_f32
     elif dtype == "bf16":
         w = _c(w, np.uint16).ravel()
-        fn = lib().oracle_quantize_nf4_dq_bf16
     else:
         raise ValueError(dtype)
     nc, nb, ng = sizes(w.size)
     codes = np.zeros(nc, np.uint8)
     q8 = np.zeros(nb, np.int8)
     s2 = np.zeros(ng, np.float32)
-    _check(fn(_p(w), w.size, _p(codes), _p(q8), _p(s2)), "quantize_nf4_dq")
+    _check(lib().oracle_quantize_nf4_dq_fmt(_p(w), int(dtype == "bf16"), w.size, int(fmt),
+                                            _p(codes), _p(q8), _p(s2)), "quantize_nf4_dq")
     return codes, q8, s2
 
 
-def dequant_dq(codes, q8, s2):
+def dequant_dq(codes, q8, s2, fmt: int = DQ_INT8):
     """(fp32 products, bf16 bit patterns) of every weight."""
     codes = _c(codes, np.uint8).ravel()
-    q8 = _c(q8, np.int8).ravel()
+    q8 = np.ascontiguousarray(q8).view(np.uint8).ravel()
     s2 = _c(s2, np.float32).ravel()
     n = codes.size * 2
     w32 = np.zeros(n, np.float32)
     wb = np.zeros(n, np.uint16)
-    _check(lib().oracle_dequant_dq(_p(codes), _p(q8), _p(s2), n, _p(w32), _p(wb)), "dequant_dq")
+    _check(lib().oracle_dequant_dq_fmt(_p(codes), _p(q8), _p(s2), n, int(fmt), _p(w32), _p(wb)),
+           "dequant_dq")
     return w32, wb
 
 
@@ -274,19 +299,22 @@ def linear_bwd(x, dY, What, A, B, r: int, alpha: float, want=("dX", "dA", "dB"))
 def merge_lora(A, B, r: int, alpha: float, nf4=None, W=None):
     """[P1] bullets (merging forces a re-quantization); [P4] "Merge friction".
     out = base + (alpha/r) (A B)^T in binary32 with the adapter sum in order
-    j = 0..r-1, one fused multiply-add per term; base = dequantized NF4 (nf4 = (codes, q8, s2, N, K)) or the
-    bf16 weight W [N, K] (uint16 bits). Returns fp32 [N, K]."""
+    j = 0..r-1, one fused multiply-add per term; base = dequantized NF4 (nf4 =
+    (codes, q8, s2, N, K[, fmt])) or the bf16 weight W [N, K] (uint16 bits).
+    Returns fp32 [N, K]."""
     A = _c(A, np.uint16)
     B = _c(B, np.uint16)
     if W is not None:
         W = _c(W, np.uint16)
         N, K = W.shape
         codes = q8 = s2 = None
+        fmt = DQ_INT8
     else:
-        codes, q8, s2, N, K = nf4
+        codes, q8, s2, N, K = nf4[:5]
+        fmt = nf4[5] if len(nf4) > 5 else DQ_INT8
         codes, q8, s2 = _c(codes, np.uint8), _c(q8, np.int8), _c(s2, np.float32)
     out = np.empty((N, K), np.float32)
-    _check(lib().oracle_merge_lora(_p(codes), _p(q8), _p(s2), _p(W), N, K, _p(A), _p(B), r,
+    _check(lib().oracle_merge_lora(_p(codes), _p(q8), _p(s2), int(fmt), _p(W), N, K, _p(A), _p(B), r,
                                    float(alpha), _p(out)), "merge_lora")
     return out
 

@@ -162,13 +162,55 @@ int oracle_nf4_codes_batch(const float* x, int64_t n, uint8_t* out) {
     return 0;
 }
 
+/* OCP FP8 E4M3 (E4M3FN): sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * no infinities; S.1111.111 is NaN; largest finite value 448; exponent field
+ * 0 holds the subnormals m * 2^-9. */
+float oracle_e4m3_to_f32(uint8_t b) {
+    const int sgn = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return (float)(sgn ? -v : v);
+}
+
+/* Nearest E4M3 value to a non-negative x, ties to the even code (the even
+ * mantissa); x >= 448 (or +inf) gives 448. Non-negative codes 0x00..0x7E
+ * increase with their value, so the code is found by walking up to the
+ * interval [v_k, v_k+1) that holds x and comparing x with its midpoint,
+ * which is exact in double. */
+uint8_t oracle_f32_to_e4m3(float x) {
+    if (!(x < 448.0f)) return 0x7E;
+    int k = 0;
+    while (k < 0x7E && (double)x >= (double)oracle_e4m3_to_f32((uint8_t)(k + 1))) ++k;
+    if (k == 0x7E) return 0x7E;
+    const double lo = oracle_e4m3_to_f32((uint8_t)k), hi = oracle_e4m3_to_f32((uint8_t)(k + 1));
+    const double mid = (lo + hi) / 2.0;
+    if ((double)x > mid) return (uint8_t)(k + 1);
+    if ((double)x < mid) return (uint8_t)k;
+    return (uint8_t)((k & 1) ? k + 1 : k);
+}
+
+/* The value of a stored 8-bit absmax code in each second-level format. */
+float oracle_q8_value(uint8_t b, int fmt) {
+    if (fmt == ORACLE_DQ_INT8) return (float)(int8_t)b;
+    if (fmt == ORACLE_DQ_UINT8) return (float)b;
+    return oracle_e4m3_to_f32(b);
+}
+
 /* [P1] bullets "double quantization quantizes the scales themselves to
- * 8-bit"; [P2] s1 "Double Quantization"; [P5] "Double Quantization". The
- * only quantizer formula on the pages ([P1] controlled-rounding equation) is
- * applied to the non-negative block constants with an 8-bit symmetric grid:
- * s2 = c2/127, q8 = round(c1/s2), over groups of 256 blocks. */
-int oracle_double_quant(const float* c1, int64_t nblocks, int8_t* q8, float* s2) {
+ * 8-bit"; [P2] s1 "Double Quantization" (the scales are quantized to FP8);
+ * [P5] "Double Quantization". Over groups of 256 blocks, with c2 the largest
+ * block constant of the group and every operation in binary32:
+ *   ORACLE_DQ_INT8:  the pages' one quantizer formula ([P1] controlled-
+ *                    rounding equation) on an 8-bit symmetric grid:
+ *                    s2 = c2/127, q8 = round(c1/s2), ties to the lower, 0..127;
+ *   ORACLE_DQ_UINT8: the same on the unsigned byte: s2 = c2/255, 0..255;
+ *   ORACLE_DQ_E4M3:  s2 = c2/448, q8 = the nearest E4M3 value of c1/s2
+ *                    (ties to even, saturating at 448).
+ * A zero constant always gets the code 0. */
+int oracle_double_quant_fmt(const float* c1, int64_t nblocks, int fmt, uint8_t* q8, float* s2) {
     if (!c1 || !q8 || !s2 || nblocks < 0) return 1;
+    if (fmt != ORACLE_DQ_INT8 && fmt != ORACLE_DQ_UINT8 && fmt != ORACLE_DQ_E4M3) return 1;
+    const float top = fmt == ORACLE_DQ_INT8 ? 127.0f : fmt == ORACLE_DQ_UINT8 ? 255.0f : 448.0f;
     int64_t ng = (nblocks + ORACLE_GROUP - 1) / ORACLE_GROUP;
     for (int64_t g = 0; g < ng; ++g) {
         int64_t b0 = g * ORACLE_GROUP;
@@ -177,57 +219,64 @@ int oracle_double_quant(const float* c1, int64_t nblocks, int8_t* q8, float* s2)
         float c2 = 0.0f;
         for (int64_t b = b0; b < b1; ++b)
             if (c1[b] > c2) c2 = c1[b];
-        float scale = c2 / 127.0f;
+        float scale = c2 / top;
         s2[g] = scale;
         for (int64_t b = b0; b < b1; ++b) {
-            int q;
             if (c1[b] == 0.0f) {
-                q = 0;
+                q8[b] = 0;
+                continue;
+            }
+            float v = c1[b] / scale; /* +inf if scale underflowed to 0 */
+            if (fmt == ORACLE_DQ_E4M3) {
+                q8[b] = oracle_f32_to_e4m3(v);
             } else {
-                float v = c1[b] / scale; /* +inf if scale underflowed to 0 */
                 double r = ceil((double)v - 0.5); /* nearest, ties to the lower */
                 if (r < 0.0) r = 0.0;
-                if (r > 127.0) r = 127.0;
-                q = (int)r;
+                if (r > (double)top) r = (double)top;
+                q8[b] = (uint8_t)(int)r;
             }
-            q8[b] = (int8_t)q;
         }
     }
     return 0;
 }
 
-int oracle_quantize_nf4_dq_f32(const float* w, int64_t n, uint8_t* codes, int8_t* q8, float* s2) {
-    if (!w || !codes || !q8 || !s2 || n < 0 || n % ORACLE_BLOCK) return 1;
-    int64_t nb = n / ORACLE_BLOCK;
-    float* c1 = (float*)malloc((size_t)(nb > 0 ? nb : 1) * sizeof(float));
-    if (!c1) return 3;
-    int rc = oracle_quantize_nf4_f32(w, n, codes, c1);
-    if (rc == 0) rc = oracle_double_quant(c1, nb, q8, s2);
-    free(c1);
-    return rc;
+int oracle_double_quant(const float* c1, int64_t nblocks, int8_t* q8, float* s2) {
+    return oracle_double_quant_fmt(c1, nblocks, ORACLE_DQ_INT8, (uint8_t*)q8, s2);
 }
 
-int oracle_quantize_nf4_dq_bf16(const uint16_t* w, int64_t n, uint8_t* codes, int8_t* q8,
-                                float* s2) {
+/* Both levels for fp32 (is_bf16 == 0) or bf16 input (raw 16-bit patterns,
+ * widened exactly) in the second-level format fmt. */
+int oracle_quantize_nf4_dq_fmt(const void* w, int is_bf16, int64_t n, int fmt, uint8_t* codes,
+                               uint8_t* q8, float* s2) {
     if (!w || !codes || !q8 || !s2 || n < 0 || n % ORACLE_BLOCK) return 1;
     float lv[16], th[15];
     oracle_nf4_codebook(lv, th);
-    /* Widen block by block (exact), then quantize as fp32. */
     float buf[ORACLE_BLOCK];
     int64_t nb = n / ORACLE_BLOCK;
     float* c1 = (float*)malloc((size_t)(nb > 0 ? nb : 1) * sizeof(float));
     if (!c1) return 3;
     for (int64_t b = 0; b < nb; ++b) {
-        for (int i = 0; i < ORACLE_BLOCK; ++i) buf[i] = oracle_bf16_to_f32(w[b * ORACLE_BLOCK + i]);
+        for (int i = 0; i < ORACLE_BLOCK; ++i)
+            buf[i] = is_bf16 ? oracle_bf16_to_f32(((const uint16_t*)w)[b * ORACLE_BLOCK + i])
+                             : ((const float*)w)[b * ORACLE_BLOCK + i];
         int rc = quantize_blocks(buf, 1, codes + b * (ORACLE_BLOCK / 2), c1 + b, th);
         if (rc) {
             free(c1);
             return rc;
         }
     }
-    int rc = oracle_double_quant(c1, nb, q8, s2);
+    int rc = oracle_double_quant_fmt(c1, nb, fmt, q8, s2);
     free(c1);
     return rc;
+}
+
+int oracle_quantize_nf4_dq_f32(const float* w, int64_t n, uint8_t* codes, int8_t* q8, float* s2) {
+    return oracle_quantize_nf4_dq_fmt(w, 0, n, ORACLE_DQ_INT8, codes, (uint8_t*)q8, s2);
+}
+
+int oracle_quantize_nf4_dq_bf16(const uint16_t* w, int64_t n, uint8_t* codes, int8_t* q8,
+                                float* s2) {
+    return oracle_quantize_nf4_dq_fmt(w, 1, n, ORACLE_DQ_INT8, codes, (uint8_t*)q8, s2);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -237,20 +286,26 @@ int oracle_quantize_nf4_dq_bf16(const uint16_t* w, int64_t n, uint8_t* codes, in
 /* in time; [P2] s3 "The Backward Pass Through Quantization" step 1.        */
 /* ------------------------------------------------------------------------ */
 
-int oracle_dequant_dq(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t n,
-                      float* w32, uint16_t* wbf16) {
+int oracle_dequant_dq_fmt(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t n,
+                          int fmt, float* w32, uint16_t* wbf16) {
     if (!codes || !q8 || !s2 || n < 0 || n % ORACLE_BLOCK) return 1;
+    if (fmt != ORACLE_DQ_INT8 && fmt != ORACLE_DQ_UINT8 && fmt != ORACLE_DQ_E4M3) return 1;
     float lv[16], th[15];
     oracle_nf4_codebook(lv, th);
     for (int64_t e = 0; e < n; ++e) {
         int64_t b = e / ORACLE_BLOCK;
-        float c1hat = (float)q8[b] * s2[b / ORACLE_GROUP];
+        float c1hat = oracle_q8_value(q8[b], fmt) * s2[b / ORACLE_GROUP];
         int code = (e & 1) ? (codes[e / 2] >> 4) : (codes[e / 2] & 15);
         float v = lv[code] * c1hat;
         if (w32) w32[e] = v;
         if (wbf16) wbf16[e] = oracle_f32_to_bf16(v);
     }
     return 0;
+}
+
+int oracle_dequant_dq(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t n,
+                      float* w32, uint16_t* wbf16) {
+    return oracle_dequant_dq_fmt(codes, (const uint8_t*)q8, s2, n, ORACLE_DQ_INT8, w32, wbf16);
 }
 
 int oracle_dequant_nodq(const uint8_t* codes, const float* c1, int64_t n, float* w32,
@@ -451,7 +506,7 @@ int oracle_linear_bwd(const uint16_t* x, const uint16_t* dY, int64_t M, int64_t 
 /* s = alpha / r in binary32. base is the dequantized NF4 weight (w_hat as  */
 /* bf16, widened) when wbf16 is NULL, else the bf16 weight.                 */
 /* ------------------------------------------------------------------------ */
-int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2,
+int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2, int fmt,
                       const uint16_t* wbf16, int64_t N, int64_t K, const uint16_t* A,
                       const uint16_t* B, int r, float alpha, float* out) {
     if (N < 1 || K < 1 || K % ORACLE_BLOCK || r < 1 || !A || !B || !out) return 1;
@@ -461,7 +516,7 @@ int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2,
     if (!wbf16) {
         base = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(N * K));
         if (!base) return 2;
-        if (oracle_dequant_dq(codes, q8, s2, N * K, NULL, base)) {
+        if (oracle_dequant_dq_fmt(codes, (const uint8_t*)q8, s2, N * K, fmt, NULL, base)) {
             free(base);
             return 1;
         }

@@ -38,6 +38,11 @@ extern "C" {
 #define ORACLE_BLOCK 64
 #define ORACLE_GROUP 256
 
+/* Second-level (double quantization) formats of the 8-bit absmax code. */
+#define ORACLE_DQ_INT8 0  /* s2 = c2/127, q8 in 0..127 (the default) */
+#define ORACLE_DQ_UINT8 1 /* s2 = c2/255, q8 in 0..255 */
+#define ORACLE_DQ_E4M3 2  /* s2 = c2/448, q8 an FP8 E4M3 value */
+
 /* Standard normal CDF and its inverse (bisection on the CDF). */
 double oracle_norm_cdf(double t);
 double oracle_norm_ppf(double p);
@@ -54,17 +59,31 @@ int oracle_nf4_codes_batch(const float* x, int64_t n, uint8_t* out);
 /* First level: per-64 absmax and packed NF4 codes. n % 64 == 0. */
 int oracle_quantize_nf4_f32(const float* w, int64_t n, uint8_t* codes, float* c1);
 
-/* Second level: q8/s2 from the fp32 block constants. */
+/* FP8 E4M3 (OCP E4M3FN) decoding, and encoding of x >= 0 to the nearest
+ * value with ties to even, saturating at 448. */
+float oracle_e4m3_to_f32(uint8_t b);
+uint8_t oracle_f32_to_e4m3(float x);
+
+/* The value of a stored 8-bit absmax code in format fmt. */
+float oracle_q8_value(uint8_t b, int fmt);
+
+/* Second level: q8/s2 from the fp32 block constants (default format, and
+ * any format). */
 int oracle_double_quant(const float* c1, int64_t nblocks, int8_t* q8, float* s2);
+int oracle_double_quant_fmt(const float* c1, int64_t nblocks, int fmt, uint8_t* q8, float* s2);
 
 /* Both levels, fp32 input and bf16 input (bf16 given as raw 16-bit patterns). */
 int oracle_quantize_nf4_dq_f32(const float* w, int64_t n, uint8_t* codes, int8_t* q8, float* s2);
 int oracle_quantize_nf4_dq_bf16(const uint16_t* w, int64_t n, uint8_t* codes, int8_t* q8, float* s2);
+int oracle_quantize_nf4_dq_fmt(const void* w, int is_bf16, int64_t n, int fmt, uint8_t* codes,
+                               uint8_t* q8, float* s2);
 
 /* Dequantization with double-quantized constants: writes fp32 product and its
  * bf16 rounding (either output may be NULL). */
 int oracle_dequant_dq(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t n,
                       float* w32, uint16_t* wbf16);
+int oracle_dequant_dq_fmt(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t n,
+                          int fmt, float* w32, uint16_t* wbf16);
 
 /* Dequantization with the exact fp32 block constants (no second level). */
 int oracle_dequant_nodq(const uint8_t* codes, const float* c1, int64_t n, float* w32,
@@ -100,7 +119,7 @@ int oracle_linear_bwd(const uint16_t* x, const uint16_t* dY, int64_t M, int64_t 
  * out = base + s * (A B)^T with the adapter sum taken in order j = 0..r-1,
  * one fused multiply-add per term.
  * base = the dequantized NF4 weight (wbf16 == NULL) or the bf16 weight. */
-int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2,
+int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2, int fmt,
                       const uint16_t* wbf16, int64_t N, int64_t K, const uint16_t* A,
                       const uint16_t* B, int r, float alpha, float* out);
 

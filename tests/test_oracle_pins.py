@@ -672,3 +672,122 @@ def test_adamw_bf16_gradient_and_bf16_copy(olib):
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
     assert np.array_equal(a[3], _rne_bf16(a[0]))
+
+
+# ------------------------------------------------ second-level format variants
+def _torch_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    torch = pytest.importorskip("torch")
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.float().numpy()
+
+
+def _torch_e4m3_encode(x: np.ndarray) -> np.ndarray:
+    torch = pytest.importorskip("torch")
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_matches_torch_float8(olib):
+    """[P2] s1 "Double Quantization" (scales in FP8): every one of the 256
+    E4M3 codes decodes to torch's float8_e4m3fn value (NaN codes included)."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = olib.e4m3_to_f32(codes)
+    ref = _torch_e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok].view(np.uint32), ref[ok].view(np.uint32))
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_matches_torch_float8_rne(olib):
+    """Nearest value with ties to even, as torch's float32 -> float8_e4m3fn
+    conversion rounds: checked on every E4M3 value, every midpoint and two
+    fp32 ulps on either side of each, random values and tiny ones. Past 448
+    the oracle saturates (torch keeps 448 up to 464 and gives NaN beyond)."""
+    vals = olib.e4m3_to_f32(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    pts = [vals, mids]
+    for k in (1, 2):
+        pts.append(np.nextafter(mids.astype(np.float32), np.float32(np.inf)).astype(np.float64))
+        pts.append(np.nextafter(mids.astype(np.float32), np.float32(0)).astype(np.float64))
+        for _ in range(k - 1):
+            pts[-1] = np.nextafter(pts[-1].astype(np.float32), np.float32(0)).astype(np.float64)
+    rng = np.random.default_rng(12)
+    pts.append(rng.uniform(0, 448, 3000))
+    pts.append(10.0 ** rng.uniform(-12, 2.6, 3000))
+    pts.append(np.array([0.0, 1e-45, 2.0 ** -10, 2.0 ** -10 * 3, 447.99, 448.0]))
+    x = np.concatenate(pts).astype(np.float32)
+    x = x[(x >= 0) & (x <= 448)]
+    got = olib.f32_to_e4m3(x)
+    ref = _torch_e4m3_encode(x)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (x[bad[:5]], got[bad[:5]], ref[bad[:5]])
+    assert list(olib.f32_to_e4m3(np.array([448.5, 500.0, 1e30, np.inf], np.float32))) == [0x7E] * 4
+
+
+def _dq_values(olib, q8, fmt):
+    b = np.ascontiguousarray(q8).view(np.uint8)
+    if fmt == olib.DQ_E4M3:
+        return _torch_e4m3_decode(b)
+    if fmt == olib.DQ_UINT8:
+        return b.astype(np.float32)
+    return b.view(np.int8).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt,top", [(0, 127), (1, 255), (2, 448)])
+def test_double_quant_formats_top_zero_and_bound(olib, fmt, top):
+    """Each format maps the group maximum to its top code value (127, 255,
+    448) with s2 = RN32(c2/top), a zero constant to code 0, and reconstructs
+    every constant within its grid's half step: s2/2 on the integer grids,
+    2^-4 relative on E4M3's 3-bit mantissa (plus the rounding of
+    value * s2)."""
+    rng = np.random.default_rng(13 + fmt)
+    c1 = np.abs(rng.standard_t(4, 256 * 5) * 0.02).astype(np.float32)
+    c1[7] = 0.0
+    q8, s2 = olib.double_quant(c1, fmt)
+    val = _dq_values(olib, q8, fmt)
+    for g in range(5):
+        sl = slice(256 * g, 256 * (g + 1))
+        c2 = c1[sl].max()
+        assert s2[g] == np.float32(c2) / np.float32(top)
+        assert val[sl][np.argmax(c1[sl])] == top
+    assert val[7] == 0.0
+    s2b = np.repeat(s2, 256)
+    chat = (val * s2b).astype(np.float32).astype(np.float64)
+    err = np.abs(chat - c1.astype(np.float64))
+    if fmt == olib.DQ_E4M3:
+        assert np.all(err <= 2.0 ** -4 * c1 * (1 + 2.0 ** -20) + 2.0 ** -9 * s2b / 2)
+    else:
+        assert np.all(err <= s2b * (0.5 + 1e-5) + 2.0 ** -23 * c1)
+
+
+def test_double_quant_unsigned_halves_the_step(olib):
+    """On heavy-tailed constants the unsigned /255 grid's worst absolute
+    error is half the /127 grid's bound, and its small constants (c1 << c2)
+    keep about twice the resolution."""
+    rng = np.random.default_rng(14)
+    c1 = np.abs(rng.standard_t(4, 256 * 40) * 0.02).astype(np.float32)
+    errs = {}
+    for fmt in (0, 1):
+        q8, s2 = olib.double_quant(c1, fmt)
+        chat = (_dq_values(olib, q8, fmt) * np.repeat(s2, 256)).astype(np.float32)
+        errs[fmt] = np.abs(chat.astype(np.float64) - c1) / np.repeat(s2 * (127 if fmt == 0 else 255), 256)
+    assert errs[0].max() <= 0.5 / 127 * 1.0001 and errs[1].max() <= 0.5 / 255 * 1.0001
+    assert errs[1].mean() < 0.6 * errs[0].mean()
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_dequant_formats_follow_the_stored_code(olib, fmt):
+    """w_hat = bf16(L[code] * RN32(value(q8) * s2)) with value() the
+    format's decoding (torch's float8_e4m3fn for E4M3)."""
+    W = syn.normal_f32((64 * 512,), 0.02, 15)
+    codes, q8, s2 = olib.quantize_nf4_dq(W, "f32", fmt)
+    w32, _ = olib.dequant_dq(codes, q8, s2, fmt)
+    lv, _ = olib.nf4_codebook()
+    c = np.empty(codes.size * 2, np.int64)
+    c[0::2] = codes & 15
+    c[1::2] = codes >> 4
+    chat = (_dq_values(olib, q8, fmt) * np.repeat(s2, 256)[: q8.size]).astype(np.float32)
+    want = (lv[c] * np.repeat(chat, 64)).astype(np.float32)
+    assert np.array_equal(w32.view(np.uint32), want.view(np.uint32))
+    assert np.all(np.abs(w32 - W) <= np.repeat(chat, 64) * 0.2)  # within the widest NF4 gap
