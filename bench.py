@@ -452,32 +452,58 @@ def gemv_ring(q, syn, torch, dev, r, alpha):
 
 def bulk_quantize(q, syn, torch, dev):
     """Quantize and dequantize bandwidth on one 8192x28672 bf16 tensor (470 MB
-    in, past the Infinity Cache)."""
+    in, past the Infinity Cache), in each second-level format, with the
+    format's error on that heavy-tailed tensor: the relative error of the
+    reconstructed block constants c1_hat against the exact block absmax
+    (median and 99th percentile over non-zero blocks) and the relative
+    Frobenius error of the dequantized weight."""
     N, K = syn.BULK_65B["tensor"]
     Wt = syn.torch_student_t_outliers_bf16((N, K), 4242, dev)
-    w = q.qlora_quantize_nf4_dq(Wt)
     out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    # measurement only: the exact block constants and the norm of W
+    c1 = Wt.float().abs().view(-1, 64).amax(dim=1)
+    nz = c1 > 0
+    wnorm = torch.linalg.norm(Wt.float())
     res = {"tensor": [N, K]}
-    for label, fn, nbytes in (("quantize", lambda: q.qlora_quantize_nf4_dq(Wt, out=w),
-                               2 * N * K + nf4_bytes(N, K)),
-                              ("dequant", lambda: q.qlora_dequant_bf16(w, out=out),
-                               nf4_bytes(N, K) + 2 * N * K)):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        gbps = nbytes / (ms * 1e-3) / 1e9
-        res[label] = {"ms": round(ms, 4), "gbps": round(gbps, 1),
-                      "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                      "params_per_s": round(N * K / (ms * 1e-3), 1)}
-    del Wt, w, out
+    for fmt, name in ((q.DQ_INT8, None), (q.DQ_UINT8, "uint8"), (q.DQ_E4M3, "e4m3")):
+        w = q.qlora_quantize_nf4_dq(Wt, dq_format=fmt)
+        sec = res if name is None else res.setdefault(name, {})
+        for label, fn, nbytes in (("quantize", lambda: q.qlora_quantize_nf4_dq(Wt, out=w),
+                                   2 * N * K + nf4_bytes(N, K)),
+                                  ("dequant", lambda: q.qlora_dequant_bf16(w, out=out),
+                                   nf4_bytes(N, K) + 2 * N * K)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            sec[label] = {"ms": round(ms, 4), "gbps": round(gbps, 1),
+                          "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                          "params_per_s": round(N * K / (ms * 1e-3), 1)}
+        qb = w.absmax_q
+        if fmt == q.DQ_E4M3:
+            val = qb.view(torch.float8_e4m3fn).float()
+        elif fmt == q.DQ_UINT8:
+            val = qb.view(torch.uint8).float()
+        else:
+            val = qb.float()
+        chat = val * w.absmax_scale.repeat_interleave(256)[: val.numel()]
+        rel = ((chat - c1).abs() / c1.clamp_min(1e-30))[nz]
+        sec["c1_rel_err_p50"] = round(float(rel.median()), 5)
+        sec["c1_rel_err_p99"] = round(float(torch.quantile(rel[:: max(1, rel.numel() // 4000000)],
+                                                           0.99)), 5)
+        q.qlora_dequant_bf16(w, out=out)
+        sec["weight_rel_frob_err"] = round(float(torch.linalg.norm(out.float() - Wt.float())
+                                                 / wnorm), 5)
+        del w
+    del Wt, out, c1, nz
     torch.cuda.empty_cache()
     return res
 

@@ -18,19 +18,29 @@
  *     bullets: small blocks of 64 weights, one scale per block);
  *   - codes   uint8[N*K/2]: NF4 code of weight e in the low nibble of byte
  *     e/2 when e is even, in the high nibble when e is odd;
- *   - absmax_q int8[N*K/64]: the block absmax quantized to 8 bits
- *     (0..127) - the double quantization of [P1] bullets, [P2] s1 "Double
- *     Quantization", [P5] "Double Quantization";
+ *   - absmax_q int8[N*K/64]: one byte per block, the block absmax quantized
+ *     to 8 bits - the double quantization of [P1] bullets ("8-bit"), [P2] s1
+ *     "Double Quantization" ("FP8"), [P5] "Double Quantization". The byte's
+ *     meaning is the second-level format (dq_format) the weight was
+ *     quantized with, and every call on the weight must pass the same one:
+ *       QLORA_DQ_INT8   signed byte 0..127, s2 = c2/127 (the default);
+ *       QLORA_DQ_UINT8  unsigned byte 0..255, s2 = c2/255;
+ *       QLORA_DQ_E4M3   an FP8 E4M3 value (OCP E4M3FN: exponent bias 7,
+ *                       subnormals m*2^-9, largest 448), s2 = c2/448; the
+ *                       NaN codes 0x7F and 0xFF never occur.
  *   - absmax_scale float[ceil(N*K/16384)]: one fp32 second-level scale per
  *     group of 256 consecutive blocks.
- *   Total 4 + 8/64 + 32/16384 = 4.126953125 bits per weight.
+ *   Total 4 + 8/64 + 32/16384 = 4.126953125 bits per weight in every format.
  *
  *   Dequantization ([P1] bullets: compute never happens in 4-bit; weights are
- *   dequantized to bf16 just in time): with L the 16 NF4 levels,
- *     c1_hat = fp32(absmax_q[b] * absmax_scale[b/256])
+ *   dequantized to bf16 just in time): with L the 16 NF4 levels and value()
+ *   the format's reading of the byte (exact in fp32),
+ *     c1_hat = fp32(value(absmax_q[b]) * absmax_scale[b/256])
  *     w_hat  = bf16_rne(fp32(L[code] * c1_hat)).
  *
  * CONVENTIONS
+ *   - dq_format (every entry point that reads or writes absmax_q) is one of
+ *     the QLORA_DQ_* formats; QLORA_ERR_INVALID_ARG otherwise.
  *   - Every pointer argument of a compute entry point is a DEVICE pointer
  *     owned by the caller; the library allocates nothing and keeps no state
  *     besides a constant codebook built on first use.
@@ -69,6 +79,11 @@ extern "C" {
 #define QLORA_DTYPE_F32 0
 #define QLORA_DTYPE_BF16 1
 
+/* Second-level formats of absmax_q (see STORAGE FORMAT). */
+#define QLORA_DQ_INT8 0
+#define QLORA_DQ_UINT8 1
+#define QLORA_DQ_E4M3 2
+
 /* Operations for qlora_workspace_bytes. */
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1
@@ -102,6 +117,12 @@ int qlora_codebook(float levels[16], float thresholds[15]);
  * in the adapter's recorded metadata. Host only; 0 if the codebook failed. */
 uint32_t qlora_codebook_id(void);
 
+/* Identifier of the quantization setup with second-level format dq_format:
+ * the codebook id's hash with that format's top code value (127, 255, 448)
+ * in place of 127, so qlora_setup_id(QLORA_DQ_INT8) == qlora_codebook_id().
+ * Host only; 0 for an unknown format or if the codebook failed. */
+uint32_t qlora_setup_id(int dq_format);
+
 /* Device workspace, in bytes, that qlora_linear_fwd (op = QLORA_OP_FWD),
  * qlora_linear_bwd (op = QLORA_OP_BWD) or qlora_merge_lora (op =
  * QLORA_OP_MERGE, M ignored) needs for these sizes, assuming no saved u. From M = 512 rows on it includes N*K*2 bytes for the dequantized
@@ -117,17 +138,20 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
  *   codes, absmax_q, absmax_scale  outputs, sizes from qlora_nf4_sizes.
  * Per block: c1 = max|w|; x = w / c1 (correctly rounded fp32 division);
  * code = #{i : x > threshold[i]}; an all-zero block gets code 7 (level 0).
- * Per group of 256 blocks: c2 = max c1; s2 = c2 / 127; absmax_q =
- * nearest integer to c1 / s2 (ties to the lower), clamped to [0,127], and 0
- * for c1 == 0. The NF4 codes use the exact fp32 c1. */
+ * Per group of 256 blocks: c2 = max c1; s2 = c2 / top (fp32 division; top =
+ * 127, 255 or 448 by dq_format); absmax_q = the nearest integer to c1 / s2
+ * (ties to the lower) clamped to [0, top] for the integer formats, or the
+ * nearest E4M3 value (ties to even, saturating at 448); 0 for c1 == 0. The
+ * NF4 codes use the exact fp32 c1. QLORA_ERR_INVALID_ARG for an unknown
+ * dq_format. */
 int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* codes,
-                          int8_t* absmax_q, float* absmax_scale, void* stream);
+                          int8_t* absmax_q, float* absmax_scale, int dq_format, void* stream);
 
 /* Dequantize to bf16 ([P1] bullets "Compute never happens in 4-bit"; [P3]
  * "How it works": each layer's 4-bit weights are unpacked into 16-bit).
  *   W_out  [N,K] bf16, w_hat as in the format section. */
 int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                       int64_t N, int64_t K, uint16_t* W_out, void* stream);
+                       int dq_format, int64_t N, int64_t K, uint16_t* W_out, void* stream);
 
 /* QLoRA linear forward ([P1] forward equation h = W_hat x + (alpha/r) B(Ax),
  * here in row-major form):
@@ -141,9 +165,10 @@ int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float
  * The weight is read through its dequantized bf16 values, products are exact
  * and accumulate in fp32. M == 0 is a successful no-op. r % 16 == 0. */
 int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int64_t N, int64_t K, const uint16_t* x, int64_t M, const uint16_t* A,
-                     const uint16_t* B, int r, float alpha, void* y, int y_dtype, float* u_out,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     int dq_format, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int r, float alpha, void* y,
+                     int y_dtype, float* u_out, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /* QLoRA linear backward ([P2] s3 "The Backward Pass Through Quantization":
  * gradients flow through the dequantized frozen base, only the adapters get
@@ -158,8 +183,8 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
  *   both dA and dB are NULL).
  * The frozen base is never written. M == 0 writes zero dA and dB. */
 int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int64_t N, int64_t K, const uint16_t* x, const uint16_t* dY, int64_t M,
-                     const uint16_t* A, const uint16_t* B, int r, float alpha,
+                     int dq_format, int64_t N, int64_t K, const uint16_t* x, const uint16_t* dY,
+                     int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
                      const float* u_saved, void* dX, int dx_dtype, void* dA, void* dB,
                      int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -179,7 +204,7 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
  * QLORA_DTYPE_F32 input. Same shape and rank rules as the linear entry
  * points; QLORA_ERR_INVALID_ARG when neither base is given. */
 int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     const uint16_t* W, int64_t N, int64_t K, const uint16_t* A,
+                     int dq_format, const uint16_t* W, int64_t N, int64_t K, const uint16_t* A,
                      const uint16_t* B, int r, float alpha, float* merged, void* workspace,
                      size_t workspace_bytes, void* stream);
 

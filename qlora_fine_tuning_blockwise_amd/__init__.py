@@ -17,10 +17,10 @@ import torch
 from . import _lib
 
 __all__ = [
-    "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_id",
+    "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_id", "qlora_setup_id",
     "qlora_workspace_bytes", "qlora_quantize_nf4_dq", "qlora_dequant_bf16",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "qlora_merge_lora", "qlora_adamw_step",
-    "NF4Weight",
+    "NF4Weight", "DQ_INT8", "DQ_UINT8", "DQ_E4M3",
 ]
 
 
@@ -45,12 +45,17 @@ def _dtype_code(dt) -> int:
     raise ValueError(f"unsupported dtype {dt}")
 
 
-class NF4Weight:
-    """The three device buffers of one quantized [N, K] weight."""
+DQ_INT8, DQ_UINT8, DQ_E4M3 = _lib.DQ_INT8, _lib.DQ_UINT8, _lib.DQ_E4M3
 
-    def __init__(self, codes, absmax_q, absmax_scale, N: int, K: int):
+
+class NF4Weight:
+    """The three device buffers of one quantized [N, K] weight and the
+    second-level format of its absmax codes (DQ_INT8, DQ_UINT8, DQ_E4M3)."""
+
+    def __init__(self, codes, absmax_q, absmax_scale, N: int, K: int, dq_format: int = DQ_INT8):
         self.codes, self.absmax_q, self.absmax_scale = codes, absmax_q, absmax_scale
         self.N, self.K = int(N), int(K)
+        self.dq_format = int(dq_format)
 
     def nbytes(self) -> int:
         return self.codes.numel() + self.absmax_q.numel() + 4 * self.absmax_scale.numel()
@@ -75,6 +80,10 @@ def qlora_codebook():
     return lv, th
 
 
+def qlora_setup_id(dq_format: int) -> int:
+    return int(_lib.load().qlora_setup_id(int(dq_format)))
+
+
 def qlora_codebook_id() -> int:
     return int(_lib.load().qlora_codebook_id())
 
@@ -90,14 +99,20 @@ def _alloc_nf4(N, K, device):
             torch.empty(sb // 4, dtype=torch.float32, device=device))
 
 
-def qlora_quantize_nf4_dq(W: torch.Tensor, out: NF4Weight | None = None, stream=None) -> NF4Weight:
-    """Quantize a [N, K] fp32 or bf16 device tensor to NF4 + double-quantized constants."""
+def qlora_quantize_nf4_dq(W: torch.Tensor, out: NF4Weight | None = None, stream=None,
+                          dq_format: int | None = None) -> NF4Weight:
+    """Quantize a [N, K] fp32 or bf16 device tensor to NF4 + double-quantized
+    constants in second-level format dq_format (default: out's format, else
+    DQ_INT8)."""
     N, K = W.shape
+    if dq_format is None:
+        dq_format = out.dq_format if out is not None else DQ_INT8
     if out is None:
-        out = NF4Weight(*_alloc_nf4(N, K, W.device), N, K)
+        out = NF4Weight(*_alloc_nf4(N, K, W.device), N, K, dq_format)
+    out.dq_format = int(dq_format)
     st = _lib.load().qlora_quantize_nf4_dq(_ptr(W), _dtype_code(W.dtype), N, K, _ptr(out.codes),
                                            _ptr(out.absmax_q), _ptr(out.absmax_scale),
-                                           _stream(stream))
+                                           out.dq_format, _stream(stream))
     _lib.check(st, "qlora_quantize_nf4_dq")
     return out
 
@@ -106,7 +121,7 @@ def qlora_dequant_bf16(w: NF4Weight, out: torch.Tensor | None = None, stream=Non
     if out is None:
         out = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=w.codes.device)
     st = _lib.load().qlora_dequant_bf16(_ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale),
-                                        w.N, w.K, _ptr(out), _stream(stream))
+                                        w.dq_format, w.N, w.K, _ptr(out), _stream(stream))
     _lib.check(st, "qlora_dequant_bf16")
     return out
 
@@ -129,7 +144,8 @@ def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, A: torch.Tensor, B: torch.Te
         y = torch.empty((M, w.N), dtype=y_dtype, device=x.device)
     workspace = _workspace(_lib.OP_FWD, M, w.N, w.K, r, x.device, workspace)
     st = _lib.load().qlora_linear_fwd(
-        _ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale), w.N, w.K, _ptr(x), M, _ptr(A),
+        _ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale), w.dq_format, w.N, w.K, _ptr(x), M,
+        _ptr(A),
         _ptr(B), r, float(alpha), _ptr(y), _dtype_code(y.dtype), _ptr(u_out), _ptr(workspace),
         workspace.numel(), _stream(stream))
     _lib.check(st, "qlora_linear_fwd")
@@ -150,7 +166,8 @@ def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: 
     dB = torch.empty((r, w.N), dtype=grad_dtype, device=dev) if want_grads else None
     workspace = _workspace(_lib.OP_BWD, M, w.N, w.K, r, dev, workspace)
     st = _lib.load().qlora_linear_bwd(
-        _ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale), w.N, w.K, _ptr(x), _ptr(dY), M,
+        _ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale), w.dq_format, w.N, w.K, _ptr(x),
+        _ptr(dY), M,
         _ptr(A), _ptr(B), r, float(alpha), _ptr(u_saved), _ptr(dX), _dtype_code(dx_dtype),
         _ptr(dA), _ptr(dB), _dtype_code(grad_dtype), _ptr(workspace), workspace.numel(),
         _stream(stream))
@@ -191,7 +208,8 @@ def qlora_merge_lora(A: torch.Tensor, B: torch.Tensor, alpha: float, w: NF4Weigh
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     nf = (w.codes, w.absmax_q, w.absmax_scale) if w is not None else (None, None, None)
-    st = _lib.load().qlora_merge_lora(_ptr(nf[0]), _ptr(nf[1]), _ptr(nf[2]), _ptr(W), N, K,
+    fmt = w.dq_format if w is not None else DQ_INT8
+    st = _lib.load().qlora_merge_lora(_ptr(nf[0]), _ptr(nf[1]), _ptr(nf[2]), fmt, _ptr(W), N, K,
                                       _ptr(A), _ptr(B), r, float(alpha), _ptr(out),
                                       _ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st, "qlora_merge_lora")

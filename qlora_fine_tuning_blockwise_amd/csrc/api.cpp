@@ -109,6 +109,18 @@ T* at(void* base, size_t off) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
 
+// The codebook as one call's kernels receive it, with that call's
+// second-level format. QLORA_ERR_INVALID_ARG for an unknown format.
+int call_codebook(int dq_format, Codebook* out) {
+  if (dq_format != QLORA_DQ_INT8 && dq_format != QLORA_DQ_UINT8 && dq_format != QLORA_DQ_E4M3)
+    return QLORA_ERR_INVALID_ARG;
+  const Codebook* cb = nullptr;
+  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+  *out = *cb;
+  out->dq_format = dq_format;
+  return QLORA_OK;
+}
+
 // The address a kernel uses for p: device memory as it is; host memory only
 // if the runtime has pinned it and mapped it for the device (hipHostMalloc),
 // translated to its device-side address; managed memory as it is. Returns
@@ -173,6 +185,8 @@ uint32_t qlora_codebook_id(void) {
   return get_codebook(nullptr, &id) == QLORA_OK ? id : 0u;
 }
 
+uint32_t qlora_setup_id(int dq_format) { return setup_id(dq_format); }
+
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
   if (M < 0 || !shape_ok(N, K) || !rank_ok(r)) return 0;
   if (op == QLORA_OP_FWD) return fwd_layout(M, N, K, r, true).total;
@@ -182,36 +196,37 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
 }
 
 int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* codes,
-                          int8_t* absmax_q, float* absmax_scale, void* stream) {
-  const Codebook* cb = nullptr;
-  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+                          int8_t* absmax_q, float* absmax_scale, int dq_format, void* stream) {
+  Codebook cb;
+  if (const int st = call_codebook(dq_format, &cb)) return st;
   if (!W || !codes || !absmax_q || !absmax_scale) return QLORA_ERR_INVALID_ARG;
   if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
   if (w_dtype != QLORA_DTYPE_F32 && w_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale))
     return QLORA_ERR_ALIGN;
   return launch_status(launch_quantize(W, w_dtype == QLORA_DTYPE_F32, N * K, codes, absmax_q,
-                                       absmax_scale, *cb, static_cast<hipStream_t>(stream)));
+                                       absmax_scale, cb, static_cast<hipStream_t>(stream)));
 }
 
 int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                       int64_t N, int64_t K, uint16_t* W_out, void* stream) {
-  const Codebook* cb = nullptr;
-  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+                       int dq_format, int64_t N, int64_t K, uint16_t* W_out, void* stream) {
+  Codebook cb;
+  if (const int st = call_codebook(dq_format, &cb)) return st;
   if (!codes || !absmax_q || !absmax_scale || !W_out) return QLORA_ERR_INVALID_ARG;
   if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
   if (!aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale) || !aligned16(W_out))
     return QLORA_ERR_ALIGN;
-  return launch_status(launch_dequant(codes, absmax_q, absmax_scale, N * K, W_out, *cb,
+  return launch_status(launch_dequant(codes, absmax_q, absmax_scale, N * K, W_out, cb,
                                       static_cast<hipStream_t>(stream)));
 }
 
 int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int64_t N, int64_t K, const uint16_t* x, int64_t M, const uint16_t* A,
-                     const uint16_t* B, int r, float alpha, void* y, int y_dtype, float* u_out,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  const Codebook* cb = nullptr;
-  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+                     int dq_format, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int r, float alpha, void* y,
+                     int y_dtype, float* u_out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  Codebook cb;
+  if (const int st = call_codebook(dq_format, &cb)) return st;
   if (M < 0) return QLORA_ERR_INVALID_ARG;
   if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
   if (y_dtype != QLORA_DTYPE_F32 && y_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
@@ -234,7 +249,7 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
     e = launch_lora_down_decode(x, A, M, K, r, down, st);
     if (e == hipSuccess)
       e = launch_gemv(x, codes, absmax_q, absmax_scale, down, decode_down_slices(K), B, M, N, K, r,
-                      s, u_out, y, ybf, *cb, st);
+                      s, u_out, y, ybf, cb, st);
   } else {
     uint16_t* At = at<uint16_t>(workspace, L.At);
     float* u = u_out ? u_out : at<float>(workspace, L.u);
@@ -247,22 +262,22 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
     if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
     if (e == hipSuccess && L.plain) {
       uint16_t* W = at<uint16_t>(workspace, L.W);
-      e = launch_dequant(codes, absmax_q, absmax_scale, N * K, W, *cb, st);
+      e = launch_dequant(codes, absmax_q, absmax_scale, N * K, W, cb, st);
       if (e == hipSuccess) e = launch_gemm_nt(x, K, W, K, ulr, Bt, M, N, K, r, y, ybf, st);
     } else if (e == hipSuccess) {
-      e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, *cb, st);
+      e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, cb, st);
     }
   }
   return launch_status(e);
 }
 
 int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int64_t N, int64_t K, const uint16_t* x, const uint16_t* dY, int64_t M,
-                     const uint16_t* A, const uint16_t* B, int r, float alpha,
+                     int dq_format, int64_t N, int64_t K, const uint16_t* x, const uint16_t* dY,
+                     int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
                      const float* u_saved, void* dX, int dx_dtype, void* dA, void* dB,
                      int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  const Codebook* cb = nullptr;
-  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+  Codebook cb;
+  if (const int st = call_codebook(dq_format, &cb)) return st;
   if (M < 0) return QLORA_ERR_INVALID_ARG;
   if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
   if ((dx_dtype != QLORA_DTYPE_F32 && dx_dtype != QLORA_DTYPE_BF16) ||
@@ -306,12 +321,12 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
                                   st);
   if (e == hipSuccess && dX && L.plain) {  // dX = dY w_hat through w_hat^T [K,N]
     uint16_t* Wt = at<uint16_t>(workspace, L.Wt);
-    e = launch_dequant_t(codes, absmax_q, absmax_scale, N, K, Wt, *cb, st);
+    e = launch_dequant_t(codes, absmax_q, absmax_scale, N, K, Wt, cb, st);
     if (e == hipSuccess)
       e = launch_gemm_nt(dY, N, Wt, N, svlr, A, M, K, N, r, dX, dx_dtype == QLORA_DTYPE_BF16, st);
   } else if (e == hipSuccess && dX) {
     e = launch_gemm_bwd(dY, codes, absmax_q, absmax_scale, svlr, A, M, N, K, r, dX,
-                        dx_dtype == QLORA_DTYPE_BF16, *cb, st);
+                        dx_dtype == QLORA_DTYPE_BF16, cb, st);
   }
   if (e == hipSuccess && dA) {  // dA = x^T (s v)
     e = launch_colred(x, vT, M, K, r, col, st);
@@ -358,11 +373,11 @@ int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_
 }
 
 int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     const uint16_t* W, int64_t N, int64_t K, const uint16_t* A,
+                     int dq_format, const uint16_t* W, int64_t N, int64_t K, const uint16_t* A,
                      const uint16_t* B, int r, float alpha, float* merged, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  const Codebook* cb = nullptr;
-  if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
+  Codebook cb;
+  if (const int st = call_codebook(dq_format, &cb)) return st;
   if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
   if (!rank_ok(r)) return QLORA_ERR_RANK;
   if (!A || !B || !merged) return QLORA_ERR_INVALID_ARG;
@@ -379,7 +394,7 @@ int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* 
   if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
   if (e == hipSuccess)
     e = launch_merge(W ? nullptr : codes, absmax_q, absmax_scale, W, N, K, At, Bt, r,
-                     alpha / (float)r, merged, *cb, st);
+                     alpha / (float)r, merged, cb, st);
   return launch_status(e);
 }
 

@@ -57,8 +57,19 @@ uint32_t fnv1a(uint32_t h, const void* data, size_t n) {
   return h;
 }
 
+// Identifier of a quantization setup: the level-bit hash extended by the
+// layout constants and the second level's top code value (127, 255 or 448,
+// one per format). The default format's identifier is the codebook id.
+uint32_t setup_hash(uint32_t level_hash, int dq_format) {
+  const uint32_t top = dq_format == kDqInt8 ? 127u : dq_format == kDqUint8 ? 255u : 448u;
+  const uint32_t meta[5] = {(uint32_t)kBlock, (uint32_t)kGroup, 1u /* even index in low nibble */,
+                            top, QLORA_FORMAT_VERSION};
+  return fnv1a(level_hash, meta, sizeof meta);
+}
+
 struct State {
-  Codebook cb;
+  Codebook cb{};
+  uint32_t level_hash = 0;
   uint32_t id = 0;
   int status = QLORA_ERR_INTERNAL;
 };
@@ -105,24 +116,35 @@ State build() {
     std::memcpy(&bits, &s.cb.level[i], 4);
     h = fnv1a(h, &bits, 4);
   }
-  const uint32_t meta[5] = {(uint32_t)kBlock, (uint32_t)kGroup, 1u /* even index in low nibble */,
-                            127u /* symmetric 8-bit second level */, QLORA_FORMAT_VERSION};
-  h = fnv1a(h, meta, sizeof meta);
-  s.id = h;
+  s.level_hash = h;
+  s.cb.dq_format = kDqInt8;
+  s.id = setup_hash(h, kDqInt8);
   s.status = QLORA_OK;
   return s;
+}
+
+const State& state() {
+  static std::once_flag once;
+  static State st;
+  std::call_once(once, [] { st = build(); });
+  return st;
 }
 
 }  // namespace
 
 int get_codebook(const Codebook** cb, uint32_t* id) {
-  static std::once_flag once;
-  static State state;
-  std::call_once(once, [] { state = build(); });
-  if (state.status != QLORA_OK) return state.status;
-  if (cb) *cb = &state.cb;
-  if (id) *id = state.id;
+  const State& st = state();
+  if (st.status != QLORA_OK) return st.status;
+  if (cb) *cb = &st.cb;
+  if (id) *id = st.id;
   return QLORA_OK;
+}
+
+uint32_t setup_id(int dq_format) {
+  const State& st = state();
+  if (st.status != QLORA_OK) return 0u;
+  if (dq_format != kDqInt8 && dq_format != kDqUint8 && dq_format != kDqE4m3) return 0u;
+  return setup_hash(st.level_hash, dq_format);
 }
 
 }  // namespace qlora

@@ -202,8 +202,10 @@ __global__ __launch_bounds__(512, 4) void gemv_kernel(GemvArgs p, Codebook cb) {
   auto pair = [&](int64_t c0, bool reload) {
     // Entry e = {bf16(L[e] c1_hat(block of chunk c0)), bf16(L[e] c1_hat(block of chunk c0+1))};
     // a block past the end of the row gets zeros.
-    const float ch0 = c0 < nch && block_of(c0) < KB ? (float)qv[0] * sv[0] : 0.0f;
-    const float ch1 = c0 + 1 < nch && block_of(c0 + 1) < KB ? (float)qv[1] * sv[1] : 0.0f;
+    const float ch0 =
+        c0 < nch && block_of(c0) < KB ? q8_value(qv[0], cb.dq_format) * sv[0] : 0.0f;
+    const float ch1 =
+        c0 + 1 < nch && block_of(c0 + 1) < KB ? q8_value(qv[1], cb.dq_format) * sv[1] : 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       tabs[w][e][lane] = pack_bf16x2(cb.level[e] * ch0, cb.level[e] * ch1);

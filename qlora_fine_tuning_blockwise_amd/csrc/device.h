@@ -58,11 +58,30 @@ __device__ __forceinline__ u32x4_t lut8(uint32_t w, const uint16_t* tab) {
   return r;
 }
 
+// Value of a stored 8-bit absmax code (the byte, loaded as int8 into `raw`)
+// in second-level format `fmt`: the signed byte, the unsigned byte, or the
+// FP8 E4M3 value (exponent bias 7, subnormals m * 2^-9). Exact in fp32.
+// Branch-free: all three readings are formed and the uniform format picks
+// one by bit masks, so a caller's loads stay batched (a branch on the format
+// would wait for them inside each arm).
+__device__ __forceinline__ float q8_value(int raw, int fmt) {
+  const uint32_t b = (uint32_t)raw & 0xFFu;
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const uint32_t nrm = ((e + 120u) << 23) | (m << 20);
+  const uint32_t sub = __float_as_uint((float)m * 0x1p-9f);
+  const uint32_t fp8 = (e ? nrm : sub) | ((b & 0x80u) << 24);
+  const uint32_t i8 = __float_as_uint((float)raw);
+  const uint32_t u8 = __float_as_uint((float)b);
+  const uint32_t sel_i8 = 0u - (uint32_t)(fmt == kDqInt8);
+  const uint32_t sel_u8 = 0u - (uint32_t)(fmt == kDqUint8);
+  return __uint_as_float((i8 & sel_i8) | (u8 & sel_u8) | (fp8 & ~(sel_i8 | sel_u8)));
+}
+
 // Build the 16-entry bf16 dequantization table of one block from its
 // 8-bit absmax code and the group scale: entry i = bf16(fp32(L[i] * c1_hat)),
-// c1_hat = fp32(q8 * s2). Writes 32 bytes at `dst` (16-byte aligned).
+// c1_hat = fp32(value(q8) * s2). Writes 32 bytes at `dst` (16-byte aligned).
 __device__ __forceinline__ void build_table(const Codebook& cb, int q8, float s2, uint16_t* dst) {
-  const float ch = (float)q8 * s2;
+  const float ch = q8_value(q8, cb.dq_format) * s2;
   u32x4_t t0, t1;
   t0.x = pack_bf16x2(cb.level[0] * ch, cb.level[1] * ch);
   t0.y = pack_bf16x2(cb.level[2] * ch, cb.level[3] * ch);

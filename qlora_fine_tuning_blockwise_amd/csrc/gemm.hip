@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
   const uint32_t region = 0x10101010u * (uint32_t)w;
   const char* tb = reinterpret_cast<const char*>(&tabs[0][0][0]);
   auto build = [&]() {
-    const float ch = drow_ok ? (float)qv * sv : 0.0f;
+    const float ch = drow_ok ? q8_value(qv, cb.dq_format) * sv : 0.0f;
     const f32x4_t la = *reinterpret_cast<const f32x4_t*>(&levels[8 * hb]);
     const f32x4_t lb = *reinterpret_cast<const f32x4_t*>(&levels[8 * hb + 4]);
     const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};

@@ -11,15 +11,26 @@ namespace qlora {
 constexpr int kBlock = 64;   // weights per first-level block
 constexpr int kGroup = 256;  // blocks per second-level group
 
-// NF4 codebook as the kernels receive it (by value, in kernel arguments).
+// Second-level formats of the 8-bit absmax code (one byte per block).
+constexpr int kDqInt8 = 0;   // s2 = c2/127, signed byte 0..127
+constexpr int kDqUint8 = 1;  // s2 = c2/255, unsigned byte 0..255
+constexpr int kDqE4m3 = 2;   // s2 = c2/448, FP8 E4M3 value
+
+// NF4 codebook and the call's second-level format, as the kernels receive
+// them (by value, in kernel arguments).
 struct Codebook {
   float level[16];
   float thr[15];
+  int dq_format;
 };
 
 // Builds the codebook once (thread safe). Returns QLORA_OK or
 // QLORA_ERR_INTERNAL; `cb` and `id` are valid only on QLORA_OK.
 int get_codebook(const Codebook** cb, uint32_t* id);
+
+// Identifier of the quantization setup with second-level format dq_format
+// (0 for an unknown format); setup_id(kDqInt8) is the codebook id.
+uint32_t setup_id(int dq_format);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error. Sizes are pre-validated.

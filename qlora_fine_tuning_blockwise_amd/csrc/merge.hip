@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint8_t* __restrict__ 
     if (kNf4Base) {
       const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + e0 / 2);
       const int64_t b = e0 / 64;
-      const float ch = (float)q8[b] * s2[b >> 8];
+      const float ch = q8_value(q8[b], cb.dq_format) * s2[b >> 8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         base[rr][i] = bf16_lo(pack_bf16x2(lv[(cw >> (4 * i)) & 15u] * ch, 0.0f));

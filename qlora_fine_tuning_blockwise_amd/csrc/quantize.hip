@@ -39,6 +39,22 @@ __device__ __forceinline__ uint32_t nf4_code(float x, const u32x2_t* lut) {
   return e.y + (x > __uint_as_float(e.x) ? 1u : 0u);
 }
 
+// Nearest FP8 E4M3 code of x >= 0 (or +inf), ties to the even code,
+// saturating at 448 (code 0x7E). Below 2^-6 the values are the subnormals
+// m * 2^-9, so the code is x * 2^9 rounded to an integer (exact scaling,
+// rint rounds ties to even; 8 lands on the smallest normal, code 0x08).
+// Above, rounding the fp32 pattern at mantissa bit 20 to nearest-even keeps
+// 3 mantissa bits (a carry moves into the exponent), and the exponent field
+// is rebased from 127 to 7.
+__device__ __forceinline__ int e4m3_code(float x) {
+  if (!(x < 448.0f)) return 0x7E;
+  if (x < 0x1p-6f) return (int)__builtin_rintf(x * 0x1p9f);
+  uint32_t b = __float_as_uint(x);
+  b += 0x7FFFFu + ((b >> 20) & 1u);
+  const int q = (int)((((b >> 23) - 120u) << 3) | ((b >> 20) & 7u));
+  return q < 0x7E ? q : 0x7E;
+}
+
 template <bool kF32In>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ W, int64_t nblocks,
                                                        uint8_t* __restrict__ codes,
@@ -147,8 +163,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   }
   __syncthreads();  // c1s complete
 
-  // Second level: c2 = max c1 over the group, s2 = c2/127,
-  // q8 = nearest integer of c1/s2 (ties to the lower), clamped to [0,127].
+  // Second level: c2 = max c1 over the group, s2 = c2/top with top = 127,
+  // 255 or 448 by format; q8 = the nearest integer of c1/s2 (ties to the
+  // lower) clamped to [0, top], or its nearest E4M3 value (ties to even).
   const float c1 = tid < nbg ? c1s[tid] : 0.0f;
   float m = c1;
 #pragma unroll
@@ -156,16 +173,22 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   const float c2 = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float sc = c2 / 127.0f;
+  const int fmt = cb.dq_format;
+  const float top = fmt == kDqInt8 ? 127.0f : fmt == kDqUint8 ? 255.0f : 448.0f;
+  const float sc = c2 / top;
   if (tid < nbg) {
     int q = 0;
     if (c1 != 0.0f) {
-      const float v = c1 / sc;              // +inf when sc underflowed to 0
-      float t = ceilf(v - 0.5f);            // v - 0.5 is exact for v >= 0.5
-      t = fminf(fmaxf(t, 0.0f), 127.0f);
-      q = (int)t;
+      const float v = c1 / sc;  // +inf when sc underflowed to 0
+      if (fmt == kDqE4m3) {
+        q = e4m3_code(v);
+      } else {
+        float t = ceilf(v - 0.5f);  // v - 0.5 is exact for v >= 0.5
+        t = fminf(fmaxf(t, 0.0f), top);
+        q = (int)t;
+      }
     }
-    q8[b0 + tid] = (int8_t)q;
+    q8[b0 + tid] = (int8_t)(uint8_t)q;
   }
   if (tid == 0) s2[g] = sc;
 }
@@ -200,7 +223,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   for (int p = 0; p < kDqPasses; ++p) {
     bk[p] = b0 + 8 * p < nblocks ? b0 + 8 * p : nblocks - 1;
     cw[p] = reinterpret_cast<const uint32_t*>(codes)[bk[p] * 8 + j];
-    ch[p] = (float)q8[bk[p]] * s2[bk[p] >> 8];
+    ch[p] = q8_value(q8[bk[p]], cb.dq_format) * s2[bk[p] >> 8];
   }
   // levels 2j and 2j+1 of this lane (uniform values, selected per lane)
   float l0 = cb.level[0], l1 = cb.level[1];
@@ -263,11 +286,11 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
     const int64_t blk = kk / 64;
     if (na < N) {
       ca = *reinterpret_cast<const u32x4_t*>(codes + na * (K / 2) + kk / 2);
-      cha = (float)q8[na * KB + blk] * s2[(na * KB + blk) >> 8];
+      cha = q8_value(q8[na * KB + blk], cb.dq_format) * s2[(na * KB + blk) >> 8];
     }
     if (nb < N) {
       cbv = *reinterpret_cast<const u32x4_t*>(codes + nb * (K / 2) + kk / 2);
-      chb = (float)q8[nb * KB + blk] * s2[(nb * KB + blk) >> 8];
+      chb = q8_value(q8[nb * KB + blk], cb.dq_format) * s2[(nb * KB + blk) >> 8];
     }
   }
   if (tid < 16) levels[tid] = cb.level[tid];

@@ -65,23 +65,35 @@ def _p(v):
 
 def test_quantize_validation(lib):
     f = lib.qlora_quantize_nf4_dq
-    assert f(None, 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), None) == 1
-    assert f(_p(FAKE), 1, 4, 96, _p(FAKE), _p(FAKE), _p(FAKE), None) == 2
-    assert f(_p(FAKE), 1, 0, 64, _p(FAKE), _p(FAKE), _p(FAKE), None) == 2
-    assert f(_p(FAKE), 7, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), None) == 4
-    assert f(_p(FAKE + 2), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), None) == 3
+    assert f(None, 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 1
+    assert f(_p(FAKE), 1, 4, 96, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 2
+    assert f(_p(FAKE), 1, 0, 64, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 2
+    assert f(_p(FAKE), 7, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 4
+    assert f(_p(FAKE + 2), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 3
+    assert f(_p(FAKE), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), 3, None) == 1   # dq format
+    assert f(_p(FAKE), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), -1, None) == 1
     d = lib.qlora_dequant_bf16
-    assert d(_p(FAKE), None, _p(FAKE), 4, 64, _p(FAKE), None) == 1
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 4, 65, _p(FAKE), None) == 2
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE + 4), 4, 64, _p(FAKE), None) == 3
+    assert d(_p(FAKE), None, _p(FAKE), 0, 4, 64, _p(FAKE), None) == 1
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 0, 4, 65, _p(FAKE), None) == 2
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE + 4), 0, 4, 64, _p(FAKE), None) == 3
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 9, 4, 64, _p(FAKE), None) == 1     # dq format
+
+
+def test_setup_ids(lib):
+    """One identifier per second-level format; the default one is the
+    codebook id; unknown formats give 0."""
+    ids = [lib.qlora_setup_id(f) for f in (0, 1, 2)]
+    assert ids[0] == lib.qlora_codebook_id() and len(set(ids)) == 3 and 0 not in ids
+    assert lib.qlora_setup_id(3) == 0 and lib.qlora_setup_id(-1) == 0
 
 
 def _fwd(lib, **kw):
-    a = dict(codes=FAKE, q8=FAKE, s2=FAKE, N=64, K=128, x=FAKE, M=32, A=FAKE, B=FAKE, r=16,
+    a = dict(codes=FAKE, q8=FAKE, s2=FAKE, fmt=0, N=64, K=128, x=FAKE, M=32, A=FAKE, B=FAKE, r=16,
              alpha=32.0, y=FAKE, ydt=0, u=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     P = lambda v: None if v is None else _p(v)
-    return lib.qlora_linear_fwd(P(a["codes"]), P(a["q8"]), P(a["s2"]), a["N"], a["K"], P(a["x"]),
+    return lib.qlora_linear_fwd(P(a["codes"]), P(a["q8"]), P(a["s2"]), a["fmt"], a["N"], a["K"],
+                                P(a["x"]),
                                 a["M"], P(a["A"]), P(a["B"]), a["r"], a["alpha"], P(a["y"]),
                                 a["ydt"], P(a["u"]), P(a["ws"]), a["wsb"], None)
 
@@ -97,26 +109,28 @@ def test_fwd_validation(lib):
     assert _fwd(lib, B=FAKE + 8) == 3
     assert _fwd(lib, wsb=16) == 6
     assert _fwd(lib, ws=None) == 6
+    assert _fwd(lib, fmt=5) == 1
     assert _fwd(lib, M=0) == 0  # empty batch: a no-op that enqueues nothing
 
 
 def test_bwd_validation(lib):
     f = lib.qlora_linear_bwd
-    base = [_p(FAKE)] * 3 + [64, 128, _p(FAKE), _p(FAKE), 32, _p(FAKE), _p(FAKE), 16, 32.0, None,
-                             _p(FAKE), 0, _p(FAKE), _p(FAKE), 0, _p(FAKE), 1 << 30, None]
+    base = [_p(FAKE)] * 3 + [0, 64, 128, _p(FAKE), _p(FAKE), 32, _p(FAKE), _p(FAKE), 16, 32.0,
+                             None, _p(FAKE), 0, _p(FAKE), _p(FAKE), 0, _p(FAKE), 1 << 30, None]
 
     def call(i, v):
         a = list(base)
         a[i] = v
         return f(*a)
-    assert call(6, None) == 1          # dY missing
-    assert call(5, None) == 1          # x missing while dA/dB wanted
-    assert call(4, 96) == 2            # K % 64
-    assert call(14, 3) == 4            # dx dtype
-    assert call(17, 9) == 4            # grad dtype
-    assert call(10, 0) == 5            # r
-    assert call(8, _p(FAKE + 1)) == 3  # A misaligned
-    assert call(19, 64) == 6           # workspace too small
+    assert call(7, None) == 1          # dY missing
+    assert call(6, None) == 1          # x missing while dA/dB wanted
+    assert call(5, 96) == 2            # K % 64
+    assert call(15, 3) == 4            # dx dtype
+    assert call(18, 9) == 4            # grad dtype
+    assert call(11, 0) == 5            # r
+    assert call(9, _p(FAKE + 1)) == 3  # A misaligned
+    assert call(20, 64) == 6           # workspace too small
+    assert call(3, 7) == 1             # dq format
 
 
 def test_gemm_nt_validation(lib):
@@ -142,19 +156,20 @@ def test_gemm_nt_validation(lib):
 
 def test_merge_validation(lib):
     f = lib.qlora_merge_lora
-    base = [_p(FAKE), _p(FAKE), _p(FAKE), None, 64, 128, _p(FAKE), _p(FAKE), 16, 32.0, _p(FAKE),
-            _p(FAKE), 1 << 30, None]
+    base = [_p(FAKE), _p(FAKE), _p(FAKE), 0, None, 64, 128, _p(FAKE), _p(FAKE), 16, 32.0,
+            _p(FAKE), _p(FAKE), 1 << 30, None]
 
     def call(i, v):
         a = list(base)
         a[i] = v
         return f(*a)
-    assert call(5, 100) == 2            # K % 64
-    assert call(8, 8) == 5              # r
-    assert call(10, None) == 1          # merged missing
+    assert call(6, 100) == 2            # K % 64
+    assert call(9, 8) == 5              # r
+    assert call(11, None) == 1          # merged missing
     assert call(0, None) == 1           # neither NF4 base nor bf16 base
-    assert call(6, _p(FAKE + 4)) == 3   # A misaligned
-    assert call(12, 64) == 6            # workspace too small
+    assert call(7, _p(FAKE + 4)) == 3   # A misaligned
+    assert call(13, 64) == 6            # workspace too small
+    assert call(3, 4) == 1              # dq format
     assert lib.qlora_workspace_bytes(2, 0, 64, 128, 16) >= 2 * 16 * (64 + 128)
 
 

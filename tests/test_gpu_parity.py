@@ -50,8 +50,8 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
-def quantize_gpu(W):
-    w = q.qlora_quantize_nf4_dq(W)
+def quantize_gpu(W, fmt=0):
+    w = q.qlora_quantize_nf4_dq(W, dq_format=fmt)
     torch.cuda.synchronize()
     return w
 
@@ -225,7 +225,7 @@ def test_quantize_deterministic():
 class Problem:
     """A seeded layer problem with both sides' inputs and the oracle's W_hat."""
 
-    def __init__(self, N, K, r, alpha, w_std=0.02, seed=0, w_dtype="bf16", zero_w=False):
+    def __init__(self, N, K, r, alpha, w_std=0.02, seed=0, w_dtype="bf16", zero_w=False, fmt=0):
         self.N, self.K, self.r, self.alpha = N, K, r, alpha
         if zero_w:
             Wb = np.zeros((N, K), np.uint16)
@@ -233,13 +233,13 @@ class Problem:
             Wb = syn.normal_bf16((N, K), w_std, seed) if w_dtype == "bf16" else None
         if w_dtype == "f32":
             Wf = syn.normal_f32((N, K), w_std, seed)
-            self.w = quantize_gpu(torch.from_numpy(Wf).to(DEV))
-            codes, q8, s2 = oracle.quantize_nf4_dq(Wf, "f32")
+            self.w = quantize_gpu(torch.from_numpy(Wf).to(DEV), fmt)
+            codes, q8, s2 = oracle.quantize_nf4_dq(Wf, "f32", fmt)
         else:
-            self.w = quantize_gpu(dev_bf16(Wb))
-            codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+            self.w = quantize_gpu(dev_bf16(Wb), fmt)
+            codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16", fmt)
         assert_nf4_equal(self.w, codes, q8, s2, "problem weight")
-        self.What = oracle.dequant_dq(codes, q8, s2)[1].reshape(N, K)
+        self.What = oracle.dequant_dq(codes, q8, s2, fmt)[1].reshape(N, K)
         self.A = syn.normal_bf16((K, r), 1.0 / np.sqrt(K), seed + 1)
         self.B = syn.normal_bf16((r, N), 0.01, seed + 2)
         self.At, self.Bt = dev_bf16(self.A), dev_bf16(self.B)
@@ -637,3 +637,100 @@ def test_adamw_rejects_pageable_host_memory():
         q.qlora_adamw_step(P, G, Mm, V, step=1, lr=1e-3)
     torch.cuda.synchronize()
     assert not P.any()
+
+
+# ------------------------------------------------ second-level format variants
+FMTS = [q.DQ_UINT8, q.DQ_E4M3]
+
+
+def _check_fmt_roundtrip(Wb, fmt, name):
+    w = quantize_gpu(dev_bf16(Wb), fmt)
+    codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16", fmt)
+    assert_nf4_equal(w, codes, q8, s2, name)
+    deq = syn.torch_bf16_to_bits(q.qlora_dequant_bf16(w)).ravel()
+    assert np.array_equal(deq, oracle.dequant_dq(codes, q8, s2, fmt)[1]), f"{name}: dequant"
+    return w
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(1, 64), (3, 192), (257, 640)])
+def test_formats_quantize_dequant_bit_exact(fmt, shape):
+    say("format quantize", fmt, shape)
+    _check_fmt_roundtrip(syn.normal_bf16(shape, 0.02, 300 + shape[0]), fmt, f"fmt {fmt} {shape}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_formats_edge_values_and_heavy_tails(fmt):
+    """The corner values, and Student-t weights with outliers (blocks whose
+    constants sit far below their group's maximum: E4M3 subnormals and small
+    integer codes)."""
+    say("format edges", fmt)
+    _check_fmt_roundtrip(_edge_weights(), fmt, f"fmt {fmt} edges")
+    heavy = syn.torch_student_t_outliers_bf16((512, 4096), 301, DEV)
+    bits = syn.torch_bf16_to_bits(heavy)
+    _check_fmt_roundtrip(bits, fmt, f"fmt {fmt} heavy tails")
+    tiny = (syn.normal_f32((64, 1024), 1.0, 302) * np.logspace(-30, 0, 64)[:, None]).astype(np.float32)
+    _check_fmt_roundtrip(syn.to_bf16_bits(tiny), fmt, f"fmt {fmt} 30 decades")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_formats_llama7b_up_bit_exact(fmt):
+    N, K = syn.LLAMA7B_TRAIN["weights"]["up"]
+    say("format up weight", fmt)
+    _check_fmt_roundtrip(syn.normal_bf16((N, K), 0.02, 303), fmt, f"fmt {fmt} up")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_formats_one_hot_fwd_and_bwd_exact(fmt):
+    """One-hot rows through the GEMV (M = 16), the tile kernels (M = 64, 40)
+    and the large-M path (M = 600) return the format's dequantized weight
+    columns and rows bit for bit: every in-kernel decoding of the absmax
+    byte follows the format."""
+    N, K, r = 640, 1024, 16
+    P = Problem(N, K, r, 32.0, seed=304, fmt=fmt)
+    P.Bt = torch.zeros_like(P.Bt)
+    Wf = oracle.bf16_to_f32(P.What)
+    for M in (16, 64, 600):
+        ks = np.random.default_rng(M).choice(K, M, replace=False)
+        x = np.zeros((M, K), np.uint16)
+        x[np.arange(M), ks] = 0x3F80
+        assert np.array_equal(host(run_fwd(P, x)), Wf[:, ks].T + 0.0), f"fwd one-hot M={M}"
+    for M in (40, 600):
+        ns = np.random.default_rng(M + 1).choice(N, M, replace=False)
+        dY = np.zeros((M, N), np.uint16)
+        dY[np.arange(M), ns] = 0x3F80
+        dX, _, _ = run_bwd(P, None, dY, want_grads=False)
+        assert np.array_equal(host(dX), Wf[ns] + 0.0), f"bwd one-hot M={M}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_formats_layer_within_tolerance(fmt):
+    N, K, r = 384, 640, 32
+    P = Problem(N, K, r, 16.0, seed=305, fmt=fmt)
+    for M in (4, 300):
+        x = syn.normal_bf16((M, K), 1.0, 306 + M)
+        dY = syn.normal_bf16((M, N), 1.0, 307 + M)
+        y = host(run_fwd(P, x))
+        yo, _ = oracle.linear_fwd(x, P.What, P.A, P.B, r, 16.0)
+        tol_check(y, yo, f"fmt {fmt} y M={M}")
+        dX, dA, dB = run_bwd(P, x, dY)
+        g = oracle.linear_bwd(x, dY, P.What, P.A, P.B, r, 16.0)
+        tol_check(host(dX), g["dX"], f"fmt {fmt} dX M={M}")
+        tol_check(host(dA), g["dA"], f"fmt {fmt} dA M={M}")
+        tol_check(host(dB), g["dB"], f"fmt {fmt} dB M={M}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_formats_merge_and_requantize_bit_exact(fmt):
+    N, K, r = 257, 640, 16
+    Wb = syn.normal_bf16((N, K), 0.02, 308)
+    A = syn.normal_bf16((K, r), 1.0 / np.sqrt(K), 309)
+    B = syn.normal_bf16((r, N), 0.01, 310)
+    w = quantize_gpu(dev_bf16(Wb), fmt)
+    codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16", fmt)
+    merged = q.qlora_merge_lora(dev_bf16(A), dev_bf16(B), 32.0, w=w)
+    ref = oracle.merge_lora(A, B, r, 32.0, nf4=(codes, q8, s2, N, K, fmt))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(merged).view(np.uint32), ref.view(np.uint32)), "merged bits"
+    wq = q.qlora_quantize_nf4_dq(merged, dq_format=fmt)
+    assert_nf4_equal(wq, *oracle.quantize_nf4_dq(ref, "f32", fmt), f"fmt {fmt} requantized")
