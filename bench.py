@@ -49,8 +49,8 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # scaled by the counters' reading for a copy of known size. Valid while the
 # kernel source hashes to `src_sha256` (None: not measured for this source).
 TRAFFIC = {"kernel": "gemm_nt_kernel", "call": "gemm_nt_up", "src": "gemm_nt.hip",
-           "src_sha256": "b36c2bdf943ce58df831ff2e73a783d235f443292e92ac9fed406942e3963d99",
-           "fetch_bytes": 593584128,   # 289836 KiB x 2.000 (copy reference)
+           "src_sha256": "3c0fe832a03b17b3cf633c63aa8e6e2351261033b928bff342dd6ec54b53da2a",
+           "fetch_bytes": 591427680,   # 288783 KiB x 2.000 (copy reference)
            "write_bytes": 180355072}   # 176128 KiB x 1.000 (copy reference)
 
 
@@ -199,12 +199,14 @@ def main():
 
     # The roofline launch: the forward's dense stage on the up weight alone.
     Nu, Ku = cfg["weights"]["up"]
-    q.qlora_dequant_bf16(nf4["up"], out=deq["up"])
+    # The weight in the K-slab layout the forward's large-M path dequantizes to.
+    w_up_slab = q.qlora_dequant_bf16(nf4["up"], layout=q.LAYOUT_KSLAB32)
     e_up = syn.torch_normal_bf16((Mt, 2 * r), 0.01, syn.seed_of(3, 50), dev)
     f_up = B["up"].t().contiguous()
     y_up = torch.empty((Mt, Nu), dtype=torch.float32, device=dev)
     roof = ("gemm_nt_up",
-            lambda: q.qlora_gemm_bf16_nt(x_train, deq["up"], e_up, f_up, y=y_up),
+            lambda: q.qlora_gemm_bf16_nt(x_train, w_up_slab, e_up, f_up, y=y_up,
+                                         b_layout=q.LAYOUT_KSLAB32),
             2 * Mt * Nu * Ku + 2 * Mt * (2 * r) * Nu, 0)
     if args.only:
         sel = [c for c in calls + [roof] if c[0] == args.only]

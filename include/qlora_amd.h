@@ -84,6 +84,17 @@ extern "C" {
 #define QLORA_DQ_UINT8 1
 #define QLORA_DQ_E4M3 2
 
+/* Layouts of a dequantized bf16 weight (and of the dense stage's b operand):
+ *   QLORA_LAYOUT_ROWS     [N, K] row-major;
+ *   QLORA_LAYOUT_KSLAB32  [K/32][N][32]: the 32 consecutive k of slab s of row
+ *                         n are the 64 bytes at ((s*N + n)*32) elements, so
+ *                         the slab's rows are contiguous. The large-batch
+ *                         path keeps its dequantized weight in this layout:
+ *                         a load of 16 rows of one slab is 1 KB of consecutive
+ *                         bytes, whole cache lines. */
+#define QLORA_LAYOUT_ROWS 0
+#define QLORA_LAYOUT_KSLAB32 1
+
 /* Operations for qlora_workspace_bytes. */
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1
@@ -149,9 +160,13 @@ int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, uint
 
 /* Dequantize to bf16 ([P1] bullets "Compute never happens in 4-bit"; [P3]
  * "How it works": each layer's 4-bit weights are unpacked into 16-bit).
- *   W_out  [N,K] bf16, w_hat as in the format section. */
+ *   W_out   N*K bf16, w_hat as in the format section, in `layout`
+ *           (QLORA_LAYOUT_ROWS or QLORA_LAYOUT_KSLAB32; the K-slab layout
+ *           needs N*K/64 < 2^32, else QLORA_ERR_SHAPE).
+ * QLORA_ERR_INVALID_ARG for another layout. */
 int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                       int dq_format, int64_t N, int64_t K, uint16_t* W_out, void* stream);
+                       int dq_format, int64_t N, int64_t K, uint16_t* W_out, int layout,
+                       void* stream);
 
 /* QLoRA linear forward ([P1] forward equation h = W_hat x + (alpha/r) B(Ax),
  * here in row-major form):
@@ -247,21 +262,25 @@ int qlora_adamw_step(float* param, const void* grad, int grad_dtype, float* exp_
  * just in time, then multiplied in bf16 with fp32 accumulation; [P3] "How it
  * works"), plus a rank extension:
  *   y = a b^T + e [f | f]^T
- *   a  [M,K] bf16, row stride lda elements;  b [N,K] bf16, row stride ldb
- *      (for instance W_out of qlora_dequant_bf16);  e [M,2r] bf16;
+ *   a  [M,K] bf16, row stride lda elements;  b [N,K] bf16 in b_layout:
+ *      QLORA_LAYOUT_ROWS with row stride ldb, or QLORA_LAYOUT_KSLAB32 (ldb
+ *      ignored; for instance W_out of qlora_dequant_bf16);  e [M,2r] bf16;
  *   f  [N,r] bf16;  y [M,N] fp32 or bf16 (y_dtype; bf16 is the
  *      round-to-nearest-even of the fp32 result).
  * From M = 512 rows on, qlora_linear_fwd dequantizes the weight once into
- * its workspace and runs this stage with a = x, b = w_hat, f = B^T and e the
+ * its workspace (K-slab layout) and runs this stage with a = x, b = w_hat,
+ * f = B^T and e the
  * two-term split [hi | lo] of (alpha/r) u (hi = bf16(v), lo = bf16(v - hi)),
  * so that e [f|f]^T adds (hi + lo) B; qlora_linear_bwd does the same for dX
- * with a = dY, b = w_hat^T, f = A. Requires K >= 32 and K % 32 == 0, lda and
- * ldb multiples of 8 with 512*lda + 2*K < 2^31 (likewise ldb), lda, ldb >= K,
- * r as for the linear entry points (QLORA_ERR_SHAPE / QLORA_ERR_RANK
- * otherwise). M == 0 is a successful no-op. */
+ * with a = dY, b = w_hat^T (K-slab), f = A. Requires K >= 32 and K % 32 ==
+ * 0, lda a multiple of 8 with 512*lda + 2*K < 2^31 and lda >= K; for
+ * QLORA_LAYOUT_ROWS ldb likewise, for QLORA_LAYOUT_KSLAB32 2*N*K < 2^31; r as
+ * for the linear entry points (QLORA_ERR_SHAPE / QLORA_ERR_RANK otherwise;
+ * QLORA_ERR_INVALID_ARG for another b_layout). M == 0 is a successful
+ * no-op. */
 int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
-                       const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t K,
-                       int r, void* y, int y_dtype, void* stream);
+                       int b_layout, const uint16_t* e, const uint16_t* f, int64_t M, int64_t N,
+                       int64_t K, int r, void* y, int y_dtype, void* stream);
 
 #ifdef __cplusplus
 }

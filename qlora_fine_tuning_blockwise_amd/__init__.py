@@ -20,7 +20,7 @@ __all__ = [
     "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_id", "qlora_setup_id",
     "qlora_workspace_bytes", "qlora_quantize_nf4_dq", "qlora_dequant_bf16",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "qlora_merge_lora", "qlora_adamw_step",
-    "NF4Weight", "DQ_INT8", "DQ_UINT8", "DQ_E4M3",
+    "NF4Weight", "DQ_INT8", "DQ_UINT8", "DQ_E4M3", "LAYOUT_ROWS", "LAYOUT_KSLAB32",
 ]
 
 
@@ -46,6 +46,7 @@ def _dtype_code(dt) -> int:
 
 
 DQ_INT8, DQ_UINT8, DQ_E4M3 = _lib.DQ_INT8, _lib.DQ_UINT8, _lib.DQ_E4M3
+LAYOUT_ROWS, LAYOUT_KSLAB32 = _lib.LAYOUT_ROWS, _lib.LAYOUT_KSLAB32
 
 
 class NF4Weight:
@@ -117,11 +118,17 @@ def qlora_quantize_nf4_dq(W: torch.Tensor, out: NF4Weight | None = None, stream=
     return out
 
 
-def qlora_dequant_bf16(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+def qlora_dequant_bf16(w: NF4Weight, out: torch.Tensor | None = None, stream=None,
+                       layout: int = LAYOUT_ROWS) -> torch.Tensor:
+    """w_hat as bf16: [N, K] (LAYOUT_ROWS) or [K/32, N, 32] (LAYOUT_KSLAB32)."""
+    shape = (w.N, w.K) if layout == LAYOUT_ROWS else (w.K // 32, w.N, 32)
     if out is None:
-        out = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=w.codes.device)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=w.codes.device)
+    if out.numel() != w.N * w.K:
+        raise ValueError("qlora_dequant_bf16: out must hold N*K elements")
     st = _lib.load().qlora_dequant_bf16(_ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale),
-                                        w.dq_format, w.N, w.K, _ptr(out), _stream(stream))
+                                        w.dq_format, w.N, w.K, _ptr(out), int(layout),
+                                        _stream(stream))
     _lib.check(st, "qlora_dequant_bf16")
     return out
 
@@ -177,17 +184,23 @@ def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: 
 
 def qlora_gemm_bf16_nt(a: torch.Tensor, b: torch.Tensor, e: torch.Tensor, f: torch.Tensor,
                        y: torch.Tensor | None = None, y_dtype=torch.float32,
-                       stream=None) -> torch.Tensor:
-    """y = a b^T + e [f|f]^T. a [M,K], b [N,K], e [M,2r], f [N,r], all bf16."""
+                       stream=None, b_layout: int = LAYOUT_ROWS) -> torch.Tensor:
+    """y = a b^T + e [f|f]^T. a [M,K], b [N,K] (LAYOUT_ROWS) or [K/32,N,32]
+    (LAYOUT_KSLAB32), e [M,2r], f [N,r], all bf16."""
     M, K = a.shape
-    N = b.shape[0]
+    if b_layout == LAYOUT_ROWS:
+        N = b.shape[0]
+        b_ok = b.shape == (N, K)
+    else:
+        N = b.shape[1]
+        b_ok = b.shape == (K // 32, N, 32)
     r = f.shape[1]
-    if b.shape[1] != K or e.shape != (M, 2 * r) or f.shape[0] != N:
+    if not b_ok or e.shape != (M, 2 * r) or f.shape[0] != N:
         raise ValueError("qlora_gemm_bf16_nt: inconsistent shapes")
     if y is None:
         y = torch.empty((M, N), dtype=y_dtype, device=a.device)
-    st = _lib.load().qlora_gemm_bf16_nt(_ptr(a), K, _ptr(b), K, _ptr(e), _ptr(f), M, N, K, r,
-                                        _ptr(y), _dtype_code(y.dtype), _stream(stream))
+    st = _lib.load().qlora_gemm_bf16_nt(_ptr(a), K, _ptr(b), K, int(b_layout), _ptr(e), _ptr(f), M,
+                                        N, K, r, _ptr(y), _dtype_code(y.dtype), _stream(stream))
     _lib.check(st, "qlora_gemm_bf16_nt")
     return y
 

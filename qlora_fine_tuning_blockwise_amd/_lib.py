@@ -16,6 +16,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "qlora_amd.h")
 OK = 0
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+LAYOUT_ROWS = 0
+LAYOUT_KSLAB32 = 1
 DQ_INT8 = 0
 DQ_UINT8 = 1
 DQ_E4M3 = 2
@@ -38,12 +40,12 @@ SIGNATURES = {
     "qlora_workspace_bytes": (SZ, [INT, I64, I64, I64, INT]),
     "qlora_setup_id": (ctypes.c_uint32, [INT]),
     "qlora_quantize_nf4_dq": (INT, [P, INT, I64, I64, P, P, P, INT, P]),
-    "qlora_dequant_bf16": (INT, [P, P, P, INT, I64, I64, P, P]),
+    "qlora_dequant_bf16": (INT, [P, P, P, INT, I64, I64, P, INT, P]),
     "qlora_linear_fwd": (INT, [P, P, P, INT, I64, I64, P, I64, P, P, INT, FLT, P, INT, P, P, SZ,
                                P]),
     "qlora_linear_bwd": (INT, [P, P, P, INT, I64, I64, P, P, I64, P, P, INT, FLT, P, P, INT, P, P,
                                INT, P, SZ, P]),
-    "qlora_gemm_bf16_nt": (INT, [P, I64, P, I64, P, P, I64, I64, I64, INT, P, INT, P]),
+    "qlora_gemm_bf16_nt": (INT, [P, I64, P, I64, INT, P, P, I64, I64, I64, INT, P, INT, P]),
     "qlora_merge_lora": (INT, [P, P, P, INT, P, I64, I64, P, P, INT, FLT, P, P, SZ, P]),
     "qlora_adamw_step": (INT, [P, P, INT, P, P, P, I64, DBL, DBL, DBL, DBL, DBL, I64, P]),
 }

@@ -17,8 +17,14 @@ constexpr int64_t kGemvMaxM = 16;  // decode sizes take the GEMV path
 // small share of the call); below it the tile kernels dequantize in place.
 constexpr int64_t kPlainMinM = 512;
 
-bool fwd_plain(int64_t M, int64_t K) { return M >= kPlainMinM && gemm_nt_supported(K, K, K); }
-bool bwd_plain(int64_t M, int64_t N) { return M >= kPlainMinM && gemm_nt_supported(N, N, N); }
+// The large-M path keeps the dequantized weight in the K-slab layout (whole
+// cache lines per direct-to-LDS load of the GEMM's b operand).
+bool fwd_plain(int64_t M, int64_t N, int64_t K) {
+  return M >= kPlainMinM && gemm_nt_supported(K, K, 0, N, true);
+}
+bool bwd_plain(int64_t M, int64_t N, int64_t K) {
+  return M >= kPlainMinM && N % 32 == 0 && gemm_nt_supported(N, N, 0, K, true);
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -55,7 +61,7 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
     L.down = c.take((size_t)lora_down_slices(K) * M * r * 4);
     L.Bt = c.take((size_t)N * r * 2);
     L.ulr = c.take((size_t)M * 2 * r * 2);
-    L.plain = fwd_plain(M, K);
+    L.plain = fwd_plain(M, N, K);
     if (L.plain) L.W = c.take((size_t)N * K * 2);
   }
   L.total = c.off;
@@ -83,7 +89,7 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   L.vT = c.take(2 * (size_t)r * Mp * 2);
   L.uT = c.take(2 * (size_t)r * Mp * 2);
   L.col = c.take((size_t)colred_splits(M) * T * r * 4);
-  L.plain = bwd_plain(M, N);
+  L.plain = bwd_plain(M, N, K);
   if (L.plain) L.Wt = c.take((size_t)K * N * 2);
   L.total = c.off;
   return L;
@@ -209,14 +215,19 @@ int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, uint
 }
 
 int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                       int dq_format, int64_t N, int64_t K, uint16_t* W_out, void* stream) {
+                       int dq_format, int64_t N, int64_t K, uint16_t* W_out, int layout,
+                       void* stream) {
   Codebook cb;
   if (const int st = call_codebook(dq_format, &cb)) return st;
   if (!codes || !absmax_q || !absmax_scale || !W_out) return QLORA_ERR_INVALID_ARG;
+  if (layout != QLORA_LAYOUT_ROWS && layout != QLORA_LAYOUT_KSLAB32) return QLORA_ERR_INVALID_ARG;
   if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
+  if (layout == QLORA_LAYOUT_KSLAB32 && N * (K / kBlock) >= ((int64_t)1 << 32))
+    return QLORA_ERR_SHAPE;
   if (!aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale) || !aligned16(W_out))
     return QLORA_ERR_ALIGN;
-  return launch_status(launch_dequant(codes, absmax_q, absmax_scale, N * K, W_out, cb,
+  return launch_status(launch_dequant(codes, absmax_q, absmax_scale, N * K, W_out,
+                                      layout == QLORA_LAYOUT_KSLAB32 ? N : 0, cb,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -262,8 +273,8 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
     if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
     if (e == hipSuccess && L.plain) {
       uint16_t* W = at<uint16_t>(workspace, L.W);
-      e = launch_dequant(codes, absmax_q, absmax_scale, N * K, W, cb, st);
-      if (e == hipSuccess) e = launch_gemm_nt(x, K, W, K, ulr, Bt, M, N, K, r, y, ybf, st);
+      e = launch_dequant(codes, absmax_q, absmax_scale, N * K, W, N, cb, st);  // K-slab
+      if (e == hipSuccess) e = launch_gemm_nt(x, K, W, 0, ulr, Bt, M, N, K, r, y, ybf, true, st);
     } else if (e == hipSuccess) {
       e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, cb, st);
     }
@@ -321,9 +332,10 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
                                   st);
   if (e == hipSuccess && dX && L.plain) {  // dX = dY w_hat through w_hat^T [K,N]
     uint16_t* Wt = at<uint16_t>(workspace, L.Wt);
-    e = launch_dequant_t(codes, absmax_q, absmax_scale, N, K, Wt, cb, st);
+    e = launch_dequant_t(codes, absmax_q, absmax_scale, N, K, Wt, true, cb, st);  // K-slab
     if (e == hipSuccess)
-      e = launch_gemm_nt(dY, N, Wt, N, svlr, A, M, K, N, r, dX, dx_dtype == QLORA_DTYPE_BF16, st);
+      e = launch_gemm_nt(dY, N, Wt, 0, svlr, A, M, K, N, r, dX, dx_dtype == QLORA_DTYPE_BF16, true,
+                         st);
   } else if (e == hipSuccess && dX) {
     e = launch_gemm_bwd(dY, codes, absmax_q, absmax_scale, svlr, A, M, N, K, r, dX,
                         dx_dtype == QLORA_DTYPE_BF16, cb, st);
@@ -357,10 +369,13 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
 }
 
 int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
-                       const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t K,
-                       int r, void* y, int y_dtype, void* stream) {
+                       int b_layout, const uint16_t* e, const uint16_t* f, int64_t M, int64_t N,
+                       int64_t K, int r, void* y, int y_dtype, void* stream) {
   if (M < 0 || N < 1 || K < 1) return M < 0 ? QLORA_ERR_INVALID_ARG : QLORA_ERR_SHAPE;
-  if (lda < K || ldb < K || !gemm_nt_supported(K, lda, ldb)) return QLORA_ERR_SHAPE;
+  if (b_layout != QLORA_LAYOUT_ROWS && b_layout != QLORA_LAYOUT_KSLAB32) return QLORA_ERR_INVALID_ARG;
+  const bool kslab = b_layout == QLORA_LAYOUT_KSLAB32;
+  if (lda < K || (!kslab && ldb < K) || !gemm_nt_supported(K, lda, ldb, N, kslab))
+    return QLORA_ERR_SHAPE;
   if (y_dtype != QLORA_DTYPE_F32 && y_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
   if (!rank_ok(r)) return QLORA_ERR_RANK;
   if (M == 0) return QLORA_OK;
@@ -368,7 +383,7 @@ int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_
   if (!aligned16(a) || !aligned16(b) || !aligned16(e) || !aligned16(f) || !aligned16(y))
     return QLORA_ERR_ALIGN;
   return launch_status(launch_gemm_nt(a, lda, b, ldb, e, f, M, N, K, r, y,
-                                      y_dtype == QLORA_DTYPE_BF16,
+                                      y_dtype == QLORA_DTYPE_BF16, kslab,
                                       static_cast<hipStream_t>(stream)));
 }
 

@@ -34,13 +34,18 @@ constexpr int kNtGroup = 4;             // tile rows per group in the tile order
 
 struct NtArgs {
   const uint16_t* a;  // [M, Kr], row stride lda elements
-  const uint16_t* b;  // [N, Kr], row stride ldb elements
+  const uint16_t* b;  // [N, Kr], row stride ldb elements, or K-slab layout (b_kslab)
   const uint16_t* e;  // [M, 2r]
   const uint16_t* f;  // [N, r]
   void* y;            // [M, N]
   int64_t M, N, Kr, lda, ldb;
   int r;
   int tiles_m, tiles_n;
+  // b in the K-slab layout [Kr/32][N][32]: the 32 reduction elements of one
+  // step of every row are one contiguous 64-byte piece, and a step's rows
+  // follow each other, so a direct-to-LDS load of 16 rows reads 1 KB of
+  // consecutive bytes (whole cache lines) instead of 16 half lines.
+  int b_kslab;
 };
 
 // Tile of workgroup `wg`. Workgroups are dealt to the eight XCDs round robin
@@ -119,12 +124,14 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
     const int64_t ar = m0 + row < M ? row : M - 1 - m0;
     const int64_t br = n0 + row < N ? row : N - 1 - n0;
     aoff[j] = (uint32_t)(ar * p.lda * 2 + 16 * c);
-    boff[j] = (uint32_t)(br * p.ldb * 2 + 16 * c);
+    boff[j] = (uint32_t)(br * (p.b_kslab ? 64 : p.ldb * 2) + 16 * c);
   }
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
       (void*)uniform_ptr(p.a + m0 * p.lda), (short)0, (int)0x7FFFFFFF, 0x00020000);
   const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(p.b + n0 * p.ldb), (short)0, (int)0x7FFFFFFF, 0x00020000);
+      (void*)uniform_ptr(p.b + n0 * (p.b_kslab ? 32 : p.ldb)), (short)0, (int)0x7FFFFFFF,
+      0x00020000);
+  const int bstep = p.b_kslab ? (int)(64 * N) : 64;  // bytes from one step to the next
   const int win = 4 * w * 512;  // element offset of this wave's first window
   typedef __attribute__((address_space(3))) void lds_void;
   auto dma = [&](int j, int kb, uint16_t* stage) {
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
                                                64 * ks, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (lds_void*)(stage + kNtOp + win + 512 * (j - 4)),
-                                               16, boff[j - 4], 64 * ks, 0, 0);
+                                               16, boff[j - 4], bstep * ks, 0, 0);
   };
   auto issue = [&](int kb, uint16_t* stage) {
 #pragma unroll
@@ -322,18 +329,18 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
 
 }  // namespace
 
-bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb) {
+bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb, int64_t N, bool b_kslab) {
   // Buffer offsets (tile row offset + step offset) stay below 2^31.
   const int64_t lim = (int64_t)1 << 31;
-  return Kr >= kNtBK && Kr % kNtBK == 0 && lda % 8 == 0 && ldb % 8 == 0 &&
-         2 * kNtBM * lda + 2 * Kr < lim && 2 * kNtBN * ldb + 2 * Kr < lim;
+  const bool b_ok = b_kslab ? 2 * N * Kr < lim : ldb % 8 == 0 && 2 * kNtBN * ldb + 2 * Kr < lim;
+  return Kr >= kNtBK && Kr % kNtBK == 0 && lda % 8 == 0 && 2 * kNtBM * lda + 2 * Kr < lim && b_ok;
 }
 
 hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                           const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t Kr,
-                          int r, void* y, bool y_bf16, hipStream_t st) {
+                          int r, void* y, bool y_bf16, bool b_kslab, hipStream_t st) {
   const int tiles_m = (int)((M + kNtBM - 1) / kNtBM), tiles_n = (int)((N + kNtBN - 1) / kNtBN);
-  const NtArgs args{a, b, e, f, y, M, N, Kr, lda, ldb, r, tiles_m, tiles_n};
+  const NtArgs args{a, b, e, f, y, M, N, Kr, lda, ldb, r, tiles_m, tiles_n, b_kslab ? 1 : 0};
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   if (y_bf16)
     hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(256), 0, st, args);

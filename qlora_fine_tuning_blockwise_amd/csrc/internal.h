@@ -36,8 +36,10 @@ uint32_t setup_id(int dq_format);
 // Each returns hipSuccess or the launch error. Sizes are pre-validated.
 hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes, int8_t* q8,
                            float* s2, const Codebook& cb, hipStream_t st);
+// w_hat as bf16, row-major [N,K] (rows = 0), or in the K-slab layout
+// [K/32][N][32] of rows = N weight rows of length K = n / N.
 hipError_t launch_dequant(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t n,
-                          uint16_t* out, const Codebook& cb, hipStream_t st);
+                          uint16_t* out, int64_t rows, const Codebook& cb, hipStream_t st);
 
 // out[c][r'] = in[r'][c] for a bf16 [rows, cols] matrix.
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
@@ -81,16 +83,21 @@ hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_
                            const Codebook& cb, hipStream_t st);
 
 // Large-M path: plain bf16 GEMM y[M,N] = a[M,Kr] b[N,Kr]^T + e[M,2r] [f|f][N,2r]^T
-// (a, b row-major with row strides lda, ldb; e the two-term split written by
-// launch_lora_down_finalize; f [N,r]). gemm_nt_supported says whether the
-// shape fits the kernel (Kr a multiple of 32, 16-byte aligned rows).
-bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb);
+// (a row-major with row stride lda; b row-major with row stride ldb, or in
+// the K-slab layout [Kr/32][N][32] when b_kslab; e the two-term split written
+// by launch_lora_down_finalize; f [N,r]). gemm_nt_supported says whether the
+// shape fits the kernel (Kr a multiple of 32, 16-byte aligned rows, 32-bit
+// buffer offsets).
+bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb, int64_t N, bool b_kslab);
 hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                           const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t Kr,
-                          int r, void* y, bool y_bf16, hipStream_t st);
-// out[k][n] = w_hat[n][k] as bf16 ([K, N], the transpose of launch_dequant's output).
+                          int r, void* y, bool y_bf16, bool b_kslab, hipStream_t st);
+// out[k][n] = w_hat[n][k] as bf16: [K, N] row-major (the transpose of
+// launch_dequant's output), or in the K-slab layout [N/32][K][32] when kslab
+// (N % 32 == 0).
 hipError_t launch_dequant_t(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t N,
-                            int64_t K, uint16_t* out, const Codebook& cb, hipStream_t st);
+                            int64_t K, uint16_t* out, bool kslab, const Codebook& cb,
+                            hipStream_t st);
 
 // merged = base + s (A B)^T in binary32 (adapter sum in order j = 0..r-1);
 // base = the dequantized NF4 weight (W == NULL) or the bf16 weight W.

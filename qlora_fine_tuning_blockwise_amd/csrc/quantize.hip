@@ -205,23 +205,44 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
 // at a time), bytes 1..3 = the region's offset. Each wave runs kDqPasses
 // passes with every load issued first. Lanes past the last block redo the
 // last block (same values to the same place), so no lane branches.
+// With kKSlab the output is the K-slab layout [K/32][rows][32] of a weight
+// with `rows` rows of kb blocks, and a wave takes 8 consecutive rows (one per
+// group) by kDqPasses consecutive blocks (one per pass) instead: per pass,
+// lanes 0-3 of the 8 groups write slab 2*blk for the 8 rows, 512 contiguous
+// bytes, and lanes 4-7 the next slab, so every store fills whole cache
+// lines; the passes walk along each row's 128-byte line of codes. Rows and
+// blocks past the end are clamped to the last (same values, same place).
 constexpr int kDqPasses = 4;
 
+template <bool kKSlab>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const int8_t* __restrict__ q8,
                                                       const float* __restrict__ s2,
                                                       int64_t nblocks, uint16_t* __restrict__ out,
-                                                      Codebook cb) {
+                                                      uint32_t rows, uint32_t kb, Codebook cb) {
   __shared__ __attribute__((aligned(1024))) uint32_t tab[4 * kDqPasses * 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 3, j = lane & 7;
   const int64_t b0 = ((int64_t)blockIdx.x * 4 + w) * (8 * kDqPasses) + g;
+  uint32_t srow = 0, sblk0 = 0;  // K-slab mode: this group's row, the wave's first block
+  if (kKSlab) {
+    // Consecutive waves take consecutive row groups of one block group, so
+    // the eight slabs a block group writes fill sequentially.
+    const uint32_t wid = (uint32_t)blockIdx.x * 4 + (uint32_t)__builtin_amdgcn_readfirstlane(w);
+    const uint32_t rgs = (rows + 7) / 8;  // row groups
+    const uint32_t cg = wid / rgs;
+    srow = min(8 * (wid - cg * rgs) + (uint32_t)g, rows - 1);
+    sblk0 = min(cg * kDqPasses, kb - 1);
+  }
   int64_t bk[kDqPasses];
   uint32_t cw[kDqPasses];
   float ch[kDqPasses];
 #pragma unroll
   for (int p = 0; p < kDqPasses; ++p) {
-    bk[p] = b0 + 8 * p < nblocks ? b0 + 8 * p : nblocks - 1;
+    if (kKSlab)
+      bk[p] = (int64_t)srow * kb + min(sblk0 + (uint32_t)p, kb - 1);
+    else
+      bk[p] = b0 + 8 * p < nblocks ? b0 + 8 * p : nblocks - 1;
     cw[p] = reinterpret_cast<const uint32_t*>(codes)[bk[p] * 8 + j];
     ch[p] = q8_value(q8[bk[p]], cb.dq_format) * s2[bk[p] >> 8];
   }
@@ -250,7 +271,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       v[2 * k] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(tl, region, sel));
       v[2 * k + 1] = *reinterpret_cast<const uint16_t*>(tb + __builtin_amdgcn_perm(th, region, sel));
     }
-    *reinterpret_cast<u32x4_t*>(out + bk[p] * 64 + 8 * j) =
+    uint16_t* dst;
+    if (kKSlab) {
+      const uint32_t s = 2 * min(sblk0 + (uint32_t)p, kb - 1) + (uint32_t)(j >> 2);
+      dst = out + ((int64_t)s * rows + srow) * 32 + 8 * (j & 3);
+    } else {
+      dst = out + bk[p] * 64 + 8 * j;
+    }
+    *reinterpret_cast<u32x4_t*>(dst) =
         u32x4_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
                 __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
                 __builtin_amdgcn_perm(v[5], v[4], 0x05040100u),
@@ -268,6 +296,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 // workgroup writes 256-byte rows of out.
 constexpr int kDtCols = 128;  // tile columns (k)
 
+template <bool kKSlab>
 __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
                                                         const int8_t* __restrict__ q8,
                                                         const float* __restrict__ s2, int64_t N,
@@ -317,6 +346,11 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
     const int64_t k = k0 + kr;
     if (k >= K) break;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&tile[kr * 64 + 4 * col]);
+    if (kKSlab) {  // N % 32 == 0: the 8 columns sit in slab nc / 32
+      if (nc < N)
+        *reinterpret_cast<u32x4_t*>(out + ((nc >> 5) * K + k) * 32 + (nc & 31)) = v;
+      continue;
+    }
     uint16_t* dst = out + k * N + nc;
     if (nc + 8 <= N && (N & 7) == 0) {
       *reinterpret_cast<u32x4_t*>(dst) = v;
@@ -346,21 +380,36 @@ hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t n,
-                          uint16_t* out, const Codebook& cb, hipStream_t st) {
+                          uint16_t* out, int64_t rows, const Codebook& cb, hipStream_t st) {
   const int64_t nb = n / kBlock;
   const int64_t per_wg = 4 * 8 * kDqPasses;  // blocks per workgroup
   const int64_t grid = (nb + per_wg - 1) / per_wg;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(256), 0, st, codes, q8, s2, nb,
-                     out, cb);
+  if (rows > 0) {
+    if (nb >= ((int64_t)1 << 32) || nb % rows) return hipErrorInvalidValue;
+    const int64_t kb = nb / rows;
+    const int64_t waves = (rows + 7) / 8 * ((kb + kDqPasses - 1) / kDqPasses);
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                       codes, q8, s2, nb, out, (uint32_t)rows, (uint32_t)kb, cb);
+  } else {
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st, codes, q8,
+                       s2, nb, out, 0u, 0u, cb);
+  }
   return hipGetLastError();
 }
 
 
 hipError_t launch_dequant_t(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t N,
-                            int64_t K, uint16_t* out, const Codebook& cb, hipStream_t st) {
+                            int64_t K, uint16_t* out, bool kslab, const Codebook& cb,
+                            hipStream_t st) {
   const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((K + kDtCols - 1) / kDtCols));
-  hipLaunchKernelGGL(dequant_t_kernel, grid, dim3(256), 0, st, codes, q8, s2, N, K, out, cb);
+  if (kslab) {
+    if (N % 32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(dequant_t_kernel<true>, grid, dim3(256), 0, st, codes, q8, s2, N, K, out, cb);
+  } else {
+    hipLaunchKernelGGL(dequant_t_kernel<false>, grid, dim3(256), 0, st, codes, q8, s2, N, K, out,
+                       cb);
+  }
   return hipGetLastError();
 }
 

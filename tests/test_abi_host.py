@@ -73,10 +73,12 @@ def test_quantize_validation(lib):
     assert f(_p(FAKE), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), 3, None) == 1   # dq format
     assert f(_p(FAKE), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), -1, None) == 1
     d = lib.qlora_dequant_bf16
-    assert d(_p(FAKE), None, _p(FAKE), 0, 4, 64, _p(FAKE), None) == 1
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 0, 4, 65, _p(FAKE), None) == 2
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE + 4), 0, 4, 64, _p(FAKE), None) == 3
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 9, 4, 64, _p(FAKE), None) == 1     # dq format
+    assert d(_p(FAKE), None, _p(FAKE), 0, 4, 64, _p(FAKE), 0, None) == 1
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 0, 4, 65, _p(FAKE), 0, None) == 2
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE + 4), 0, 4, 64, _p(FAKE), 0, None) == 3
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 9, 4, 64, _p(FAKE), 0, None) == 1     # dq format
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 0, 4, 64, _p(FAKE), 2, None) == 1     # layout
+    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 0, 1 << 22, 1 << 16, _p(FAKE), 1, None) == 2
 
 
 def test_setup_ids(lib):
@@ -135,23 +137,28 @@ def test_bwd_validation(lib):
 
 def test_gemm_nt_validation(lib):
     f = lib.qlora_gemm_bf16_nt
-    base = [_p(FAKE), 64, _p(FAKE), 64, _p(FAKE), _p(FAKE), 8, 128, 64, 16, _p(FAKE), 0, None]
+    base = [_p(FAKE), 64, _p(FAKE), 64, 0, _p(FAKE), _p(FAKE), 8, 128, 64, 16, _p(FAKE), 0, None]
 
-    def call(i, v):
+    def call(i, v, **kw):
         a = list(base)
         a[i] = v
+        for j, w in kw.items():
+            a[int(j[1:])] = w
         return f(*a)
-    assert call(6, -1) == 1            # M < 0
-    assert call(7, 0) == 2             # N < 1
-    assert call(8, 48) == 2            # K % 32
+    assert call(7, -1) == 1            # M < 0
+    assert call(8, 0) == 2             # N < 1
+    assert call(9, 48) == 2            # K % 32
     assert call(1, 32) == 2            # lda < K
     assert call(3, 68) == 2            # ldb % 8
     assert call(1, 1 << 22) == 2       # tile row offsets past 2^31 bytes
-    assert call(11, 3) == 4            # y dtype
-    assert call(9, 8) == 5             # r
+    assert call(12, 3) == 4            # y dtype
+    assert call(10, 8) == 5            # r
     assert call(0, None) == 1          # a missing
-    assert call(4, _p(FAKE + 8)) == 3  # e misaligned
-    assert call(6, 0) == 0             # empty: a no-op
+    assert call(5, _p(FAKE + 8)) == 3  # e misaligned
+    assert call(4, 2) == 1             # b layout
+    assert call(4, 1, a1=2048, a8=1 << 20, a9=2048) == 2  # K-slab: 2 N K past 2^31 bytes
+    assert call(4, 1, a3=3, a7=-1) == 1  # K-slab ignores ldb (M < 0 still rejected first)
+    assert call(7, 0) == 0             # empty: a no-op
 
 
 def test_merge_validation(lib):

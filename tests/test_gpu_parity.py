@@ -357,9 +357,9 @@ def test_gemm_bf16_nt_dense_stage(M, N, K, r, pad):
     y = torch.empty((M, N), dtype=torch.float32, device=DEV)
     L = q._lib.load()
     P_ = ctypes.c_void_p
-    st = L.qlora_gemm_bf16_nt(P_(at.data_ptr()), K + pad, P_(bt.data_ptr()), K, P_(et.data_ptr()),
-                              P_(ft.data_ptr()), M, N, K, r, P_(y.data_ptr()), 0,
-                              P_(torch.cuda.current_stream().cuda_stream))
+    st = L.qlora_gemm_bf16_nt(P_(at.data_ptr()), K + pad, P_(bt.data_ptr()), K, q.LAYOUT_ROWS,
+                              P_(et.data_ptr()), P_(ft.data_ptr()), M, N, K, r, P_(y.data_ptr()),
+                              0, P_(torch.cuda.current_stream().cuda_stream))
     assert st == 0
     torch.cuda.synchronize()
     f64 = lambda v: oracle.bf16_to_f32(v).astype(np.float64)
@@ -368,6 +368,28 @@ def test_gemm_bf16_nt_dense_stage(M, N, K, r, pad):
     if pad == 0:
         yb = q.qlora_gemm_bf16_nt(at, bt, et, ft, y_dtype=torch.bfloat16)
         assert torch.equal(yb, y.to(torch.bfloat16))
+    # b in the K-slab layout [K/32, N, 32]: the same tiles reach the MFMAs,
+    # so y is the same bit for bit
+    b_slab = bt.view(N, K // 32, 32).transpose(0, 1).contiguous()
+    ys = torch.empty_like(y)
+    st = L.qlora_gemm_bf16_nt(P_(at.data_ptr()), K + pad, P_(b_slab.data_ptr()), 0,
+                              q.LAYOUT_KSLAB32, P_(et.data_ptr()), P_(ft.data_ptr()), M, N, K, r,
+                              P_(ys.data_ptr()), 0, P_(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(ys, y), "K-slab b"
+
+
+@pytest.mark.parametrize("N,K", [(257, 640), (64, 64), (11008, 4096)])
+def test_dequant_kslab_layout_bit_exact(N, K):
+    """The K-slab layout [K/32, N, 32] holds exactly the oracle's w_hat."""
+    say("dequant kslab", N, K)
+    Wb = syn.normal_bf16((N, K), 0.02, 70 + N)
+    w = quantize_gpu(dev_bf16(Wb))
+    got = syn.torch_bf16_to_bits(q.qlora_dequant_bf16(w, layout=q.LAYOUT_KSLAB32))
+    codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+    want = oracle.dequant_dq(codes, q8, s2)[1].reshape(N, K // 32, 32).transpose(1, 0, 2)
+    assert np.array_equal(got, want)
 
 
 # ------------------------------------------------------------------ backward
