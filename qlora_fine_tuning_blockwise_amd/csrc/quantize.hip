@@ -32,11 +32,27 @@ __device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t v) {
 
 // Code of a normalised value x in [-1,1]: bucket b = floor(32x + 32), then
 // code = (#thresholds below the bucket) + (x > the bucket's threshold).
-// The index is masked, so a non-finite x still reads inside the table.
+// The byte offset 8b of the bucket's 8-byte entry is floor(256x + 256) with
+// its low three bits cleared (scaling by 8 commutes with the rounding, and
+// floor(8y) & ~7 = 8 floor(y) for y >= 0), so one AND both scales and masks;
+// the mask keeps a non-finite x inside the table.
 __device__ __forceinline__ uint32_t nf4_code(float x, const u32x2_t* lut) {
-  const int b = ((int)__builtin_fmaf(x, 32.0f, 32.0f)) & (kLut - 1);
-  const u32x2_t e = lut[b];
+  const uint32_t off = ((uint32_t)(int)__builtin_fmaf(x, 256.0f, 256.0f)) & (8u * kLut - 8u);
+  const u32x2_t e = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const char*>(lut) + off);
   return e.y + (x > __uint_as_float(e.x) ? 1u : 0u);
+}
+
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
+
+// Largest |w| bit pattern of the bf16 pairs in four words, as fp32 bits:
+// packed 16-bit maxima of the magnitudes, then the larger half.
+__device__ __forceinline__ uint32_t absmax_bf16x8(const uint32_t (&v)[4]) {
+  u16x2_t m[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m[j] = __builtin_bit_cast(u16x2_t, v[j] & 0x7FFF7FFFu);
+  const u16x2_t a = __builtin_elementwise_max(__builtin_elementwise_max(m[0], m[1]),
+                                              __builtin_elementwise_max(m[2], m[3]));
+  return (uint32_t)max(a.x, a.y) << 16;
 }
 
 // Nearest FP8 E4M3 code of x >= 0 (or +inf), ties to the even code,
@@ -84,54 +100,77 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   }
 
   // Issue every load of the group up front (8 passes x 8 weights).
+  // Blocks past the group's end (last group only) load the group's last
+  // block instead: no branch around the loads, so each pass waits only for
+  // its own. Their constants and codes are never stored.
   constexpr int kWords = kF32In ? 8 : 4;  // dwords per 8 weights
   uint32_t raw[8][kWords];
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
-    const int bl = it * 32 + (tid >> 3);
+    const int bl = min(it * 32 + (tid >> 3), nbg - 1);
     const int64_t e0 = (b0 + bl) * kBlock + (tid & 7) * 8;
-    if (bl < nbg) {
-      if (kF32In) {
-        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(W) + e0);
-        const u32x4_t a = p[0], b = p[1];
-        raw[it][0] = a.x; raw[it][1] = a.y; raw[it][2] = a.z; raw[it][3] = a.w;
-        raw[it][4] = b.x; raw[it][5] = b.y; raw[it][6] = b.z; raw[it][7] = b.w;
-      } else {
-        const u32x4_t a =
-            *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(W) + e0);
-        raw[it][0] = a.x; raw[it][1] = a.y; raw[it][2] = a.z; raw[it][3] = a.w;
-      }
+    if (kF32In) {
+      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(W) + e0);
+      const u32x4_t a = p[0], b = p[1];
+      raw[it][0] = a.x; raw[it][1] = a.y; raw[it][2] = a.z; raw[it][3] = a.w;
+      raw[it][4] = b.x; raw[it][5] = b.y; raw[it][6] = b.z; raw[it][7] = b.w;
     } else {
-#pragma unroll
-      for (int j = 0; j < kWords; ++j) raw[it][j] = 0u;
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(W) + e0);
+      raw[it][0] = a.x; raw[it][1] = a.y; raw[it][2] = a.z; raw[it][3] = a.w;
     }
   }
-  __syncthreads();  // lut ready
+  // The table is ready once every wave's LDS writes are done. A plain
+  // barrier after an LDS-only wait: a full __syncthreads would also wait for
+  // the weight loads above, and each pass should start when its own arrive.
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
 
+  // Block constants of all eight passes first: lane j of each 8-lane group
+  // then computes the correctly rounded reciprocal for pass j alone, and
+  // every pass fetches its reciprocal from that lane (one division per lane
+  // instead of one per pass).
+  float c1v[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    uint32_t amax = 0;
+    if (kF32In) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = max(amax, raw[it][j] & 0x7FFFFFFFu);
+    } else {
+      amax = absmax_bf16x8(*reinterpret_cast<const uint32_t(*)[4]>(&raw[it][0]));
+    }
+    c1v[it] = __uint_as_float(max_over_8_lanes(amax));
+    const int bl = it * 32 + (tid >> 3);
+    if (bl < nbg && (tid & 7) == 0) c1s[bl] = c1v[it];
+  }
+  float rc_mine = 1.0f;
+  if (!kF32In) {
+    float c1_mine = c1v[0];
+#pragma unroll
+    for (int it = 1; it < 8; ++it)
+      if ((tid & 7) == it) c1_mine = c1v[it];
+    rc_mine = 1.0f / c1_mine;  // +inf for an all-zero block (unused)
+  }
+
+  // This thread's code word of pass `it`: block it*32 + tid/8 of the group,
+  // word tid%8, i.e. dword tid + 256*it of the group's codes.
+  uint32_t* const cwp = reinterpret_cast<uint32_t*>(codes + b0 * (kBlock / 2)) + tid;
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int bl = it * 32 + (tid >> 3);
     float w[8];
-    uint32_t amax = 0;
     if (kF32In) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        w[j] = __uint_as_float(raw[it][j]);
-        amax = max(amax, raw[it][j] & 0x7FFFFFFFu);
-      }
+      for (int j = 0; j < 8; ++j) w[j] = __uint_as_float(raw[it][j]);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t v = raw[it][j];
         w[2 * j] = __uint_as_float(v << 16);
         w[2 * j + 1] = __uint_as_float(v & 0xFFFF0000u);
-        amax = max(amax, max(v & 0x7FFFu, (v >> 16) & 0x7FFFu));
       }
-      amax <<= 16;
     }
-    amax = max_over_8_lanes(amax);
-    const float c1 = __uint_as_float(amax);
-    if (bl < nbg && (tid & 7) == 0) c1s[bl] = c1;
+    const float c1 = c1v[it];
 
     uint32_t word = 0;
     if (c1 == 0.0f) {
@@ -143,8 +182,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
       // with c1 in this range and |w| <= c1: x equals the IEEE quotient
       // whenever |w/c1| >= 2^-10, and always yields the same NF4 code (the
       // smaller quotients that can differ in low bits sit far below every
-      // threshold).
-      const float rc = 1.0f / c1;
+      // threshold). r comes from lane it of this lane's group.
+      const float rc = __shfl(rc_mine, (tid & 56) | it);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float x0 = w[j] * rc;
@@ -156,10 +195,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
 #pragma unroll
       for (int j = 0; j < 8; ++j) word |= nf4_code(w[j] / c1, lut) << (4 * j);
     }
-    if (bl < nbg) {
-      const int64_t e0 = (b0 + bl) * kBlock + (tid & 7) * 8;
-      *reinterpret_cast<uint32_t*>(codes + e0 / 2) = word;
-    }
+    if (bl < nbg) cwp[256 * it] = word;
   }
   __syncthreads();  // c1s complete
 

@@ -7,10 +7,12 @@
  *    e = RN(w - x0*c1) (one FMA), x = RN(x0 + e*rc) (one FMA). check_division
  *    compares that against the IEEE quotient for every such bf16 pair: the
  *    NF4 code must always agree, and the value itself whenever |w/c1| >= 2^-10.
- * 2. Code search. The kernel maps x in [-1,1] to bucket floor(32x + 32) (one
- *    FMA), and takes code = (#thresholds below the bucket) + (x > the one
- *    threshold inside the bucket). check_buckets compares that with
- *    #{i : x > T[i]} for every fp32 x in [-1, 1].
+ * 2. Code search. The kernel maps x in [-1,1] to bucket floor(32x + 32),
+ *    computed as the byte offset (int)fmaf(x, 256, 256) & 0x3F8 = 8 * bucket
+ *    (one FMA, one AND), and takes code = (#thresholds below the bucket) +
+ *    (x > the one threshold inside the bucket). check_buckets checks the
+ *    offset against 8 floor(32x + 32) and the code against #{i : x > T[i]}
+ *    for every fp32 x in [-1, 1].
  * IEEE binary32 arithmetic, round to nearest even, no flush to zero; fmaf is
  * the fused multiply-add of the C library.
  */
@@ -76,7 +78,9 @@ int64_t check_buckets(const float thr[15], int64_t* checked) {
         for (int sgn = 0; sgn < 2; ++sgn) {
             float x = f_of(u | (sgn ? 0x80000000u : 0u));
             int b = ((int)fmaf(x, 32.0f, 32.0f)) & 127;
-            if (b > 64) { bad++; continue; }
+            /* the kernel's form: byte offset of the 8-byte entry */
+            int off = (int)((uint32_t)(int)fmaf(x, 256.0f, 256.0f) & 0x3F8u);
+            if (b > 64 || off != 8 * b) { bad++; continue; }
             uint32_t code = lut_below[b] + (x > f_of(lut_thr[b]) ? 1u : 0u);
             uint32_t ref = 0;
             for (int i = 0; i < 15; ++i) ref += x > thr[i];
