@@ -12,15 +12,17 @@
 // (bf16(L[code] * c1_hat), widened) or the bf16 weight. Requantizing the
 // result is the fp32 path of the quantizer.
 //
-// A thread takes the same 8 consecutive columns of two adjacent rows
+// A thread takes the same 8 consecutive columns of four adjacent rows
 // (K % 64 == 0, so they never straddle rows): every A value it unpacks feeds
-// two FMAs. The adapter operands arrive transposed (A^T [r,K], B^T [N,r]) so
+// four FMAs, and A^T is read once per four rows. The adapter operands arrive transposed (A^T [r,K], B^T [N,r]) so
 // that every load is a contiguous 16-byte vector: per 8 terms one load of
 // B^T[n][j..j+7] per row and eight loads of A^T[j][k..k+7].
 #include "device.h"
 
 namespace qlora {
 namespace {
+
+constexpr int kRows = 4;  // rows per thread: each unpacked A value feeds kRows FMAs
 
 template <bool kNf4Base>
 __global__ __launch_bounds__(256) void merge_kernel(const uint8_t* __restrict__ codes,
@@ -35,69 +37,89 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint8_t* __restrict__ 
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t kg = K / 8;
-  if (t >= (N + 1) / 2 * kg) return;
-  const int64_t n0 = 2 * (t / kg), k0 = 8 * (t % kg);
-  const bool two = n0 + 1 < N;  // the second row exists
-  const int64_t n1 = two ? n0 + 1 : n0;
+  if (t >= (N + kRows - 1) / kRows * kg) return;
+  const int64_t n0 = kRows * (t / kg), k0 = 8 * (t % kg);
+  int64_t nr[kRows];  // rows past N repeat the last row (computed, not stored)
+#pragma unroll
+  for (int rr = 0; rr < kRows; ++rr) nr[rr] = n0 + rr < N ? n0 + rr : N - 1;
 
-  float base[2][8];
+  // The base's raw words are loaded now and decoded after the adapter sum,
+  // so only they (not 8 floats per row) stay live across the sum.
+  uint32_t braw[kRows][4];
+  float bch[kRows];
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int64_t e0 = (rr ? n1 : n0) * K + k0;
+  for (int rr = 0; rr < kRows; ++rr) {
+    const int64_t e0 = nr[rr] * K + k0;
     if (kNf4Base) {
-      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + e0 / 2);
+      braw[rr][0] = *reinterpret_cast<const uint32_t*>(codes + e0 / 2);
       const int64_t b = e0 / 64;
-      const float ch = q8_value(q8[b], cb.dq_format) * s2[b >> 8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        base[rr][i] = bf16_lo(pack_bf16x2(lv[(cw >> (4 * i)) & 15u] * ch, 0.0f));
+      bch[rr] = q8_value(q8[b], cb.dq_format) * s2[b >> 8];
     } else {
       const u32x4_t w = *reinterpret_cast<const u32x4_t*>(wb + e0);
-      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        base[rr][2 * i] = bf16_lo(wv[i]);
-        base[rr][2 * i + 1] = bf16_hi(wv[i]);
-      }
+      braw[rr][0] = w.x;
+      braw[rr][1] = w.y;
+      braw[rr][2] = w.z;
+      braw[rr][3] = w.w;
+      bch[rr] = 0.0f;
     }
   }
 
-  float d[2][8];
+  float d[kRows][8];
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr)
+  for (int rr = 0; rr < kRows; ++rr)
 #pragma unroll
     for (int i = 0; i < 8; ++i) d[rr][i] = 0.0f;
   for (int j0 = 0; j0 < r; j0 += 8) {
-    const u32x4_t bq0 = *reinterpret_cast<const u32x4_t*>(Bt + n0 * r + j0);
-    const u32x4_t bq1 = *reinterpret_cast<const u32x4_t*>(Bt + n1 * r + j0);
-    const uint32_t bw[2][4] = {{bq0.x, bq0.y, bq0.z, bq0.w}, {bq1.x, bq1.y, bq1.z, bq1.w}};
+    uint32_t bw[kRows][4];
+#pragma unroll
+    for (int rr = 0; rr < kRows; ++rr) {
+      const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(Bt + nr[rr] * r + j0);
+      bw[rr][0] = bq.x;
+      bw[rr][1] = bq.y;
+      bw[rr][2] = bq.z;
+      bw[rr][3] = bq.w;
+    }
     u32x4_t a[8];
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj)
       a[jj] = *reinterpret_cast<const u32x4_t*>(At + (int64_t)(j0 + jj) * K + k0);
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const float b0 = (jj & 1) ? bf16_hi(bw[0][jj >> 1]) : bf16_lo(bw[0][jj >> 1]);
-      const float b1 = (jj & 1) ? bf16_hi(bw[1][jj >> 1]) : bf16_lo(bw[1][jj >> 1]);
+      float bj[kRows];
+#pragma unroll
+      for (int rr = 0; rr < kRows; ++rr)
+        bj[rr] = (jj & 1) ? bf16_hi(bw[rr][jj >> 1]) : bf16_lo(bw[rr][jj >> 1]);
       const uint32_t av[4] = {a[jj].x, a[jj].y, a[jj].z, a[jj].w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float ai = (i & 1) ? bf16_hi(av[i >> 1]) : bf16_lo(av[i >> 1]);
-        d[0][i] = __builtin_fmaf(ai, b0, d[0][i]);
-        d[1][i] = __builtin_fmaf(ai, b1, d[1][i]);
+#pragma unroll
+        for (int rr = 0; rr < kRows; ++rr) d[rr][i] = __builtin_fmaf(ai, bj[rr], d[rr][i]);
       }
     }
   }
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    if (rr == 1 && !two) break;
+  for (int rr = 0; rr < kRows; ++rr) {
+    if (n0 + rr >= N) break;
+    float base[8];
+    if (kNf4Base) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        base[i] = bf16_lo(pack_bf16x2(lv[(braw[rr][0] >> (4 * i)) & 15u] * bch[rr], 0.0f));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        base[2 * i] = bf16_lo(braw[rr][i]);
+        base[2 * i + 1] = bf16_hi(braw[rr][i]);
+      }
+    }
     float o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float tv = s * d[rr][i];
-      o[i] = base[rr][i] + tv;
+      o[i] = base[i] + tv;
     }
-    float* dst = out + (rr ? n1 : n0) * K + k0;
+    float* dst = out + (n0 + rr) * K + k0;
     *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{o[0], o[1], o[2], o[3]};
     *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
   }
@@ -109,7 +131,7 @@ hipError_t launch_merge(const uint8_t* codes, const int8_t* q8, const float* s2,
                         const uint16_t* W, int64_t N, int64_t K, const uint16_t* At,
                         const uint16_t* Bt, int r, float s, float* out, const Codebook& cb,
                         hipStream_t st) {
-  const int64_t threads = (N + 1) / 2 * (K / 8);
+  const int64_t threads = (N + kRows - 1) / kRows * (K / 8);
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (W)
     hipLaunchKernelGGL(merge_kernel<false>, grid, dim3(256), 0, st, codes, q8, s2, W, N, K, At,
