@@ -56,11 +56,20 @@ __device__ __forceinline__ u32x4_t load8(const uint16_t* __restrict__ a, int64_t
 }
 
 // grid: (ceil(M/16), ceil(r/64), slices). part[slice][m][j].
+// X is the large operand (read once from HBM): on the fast path each wave
+// loads its 16 rows x 256 t with every instruction covering 2 rows x 512
+// bytes (whole cache lines), stages them in LDS with a 528-byte row stride
+// (the 16 lanes of each phase of a fragment read then hit 16 distinct bank
+// groups) and reads the MFMA fragments back from there. P is small and
+// stays in L2; its fragments load directly.
+constexpr int kDownLd = 264;  // staged X row stride in bf16 (528 bytes)
+
 __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restrict__ X,
                                                         const uint16_t* __restrict__ P, int64_t M,
                                                         int64_t T, int r,
                                                         float* __restrict__ part) {
-  __shared__ float red[4][16][65];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[4][16 * kDownLd];
+  float(*red)[16][65] = reinterpret_cast<float(*)[16][65]>(&xs[0][0]);  // reused after the MFMAs
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
   const int j0 = blockIdx.y * 64;
@@ -78,16 +87,29 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
     // the matrix and the steps past this wave's range (or rows past M) are
     // zeroed, which adds +0 to the same accumulation order.
     constexpr int kSteps = kDownTC / 4 / 32;
-    const bool rok = m0 + c < M;
-    const int64_t xrow = rok ? m0 + c : M - 1;
+    {
+      // Staging: instruction q loads rows 2q, 2q+1 of the wave's tile; lane
+      // L takes 8 t at tw0 + 8*(L%32) of row 2q + L/32. Past T: zero.
+      const int half = lane >> 5, ch = lane & 31;
+      const int64_t t = tw0 + 8 * ch;
+      const bool tok = t < tw1;
+      const int64_t tc = tok ? t : T - 8;
+      u32x4_t xv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t row = min(m0 + 2 * q + half, M - 1);
+        xv[q] = *reinterpret_cast<const u32x4_t*>(X + row * T + tc);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        *reinterpret_cast<u32x4_t*>(&xs[w][(2 * q + half) * kDownLd + 8 * ch]) =
+            tok ? xv[q] : zero4();
+    }
+    // the wave reads back only what it wrote: no barrier, LDS keeps its order
     u32x4_t av[kSteps];
 #pragma unroll
-    for (int it = 0; it < kSteps; ++it) {
-      const int64_t t = tw0 + 32 * it;
-      const int64_t tc = t + 32 <= T ? t : T - 32;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(X + xrow * T + tc + 8 * g);
-      av[it] = (rok && t < tw1) ? v : zero4();
-    }
+    for (int it = 0; it < kSteps; ++it)
+      av[it] = *reinterpret_cast<const u32x4_t*>(&xs[w][c * kDownLd + 32 * it + 8 * g]);
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
       if (jt < ntile) {
@@ -116,6 +138,7 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
       }
     }
   }
+  __syncthreads();  // every wave is done with its staged X before red reuses it
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
