@@ -49,8 +49,8 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # scaled by the counters' reading for a copy of known size. Valid while the
 # kernel source hashes to `src_sha256` (None: not measured for this source).
 TRAFFIC = {"kernel": "gemm_nt_kernel", "call": "gemm_nt_up", "src": "gemm_nt.hip",
-           "src_sha256": "3c0fe832a03b17b3cf633c63aa8e6e2351261033b928bff342dd6ec54b53da2a",
-           "fetch_bytes": 591427680,   # 288783 KiB x 2.000 (copy reference)
+           "src_sha256": "bd18272f248079780132020c565b3573d3670bae25308ad6f52d9974951eea0f",
+           "fetch_bytes": 591146944,   # 288646 KiB x 2.000 (copy reference)
            "write_bytes": 180355072}   # 176128 KiB x 1.000 (copy reference)
 
 

@@ -16,9 +16,11 @@
 //    the scaled adapter product, so the extension adds s*u B exactly as the
 //    split represents it). 256 x 256 output tiles, four waves of 128 x 128
 //    on v_mfma_f32_32x32x16_bf16; both operand tiles arrive by direct-to-LDS
-//    loads (global_load_lds_dwordx4) in a four-deep ring of 32-wide K steps;
-//    the fragments of the next substep are read while the MFMAs of the
-//    current one run, so the one barrier per step never waits on LDS.
+//    loads (buffer_load_dwordx4 ... lds): a in a three-slot ring of 64-wide
+//    pairs of K steps (whole 128-byte lines of a row-major a per load), b in
+//    a four-deep ring of 32-wide steps; the fragments of the next substep are
+//    read while the MFMAs of the current one run, so the one barrier per
+//    step never waits on LDS.
 //    Workgroups are mapped to tiles so that each XCD works on a compact block
 //    of tiles (shared operand panels stay in that XCD's L2).
 #include "device.h"
@@ -82,27 +84,40 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
 
-template <int S>
-__device__ __forceinline__ uint16_t* pick4(uint16_t* s0, uint16_t* s1, uint16_t* s2, uint16_t* s3) {
-  if constexpr (S == 0) return s0;
-  else if constexpr (S == 1) return s1;
-  else if constexpr (S == 2) return s2;
-  else return s3;
+template <int S, int N, typename T>
+__device__ __forceinline__ T* pick(T* const (&arr)[N]) {
+  static_assert(S >= 0 && S < N, "stage index");
+  return arr[S];
 }
 
-// Operand tile layout in LDS (per stage: the a tile, then the b tile): tile
-// row r (0..255) holds 32 bf16 = 64 bytes; its 16-byte chunk c sits at slot
-// c ^ ((r >> 2) & 3). A fragment read (32 rows, one chunk each, 16 lanes per
-// LDS cycle) then touches 16 distinct 16-byte bank groups.
-// Direct-to-LDS load q (0..15) of an operand tile covers tile rows
-// 16q .. 16q+15: lane L writes LDS bytes [16L, 16L+16) of that 1 KB window,
-// i.e. row 16q + L/4, slot L%4, so it reads global chunk (L%4) ^ ((row>>2)&3).
+// LDS rings (160 KB in all):
+//  - a: three slots of a 256 x 64 tile (two 32-wide K steps, a "pair"), rows
+//    of 128 bytes; 16-byte chunk c (0..7: step half c/4, then 8 k each) of
+//    row r sits at position c ^ ((r >> 1) & 7). A direct-to-LDS load of 8
+//    rows x 128 bytes fills 1 KB with whole cache lines of a row-major a; a
+//    fragment read (16 rows per LDS phase, one chunk each) touches 16
+//    distinct 16-byte bank groups. Pair p lives in slot p % 3 and is loaded
+//    during steps 2p-4 and 2p-3 (four loads per wave in each).
+//  - b: four stages of a 256 x 32 tile, rows of 64 bytes, chunk c (0..3) of
+//    row r at c ^ ((r >> 2) & 3); step kb lives in stage kb % 4 and is
+//    loaded during step kb-3. A load covers 16 rows x 64 bytes: 1 KB of
+//    consecutive bytes in the K-slab layout, 16 half lines in row-major.
+// Every load of a step lands by the end of the next step (wait for all but
+// the step's own eight), and the barrier then publishes it; what a load
+// overwrites was last read before the previous barrier.
+constexpr int kNtPair = kNtBM * 2 * kNtBK;  // bf16 elements of one a pair slot (32 KB)
+
 template <bool kOutBf16>
 __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * kNtOp];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * kNtOp];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * kNtOp];
-  __shared__ __attribute__((aligned(1024))) uint16_t st3[2 * kNtOp];
+  __shared__ __attribute__((aligned(1024))) uint16_t sa0[kNtPair];
+  __shared__ __attribute__((aligned(1024))) uint16_t sa1[kNtPair];
+  __shared__ __attribute__((aligned(1024))) uint16_t sa2[kNtPair];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb0[kNtOp];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb1[kNtOp];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb2[kNtOp];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb3[kNtOp];
+  uint16_t* const sa[3] = {sa0, sa1, sa2};
+  uint16_t* const sb[4] = {sb0, sb1, sb2, sb3};
   const int tid = threadIdx.x, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = w >> 1, wn = w & 1;
@@ -111,51 +126,65 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
   const int64_t M = p.M, N = p.N;
   const int64_t m0 = (int64_t)tm * kNtBM, n0 = (int64_t)tn * kNtBN;
   const int nsteps = (int)(p.Kr / kNtBK);
+  const int npairs = (nsteps + 1) / 2;
 
-  // Direct-to-LDS role: wave w loads windows 4w .. 4w+3 of both tiles through
-  // buffer resources based at the tile's first row: the per-lane byte offset
-  // is fixed, the step's offset (64 bytes per step) is a scalar. Rows past
-  // the matrix read its last row (their results are never stored).
-  uint32_t aoff[4], boff[4];
+  // Direct-to-LDS roles. a: wave w loads rows 64w + 8q + L/8 (q = 0..7) of
+  // each pair, lane L at LDS position L%8 (global chunk (L%8) ^ ((row>>1)&7));
+  // the pair's scalar offset is 128 bytes per pair. The a resource ends at
+  // the last element of the matrix, so the missing half of a final odd pair
+  // reads zeros. b: wave w loads windows 4w .. 4w+3 (16 rows each) of each
+  // step, as before. Rows past the matrix read its last row (their results
+  // are never stored).
+  uint32_t aoff[8], boff[4];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = 64 * w + 8 * q + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    const int64_t ar = m0 + row < M ? row : M - 1 - m0;
+    aoff[q] = (uint32_t)(ar * p.lda * 2 + 16 * c);
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 16 * (4 * w + j) + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);
-    const int64_t ar = m0 + row < M ? row : M - 1 - m0;
     const int64_t br = n0 + row < N ? row : N - 1 - n0;
-    aoff[j] = (uint32_t)(ar * p.lda * 2 + 16 * c);
     boff[j] = (uint32_t)(br * (p.b_kslab ? 64 : p.ldb * 2) + 16 * c);
   }
+  // Bytes from the tile's first row to the matrix's last element; a tile's
+  // own offsets stay below 2^31 (gemm_nt_supported), so clamping a longer
+  // range only matters for tiles that are not the last and read in bounds.
+  const int64_t a_bytes = min(((M - 1 - m0) * p.lda + p.Kr) * 2, (int64_t)0x7FFFFFFF);
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(p.a + m0 * p.lda), (short)0, (int)0x7FFFFFFF, 0x00020000);
+      (void*)uniform_ptr(p.a + m0 * p.lda), (short)0, (int)a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)uniform_ptr(p.b + n0 * (p.b_kslab ? 32 : p.ldb)), (short)0, (int)0x7FFFFFFF,
       0x00020000);
   const int bstep = p.b_kslab ? (int)(64 * N) : 64;  // bytes from one step to the next
-  const int win = 4 * w * 512;  // element offset of this wave's first window
   typedef __attribute__((address_space(3))) void lds_void;
-  auto dma = [&](int j, int kb, uint16_t* stage) {
-    const int ks = kb < nsteps ? kb : nsteps - 1;
-    if (j < 4)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_void*)(stage + win + 512 * j), 16, aoff[j],
-                                               64 * ks, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (lds_void*)(stage + kNtOp + win + 512 * (j - 4)),
-                                               16, boff[j - 4], bstep * ks, 0, 0);
+  auto dma_a = [&](int q, int pair, uint16_t* slot) {
+    const int ps = pair < npairs ? pair : npairs - 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_void*)(slot + (64 * w + 8 * q) * 64), 16,
+                                             aoff[q], 128 * ps, 0, 0);
   };
-  auto issue = [&](int kb, uint16_t* stage) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dma(j, kb, stage);
+  auto dma_b = [&](int j, int kb, uint16_t* stage) {
+    const int ks = kb < nsteps ? kb : nsteps - 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (lds_void*)(stage + 512 * (4 * w + j)), 16,
+                                             boff[j], bstep * ks, 0, 0);
   };
 
-  // Fragment reads: A fragment (mt, substep s): tile row 128wm + 32mt + i,
-  // chunk 2s + h; B fragment (nt, s): tile row 128wn + 32nt + i. Bits 2..3 of
-  // the row are those of i, so the slot is (2s + h) ^ ((i >> 2) & 3).
-  const int sw = (i >> 2) & 3;
-  const int fa0 = (128 * wm + i) * 32 + 8 * (h ^ sw);
-  const int fa1 = (128 * wm + i) * 32 + 8 * ((2 + h) ^ sw);
-  const int fb0 = kNtOp + (128 * wn + i) * 32 + 8 * (h ^ sw);
-  const int fb1 = kNtOp + (128 * wn + i) * 32 + 8 * ((2 + h) ^ sw);
+  // Fragment reads: A fragment (mt, step half par, substep s): tile row
+  // 128wm + 32mt + i, chunk 4par + 2s + h, at position chunk ^ ((i >> 1) & 7)
+  // (bits 1..3 of the row are those of i). B fragment (nt, s): tile row
+  // 128wn + 32nt + i, chunk 2s + h at (2s + h) ^ ((i >> 2) & 3).
+  const int swa = (i >> 1) & 7, swb = (i >> 2) & 3;
+  int fa[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+      fa[par][ss] = (128 * wm + i) * 64 + 8 * ((4 * par + 2 * ss + h) ^ swa);
+  const int fb0 = (128 * wn + i) * 32 + 8 * (h ^ swb);
+  const int fb1 = (128 * wn + i) * 32 + 8 * ((2 + h) ^ swb);
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -194,30 +223,46 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
   ext_load(0, e0, f0);
   ext_load(1, e1, f1);  // r2 >= 32: groups 0 and 1 always exist
 
-  // Prologue: steps 0, 1, 2 in flight; wait for 0 and 1; fragments (0, 0).
-  issue(0, st0);
-  issue(1, st1);
-  issue(2, st2);
-  wait_vmem_lgkm0<8>();
+  // Prologue: pair 0, steps 0 and 1 of b, pair 1, step 2 of b; wait for the
+  // first three (all that steps 0 and 1 read before the first barrier of the
+  // loop); fragments of step 0, substep 0.
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_a(q, 0, sa0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma_b(j, 0, sb0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma_b(j, 1, sb1);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_a(q, 1, sa1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma_b(j, 2, sb2);
+  wait_vmem_lgkm0<12>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   u32x4_t a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    a0[t] = *reinterpret_cast<const u32x4_t*>(&st0[fa0 + 1024 * t]);
-    b0[t] = *reinterpret_cast<const u32x4_t*>(&st0[fb0 + 1024 * t]);
+    a0[t] = *reinterpret_cast<const u32x4_t*>(&sa0[fa[0][0] + 2048 * t]);
+    b0[t] = *reinterpret_cast<const u32x4_t*>(&sb0[fb0 + 1024 * t]);
   }
 
-  // One step on stage S: loads for step kb+3 go to stage S+3 (read last in
-  // the previous step, before its barrier), one after every fourth MFMA.
-  // Substep 0 computes on (a0, b0) while (kb, 1) is read into (a1, b1);
-  // substep 1 computes on (a1, b1) while (kb+1, 0) is read from stage S+1
-  // (complete since the previous barrier).
-  auto step = [&](int kb, auto sc) {
-    constexpr int S = decltype(sc)::value;
-    uint16_t* const cur = pick4<S>(st0, st1, st2, st3);
-    uint16_t* const nxt = pick4<(S + 1) & 3>(st0, st1, st2, st3);
-    uint16_t* const ld = pick4<(S + 3) & 3>(st0, st1, st2, st3);
+  // One step kb (B stage kb % 4 = SB, A slot (kb / 2) % 3 = SA, half PAR):
+  // substep 0 computes on (a0, b0) while (kb, 1) is read into (a1, b1);
+  // substep 1 computes on (a1, b1) while (kb+1, 0) is read into (a0, b0)
+  // (complete since the previous barrier). One load after every fourth
+  // MFMA: b of step kb+3 in substep 0, four a loads of pair kb/2 + 2 in
+  // substep 1.
+  auto step = [&](int kb, auto sbc, auto sac, auto parc) {
+    constexpr int SB = decltype(sbc)::value, SA = decltype(sac)::value;
+    constexpr int PAR = decltype(parc)::value;
+    constexpr int SA1 = PAR ? (SA + 1) % 3 : SA;  // slot of step kb+1
+    constexpr int PAR1 = PAR ^ 1;
+    uint16_t* const acur = pick<SA>(sa);
+    uint16_t* const anxt = pick<SA1>(sa);
+    uint16_t* const ald = pick<(SA + 2) % 3>(sa);
+    uint16_t* const bcur = pick<SB>(sb);
+    uint16_t* const bnxt = pick<(SB + 1) % 4>(sb);
+    uint16_t* const bld = pick<(SB + 3) % 4>(sb);
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       const int mt = g >> 2, nt = g & 3;
@@ -226,13 +271,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
       if (g < 8) {
         const int t = g >> 1;
         if (g & 1)
-          b1[t] = *reinterpret_cast<const u32x4_t*>(&cur[fb1 + 1024 * t]);
+          b1[t] = *reinterpret_cast<const u32x4_t*>(&bcur[fb1 + 1024 * t]);
         else
-          a1[t] = *reinterpret_cast<const u32x4_t*>(&cur[fa1 + 1024 * t]);
+          a1[t] = *reinterpret_cast<const u32x4_t*>(&acur[fa[PAR][1] + 2048 * t]);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       if ((g & 3) == 3) {
-        dma(g >> 2, kb + 3, ld);
+        dma_b(g >> 2, kb + 3, bld);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     }
@@ -245,33 +290,55 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
       if (g < 8) {
         const int t = g >> 1;
         if (g & 1)
-          b0[t] = *reinterpret_cast<const u32x4_t*>(&nxt[fb0 + 1024 * t]);
+          b0[t] = *reinterpret_cast<const u32x4_t*>(&bnxt[fb0 + 1024 * t]);
         else
-          a0[t] = *reinterpret_cast<const u32x4_t*>(&nxt[fa0 + 1024 * t]);
+          a0[t] = *reinterpret_cast<const u32x4_t*>(&anxt[fa[PAR1][0] + 2048 * t]);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       if ((g & 3) == 3) {
-        dma(4 + (g >> 2), kb + 3, ld);
+        dma_a(4 * PAR + (g >> 2), kb / 2 + 2, ald);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Loads of step kb+2 complete (kb+3 may still fly), this wave's LDS reads
-    // done; then every wave's stage kb+2 is visible and stage S is free.
+    // This step's eight loads may still fly; everything earlier has landed,
+    // this wave's LDS reads are done; then every wave's loads are visible
+    // and the stage and slot read last before this barrier are free.
     wait_vmem_lgkm0<8>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // Twelve steps bring both rings back to their first stage and slot.
   int kb = 0;
-  for (; kb + 4 <= nsteps; kb += 4) {
-    step(kb, std::integral_constant<int, 0>());
-    step(kb + 1, std::integral_constant<int, 1>());
-    step(kb + 2, std::integral_constant<int, 2>());
-    step(kb + 3, std::integral_constant<int, 3>());
+  for (; kb + 12 <= nsteps; kb += 12) {
+    step(kb + 0, I0(), I0(), I0());
+    step(kb + 1, I1(), I0(), I1());
+    step(kb + 2, I2(), I1(), I0());
+    step(kb + 3, I3(), I1(), I1());
+    step(kb + 4, I0(), I2(), I0());
+    step(kb + 5, I1(), I2(), I1());
+    step(kb + 6, I2(), I0(), I0());
+    step(kb + 7, I3(), I0(), I1());
+    step(kb + 8, I0(), I1(), I0());
+    step(kb + 9, I1(), I1(), I1());
+    step(kb + 10, I2(), I2(), I0());
+    step(kb + 11, I3(), I2(), I1());
   }
-  if (kb < nsteps) step(kb, std::integral_constant<int, 0>());
-  if (kb + 1 < nsteps) step(kb + 1, std::integral_constant<int, 1>());
-  if (kb + 2 < nsteps) step(kb + 2, std::integral_constant<int, 2>());
+  if (kb + 0 < nsteps) step(kb + 0, I0(), I0(), I0());
+  if (kb + 1 < nsteps) step(kb + 1, I1(), I0(), I1());
+  if (kb + 2 < nsteps) step(kb + 2, I2(), I1(), I0());
+  if (kb + 3 < nsteps) step(kb + 3, I3(), I1(), I1());
+  if (kb + 4 < nsteps) step(kb + 4, I0(), I2(), I0());
+  if (kb + 5 < nsteps) step(kb + 5, I1(), I2(), I1());
+  if (kb + 6 < nsteps) step(kb + 6, I2(), I0(), I0());
+  if (kb + 7 < nsteps) step(kb + 7, I3(), I0(), I1());
+  if (kb + 8 < nsteps) step(kb + 8, I0(), I1(), I0());
+  if (kb + 9 < nsteps) step(kb + 9, I1(), I1(), I1());
+  if (kb + 10 < nsteps) step(kb + 10, I2(), I2(), I0());
   // Direct-to-LDS loads still in flight must land before the workgroup ends.
   wait_vmem_lgkm0<0>();
 
