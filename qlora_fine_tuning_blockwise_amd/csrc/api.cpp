@@ -267,9 +267,13 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
     uint16_t* Bt = at<uint16_t>(workspace, L.Bt);
     uint16_t* ulr = at<uint16_t>(workspace, L.ulr);
     e = launch_transpose_bf16(A, K, r, At, st);  // A^T [r,K]
-    if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
-    if (e == hipSuccess)
-      e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, u, ulr, nullptr, st);
+    if (e == hipSuccess && lora_down_full_ok(M, K, r)) {
+      e = launch_lora_down_full(x, At, M, K, r, s, u, ulr, nullptr, st);
+    } else {
+      if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
+      if (e == hipSuccess)
+        e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, u, ulr, nullptr, st);
+    }
     if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
     if (e == hipSuccess && L.plain) {
       uint16_t* W = at<uint16_t>(workspace, L.W);
@@ -326,10 +330,14 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
   hipError_t e = hipSuccess;
   // v = dY B^T (B [r,N] is already contiguous along N); the finalize writes
   // the split of s*v both row-major (dX tiles) and transposed (dA).
-  e = launch_lora_down_parts(dY, B, M, N, r, down, st);
-  if (e == hipSuccess)
-    e = launch_lora_down_finalize(down, lora_down_slices(N), M, r, s, v, svlr, dA ? vT : nullptr,
-                                  st);
+  if (lora_down_full_ok(M, N, r)) {
+    e = launch_lora_down_full(dY, B, M, N, r, s, v, svlr, dA ? vT : nullptr, st);
+  } else {
+    e = launch_lora_down_parts(dY, B, M, N, r, down, st);
+    if (e == hipSuccess)
+      e = launch_lora_down_finalize(down, lora_down_slices(N), M, r, s, v, svlr,
+                                    dA ? vT : nullptr, st);
+  }
   if (e == hipSuccess && dX && L.plain) {  // dX = dY w_hat through w_hat^T [K,N]
     uint16_t* Wt = at<uint16_t>(workspace, L.Wt);
     e = launch_dequant_t(codes, absmax_q, absmax_scale, N, K, Wt, true, cb, st);  // K-slab
@@ -354,10 +362,14 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
     } else if (need_u) {
       uint16_t* At = at<uint16_t>(workspace, L.At);
       e = launch_transpose_bf16(A, K, r, At, st);
-      if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
-      if (e == hipSuccess)
-        e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, nullptr, nullptr, uT,
-                                      st);
+      if (e == hipSuccess && lora_down_full_ok(M, K, r)) {
+        e = launch_lora_down_full(x, At, M, K, r, s, nullptr, nullptr, uT, st);
+      } else {
+        if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
+        if (e == hipSuccess)
+          e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, nullptr, nullptr, uT,
+                                        st);
+      }
     } else {
       e = launch_lora_down_finalize(u_saved, 1, M, r, s, nullptr, nullptr, uT, st);
     }

@@ -55,6 +55,12 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
 int lora_down_slices(int64_t T);
 hipError_t launch_lora_down_parts(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
                                   int r, float* part, hipStream_t st);
+// lora_down and lora_down_finalize in one pass, for large M (see
+// lora_down_full_ok): out, lr, lrT as lora_down_finalize writes them.
+bool lora_down_full_ok(int64_t M, int64_t T, int r);
+hipError_t launch_lora_down_full(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
+                                 int r, float s, float* out, uint16_t* lr, uint16_t* lrT,
+                                 hipStream_t st);
 hipError_t launch_lora_down_finalize(const float* part, int slices, int64_t M, int r, float s,
                                      float* out, uint16_t* lr, uint16_t* lrT, hipStream_t st);
 
