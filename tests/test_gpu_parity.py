@@ -7,6 +7,7 @@ element error <= 1e-2 x RMS of the oracle output, for y, dX, dA, dB.
 import concurrent.futures as cf
 import ctypes
 import os
+import types
 
 import numpy as np
 import pytest
@@ -343,6 +344,77 @@ def test_fwd_deterministic(M):
     assert torch.equal(a, b)
 
 
+# hipStreamPerThread, a second stream beside torch's current one.
+PER_THREAD_STREAM = types.SimpleNamespace(cuda_stream=2)
+
+
+def run_fwd_other_stream(P, x, **kw):
+    torch.cuda.synchronize()
+    y = q.qlora_linear_fwd(P.w, dev_bf16(x), P.At, P.Bt, P.alpha, stream=PER_THREAD_STREAM, **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("M,N,K,r", [(1, 72, 64, 16), (3, 330, 192, 32), (16, 100, 320, 16),
+                                     (7, 1000, 1600, 64), (2, 40, 4096, 144),
+                                     # four waves per tile (>= 512 tiles), ragged rows
+                                     (16, 8200, 512, 16), (3, 8200, 256, 80)])
+def test_fwd_decode_ragged(M, N, K, r):
+    """Decode (M <= 16): ragged rows, chunks and adapter column groups against
+    the oracle; a call on another stream gives the same bits."""
+    say("fwd decode ragged", M, N, K, r)
+    P = Problem(N, K, r, 24.0, seed=N + K + r)
+    x = syn.normal_bf16((M, K), 1.0, 11 + M)
+    u1 = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    y1 = run_fwd(P, x, u_out=u1)
+    yo, uo = oracle.linear_fwd(x, P.What, P.A, P.B, r, 24.0)
+    tol_check(host(y1), yo, f"y decode {M}x{N}x{K} r{r}")
+    tol_check(host(u1), uo, f"u decode {M}x{N}x{K} r{r}")
+    u2 = torch.empty_like(u1)
+    y2 = run_fwd_other_stream(P, x, u_out=u2)
+    assert torch.equal(y1, y2), "y differs between streams"
+    assert torch.equal(u1, u2), "u differs between streams"
+    yb = run_fwd(P, x, y_dtype=torch.bfloat16)
+    assert torch.equal(yb, y1.to(torch.bfloat16))
+
+
+def test_fwd_decode_repeat_streams_and_graph():
+    """Back-to-back decode calls on one stream, calls on two streams and the
+    replays of a captured call (eager work in between) each match a separate
+    call on another stream for their input, bit for bit."""
+    N, K, r, M, alpha = 4100, 1024, 32, 4, 32.0
+    P = Problem(N, K, r, alpha, seed=21)
+    xs = [syn.normal_bf16((M, K), 1.0, 300 + t) for t in range(3)]
+    ref = [run_fwd_other_stream(P, x) for x in xs]
+    xd = [dev_bf16(x) for x in xs]
+    torch.cuda.synchronize()
+    ys = [q.qlora_linear_fwd(P.w, xv, P.At, P.Bt, alpha) for xv in xd]  # no sync in between
+    torch.cuda.synchronize()
+    for t in range(3):
+        assert torch.equal(ys[t], ref[t]), f"back-to-back call {t}"
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        ya = q.qlora_linear_fwd(P.w, xd[0], P.At, P.Bt, alpha)
+    with torch.cuda.stream(s2):
+        yb = q.qlora_linear_fwd(P.w, xd[1], P.At, P.Bt, alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, ref[0]) and torch.equal(yb, ref[1]), "two streams"
+    xin = xd[0].clone()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        yg = q.qlora_linear_fwd(P.w, xin, P.At, P.Bt, alpha)
+    for rep in range(6):
+        t = rep % 3
+        xin.copy_(xd[t])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ref[t]), f"graph replay {rep}"
+        ye = q.qlora_linear_fwd(P.w, xd[(t + 1) % 3], P.At, P.Bt, alpha)
+        torch.cuda.synchronize()
+        assert torch.equal(ye, ref[(t + 1) % 3]), f"eager call after replay {rep}"
+
+
 @pytest.mark.parametrize("M,N,K,r,pad", [(300, 520, 96, 16, 0), (513, 256, 64, 32, 24),
                                          (256, 256, 32, 16, 0), (40, 1030, 320, 64, 8)])
 def test_gemm_bf16_nt_dense_stage(M, N, K, r, pad):
@@ -418,6 +490,23 @@ def test_bwd_full_small(M, N, K, r):
     dXb, dAb, dBb = run_bwd(P, x, dY, dx_dtype=torch.bfloat16, grad_dtype=torch.bfloat16)
     assert torch.equal(dXb, dX.to(torch.bfloat16))
     assert torch.equal(dAb, dA.to(torch.bfloat16)) and torch.equal(dBb, dB.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("M,N,K,r", [(5, 520, 1024, 32), (16, 300, 4096, 16)])
+def test_bwd_decode_recomputed_u_matches_saved(M, N, K, r):
+    """At decode sizes the backward recomputes u with the forward's down
+    projection and slice sum: the same bits as the u the forward returns, so
+    dA and dB agree exactly with u_saved given or not."""
+    P = Problem(N, K, r, 24.0, seed=M + N)
+    x = syn.normal_bf16((M, K), 1.0, 40 + M)
+    dY = syn.normal_bf16((M, N), 1.0, 41 + M)
+    u = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    run_fwd(P, x, u_out=u)
+    _, dA1, dB1 = run_bwd(P, x, dY, u_saved=u, want_dx=False)
+    _, dA2, dB2 = run_bwd(P, x, dY, want_dx=False)
+    assert torch.equal(dA1, dA2) and torch.equal(dB1, dB2)
+    go = oracle.linear_bwd(x, dY, P.What, P.A, P.B, r, 24.0, ("dA", "dB"))
+    tol_check(host(dB2), go["dB"], "dB decode")
 
 
 def test_bwd_linear_1024_f32_weight():
