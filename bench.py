@@ -8,12 +8,16 @@ two Llama-7B-shaped weights (q 4096x4096 and up 11008x4096, bf16 ~N(0,0.02)):
   3. decode forward (GEMV path) at M = 1, 4 and 16 tokens, each weight,
   4. training forward at M = 4096 tokens (batch 4 x seq 1024), each weight,
   5. backward dX, dA, dB at M = 4096, each weight (dY ~ N(0,1)),
-with LoRA r = 16, alpha = 32, A ~ N(0, 1/K), B ~ N(0, 0.01).
+with LoRA r = 16, alpha = 32, A ~ N(0, 1/K), B ~ N(0, 0.01). The layer
+outputs y and the input gradients dX are written in bf16, the compute dtype
+of the activations (products accumulate in fp32); dA and dB in fp32. The
+same up-weight forward writing an fp32 y is timed beside the step.
 `value` is the step's multiply-add work (2 flops per MAC; dequantization and
 quantization count no flops) over the host-clock time of exactly K steps
 bracketed by device synchronisation, inputs resident in HBM. Per-call
 durations (the breakdown) come from HIP events around each call on the stream
-the library launches on; their sum is reported as ms_per_step_device_calls. The roofline entry is the dominant kernel: the bf16 MFMA GEMM of
+the library launches on; their sum is reported as ms_per_step_device_calls.
+The roofline entry is the dominant kernel: the bf16 MFMA GEMM of
 the training forward on the 11008x4096 weight (gemm_nt_kernel, the longest
 single dispatch of the step), launched alone through qlora_gemm_bf16_nt on the
 same operands (x, the dequantized weight, the rank-r extension) and timed by
@@ -48,10 +52,15 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # bf16, y fp32, from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
 # scaled by the counters' reading for a copy of known size. Valid while the
 # kernel source hashes to `src_sha256` (None: not measured for this source).
+# Layer outputs y and input gradients dX are produced in bf16, the compute
+# dtype of the activations; products accumulate in fp32 either way.
+ACT_DTYPE_NAME = "bfloat16"
+
 TRAFFIC = {"kernel": "gemm_nt_kernel", "call": "gemm_nt_up", "src": "gemm_nt.hip",
+           "y_dtype": "torch.bfloat16",
            "src_sha256": "bd18272f248079780132020c565b3573d3670bae25308ad6f52d9974951eea0f",
-           "fetch_bytes": 591146944,   # 288646 KiB x 2.000 (copy reference)
-           "write_bytes": 180355072}   # 176128 KiB x 1.000 (copy reference)
+           "fetch_bytes": 591671954,   # 288929 KiB x 2.000 (copy reference)
+           "write_bytes": 90177536}    # 88064 KiB x 1.000 (copy reference)
 
 
 def log(*a):
@@ -121,6 +130,8 @@ def main():
     import qlora_fine_tuning_blockwise_amd as q
     from qlora_fine_tuning_blockwise_amd import synthetic as syn
 
+    ACT_DTYPE = getattr(torch, ACT_DTYPE_NAME)
+
     q._lib.load()  # fail loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -151,8 +162,8 @@ def main():
     for name in names:
         N, K = cfg["weights"][name]
         out[name] = dict(
-            ydec={M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Mdec},
-            y=torch.empty((Mt, N), dtype=torch.float32, device=dev),
+            ydec={M: torch.empty((M, N), dtype=ACT_DTYPE, device=dev) for M in Mdec},
+            y=torch.empty((Mt, N), dtype=ACT_DTYPE, device=dev),
             u=torch.empty((Mt, r), dtype=torch.float32, device=dev))
 
     # ------------------------------------------------------------ flops per call
@@ -193,7 +204,7 @@ def main():
         calls.append((f"bwd_train_{name}",
                       lambda w=w, o=o, name=name: q.qlora_linear_bwd(
                           w, x_train, dY[name], A[name], B[name], alpha, u_saved=o["u"],
-                          workspace=ws),
+                          dx_dtype=ACT_DTYPE, workspace=ws),
                       bwd_flops(Mt, N, K), 0))
     step_flops = sum(c[2] for c in calls)
 
@@ -203,7 +214,7 @@ def main():
     w_up_slab = q.qlora_dequant_bf16(nf4["up"], layout=q.LAYOUT_KSLAB32)
     e_up = syn.torch_normal_bf16((Mt, 2 * r), 0.01, syn.seed_of(3, 50), dev)
     f_up = B["up"].t().contiguous()
-    y_up = torch.empty((Mt, Nu), dtype=torch.float32, device=dev)
+    y_up = torch.empty((Mt, Nu), dtype=ACT_DTYPE, device=dev)
     roof = ("gemm_nt_up",
             lambda: q.qlora_gemm_bf16_nt(x_train, w_up_slab, e_up, f_up, y=y_up,
                                          b_layout=q.LAYOUT_KSLAB32),
@@ -287,8 +298,26 @@ def main():
     dms = e0.elapsed_time(e1) / args.steps
     achieved = dflops / (dms * 1e-3) / 1e12
     traffic = None
-    if TRAFFIC["src_sha256"] and TRAFFIC["src_sha256"] == kernel_src_sha(TRAFFIC["src"]):
+    if (TRAFFIC["src_sha256"] and TRAFFIC["src_sha256"] == kernel_src_sha(TRAFFIC["src"])
+            and TRAFFIC["y_dtype"] == str(ACT_DTYPE)):
         traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+    # The forward on the up weight with an fp32 y, beside the bf16-y step.
+    o_up = out["up"]
+    y_f32 = torch.empty((Mt, Nu), dtype=torch.float32, device=dev)
+    f32fn = lambda: q.qlora_linear_fwd(nf4["up"], x_train, A["up"], B["up"], alpha, y=y_f32,
+                                       u_out=o_up["u"], workspace=ws)
+    for _ in range(args.warmup):
+        f32fn()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        f32fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    f32ms = e0.elapsed_time(e1) / args.steps
+    breakdown["fwd_train_up_y_f32"] = {
+        "ms": round(f32ms, 5), "tflops": round(fwd_flops(Mt, Nu, Ku) / (f32ms * 1e-3) / 1e12, 2),
+        "note": "outside the step: the same forward writing y in fp32"}
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": TRAFFIC["kernel"], "kernel_call": roof[0],
@@ -301,7 +330,8 @@ def main():
         "ms_per_step_device_calls": round(ms_step_dev, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "llama7b_nf4_layer_pair: q 4096x4096 + up 11008x4096 bf16 "
-                               "N(0,0.02) -> NF4+DQ; decode M=1,4,16; train M=4096 fwd+bwd",
+                               "N(0,0.02) -> NF4+DQ; decode M=1,4,16; train M=4096 fwd+bwd; "
+                               "y and dX bf16 (fp32 accumulation), dA and dB fp32",
                    "weights": {n: list(cfg["weights"][n]) for n in names},
                    "M_decode": list(Mdec), "M_train": Mt, "r": r, "alpha": alpha},
         "roofline": roofline, "breakdown": breakdown,
