@@ -324,13 +324,19 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 // w_hat^T: out[k][n] = bf16(L[code(n,k)] * c1_hat(n, k/64)), c1_hat =
 // fp32(q8 * s2) (the same roundings as the row-major dequantization).
-// Workgroup tile: 128 weight rows x 128 columns (32 KB of LDS, so four
-// workgroups share a CU). Lane p of wave w owns rows n0 + 2p, n0 + 2p + 1 and
-// columns [32w, 32w + 32) of the tile; it packs the pair (row 2p, row 2p+1)
-// of each column into one dword of the transposed LDS tile (row k: 64 dwords,
-// so a wave's 64 stores of one k hit 64 consecutive dwords), then the
-// workgroup writes 256-byte rows of out.
-constexpr int kDtCols = 128;  // tile columns (k)
+// Workgroup tile: 64 weight rows x 256 columns. Thread t owns the row pair
+// (n0 + 2p, n0 + 2p + 1), p = t / 8, and the 32 columns [32c, 32c + 32),
+// c = t % 8, of the tile, so eight consecutive lanes read a row's 128 bytes
+// of codes (whole cache lines). It packs the pair of each column into one
+// dword of the transposed LDS tile: row k holds the 32 pair dwords, dword p
+// at position p ^ (8 ((k / 32) % 4)), which puts the 64 lanes of a write
+// (fixed column offset, eight c and eight p) on 32 distinct banks and keeps
+// every aligned group of four dwords together. The workgroup then writes
+// out: in the K-slab layout [N/32][K][32] a wave store covers 16 consecutive
+// k rows of one slab, 1 KB of consecutive bytes; row-major, a wave store
+// covers 8 k rows x 128 bytes.
+constexpr int kDtRows = 64;    // tile rows (n)
+constexpr int kDtCols = 256;   // tile columns (k)
 
 template <bool kKSlab>
 __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
@@ -338,13 +344,14 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
                                                         const float* __restrict__ s2, int64_t N,
                                                         int64_t K, uint16_t* __restrict__ out,
                                                         Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint32_t tile[kDtCols * 64];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[kDtCols * 32];
   __shared__ float levels[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * 128, k0 = (int64_t)blockIdx.y * kDtCols;
+  const int64_t n0 = (int64_t)blockIdx.x * kDtRows, k0 = (int64_t)blockIdx.y * kDtCols;
   const int64_t KB = K / 64;
-  const int64_t na = n0 + 2 * lane, nb = na + 1;
-  const int64_t kk = k0 + 32 * w;
+  const int p = tid >> 3, c = tid & 7;
+  const int64_t na = n0 + 2 * p, nb = na + 1;
+  const int64_t kk = k0 + 32 * c;
   u32x4_t ca = zero4(), cbv = zero4();
   float cha = 0.0f, chb = 0.0f;
   if (kk < K) {
@@ -363,30 +370,46 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
   {
     const uint32_t wa[4] = {ca.x, ca.y, ca.z, ca.w};
     const uint32_t wb[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
+    uint32_t* trow = tile + (32 * c) * 32 + (p ^ (8 * (c & 3)));
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float va = levels[(wa[d] >> (4 * s)) & 15u] * cha;
-        const float vb = levels[(wb[d] >> (4 * s)) & 15u] * chb;
-        tile[(32 * w + 8 * d + s) * 64 + lane] = pack_bf16x2(va, vb);
+      for (int e = 0; e < 8; ++e) {
+        const float va = levels[(wa[d] >> (4 * e)) & 15u] * cha;
+        const float vb = levels[(wb[d] >> (4 * e)) & 15u] * chb;
+        trow[(8 * d + e) * 32] = pack_bf16x2(va, vb);
       }
   }
   __syncthreads();
-  // kDtCols rows x 256 bytes: 16 lanes per row, 16 rows per pass.
-  const int col = tid & 15, rsub = tid >> 4;
-  const int64_t nc = n0 + 8 * col;
+  if (kKSlab) {
+    // Wave w: slab w % 2 of the tile (32 rows, pair dwords 16s .. 16s+15),
+    // columns [128 (w / 2), +128), 16 per store; lane: column l / 4, 16-byte
+    // piece l % 4 of the slab row.
+    const int sl = w & 1, pc = lane & 3;
+    const int64_t slab = n0 / 32 + sl;
+    if (32 * slab >= N) return;  // N % 32 == 0: whole slabs only
 #pragma unroll
-  for (int pass = 0; pass < kDtCols / 16; ++pass) {
-    const int kr = 16 * pass + rsub;
-    const int64_t k = k0 + kr;
-    if (k >= K) break;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&tile[kr * 64 + 4 * col]);
-    if (kKSlab) {  // N % 32 == 0: the 8 columns sit in slab nc / 32
-      if (nc < N)
-        *reinterpret_cast<u32x4_t*>(out + ((nc >> 5) * K + k) * 32 + (nc & 31)) = v;
-      continue;
+    for (int it = 0; it < 8; ++it) {
+      const int kl = 128 * (w >> 1) + 16 * it + (lane >> 2);
+      const int64_t k = k0 + kl;
+      if (k >= K) break;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+          &tile[kl * 32 + ((16 * sl + 4 * pc) ^ (8 * ((kl >> 5) & 3)))]);
+      *reinterpret_cast<u32x4_t*>(out + (slab * K + k) * 32 + 8 * pc) = v;
     }
+    return;
+  }
+  // Row-major: wave w writes columns [64w, 64w + 64) of the tile, 8 per
+  // store; lane: column l / 8, eight weight rows 8 (l % 8) .. +7.
+  const int pc = lane & 7;
+  const int64_t nc = n0 + 8 * pc;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int kl = 64 * w + 8 * it + (lane >> 3);
+    const int64_t k = k0 + kl;
+    if (k >= K) break;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+        &tile[kl * 32 + ((4 * pc) ^ (8 * ((kl >> 5) & 3)))]);
     uint16_t* dst = out + k * N + nc;
     if (nc + 8 <= N && (N & 7) == 0) {
       *reinterpret_cast<u32x4_t*>(dst) = v;
@@ -438,7 +461,7 @@ hipError_t launch_dequant(const uint8_t* codes, const int8_t* q8, const float* s
 hipError_t launch_dequant_t(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t N,
                             int64_t K, uint16_t* out, bool kslab, const Codebook& cb,
                             hipStream_t st) {
-  const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((K + kDtCols - 1) / kDtCols));
+  const dim3 grid((unsigned)((N + kDtRows - 1) / kDtRows), (unsigned)((K + kDtCols - 1) / kDtCols));
   if (kslab) {
     if (N % 32) return hipErrorInvalidValue;
     hipLaunchKernelGGL(dequant_t_kernel<true>, grid, dim3(256), 0, st, codes, q8, s2, N, K, out, cb);
