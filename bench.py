@@ -25,7 +25,10 @@ HIP events around back-to-back launches; `traffic` is that kernel's HBM bytes pe
 launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters scaled by the same
 counters' reading for a copy of known size, and null when the kernel source no
 longer matches the one the counters were taken on. The CPU baseline times the
-oracle on a bounded sample of the same workload.
+oracle on a bounded sample of the same workload. Extra sections (skipped
+with --no-extras): the decode GEMV on a ring of distinct weights, bulk
+quantize/dequant throughput, merge + requantize, the AdamW step, and the
+70B-shaped layer (seven projections, M = 2048, r = 64) forward + backward.
 
 Counter helpers: `--only CALL` runs one call of the step (e.g. fwd_train_up)
 or the roofline launch (gemm_nt_up) for the timed iterations and prints its
@@ -346,6 +349,8 @@ def main():
         result["merge"] = merge_section(q, syn, torch, dev, cfg, nf4, W, A, B, r, alpha)
         log("adamw step on the adapter arena")
         result["adamw"] = adamw_section(q, syn, torch, dev)
+        log("70B-shaped layer fwd + bwd")
+        result["layer_70b"] = layer_70b(q, syn, torch, dev, ACT_DTYPE)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(np, syn, cfg, step_flops, ms_step_host)
@@ -441,6 +446,64 @@ def adamw_section(q, syn, torch, dev, iters=10):
     del P, M, V
     run("pinned_host", Ph, Mh, Vh)
     return res
+
+
+def layer_70b(q, syn, torch, dev, act_dtype, iters=5):
+    """The 70B-shaped decoder layer: all seven projections (q, o 8192x8192;
+    k, v 1024x8192; gate, up 28672x8192; down 8192x28672) quantized to NF4 +
+    DQ from bf16 N(0, 0.015), then forward and backward (dX, dA, dB) of each
+    at M = 2048 tokens, LoRA r = 64, alpha = 16, y and dX in the activations'
+    bf16. Timed by HIP events around `iters` passes over the seven
+    projections (after one warmup pass)."""
+    cfg = syn.LAYER_70B
+    M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
+    names = list(cfg["weights"])
+    ws_bytes = max(max(q.qlora_workspace_bytes(op, M, N, K, r) for op in (0, 1))
+                   for N, K in cfg["weights"].values())
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    layer = {}
+    for t, name in enumerate(names):
+        N, K = cfg["weights"][name]
+        Wb = syn.torch_normal_bf16((N, K), cfg["w_std"], syn.seed_of(4, t), dev)
+        w = q.qlora_quantize_nf4_dq(Wb)
+        del Wb
+        layer[name] = dict(
+            w=w, A=syn.torch_normal_bf16((K, r), 1.0 / K ** 0.5, syn.seed_of(4, 10 + t), dev),
+            B=syn.torch_normal_bf16((r, N), 0.01, syn.seed_of(4, 20 + t), dev),
+            x=syn.torch_normal_bf16((M, K), 1.0, syn.seed_of(4, 30 + t), dev),
+            dY=syn.torch_normal_bf16((M, N), 1.0, syn.seed_of(4, 40 + t), dev),
+            y=torch.empty((M, N), dtype=act_dtype, device=dev),
+            u=torch.empty((M, r), dtype=torch.float32, device=dev))
+    flops = 0
+    for name in names:
+        N, K = cfg["weights"][name]
+        flops += 2 * M * N * K + 2 * M * r * (K + N)  # forward
+        flops += 2 * M * N * K + 2 * M * r * (N + K) + 2 * M * K * r + 2 * M * N * r  # backward
+
+    def one_pass():
+        for name in names:
+            L = layer[name]
+            q.qlora_linear_fwd(L["w"], L["x"], L["A"], L["B"], alpha, y=L["y"], u_out=L["u"],
+                               workspace=ws)
+            q.qlora_linear_bwd(L["w"], L["x"], L["dY"], L["A"], L["B"], alpha, u_saved=L["u"],
+                               dx_dtype=act_dtype, workspace=ws)
+
+    one_pass()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        one_pass()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    tf = flops / (ms * 1e-3) / 1e12
+    del layer, ws
+    torch.cuda.empty_cache()
+    return {"projections": {n: list(cfg["weights"][n]) for n in names}, "M": M, "r": r,
+            "alpha": alpha, "ms_fwd_bwd": round(ms, 4), "tflops": round(tf, 2),
+            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "tokens_per_s": round(M / (ms * 1e-3), 1)}
 
 
 def gemv_ring(q, syn, torch, dev, r, alpha):
