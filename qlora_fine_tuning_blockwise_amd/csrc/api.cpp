@@ -266,7 +266,7 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
     float* u = u_out ? u_out : at<float>(workspace, L.u);
     uint16_t* Bt = at<uint16_t>(workspace, L.Bt);
     uint16_t* ulr = at<uint16_t>(workspace, L.ulr);
-    e = launch_transpose_bf16(A, K, r, At, st);  // A^T [r,K]
+    e = launch_transpose2_bf16(A, K, r, At, B, r, N, Bt, st);  // A^T [r,K], B^T [N,r]
     if (e == hipSuccess && lora_down_full_ok(M, K, r)) {
       e = launch_lora_down_full(x, At, M, K, r, s, u, ulr, nullptr, st);
     } else {
@@ -274,7 +274,6 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
       if (e == hipSuccess)
         e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, u, ulr, nullptr, st);
     }
-    if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
     if (e == hipSuccess && L.plain) {
       uint16_t* W = at<uint16_t>(workspace, L.W);
       e = launch_dequant(codes, absmax_q, absmax_scale, N * K, W, N, cb, st);  // K-slab
@@ -417,8 +416,7 @@ int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint16_t* At = at<uint16_t>(workspace, L.At);
   uint16_t* Bt = at<uint16_t>(workspace, L.Bt);
-  hipError_t e = launch_transpose_bf16(A, K, r, At, st);      // A^T [r,K]
-  if (e == hipSuccess) e = launch_transpose_bf16(B, r, N, Bt, st);  // B^T [N,r]
+  hipError_t e = launch_transpose2_bf16(A, K, r, At, B, r, N, Bt, st);  // A^T [r,K], B^T [N,r]
   if (e == hipSuccess)
     e = launch_merge(W ? nullptr : codes, absmax_q, absmax_scale, W, N, K, At, Bt, r,
                      alpha / (float)r, merged, cb, st);

@@ -41,9 +41,13 @@ hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes
 hipError_t launch_dequant(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t n,
                           uint16_t* out, int64_t rows, const Codebook& cb, hipStream_t st);
 
-// out[c][r'] = in[r'][c] for a bf16 [rows, cols] matrix.
+// out[c][r'] = in[r'][c] for a bf16 [rows, cols] matrix; the second form
+// transposes two matrices in one launch (in1 may be NULL).
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
                                  hipStream_t st);
+hipError_t launch_transpose2_bf16(const uint16_t* in0, int64_t rows0, int64_t cols0,
+                                  uint16_t* out0, const uint16_t* in1, int64_t rows1,
+                                  int64_t cols1, uint16_t* out1, hipStream_t st);
 
 // Rank-r down projection out[m][j] = sum_t X[m][t] * P[j][t] (X [M,T] bf16,
 // P [r,T] bf16, fp32 result) in t-slices: launch_lora_down_parts writes

@@ -20,22 +20,34 @@ namespace qlora {
 namespace {
 
 // ----------------------------------------------------------------- transpose
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ in,
-                                                        int64_t rows, int64_t cols,
-                                                        uint16_t* __restrict__ out) {
+// out[c][r'] = in[r'][c] for up to two bf16 matrices in one launch: the 1-D
+// grid holds the 32 x 32 tiles of the first matrix, then those of the second.
+struct TransposeJob {
+  const uint16_t* in;
+  uint16_t* out;
+  int64_t rows, cols;
+  unsigned tiles_c, tiles;  // tiles per tile row, tiles in all
+};
+
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeJob j0, TransposeJob j1) {
   __shared__ uint16_t tile[32][33];
+  const unsigned b = blockIdx.x;
+  const bool second = b >= j0.tiles;
+  const TransposeJob& j = second ? j1 : j0;
+  const unsigned t = second ? b - j0.tiles : b;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  const int64_t r0 = (int64_t)blockIdx.y * 32, c0 = (int64_t)blockIdx.x * 32;
+  const int64_t r0 = (int64_t)(t / j.tiles_c) * 32, c0 = (int64_t)(t % j.tiles_c) * 32;
+  const int64_t rows = j.rows, cols = j.cols;
 #pragma unroll
   for (int i = 0; i < 32; i += 8) {
     const int64_t rr = r0 + ty + i, cc = c0 + tx;
-    tile[ty + i][tx] = (rr < rows && cc < cols) ? in[rr * cols + cc] : (uint16_t)0;
+    tile[ty + i][tx] = (rr < rows && cc < cols) ? j.in[rr * cols + cc] : (uint16_t)0;
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 32; i += 8) {
     const int64_t cc = c0 + ty + i, rr = r0 + tx;
-    if (cc < cols && rr < rows) out[cc * rows + rr] = tile[tx][ty + i];
+    if (cc < cols && rr < rows) j.out[cc * rows + rr] = tile[tx][ty + i];
   }
 }
 
@@ -452,10 +464,26 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int
 
 }  // namespace
 
+namespace {
+TransposeJob transpose_job(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out) {
+  const unsigned tc = (unsigned)((cols + 31) / 32), tr = (unsigned)((rows + 31) / 32);
+  return TransposeJob{in, out, rows, cols, tc, in ? tc * tr : 0u};
+}
+}  // namespace
+
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
                                  hipStream_t st) {
-  const dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32));
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, st, in, rows, cols, out);
+  return launch_transpose2_bf16(in, rows, cols, out, nullptr, 0, 0, nullptr, st);
+}
+
+hipError_t launch_transpose2_bf16(const uint16_t* in0, int64_t rows0, int64_t cols0,
+                                  uint16_t* out0, const uint16_t* in1, int64_t rows1,
+                                  int64_t cols1, uint16_t* out1, hipStream_t st) {
+  const TransposeJob j0 = transpose_job(in0, rows0, cols0, out0);
+  const TransposeJob j1 = transpose_job(in1, rows1, cols1, out1);
+  const unsigned tiles = j0.tiles + j1.tiles;
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_kernel, dim3(tiles), dim3(256), 0, st, j0, j1);
   return hipGetLastError();
 }
 
