@@ -122,6 +122,15 @@ int qlora_nf4_sizes(int64_t N, int64_t K, size_t* codes_bytes, size_t* absmax_q_
  * ties to the lower code. */
 int qlora_codebook(float levels[16], float thresholds[15]);
 
+/* The same decisions for bf16 weights, stated on the weight and the block
+ * absmax directly (the quantizer's bf16 path uses these): thresholds_q[i] is
+ * thresholds[i] or its fp32 successor, such that for bf16 values w and c1
+ * with c1 in [2^-60, 2^60] and |w| <= c1 the exact comparison
+ * w > thresholds_q[i] * c1 holds exactly when RN(w / c1) > thresholds[i]
+ * (RN: fp32 division, round to nearest even). Host only; QLORA_ERR_INVALID_ARG
+ * for a NULL array. */
+int qlora_codebook_quotient_thresholds(float thresholds_q[15]);
+
 /* Identifier of the quantization setup (FNV-1a over the 16 level bit
  * patterns, the block and group sizes, the nibble order and the form of the
  * second level). [P4] "Operational coupling": the quantization setup belongs

@@ -17,7 +17,8 @@ import torch
 from . import _lib
 
 __all__ = [
-    "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_id", "qlora_setup_id",
+    "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_quotient_thresholds",
+    "qlora_codebook_id", "qlora_setup_id",
     "qlora_workspace_bytes", "qlora_quantize_nf4_dq", "qlora_dequant_bf16",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "qlora_merge_lora", "qlora_adamw_step",
     "NF4Weight", "DQ_INT8", "DQ_UINT8", "DQ_E4M3", "LAYOUT_ROWS", "LAYOUT_KSLAB32",
@@ -79,6 +80,13 @@ def qlora_codebook():
     _lib.check(_lib.load().qlora_codebook(lv.ctypes.data_as(ctypes.c_void_p),
                                           th.ctypes.data_as(ctypes.c_void_p)), "qlora_codebook")
     return lv, th
+
+
+def qlora_codebook_quotient_thresholds():
+    tq = np.zeros(15, np.float32)
+    _lib.check(_lib.load().qlora_codebook_quotient_thresholds(tq.ctypes.data_as(ctypes.c_void_p)),
+               "qlora_codebook_quotient_thresholds")
+    return tq
 
 
 def qlora_setup_id(dq_format: int) -> int:

@@ -36,6 +36,7 @@ SIGNATURES = {
     "qlora_strerror": (ctypes.c_char_p, [INT]),
     "qlora_nf4_sizes": (INT, [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
     "qlora_codebook": (INT, [P, P]),
+    "qlora_codebook_quotient_thresholds": (INT, [P]),
     "qlora_codebook_id": (ctypes.c_uint32, []),
     "qlora_workspace_bytes": (SZ, [INT, I64, I64, I64, INT]),
     "qlora_setup_id": (ctypes.c_uint32, [INT]),

@@ -186,6 +186,15 @@ int qlora_codebook(float levels[16], float thresholds[15]) {
   return QLORA_OK;
 }
 
+int qlora_codebook_quotient_thresholds(float thresholds_q[15]) {
+  const Codebook* cb = nullptr;
+  const int st = get_codebook(&cb, nullptr);
+  if (st != QLORA_OK) return st;
+  if (!thresholds_q) return QLORA_ERR_INVALID_ARG;
+  std::memcpy(thresholds_q, cb->thr_q, sizeof cb->thr_q);
+  return QLORA_OK;
+}
+
 uint32_t qlora_codebook_id(void) {
   uint32_t id = 0;
   return get_codebook(nullptr, &id) == QLORA_OK ? id : 0u;

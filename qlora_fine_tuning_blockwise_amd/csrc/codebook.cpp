@@ -67,6 +67,47 @@ uint32_t setup_hash(uint32_t level_hash, int dq_format) {
   return fnv1a(level_hash, meta, sizeof meta);
 }
 
+// Quotient threshold of decision threshold t (see Codebook::thr_q). A
+// quotient of two normal bf16 numbers is q = a 2^j / b with significands a, b
+// in [128, 255]. Every such q of t's sign within a factor of four of t is
+// compared, exactly in integers (values in units of 2^-61), against t and
+// against its fp32 successor s, and the result set against RN(q) > t, which
+// holds when q is above the midpoint of t and s, or on it with s even (ties
+// round to the even neighbour). The first candidate that agrees for every q
+// is taken; false if neither does.
+bool quotient_threshold(float t, float* out) {
+  if (!(std::fabs(t) >= 0x1p-20f && std::fabs(t) < 1.0f)) return false;
+  const float s = std::nextafter(t, INFINITY);
+  const int64_t T = (int64_t)std::ldexp((double)t, 61), S = (int64_t)std::ldexp((double)s, 61);
+  const int64_t mid = (T + S) / 2;  // T and S are even: t's last bit is 2^-43 or above
+  uint32_t sbits;
+  std::memcpy(&sbits, &s, 4);
+  const bool tie_up = (sbits & 1u) == 0;
+  const int sg = t < 0.0f ? -1 : 1;
+  int e;
+  std::frexp(std::fabs((double)t), &e);  // |t| in [2^(e-1), 2^e)
+  bool t_ok = true, s_ok = true;
+  for (int j = e - 3; j <= e + 1; ++j)
+    for (int a = 128; a < 256; ++a) {
+      const __int128 qs = (__int128)(sg * a) * ((__int128)1 << (j + 61));  // q * b * 2^61
+      for (int b = 128; b < 256; ++b) {
+        auto cmp = [&](int64_t X) {
+          const __int128 r = (__int128)X * b;
+          return (qs > r) - (qs < r);
+        };
+        const int cm = cmp(mid);
+        const bool above = cm > 0 || (cm == 0 && tie_up);
+        t_ok = t_ok && (cmp(T) > 0) == above;
+        s_ok = s_ok && (cmp(S) > 0) == above;
+      }
+    }
+  if (t_ok)
+    *out = t;
+  else if (s_ok)
+    *out = s;
+  return t_ok || s_ok;
+}
+
 struct State {
   Codebook cb{};
   uint32_t level_hash = 0;
@@ -101,13 +142,17 @@ State build() {
   }
   // Self-checks the quantize kernel relies on: strictly increasing levels,
   // interleaved thresholds, at most one threshold per 1/32-wide bucket of
-  // [-1,1], and no threshold within 2^-20 of a bucket edge.
+  // [-1,1], no threshold within 2^-20 of a bucket edge nor in the last 1/16
+  // of its bucket (the bf16 path's bucket index rounds to nearest and may
+  // move such values up one bucket), and a quotient threshold for each.
   bool ok = s.cb.level[0] == -1.0f && s.cb.level[7] == 0.0f && s.cb.level[15] == 1.0f;
   for (int i = 0; i < 15; ++i) {
     ok = ok && s.cb.level[i] < s.cb.thr[i] && s.cb.thr[i] < s.cb.level[i + 1];
     const double pos = ((double)s.cb.thr[i] + 1.0) * 32.0;
     ok = ok && std::fabs(pos - std::nearbyint(pos)) > 32.0 * std::ldexp(1.0, -20);
+    ok = ok && pos - std::floor(pos) < 15.0 / 16.0 - std::ldexp(1.0, -10);
     if (i > 0) ok = ok && std::floor(pos) != std::floor(((double)s.cb.thr[i - 1] + 1.0) * 32.0);
+    ok = ok && quotient_threshold(s.cb.thr[i], &s.cb.thr_q[i]);
   }
   if (!ok) return s;
   uint32_t h = 2166136261u;

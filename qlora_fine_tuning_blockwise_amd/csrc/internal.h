@@ -21,6 +21,10 @@ constexpr int kDqE4m3 = 2;   // s2 = c2/448, FP8 E4M3 value
 struct Codebook {
   float level[16];
   float thr[15];
+  // thr_q[i] is thr[i] or its fp32 successor, chosen so that for bf16 w and
+  // c1 (c1 in [2^-60, 2^60], |w| <= c1) the exact comparison w > thr_q[i]*c1
+  // agrees with RN(w/c1) > thr[i].
+  float thr_q[15];
   int dq_format;
 };
 

@@ -11,15 +11,23 @@
 // the wave), 8 lanes cover one block; the block absmax is reduced across those
 // 8 lanes with DPP moves. Codes come from a 65-bucket table in LDS: the bucket
 // of x in [-1,1] (width 1/32) holds at most one decision threshold, so one
-// compare finishes the search. The 8 codes of a thread are packed into one
-// dword and stored. After all 8 passes the 256 block constants are in LDS and
-// the workgroup writes their 8-bit codes and the group's fp32 scale.
+// compare finishes the search. For bf16 weights the compare is made on the
+// weight itself, w > t' c1 (the sign of one FMA), with the quotient threshold
+// t' of the codebook, so no quotient is formed. The 8 codes of a thread are
+// packed into one dword and stored. After all passes the 256 block constants
+// are in LDS and the workgroup writes their 8-bit codes and the group's fp32
+// scale.
 #include "device.h"
 
 namespace qlora {
 namespace {
 
 constexpr int kLut = 128;  // 65 live buckets, padded so a masked index stays in bounds
+constexpr int kQThreads = 256;                               // threads per group
+constexpr int kQPasses = kGroup * kBlock / (8 * kQThreads);  // passes per thread
+constexpr int kQBlocksPerPass = kQThreads / 8;
+static_assert(kQPasses >= 1 && kQPasses <= 8 && kQBlocksPerPass * kQPasses == kGroup, "");
+static_assert(kGroup == 4 * 64 && kQThreads >= kGroup && kQThreads >= 2 * kLut, "");
 
 // Max of a non-negative value over each aligned group of 8 lanes.
 __device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t v) {
@@ -72,11 +80,13 @@ __device__ __forceinline__ int e4m3_code(float x) {
 }
 
 template <bool kF32In>
-__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ W, int64_t nblocks,
-                                                       uint8_t* __restrict__ codes,
-                                                       int8_t* __restrict__ q8,
-                                                       float* __restrict__ s2, Codebook cb) {
+__global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restrict__ W,
+                                                             int64_t nblocks,
+                                                             uint8_t* __restrict__ codes,
+                                                             int8_t* __restrict__ q8,
+                                                             float* __restrict__ s2, Codebook cb) {
   __shared__ u32x2_t lut[kLut];
+  __shared__ u32x2_t lutq[kLut];  // entry j: bucket j - 1, quotient threshold
   __shared__ float c1s[kGroup];
   __shared__ float red[4];
   const int tid = threadIdx.x;
@@ -84,30 +94,39 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   const int64_t b0 = g * kGroup;
   const int nbg = (int)min((int64_t)kGroup, nblocks - b0);
 
-  if (tid < kLut) {
-    // bucket [lo, lo + 1/32); buckets past 64 repeat bucket 64
-    const float lo = -1.0f + (float)min(tid, 64) * 0.03125f;
-    const float hi = lo + 0.03125f;
-    uint32_t below = 0;
-    float inside = 2.0f;
+  if (tid < 2 * kLut) {
+    // bucket [lo, lo + 1/32); buckets past 64 repeat bucket 64. lutq is the
+    // same table shifted up one entry (entry 0 repeats bucket 0) and holding
+    // the quotient threshold in place of the threshold. Threads kLut.. build
+    // lutq, so each wave builds half a table.
+    auto entry = [&](int b, bool quotient) {
+      const float lo = -1.0f + (float)b * 0.03125f;
+      const float hi = lo + 0.03125f;
+      uint32_t below = 0;
+      float inside = 2.0f;
 #pragma unroll
-    for (int i = 0; i < 15; ++i) {
-      const float t = cb.thr[i];
-      below += (t < lo) ? 1u : 0u;
-      if (t >= lo && t < hi) inside = t;
-    }
-    lut[tid] = u32x2_t{__float_as_uint(inside), below};
+      for (int i = 0; i < 15; ++i) {
+        const float t = cb.thr[i];
+        below += (t < lo) ? 1u : 0u;
+        if (t >= lo && t < hi) inside = quotient ? cb.thr_q[i] : t;
+      }
+      return u32x2_t{__float_as_uint(inside), below};
+    };
+    if (tid < kLut)
+      lut[tid] = entry(min(tid, 64), false);
+    else
+      lutq[tid - kLut] = entry(min(max(tid - kLut - 1, 0), 64), true);
   }
 
-  // Issue every load of the group up front (8 passes x 8 weights).
+  // Issue every load of the group up front (kQPasses passes x 8 weights).
   // Blocks past the group's end (last group only) load the group's last
   // block instead: no branch around the loads, so each pass waits only for
   // its own. Their constants and codes are never stored.
   constexpr int kWords = kF32In ? 8 : 4;  // dwords per 8 weights
-  uint32_t raw[8][kWords];
+  uint32_t raw[kQPasses][kWords];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int bl = min(it * 32 + (tid >> 3), nbg - 1);
+  for (int it = 0; it < kQPasses; ++it) {
+    const int bl = min(it * kQBlocksPerPass + (tid >> 3), nbg - 1);
     const int64_t e0 = (b0 + bl) * kBlock + (tid & 7) * 8;
     if (kF32In) {
       const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(W) + e0);
@@ -125,13 +144,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
   __builtin_amdgcn_s_barrier();
 
-  // Block constants of all eight passes first: lane j of each 8-lane group
-  // then computes the correctly rounded reciprocal for pass j alone, and
-  // every pass fetches its reciprocal from that lane (one division per lane
-  // instead of one per pass).
-  float c1v[8];
+  // Block constants of all passes first: lane j < kQPasses of each 8-lane
+  // group then computes the correctly rounded reciprocal for pass j alone,
+  // and every pass fetches its reciprocal from that lane (one division per
+  // lane instead of one per pass).
+  float c1v[kQPasses];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
+  for (int it = 0; it < kQPasses; ++it) {
     uint32_t amax = 0;
     if (kF32In) {
 #pragma unroll
@@ -140,24 +159,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
       amax = absmax_bf16x8(*reinterpret_cast<const uint32_t(*)[4]>(&raw[it][0]));
     }
     c1v[it] = __uint_as_float(max_over_8_lanes(amax));
-    const int bl = it * 32 + (tid >> 3);
+    const int bl = it * kQBlocksPerPass + (tid >> 3);
     if (bl < nbg && (tid & 7) == 0) c1s[bl] = c1v[it];
   }
   float rc_mine = 1.0f;
   if (!kF32In) {
     float c1_mine = c1v[0];
 #pragma unroll
-    for (int it = 1; it < 8; ++it)
+    for (int it = 1; it < kQPasses; ++it)
       if ((tid & 7) == it) c1_mine = c1v[it];
     rc_mine = 1.0f / c1_mine;  // +inf for an all-zero block (unused)
   }
 
-  // This thread's code word of pass `it`: block it*32 + tid/8 of the group,
-  // word tid%8, i.e. dword tid + 256*it of the group's codes.
+  // This thread's code word of pass `it`: block it*kQBlocksPerPass + tid/8 of
+  // the group, word tid%8, i.e. dword tid + kQThreads*it of the group's codes.
   uint32_t* const cwp = reinterpret_cast<uint32_t*>(codes + b0 * (kBlock / 2)) + tid;
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int bl = it * 32 + (tid >> 3);
+  for (int it = 0; it < kQPasses; ++it) {
+    const int bl = it * kQBlocksPerPass + (tid >> 3);
     float w[8];
     if (kF32In) {
 #pragma unroll
@@ -176,37 +195,45 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     if (c1 == 0.0f) {
       word = 0x77777777u;  // all-zero block: every weight at the zero level
     } else if (!kF32In && c1 >= 0x1p-60f && c1 <= 0x1p60f) {
-      // w / c1 from a correctly rounded reciprocal and one residual
-      // correction (Markstein's division step): x0 = w*r, e = w - x0*c1
-      // (one FMA), x = x0 + e*r. Checked exhaustively over every bf16 pair
-      // with c1 in this range and |w| <= c1: x equals the IEEE quotient
-      // whenever |w/c1| >= 2^-10, and always yields the same NF4 code (the
-      // smaller quotients that can differ in low bits sit far below every
-      // threshold). r comes from lane it of this lane's group.
-      const float rc = __shfl(rc_mine, (tid & 56) | it);
+      // No quotient: the bucket comes from w * (256 r) + (2^23 + 264) in one
+      // FMA (r the correctly rounded 1/c1, from lane it of this lane's
+      // group); at that magnitude the fp32 ulp is 1, so the low mantissa bits
+      // hold round(256x + 264) and clearing the low three gives the byte
+      // offset 8 (bucket + 1) of lutq. Rounding to nearest instead of down
+      // can move x up one bucket from the last 1/16 of its bucket, where the
+      // codebook has no threshold, so the code is unchanged. The one compare
+      // is then w > t' c1 for the bucket's quotient threshold t': the sign of
+      // fma(-t', c1, w), exact. Checked exhaustively on the host over every
+      // bf16 pair with c1 in this range and |w| <= c1 against the code of the
+      // IEEE quotient.
+      const float rc256 = __shfl(rc_mine, (tid & 56) | it) * 256.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float x0 = w[j] * rc;
-        const float e = __builtin_fmaf(-x0, c1, w[j]);
-        const float x = __builtin_fmaf(e, rc, x0);
-        word |= nf4_code(x, lut) << (4 * j);
+        const float f = __builtin_fmaf(w[j], rc256, 8388872.0f);
+        const u32x2_t e = *reinterpret_cast<const u32x2_t*>(
+            reinterpret_cast<const char*>(lutq) + (__float_as_uint(f) & 0x3F8u));
+        const float d = __builtin_fmaf(-__uint_as_float(e.x), c1, w[j]);
+        word |= (e.y + (d > 0.0f ? 1u : 0u)) << (4 * j);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) word |= nf4_code(w[j] / c1, lut) << (4 * j);
     }
-    if (bl < nbg) cwp[256 * it] = word;
+    if (bl < nbg) cwp[kQThreads * it] = word;
   }
   __syncthreads();  // c1s complete
 
   // Second level: c2 = max c1 over the group, s2 = c2/top with top = 127,
   // 255 or 448 by format; q8 = the nearest integer of c1/s2 (ties to the
   // lower) clamped to [0, top], or its nearest E4M3 value (ties to even).
+  // The first kGroup threads (whole waves) hold one block constant each.
   const float c1 = tid < nbg ? c1s[tid] : 0.0f;
-  float m = c1;
+  if (tid < kGroup) {
+    float m = c1;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+  }
   __syncthreads();
   const float c2 = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int fmt = cb.dq_format;
@@ -430,11 +457,11 @@ hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes
   const int64_t ng = (nb + kGroup - 1) / kGroup;
   if (ng == 0) return hipSuccess;
   if (f32_in)
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)ng), dim3(256), 0, st, W, nb, codes,
-                       q8, s2, cb);
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)ng), dim3(kQThreads), 0, st, W, nb,
+                       codes, q8, s2, cb);
   else
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)ng), dim3(256), 0, st, W, nb, codes,
-                       q8, s2, cb);
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)ng), dim3(kQThreads), 0, st, W, nb,
+                       codes, q8, s2, cb);
   return hipGetLastError();
 }
 

@@ -13,6 +13,13 @@
  *    (x > the one threshold inside the bucket). check_buckets checks the
  *    offset against 8 floor(32x + 32) and the code against #{i : x > T[i]}
  *    for every fp32 x in [-1, 1].
+ * 3. Code from the weight (the bf16 path). The kernel forms no quotient:
+ *    with rc = RN(1/c1), f = RN(w * (256 rc) + 2^23 + 264) (one FMA) has ulp
+ *    1, so (bits(f) & 0x3F8) / 8 = round(256x + 264) / 8 rounded down is
+ *    bucket + 1, an entry of a table that holds each bucket's quotient
+ *    threshold t' and threshold count; code = count + (RN(w - t' c1) > 0)
+ *    (one FMA). check_quotient_codes compares that against the code of the
+ *    IEEE quotient for every bf16 pair with c1 in [2^-60, 2^60], |w| <= c1.
  * IEEE binary32 arithmetic, round to nearest even, no flush to zero; fmaf is
  * the fused multiply-add of the C library.
  */
@@ -86,6 +93,42 @@ int64_t check_buckets(const float thr[15], int64_t* checked) {
             for (int i = 0; i < 15; ++i) ref += x > thr[i];
             n++;
             if (code != ref) bad++;
+        }
+    }
+    *checked = n;
+    return bad;
+}
+
+int64_t check_quotient_codes(const float thr[15], const float thr_q[15], int64_t* checked) {
+    uint32_t lut_thr[128];
+    uint32_t lut_below[128];
+    for (int j = 0; j < 128; ++j) {
+        int b = j - 1 < 0 ? 0 : (j - 1 > 64 ? 64 : j - 1);
+        float lo = -1.0f + (float)b * 0.03125f, hi = lo + 0.03125f;
+        uint32_t below = 0;
+        float inside = 2.0f;
+        for (int i = 0; i < 15; ++i) {
+            below += thr[i] < lo;
+            if (thr[i] >= lo && thr[i] < hi) inside = thr_q[i];
+        }
+        lut_thr[j] = u_of(inside);
+        lut_below[j] = below;
+    }
+    int64_t bad = 0, n = 0;
+    for (uint32_t cb = 0; cb < 0x8000u; ++cb) {          /* positive bf16 c1 */
+        float c1 = f_of(cb << 16);
+        if (!(c1 >= 0x1p-60f && c1 <= 0x1p60f)) continue;
+        volatile float one = 1.0f;
+        float rc256 = (one / c1) * 256.0f;
+        for (uint32_t wb = 0; wb < 0x10000u; ++wb) {     /* every bf16 w */
+            float w = f_of(wb << 16);
+            if (!(fabsf(w) <= c1)) continue;
+            float f = fmaf(w, rc256, 8388872.0f);
+            uint32_t j = (u_of(f) & 0x3F8u) >> 3;
+            float d = fmaf(-f_of(lut_thr[j]), c1, w);
+            uint32_t code = lut_below[j] + (d > 0.0f ? 1u : 0u);
+            n++;
+            if (code != count_above(w / c1, thr)) bad++;
         }
     }
     *checked = n;

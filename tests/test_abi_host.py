@@ -206,6 +206,9 @@ def arith(tmp_path_factory):
                                  ctypes.POINTER(ctypes.c_int64)]
     L.check_buckets.restype = ctypes.c_int64
     L.check_buckets.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
+    L.check_quotient_codes.restype = ctypes.c_int64
+    L.check_quotient_codes.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_int64)]
     return L
 
 
@@ -224,6 +227,25 @@ def test_bucket_code_search_exhaustive(arith, lib):
     n = ctypes.c_int64()
     bad = arith.check_buckets(th.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n))
     assert n.value == 2 * (0x3F800000 + 1) and bad == 0
+
+
+def test_quotient_thresholds_are_threshold_or_successor(lib):
+    _, th = q.qlora_codebook()
+    tq = q.qlora_codebook_quotient_thresholds()
+    succ = np.nextafter(th, np.float32(np.inf))
+    assert np.all((tq == th) | (tq == succ))
+    assert lib.qlora_codebook_quotient_thresholds(None) == 1
+
+
+def test_quotient_code_path_exact_for_all_bf16_pairs(arith, lib):
+    _, th = q.qlora_codebook()
+    th = np.ascontiguousarray(th)
+    tq = np.ascontiguousarray(q.qlora_codebook_quotient_thresholds())
+    n = ctypes.c_int64()
+    bad = arith.check_quotient_codes(th.ctypes.data_as(ctypes.c_void_p),
+                                     tq.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n))
+    assert n.value > 4.9e8
+    assert bad == 0
 
 
 def test_adamw_validation(lib):

@@ -106,6 +106,36 @@ def test_quantize_edge_values_bit_exact():
     assert np.array_equal(deq, wb)
 
 
+def _near_threshold_rows():
+    """Blocks whose quotients w/c1 sit within 4 bf16 steps of every decision
+    threshold, for every 8-bit absmax significand at three scales and both
+    signs of the absmax element: the cases where the code decision is closest."""
+    _, thr = oracle.nf4_codebook()
+    rows = []
+    for e in (0, -40, 40):
+        for m in range(128):
+            c1_bits = np.uint16(((127 + e) << 7) | m)
+            c1 = float(oracle.bf16_to_f32(np.array([c1_bits], np.uint16))[0])
+            centre = syn.to_bf16_bits((thr.astype(np.float64) * c1).astype(np.float32))
+            cand = (centre.astype(np.int32)[:, None] + np.arange(-4, 5)[None, :]).ravel()
+            cand = cand.astype(np.uint16)
+            for sign in (0, 0x8000):
+                for k in range(0, cand.size, 63):
+                    part = cand[k:k + 63]
+                    row = np.zeros(64, np.uint16)
+                    row[0] = c1_bits | sign
+                    row[1:1 + part.size] = part
+                    rows.append(row)
+    return np.stack(rows)
+
+
+def test_quantize_near_threshold_quotients_bit_exact():
+    Wb = _near_threshold_rows()
+    say("quantize near-threshold quotients", Wb.shape)
+    w = quantize_gpu(dev_bf16(Wb))
+    assert_nf4_equal(w, *oracle.quantize_nf4_dq(Wb, "bf16"), "near-threshold quotients")
+
+
 def test_quantize_f32_linear_1024_bit_exact():
     cfg = syn.LINEAR_1024
     W = syn.normal_f32(cfg["weights"]["w"], cfg["w_std"], syn.seed_of(1, 0))
