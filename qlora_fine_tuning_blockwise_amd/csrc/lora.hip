@@ -171,16 +171,17 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
 }
 
 // Single-pass form for large M (enough 16-row tiles to fill the GPU) and
-// r <= 32: one 8-wave workgroup per 16 rows (and 32 columns of r) walks the
-// whole of T, wave w taking the 256-wide chunks w, w+8, .... Per chunk the
-// wave first loads its P fragments (clamped into P: past T the staged X is
-// zero, so they multiply zeros), then the next chunk's X (two rows x 512
-// bytes per instruction), then stages the current X through LDS and runs the
-// MFMAs, which wait for P only; the next chunk's X stays in flight. The
-// eight waves' sums are added in a fixed order in LDS and the workgroup
-// writes the outputs of lora_down_finalize (out, the row-major and
+// r = 16 kTiles <= 32: one 8-wave workgroup per 16 rows walks the whole of T,
+// wave w taking the 256-wide chunks w, w+8, .... Each iteration first issues
+// the next chunk's loads, its P fragments (clamped into P: past T the staged
+// X is zero, so they multiply zeros) and its X (two rows x 512 bytes per
+// instruction), then stages the current X through LDS and runs the MFMAs on
+// the current P fragments; both of the next chunk's operands stay in flight
+// meanwhile. The eight waves' sums are added in a fixed order in LDS and the
+// workgroup writes the outputs of lora_down_finalize (out, the row-major and
 // transposed two-term splits of s*out, zero rows of lrT for M <= m < Mp)
 // itself. Requires T % 32 == 0.
+template <int kTiles>
 __global__ __launch_bounds__(512) void lora_down_full_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ P, int64_t M, int64_t Mp,
     int64_t T, int r, float s, float* __restrict__ out, uint16_t* __restrict__ lr,
@@ -189,10 +190,10 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
   float(*red)[16][33] = reinterpret_cast<float(*)[16][33]>(&xs[0][0]);  // reused after the MFMAs
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int j0 = blockIdx.y * 32;
-  const int ntile = min(2, (r - j0) / 16);
+  constexpr int j0 = 0, ntile = kTiles;
   const int nchunks = (int)((T + 255) / 256);
   const int half = lane >> 5, ch = lane & 31;
+  constexpr int kSteps = 8;
 
   auto load_chunk = [&](int ck, u32x4_t (&xv)[8]) {  // clamped: always in bounds
     const int64_t t = (int64_t)min(ck, nchunks - 1) * 256 + 8 * ch;
@@ -203,18 +204,11 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
       xv[q] = *reinterpret_cast<const u32x4_t*>(X + row * T + tc);
     }
   };
-  f32x4_t acc[2];
+  auto load_p = [&](int ck, u32x4_t (&bv)[kTiles][kSteps]) {  // clamped: always in bounds
+    const int64_t tw0 = (int64_t)min(ck, nchunks - 1) * 256;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  constexpr int kSteps = 8;
-  u32x4_t xv[8];
-  load_chunk(w, xv);
-  for (int ck = w; ck < nchunks; ck += 8) {
-    const int64_t tw0 = (int64_t)ck * 256, tw1 = min(T, tw0 + 256);
-    u32x4_t bv[2][kSteps];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      const int64_t prow = min(j0 + 16 * jt + c, r - 1);
+    for (int jt = 0; jt < kTiles; ++jt) {
+      const int64_t prow = 16 * jt + c;
 #pragma unroll
       for (int it = 0; it < kSteps; ++it) {
         const int64_t t = tw0 + 32 * it;
@@ -222,8 +216,18 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
         bv[jt][it] = *reinterpret_cast<const u32x4_t*>(P + prow * T + tc + 8 * g);
       }
     }
-    u32x4_t xn[8];
-    load_chunk(ck + 8, xn);  // the next chunk's loads fly while this one is used
+  };
+  f32x4_t acc[kTiles];
+#pragma unroll
+  for (int i = 0; i < kTiles; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t xv[8], bv[kTiles][kSteps];
+  load_p(w, bv);
+  load_chunk(w, xv);
+  for (int ck = w; ck < nchunks; ck += 8) {
+    const int64_t tw0 = (int64_t)ck * 256, tw1 = min(T, tw0 + 256);
+    u32x4_t bn[kTiles][kSteps], xn[8];
+    load_p(ck + 8, bn);  // the next chunk's loads fly while this one is used
+    load_chunk(ck + 8, xn);
     const bool tok = tw0 + 8 * ch < tw1;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -234,17 +238,19 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
     for (int it = 0; it < kSteps; ++it)
       av[it] = *reinterpret_cast<const u32x4_t*>(&xs[w][c * kDownLd + 32 * it + 8 * g]);
 #pragma unroll
-    for (int it = 0; it < kSteps; ++it) acc[0] = mfma_16x16x32(av[it], bv[0][it], acc[0]);
-    if (ntile > 1) {
+    for (int jt = 0; jt < kTiles; ++jt)
 #pragma unroll
-      for (int it = 0; it < kSteps; ++it) acc[1] = mfma_16x16x32(av[it], bv[1][it], acc[1]);
-    }
+      for (int it = 0; it < kSteps; ++it) acc[jt] = mfma_16x16x32(av[it], bv[jt][it], acc[jt]);
 #pragma unroll
     for (int q = 0; q < 8; ++q) xv[q] = xn[q];
+#pragma unroll
+    for (int jt = 0; jt < kTiles; ++jt)
+#pragma unroll
+      for (int it = 0; it < kSteps; ++it) bv[jt][it] = bn[jt][it];
   }
   __syncthreads();  // every wave is done with its staged X before red reuses it
 #pragma unroll
-  for (int jt = 0; jt < 2; ++jt)
+  for (int jt = 0; jt < kTiles; ++jt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[w][4 * g + v][16 * jt + c] = acc[jt][v];
   __syncthreads();
@@ -507,16 +513,22 @@ hipError_t launch_lora_down_finalize(const float* part, int slices, int64_t M, i
 }
 
 bool lora_down_full_ok(int64_t M, int64_t T, int r) {
-  return M >= 2048 && T % 32 == 0 && r <= 32;
+  return M >= 2048 && T % 32 == 0 && (r == 16 || r == 32);
 }
 
 hipError_t launch_lora_down_full(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
                                  int r, float s, float* out, uint16_t* lr, uint16_t* lrT,
                                  hipStream_t st) {
   const int64_t Mp = (M + 7) & ~(int64_t)7;
-  const dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 31) / 32));
-  hipLaunchKernelGGL(lora_down_full_kernel, grid, dim3(512), 0, st, X, P, M, Mp, T, r, s, out, lr,
-                     lrT);
+  const dim3 grid((unsigned)((M + 15) / 16));
+  if (r == 16)
+    hipLaunchKernelGGL(lora_down_full_kernel<1>, grid, dim3(512), 0, st, X, P, M, Mp, T, r, s, out,
+                       lr, lrT);
+  else if (r == 32)
+    hipLaunchKernelGGL(lora_down_full_kernel<2>, grid, dim3(512), 0, st, X, P, M, Mp, T, r, s, out,
+                       lr, lrT);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
