@@ -88,7 +88,7 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   const size_t Mp = (size_t)((M + 7) & ~(int64_t)7);
   L.vT = c.take(2 * (size_t)r * Mp * 2);
   L.uT = c.take(2 * (size_t)r * Mp * 2);
-  L.col = c.take((size_t)colred_splits(M) * T * r * 4);
+  L.col = c.take((size_t)colred_splits(M) * (K + N) * r * 4);  // dA's partials, then dB's
   L.plain = bwd_plain(M, N, K);
   if (L.plain) L.Wt = c.take((size_t)K * N * 2);
   L.total = c.off;
@@ -356,12 +356,10 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
     e = launch_gemm_bwd(dY, codes, absmax_q, absmax_scale, svlr, A, M, N, K, r, dX,
                         dx_dtype == QLORA_DTYPE_BF16, cb, st);
   }
-  if (e == hipSuccess && dA) {  // dA = x^T (s v)
-    e = launch_colred(x, vT, M, K, r, col, st);
-    if (e == hipSuccess)
-      e = launch_colred_finalize(col, colred_splits(M), K, r, 1.0f, false, dA, gbf, st);
-  }
-  if (e == hipSuccess && dB) {  // dB = (s u)^T dY
+  // The split of s u first (it depends only on x, A or the saved u), so that
+  // both reductions over M, dA = x^T (s v) and dB = (s u)^T dY, run as one
+  // launch and one finalize.
+  if (e == hipSuccess && dB) {
     if (need_u && M <= kGemvMaxM) {
       e = launch_lora_down_decode(x, A, M, K, r, down, st);
       if (e == hipSuccess)
@@ -381,9 +379,16 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
     } else {
       e = launch_lora_down_finalize(u_saved, 1, M, r, s, nullptr, nullptr, uT, st);
     }
-    if (e == hipSuccess) e = launch_colred(dY, uT, M, N, r, col, st);
+  }
+  if (e == hipSuccess && (dA || dB)) {
+    // Partial sums: dA's [splits, K, r] at col, dB's [splits, N, r] after it.
+    float* colB = col + (size_t)colred_splits(M) * K * r;
+    e = launch_colred2(dA ? x : dY, dA ? vT : uT, dA ? K : N, dA ? col : colB,
+                       dA && dB ? dY : nullptr, uT, N, colB, M, r, st);
     if (e == hipSuccess)
-      e = launch_colred_finalize(col, colred_splits(M), N, r, 1.0f, true, dB, gbf, st);
+      e = launch_colred_finalize2(dA ? col : colB, dA ? K : N, !dA, dA ? dA : dB,
+                                  dA && dB ? colB : nullptr, N, true, dB, colred_splits(M), r,
+                                  1.0f, gbf, st);
   }
   return launch_status(e);
 }

@@ -145,6 +145,15 @@ hipError_t launch_colred(const uint16_t* X, const uint16_t* PT, int64_t M, int64
                          float* part, hipStream_t st);
 hipError_t launch_colred_finalize(const float* part, int splits, int64_t C, int r, float s,
                                   bool transpose_out, void* out, bool out_bf16, hipStream_t st);
+// The same for two reductions over the same M rows in one launch each (the
+// second job is skipped when X1 / part1 is NULL).
+hipError_t launch_colred2(const uint16_t* X0, const uint16_t* PT0, int64_t C0, float* part0,
+                          const uint16_t* X1, const uint16_t* PT1, int64_t C1, float* part1,
+                          int64_t M, int r, hipStream_t st);
+hipError_t launch_colred_finalize2(const float* part0, int64_t C0, bool transpose_out0,
+                                   void* out0, const float* part1, int64_t C1,
+                                   bool transpose_out1, void* out1, int splits, int r, float s,
+                                   bool out_bf16, hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace qlora

@@ -332,15 +332,28 @@ constexpr int kColLdP = 72;   // P tile row stride in bf16 (144 B)
 // element (row stride 132 B puts the four 8-row groups of a read in distinct
 // banks); the P operand is one 16-byte LDS read per lane.
 // grid: (ceil(C/64), slices, ceil(r/64)); wave w owns columns 16w..16w+15.
+// Two reductions over the same rows share a launch: workgroup columns
+// 0 .. j0.tiles-1 take job j0, the rest job j1 (tiles = 0: no second job).
+struct ColJob {
+  const uint16_t* X;
+  const uint16_t* PT;
+  int64_t C;
+  float* part;
+  unsigned tiles;  // 64-column tiles
+};
+
 template <bool kVec>
-__global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict__ X,
-                                                     const uint16_t* __restrict__ PT, int64_t M,
-                                                     int64_t Mp, int64_t C, int r,
-                                                     float* __restrict__ part) {
+__global__ __launch_bounds__(256) void colred_kernel(ColJob j0, ColJob j1, int64_t M, int64_t Mp,
+                                                     int r) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kColStep][kColLdX];
   __shared__ __attribute__((aligned(16))) uint16_t ps[2][64][kColLdP];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const bool second = blockIdx.x >= j0.tiles;
+  const uint16_t* __restrict__ X = second ? j1.X : j0.X;
+  const uint16_t* __restrict__ PT = second ? j1.PT : j0.PT;
+  const int64_t C = second ? j1.C : j0.C;
+  float* __restrict__ part = second ? j1.part : j0.part;
+  const int64_t c0 = (int64_t)(second ? blockIdx.x - j0.tiles : blockIdx.x) * 64;
   const int slice = blockIdx.y;
   const int jt0 = blockIdx.z * 4;
   const int ntile = min(4, r / 16 - jt0);
@@ -445,13 +458,26 @@ __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict_
   }
 }
 
-// out = s * sum_slice part[slice][c][j], as [C, r] or transposed [r, C].
+// out = s * sum_slice part[slice][c][j], as [C, r] or transposed [r, C];
+// workgroups 0 .. j0.blocks-1 take job j0, the rest job j1.
+struct FinJob {
+  const float* part;
+  int64_t C;
+  void* out;
+  bool transpose_out;
+  unsigned blocks;  // 256-element blocks
+};
+
 template <bool kBf16>
-__global__ __launch_bounds__(256) void colred_finalize_kernel(const float* __restrict__ part,
-                                                              int slices, int64_t C, int r,
-                                                              float s, bool transpose_out,
-                                                              void* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index in [C, r] order
+__global__ __launch_bounds__(256) void colred_finalize_kernel(FinJob j0, FinJob j1, int slices,
+                                                              int r, float s) {
+  const bool second = blockIdx.x >= j0.blocks;
+  const float* __restrict__ part = second ? j1.part : j0.part;
+  const int64_t C = second ? j1.C : j0.C;
+  void* __restrict__ out = second ? j1.out : j0.out;
+  const bool transpose_out = second ? j1.transpose_out : j0.transpose_out;
+  const int64_t i = (int64_t)(second ? blockIdx.x - j0.blocks : blockIdx.x) * 256 +
+                    threadIdx.x;  // index in [C, r] order
   if (i >= C * r) return;
   const float v = s * sum_strided<8>(part + i, C * r, slices);
   const int64_t c = i / r;
@@ -536,25 +562,41 @@ int colred_splits(int64_t M) { return (int)((M + kColMS - 1) / kColMS); }
 
 hipError_t launch_colred(const uint16_t* X, const uint16_t* PT, int64_t M, int64_t C, int r,
                          float* part, hipStream_t st) {
+  return launch_colred2(X, PT, C, part, nullptr, nullptr, 0, nullptr, M, r, st);
+}
+
+hipError_t launch_colred2(const uint16_t* X0, const uint16_t* PT0, int64_t C0, float* part0,
+                          const uint16_t* X1, const uint16_t* PT1, int64_t C1, float* part1,
+                          int64_t M, int r, hipStream_t st) {
   const int64_t Mp = (M + 7) & ~(int64_t)7;
-  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)colred_splits(M),
-                  (unsigned)((r / 16 + 3) / 4));
-  if (C % 8 == 0)
-    hipLaunchKernelGGL(colred_kernel<true>, grid, dim3(256), 0, st, X, PT, M, Mp, C, r, part);
+  const ColJob j0{X0, PT0, C0, part0, (unsigned)((C0 + 63) / 64)};
+  const ColJob j1{X1, PT1, C1, part1, X1 ? (unsigned)((C1 + 63) / 64) : 0u};
+  const dim3 grid(j0.tiles + j1.tiles, (unsigned)colred_splits(M), (unsigned)((r / 16 + 3) / 4));
+  if (C0 % 8 == 0 && (!X1 || C1 % 8 == 0))
+    hipLaunchKernelGGL(colred_kernel<true>, grid, dim3(256), 0, st, j0, j1, M, Mp, r);
   else
-    hipLaunchKernelGGL(colred_kernel<false>, grid, dim3(256), 0, st, X, PT, M, Mp, C, r, part);
+    hipLaunchKernelGGL(colred_kernel<false>, grid, dim3(256), 0, st, j0, j1, M, Mp, r);
   return hipGetLastError();
 }
 
 hipError_t launch_colred_finalize(const float* part, int splits, int64_t C, int r, float s,
                                   bool transpose_out, void* out, bool out_bf16, hipStream_t st) {
-  const dim3 grid((unsigned)((C * r + 255) / 256));
+  return launch_colred_finalize2(part, C, transpose_out, out, nullptr, 0, false, nullptr, splits,
+                                 r, s, out_bf16, st);
+}
+
+hipError_t launch_colred_finalize2(const float* part0, int64_t C0, bool transpose_out0,
+                                   void* out0, const float* part1, int64_t C1,
+                                   bool transpose_out1, void* out1, int splits, int r, float s,
+                                   bool out_bf16, hipStream_t st) {
+  const FinJob j0{part0, C0, out0, transpose_out0, (unsigned)((C0 * r + 255) / 256)};
+  const FinJob j1{part1, C1, out1, transpose_out1, part1 ? (unsigned)((C1 * r + 255) / 256) : 0u};
+  const dim3 grid(j0.blocks + j1.blocks);
   if (out_bf16)
-    hipLaunchKernelGGL(colred_finalize_kernel<true>, grid, dim3(256), 0, st, part, splits, C, r, s,
-                       transpose_out, out);
+    hipLaunchKernelGGL(colred_finalize_kernel<true>, grid, dim3(256), 0, st, j0, j1, splits, r, s);
   else
-    hipLaunchKernelGGL(colred_finalize_kernel<false>, grid, dim3(256), 0, st, part, splits, C, r,
-                       s, transpose_out, out);
+    hipLaunchKernelGGL(colred_finalize_kernel<false>, grid, dim3(256), 0, st, j0, j1, splits, r,
+                       s);
   return hipGetLastError();
 }
 
