@@ -23,11 +23,10 @@ namespace qlora {
 namespace {
 
 constexpr int kLut = 128;  // 65 live buckets, padded so a masked index stays in bounds
-constexpr int kQThreads = 256;                               // threads per group
-constexpr int kQPasses = kGroup * kBlock / (8 * kQThreads);  // passes per thread
-constexpr int kQBlocksPerPass = kQThreads / 8;
-static_assert(kQPasses >= 1 && kQPasses <= 8 && kQBlocksPerPass * kQPasses == kGroup, "");
-static_assert(kGroup == 4 * 64 && kQThreads >= kGroup && kQThreads >= 2 * kLut, "");
+// Threads per group: 256 (8 passes) for large tensors; 512 (4 passes) when
+// there are too few groups to fill the GPU with 256-thread workgroups.
+constexpr int kQSmallGroups = 4096;
+static_assert(kGroup == 4 * 64 && 2 * kLut == 256, "");
 
 // Max of a non-negative value over each aligned group of 8 lanes.
 __device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t v) {
@@ -79,7 +78,7 @@ __device__ __forceinline__ int e4m3_code(float x) {
   return q < 0x7E ? q : 0x7E;
 }
 
-template <bool kF32In>
+template <bool kF32In, int kQThreads>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restrict__ W,
                                                              int64_t nblocks,
                                                              uint8_t* __restrict__ codes,
@@ -89,6 +88,9 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
   __shared__ u32x2_t lutq[kLut];  // entry j: bucket j - 1, quotient threshold
   __shared__ float c1s[kGroup];
   __shared__ float red[4];
+  constexpr int kQPasses = kGroup * kBlock / (8 * kQThreads);  // passes per thread
+  constexpr int kQBlocksPerPass = kQThreads / 8;
+  static_assert(kQPasses >= 1 && kQPasses <= 8 && kQBlocksPerPass * kQPasses == kGroup, "");
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.x;
   const int64_t b0 = g * kGroup;
@@ -456,12 +458,22 @@ hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes
   const int64_t nb = n / kBlock;
   const int64_t ng = (nb + kGroup - 1) / kGroup;
   if (ng == 0) return hipSuccess;
-  if (f32_in)
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)ng), dim3(kQThreads), 0, st, W, nb,
-                       codes, q8, s2, cb);
-  else
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)ng), dim3(kQThreads), 0, st, W, nb,
-                       codes, q8, s2, cb);
+  const dim3 grid((unsigned)ng);
+  if (ng < kQSmallGroups) {
+    if (f32_in)
+      hipLaunchKernelGGL((quantize_kernel<true, 512>), grid, dim3(512), 0, st, W, nb, codes, q8,
+                         s2, cb);
+    else
+      hipLaunchKernelGGL((quantize_kernel<false, 512>), grid, dim3(512), 0, st, W, nb, codes, q8,
+                         s2, cb);
+  } else {
+    if (f32_in)
+      hipLaunchKernelGGL((quantize_kernel<true, 256>), grid, dim3(256), 0, st, W, nb, codes, q8,
+                         s2, cb);
+    else
+      hipLaunchKernelGGL((quantize_kernel<false, 256>), grid, dim3(256), 0, st, W, nb, codes, q8,
+                         s2, cb);
+  }
   return hipGetLastError();
 }
 
