@@ -539,6 +539,38 @@ def test_bwd_decode_recomputed_u_matches_saved(M, N, K, r):
     tol_check(host(dB2), go["dB"], "dB decode")
 
 
+def _bwd_abi(P, xd, dYd, dA, dB):
+    """qlora_linear_bwd through the C ABI with either adapter gradient
+    optional (NULL), no dX; fp32 gradients."""
+    M, r = dYd.shape[0], P.At.shape[1]
+    ws = torch.empty(q.qlora_workspace_bytes(1, M, P.w.N, P.w.K, r), dtype=torch.uint8, device=DEV)
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    st = q._lib.load().qlora_linear_bwd(
+        ptr(P.w.codes), ptr(P.w.absmax_q), ptr(P.w.absmax_scale), P.w.dq_format, P.w.N, P.w.K,
+        ptr(xd), ptr(dYd), M, ptr(P.At), ptr(P.Bt), r, float(P.alpha), None, None, 0,
+        ptr(dA), ptr(dB), 0, ptr(ws), ws.numel(), None)
+    torch.cuda.synchronize()
+    assert st == 0, q.qlora_strerror(st)
+
+
+@pytest.mark.parametrize("M,N,K,r", [(4096, 1100, 640, 16), (300, 100, 192, 32), (16, 520, 1024, 16)])
+def test_bwd_single_adapter_gradient_matches_both(M, N, K, r):
+    """dA alone and dB alone (the other NULL) run the reduction launches with
+    one job instead of two; each equals the same gradient of the call that
+    asks for both, bit for bit."""
+    say("bwd single gradient", M, N, K, r)
+    P = Problem(N, K, r, 32.0, seed=M + 3 * N)
+    x = syn.normal_bf16((M, K), 1.0, 50 + M)
+    dY = syn.normal_bf16((M, N), 1.0, 51 + M)
+    xd, dYd = dev_bf16(x), dev_bf16(dY)
+    _, dA, dB = run_bwd(P, x, dY, want_dx=False)
+    dA1 = torch.full_like(dA, float("nan"))
+    dB1 = torch.full_like(dB, float("nan"))
+    _bwd_abi(P, xd, dYd, dA1, None)
+    _bwd_abi(P, xd, dYd, None, dB1)
+    assert torch.equal(dA1, dA) and torch.equal(dB1, dB)
+
+
 def test_bwd_linear_1024_f32_weight():
     cfg = syn.LINEAR_1024
     N, K = cfg["weights"]["w"]
