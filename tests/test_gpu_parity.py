@@ -299,7 +299,10 @@ def test_fwd_decode_llama7b(M, name):
 @pytest.mark.parametrize("M,N,K,r", [(17, 320, 640, 16), (300, 100, 192, 32), (256, 512, 1024, 64),
                                      (33, 1024, 128, 16), (8, 72, 64, 16),
                                      # large-M path: ragged tile rows and columns, step tails
-                                     (600, 520, 192, 16), (512, 256, 64, 32), (700, 300, 1024, 64)])
+                                     (600, 520, 192, 16), (512, 256, 64, 32), (700, 300, 1024, 64),
+                                     # single-pass down projection with two rank tiles
+                                     # (M >= 2048, r = 32), ragged last 16-row tile
+                                     (2056, 544, 640, 32)])
 def test_fwd_full_small(M, N, K, r):
     say("fwd small", M, N, K, r)
     P = Problem(N, K, r, 32.0, seed=M + N + K)
@@ -505,7 +508,10 @@ def run_bwd(P, x, dY, **kw):
 @pytest.mark.parametrize("M,N,K,r", [(16, 1024, 1024, 16), (300, 100, 192, 32), (64, 512, 640, 64),
                                      (8, 72, 64, 16), (257, 256, 256, 16),
                                      # large-M path (reduction over N = 544, 320)
-                                     (600, 544, 192, 16), (520, 320, 640, 32)])
+                                     (600, 544, 192, 16), (520, 320, 640, 32),
+                                     # single-pass down projections (v over N, the
+                                     # recomputed u over K) with r = 32, M >= 2048
+                                     (2056, 544, 640, 32)])
 def test_bwd_full_small(M, N, K, r):
     say("bwd small", M, N, K, r)
     P = Problem(N, K, r, 24.0, seed=M + 2 * N + K)
