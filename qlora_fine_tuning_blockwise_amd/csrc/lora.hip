@@ -172,12 +172,12 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
 
 // Single-pass form for large M (enough 16-row tiles to fill the GPU) and
 // r = 16 kTiles <= 32: one 8-wave workgroup per 16 rows walks the whole of T,
-// wave w taking the 256-wide chunks w, w+8, .... Each iteration first issues
-// the next chunk's loads, its P fragments (clamped into P: past T the staged
-// X is zero, so they multiply zeros) and its X (two rows x 512 bytes per
-// instruction), then stages the current X through LDS and runs the MFMAs on
-// the current P fragments; both of the next chunk's operands stay in flight
-// meanwhile. The eight waves' sums are added in a fixed order in LDS and the
+// wave w taking the 256-wide chunks w, w+8, .... Each iteration but the
+// wave's last first issues the next chunk's loads, its P fragments (clamped
+// into P: past T the staged X is zero, so they multiply zeros) and its X (two
+// rows x 512 bytes per instruction), then stages the current X through LDS
+// and runs the MFMAs on the current P fragments; both of the next chunk's
+// operands stay in flight meanwhile. The eight waves' sums are added in a fixed order in LDS and the
 // workgroup writes the outputs of lora_down_finalize (out, the row-major and
 // transposed two-term splits of s*out, zero rows of lrT for M <= m < Mp)
 // itself. Requires T % 32 == 0.
@@ -221,13 +221,9 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
 #pragma unroll
   for (int i = 0; i < kTiles; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   u32x4_t xv[8], bv[kTiles][kSteps];
-  load_p(w, bv);
-  load_chunk(w, xv);
-  for (int ck = w; ck < nchunks; ck += 8) {
+  // One chunk: stage the current X through LDS and run its MFMAs.
+  auto compute = [&](int ck) {
     const int64_t tw0 = (int64_t)ck * 256, tw1 = min(T, tw0 + 256);
-    u32x4_t bn[kTiles][kSteps], xn[8];
-    load_p(ck + 8, bn);  // the next chunk's loads fly while this one is used
-    load_chunk(ck + 8, xn);
     const bool tok = tw0 + 8 * ch < tw1;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -241,12 +237,27 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
     for (int jt = 0; jt < kTiles; ++jt)
 #pragma unroll
       for (int it = 0; it < kSteps; ++it) acc[jt] = mfma_16x16x32(av[it], bv[jt][it], acc[jt]);
+  };
+  if (w < nchunks) {
+    load_p(w, bv);
+    load_chunk(w, xv);
+    int ck = w;
+    // Every chunk but the wave's last: the next chunk's loads fly while this
+    // one is used. The last chunk issues no loads, so nothing is left in
+    // flight for the epilogue's barrier to wait on.
+    for (; ck + 8 < nchunks; ck += 8) {
+      u32x4_t bn[kTiles][kSteps], xn[8];
+      load_p(ck + 8, bn);
+      load_chunk(ck + 8, xn);
+      compute(ck);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) xv[q] = xn[q];
+      for (int q = 0; q < 8; ++q) xv[q] = xn[q];
 #pragma unroll
-    for (int jt = 0; jt < kTiles; ++jt)
+      for (int jt = 0; jt < kTiles; ++jt)
 #pragma unroll
-      for (int it = 0; it < kSteps; ++it) bv[jt][it] = bn[jt][it];
+        for (int it = 0; it < kSteps; ++it) bv[jt][it] = bn[jt][it];
+    }
+    compute(ck);
   }
   __syncthreads();  // every wave is done with its staged X before red reuses it
 #pragma unroll
