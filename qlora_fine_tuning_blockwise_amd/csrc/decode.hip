@@ -47,23 +47,32 @@ __global__ __launch_bounds__(256) void lora_down_decode_kernel(const uint16_t* _
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int64_t kp = k0; kp < k1; kp += 256) {
     const int64_t kw = kp + 64 * w;
-    // Panel A[kw .. kw+63][j0 .. j0+15]: 128 chunks of 16 bytes, 2 per lane.
+    // Panel A[kw .. kw+63][j0 .. j0+15]: 128 chunks of 16 bytes, 2 per lane;
+    // then the x fragments, so that both loads are in flight together.
+    u32x4_t pv[2], xa[2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int q = lane + 64 * it, row = q >> 1, half = q & 1;
       const int64_t k = kw + row;
-      const u32x4_t v =
-          k < k1 ? *reinterpret_cast<const u32x4_t*>(A + k * r + j0 + 8 * half) : zero4();
-      uint32_t* d = reinterpret_cast<uint32_t*>(&as[w][row][8 * half]);
-      d[0] = v.x;
-      d[1] = v.y;
-      d[2] = v.z;
-      d[3] = v.w;
+      pv[it] = k < k1 ? *reinterpret_cast<const u32x4_t*>(A + k * r + j0 + 8 * half) : zero4();
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int64_t k = kw + 32 * s + 8 * g;
-      const u32x4_t a = k < k1 ? *reinterpret_cast<const u32x4_t*>(x + mrow * K + k) : zero4();
+      xa[s] = k < k1 ? *reinterpret_cast<const u32x4_t*>(x + mrow * K + k) : zero4();
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int q = lane + 64 * it, row = q >> 1, half = q & 1;
+      uint32_t* d = reinterpret_cast<uint32_t*>(&as[w][row][8 * half]);
+      d[0] = pv[it].x;
+      d[1] = pv[it].y;
+      d[2] = pv[it].z;
+      d[3] = pv[it].w;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4_t a = xa[s];
       const uint16_t* pa = &as[w][32 * s + 8 * g][i];
       u32x4_t b;
       b.x = (uint32_t)pa[0 * kDecLd] | ((uint32_t)pa[1 * kDecLd] << 16);
