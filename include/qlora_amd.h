@@ -218,8 +218,9 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
  * 16-bit weights and quantizes once afterwards):
  *   merged[n][k] = base[n][k] + s * d[n][k],  s = alpha / r (binary32),
  *   d[n][k] = sum_j A[k][j] B[j][n], starting from +0 and taking the terms
- *   j = 0..r-1 in order, each as one fused multiply-add (one rounding per
- *   term); then s*d rounds, then the final sum rounds (nearest-even).
+ *   j = 0..r-1 in order, each product rounded to binary32 and then each
+ *   addition rounded (nothing fused); then s*d rounds, then the final sum
+ *   rounds (nearest-even).
  *   base = w_hat (the dequantized NF4 weight: codes, absmax_q, absmax_scale)
  *          when W is NULL, else the bf16 weight W [N,K].
  *   A [K,r] bf16; B [r,N] bf16; merged fp32 [N,K] (caller-owned output).

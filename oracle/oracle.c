@@ -500,11 +500,12 @@ int oracle_linear_bwd(const uint16_t* x, const uint16_t* dY, int64_t M, int64_t 
 /* friction" (the clean path merges into the 16-bit weights and quantizes   */
 /* afterwards).                                                             */
 /*   out[n][k] = base[n][k] + s * d[n][k],  d[n][k] = sum_j A[k][j] B[j][n] */
-/* evaluated in binary32: d starts at +0 and takes the terms j = 0, 1, ...  */
-/* r-1 in order, each as one fused multiply-add (d = fmaf(A, B, d): the    */
-/* exact d + A*B rounded once), then t = s*d rounds, then base + t rounds.  */
-/* s = alpha / r in binary32. base is the dequantized NF4 weight (w_hat as  */
-/* bf16, widened) when wbf16 is NULL, else the bf16 weight.                 */
+/* evaluated in binary32 as written: d starts at +0 and takes the terms     */
+/* j = 0, 1, ... r-1 in order; each product A*B rounds to binary32 (exact   */
+/* unless it falls below the normal range) and each addition rounds, then  */
+/* t = s*d rounds, then base + t rounds. No operation is fused. s = alpha/r */
+/* in binary32. base is the dequantized NF4 weight (w_hat as bf16,          */
+/* widened) when wbf16 is NULL, else the bf16 weight.                       */
 /* ------------------------------------------------------------------------ */
 int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2, int fmt,
                       const uint16_t* wbf16, int64_t N, int64_t K, const uint16_t* A,
@@ -525,8 +526,10 @@ int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2, i
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t k = 0; k < K; ++k) {
             float d = 0.0f;
-            for (int j = 0; j < r; ++j)
-                d = fmaf(oracle_bf16_to_f32(A[k * r + j]), oracle_bf16_to_f32(B[(int64_t)j * N + n]), d);
+            for (int j = 0; j < r; ++j) {
+                const float p = oracle_bf16_to_f32(A[k * r + j]) * oracle_bf16_to_f32(B[(int64_t)j * N + n]);
+                d = d + p;
+            }
             const float t = s * d;
             out[n * K + k] = oracle_bf16_to_f32(w[n * K + k]) + t;
         }

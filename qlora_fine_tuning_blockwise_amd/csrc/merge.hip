@@ -6,9 +6,10 @@
 // weights and quantizes once afterwards).
 //
 // out[n][k] = base[n][k] + s * d[n][k],  d[n][k] = sum_j A[k][j] B[j][n],
-// in binary32: d starts at +0 and takes the terms j = 0..r-1 in order, each
-// as one fused multiply-add (one rounding per step), then s*d rounds, then
-// the sum with the base rounds. base is the dequantized NF4 weight
+// in binary32 as written: d starts at +0 and takes the terms j = 0..r-1 in
+// order, each product rounded, then each addition rounded (nothing fused:
+// the build's -ffp-contract=off keeps the multiply and the add apart), then
+// s*d rounds, then the sum with the base rounds. base is the dequantized NF4 weight
 // (bf16(L[code] * c1_hat), widened) or the bf16 weight. Requantizing the
 // result is the fp32 path of the quantizer.
 //
@@ -94,7 +95,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint8_t* __restrict__ 
       for (int i = 0; i < 8; ++i) {
         const float ai = (i & 1) ? bf16_hi(av[i >> 1]) : bf16_lo(av[i >> 1]);
 #pragma unroll
-        for (int rr = 0; rr < kRows; ++rr) d[rr][i] = __builtin_fmaf(ai, bj[rr], d[rr][i]);
+        for (int rr = 0; rr < kRows; ++rr) {
+          const float prod = ai * bj[rr];
+          d[rr][i] = d[rr][i] + prod;
+        }
       }
     }
   }

@@ -709,6 +709,39 @@ def test_merge_and_requantize_bit_exact(N, K, r, base):
     assert_nf4_equal(wq, *oracle.quantize_nf4_dq(ref, "f32"), f"requantized {base}")
 
 
+@pytest.mark.parametrize("base", ["nf4", "bf16"])
+def test_merge_subnormal_products_bit_exact(base):
+    """Products of the adapter terms below the normal range, where rounding
+    each product before the add differs from a fused multiply-add: A and B
+    ~ N(0,1) x 2^-72, zero base, alpha = r, so merged = the adapter sum
+    itself. Bit for bit against the oracle, plus the closed-form rank-2 case
+    (products 2^-149 and 2^-150 sum to exactly 2^-149)."""
+    N, K, r = 136, 192, 16
+    say("merge subnormal products", base)
+    rng = np.random.default_rng(64)
+    A = syn.to_bf16_bits(rng.standard_normal((K, r)).astype(np.float32) * np.float32(2.0 ** -72))
+    B = syn.to_bf16_bits(rng.standard_normal((r, N)).astype(np.float32) * np.float32(2.0 ** -72))
+    one = lambda v: syn.to_bf16_bits(np.array([v], np.float32))[0]
+    A[0, :2] = one(2.0 ** -75)
+    A[0, 2:] = 0
+    B[:2, 0] = [one(2.0 ** -74), one(2.0 ** -75)]
+    B[2:, 0] = 0
+    Wb = np.zeros((N, K), np.uint16)
+    if base == "nf4":
+        w = quantize_gpu(dev_bf16(Wb))
+        codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+        merged = q.qlora_merge_lora(dev_bf16(A), dev_bf16(B), float(r), w=w)
+        ref = oracle.merge_lora(A, B, r, float(r), nf4=(codes, q8, s2, N, K))
+    else:
+        merged = q.qlora_merge_lora(dev_bf16(A), dev_bf16(B), float(r), W=dev_bf16(Wb))
+        ref = oracle.merge_lora(A, B, r, float(r), W=Wb)
+    torch.cuda.synchronize()
+    got = host(merged)
+    assert ref[0, 0] == np.float32(2.0 ** -149)
+    assert np.count_nonzero(ref) > N * K // 2  # the sums are mostly nonzero subnormals
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), "merged weight bits"
+
+
 def test_merge_zero_adapter_gives_the_dequantized_base():
     N, K, r = 320, 512, 16
     Wb = syn.normal_bf16((N, K), 0.02, 70)

@@ -482,9 +482,11 @@ def test_merge_zero_adapter_returns_the_base(olib):
 
 def test_merge_adapter_sum_within_the_sequential_rounding_bound(olib):
     """Zero base and alpha = r (s = 1): the output is the binary32 adapter sum.
-    It must lie within the error bound of r sequential roundings of the exact
-    sum, r 2^-24 sum_j |A[k,j] B[j,n]| (plus one half-ulp for the final
-    additions), for a non-square shape, so a transposed A or B fails."""
+    Every product of two bf16 values in the normal range is exact in
+    binary32 and the first addition (to +0) is exact, so the sum carries at
+    most r-1 roundings: (r-1) 2^-24 sum_j |A[k,j] B[j,n]| (plus one half-ulp
+    for the final additions), for a non-square shape, so a transposed A or B
+    fails."""
     N, K, r = 24, 64, 16
     A = syn.normal_bf16((K, r), 0.5, 33)
     B = syn.normal_bf16((r, N), 0.5, 34)
@@ -493,8 +495,38 @@ def test_merge_adapter_sum_within_the_sequential_rounding_bound(olib):
     Af, Bf = olib.bf16_to_f32(A).astype(np.float64), olib.bf16_to_f32(B).astype(np.float64)
     exact = _exact_adapter_sum(Af, Bf)
     mag = (np.abs(Bf).T @ np.abs(Af).T)  # [N, K] sum of |terms|
-    bound = r * 2.0 ** -24 * mag + 2.0 ** -24 * np.abs(exact)
+    bound = (r - 1) * 2.0 ** -24 * mag + 2.0 ** -24 * np.abs(exact)
     assert np.all(np.abs(got - exact) <= bound + 1e-300)
+
+
+def test_merge_rounds_each_product_before_adding(olib):
+    """The merge is binary32 as written: each product rounds to binary32, then
+    the addition rounds; nothing is fused. Column 0: rank 2 with products
+    2^-149 and 2^-150 (A[0] = [2^-75, 2^-75], B[:,0] = [2^-74, 2^-75]), zero
+    base, alpha = r. The second product is half the smallest subnormal and
+    rounds to +0 (ties to even), so the sum is exactly 2^-149; a fused
+    multiply-add would round 1.5 * 2^-149 to 2^-148 instead. Column 1:
+    products 2^-148 and 2^-150 + 2^-157, which is above half a subnormal step
+    and rounds up to 2^-149, so the sum is 2^-148 + 2^-149 (a product
+    truncated toward zero would give 2^-148)."""
+    def bf(v):
+        return np.array([v], np.float32).view(np.uint32).astype(np.uint64) >> 16
+
+    N, K, r = 2, 64, 2
+    A = np.zeros((K, r), np.uint16)
+    B = np.zeros((r, N), np.uint16)
+    A[0, 0] = bf(2.0 ** -75)[0]
+    A[0, 1] = bf(2.0 ** -75)[0]
+    B[0, 0] = bf(2.0 ** -74)[0]
+    B[1, 0] = bf(2.0 ** -75)[0]
+    # column 1: products 2^-73 * 2^-75 = 2^-148 and 2^-75 * (2^-75 + 2^-82)
+    B[0, 1] = bf(2.0 ** -73)[0]
+    B[1, 1] = bf(2.0 ** -75 + 2.0 ** -82)[0]
+    W = np.zeros((N, K), np.uint16)
+    got = olib.merge_lora(A, B, r, float(r), W=W)
+    assert got[0, 0] == np.float32(2.0 ** -149)
+    assert got[1, 0] == np.float32(2.0 ** -148 + 2.0 ** -149)
+    assert np.all(got[:, 1:] == 0.0)
 
 
 def test_merge_scales_by_alpha_over_r(olib):
