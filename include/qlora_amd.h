@@ -39,8 +39,9 @@
  *     w_hat  = bf16_rne(fp32(L[code] * c1_hat)).
  *
  * CONVENTIONS
- *   - dq_format (every entry point that reads or writes absmax_q) is one of
- *     the QLORA_DQ_* formats; QLORA_ERR_INVALID_ARG otherwise.
+ *   - A quantized weight travels as a qlora_nf4 descriptor (below): its
+ *     buffers plus the format version and quantization setup it was made
+ *     with. dq_format is one of the QLORA_DQ_* formats.
  *   - Every pointer argument of a compute entry point is a DEVICE pointer
  *     owned by the caller; the library allocates nothing and keeps no state
  *     besides a constant codebook built on first use.
@@ -74,6 +75,8 @@ extern "C" {
 #define QLORA_ERR_WORKSPACE 6   /* workspace smaller than qlora_workspace_bytes() */
 #define QLORA_ERR_LAUNCH 7      /* the HIP runtime reported an error on launch */
 #define QLORA_ERR_INTERNAL 8    /* codebook construction failed its self-check */
+#define QLORA_ERR_SETUP 9       /* weight descriptor from another format version or
+                                   quantization setup than this library's */
 
 /* Element types. */
 #define QLORA_DTYPE_F32 0
@@ -102,6 +105,29 @@ extern "C" {
 
 /* Format version of the storage layout above. */
 #define QLORA_FORMAT_VERSION 1u
+
+/* Descriptor of one quantized weight: its shape, its three device buffers
+ * and the metadata that says how it was quantized. [P4] "Operational
+ * coupling": the quantization setup belongs in the adapter's recorded
+ * metadata, because an adapter trained against one quantized base is tied
+ * to exactly that base. qlora_quantize_nf4_dq writes every field except the
+ * three buffer pointers, which the caller sets; a caller that stores a
+ * quantized weight stores the metadata fields with it and restores them.
+ * Every entry point that reads the weight first checks the descriptor with
+ * qlora_nf4_check and fails with its status (QLORA_ERR_SETUP when
+ * format_version or setup_id do not match this library), so a weight is
+ * never decoded with another codebook or second-level format than the one
+ * it was quantized with. */
+typedef struct qlora_nf4 {
+  int64_t N, K;           /* W is [N, K] row-major, K % 64 == 0 */
+  uint8_t* codes;         /* device, N*K/2 bytes (see STORAGE FORMAT) */
+  int8_t* absmax_q;       /* device, N*K/64 bytes */
+  float* absmax_scale;    /* device, ceil(N*K/16384) floats */
+  int32_t dq_format;      /* QLORA_DQ_* second-level format of absmax_q */
+  uint32_t format_version; /* QLORA_FORMAT_VERSION of the storage layout */
+  uint32_t setup_id;      /* qlora_setup_id(dq_format) of the quantizing library */
+  uint32_t reserved;      /* 0 */
+} qlora_nf4;
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* qlora_strerror(int status);
@@ -143,6 +169,14 @@ uint32_t qlora_codebook_id(void);
  * Host only; 0 for an unknown format or if the codebook failed. */
 uint32_t qlora_setup_id(int dq_format);
 
+/* Checks a weight descriptor on the host: QLORA_ERR_INVALID_ARG for a NULL
+ * descriptor or buffer, an unknown dq_format or reserved != 0;
+ * QLORA_ERR_SHAPE unless N >= 1, K >= 64 and K % 64 == 0; QLORA_ERR_ALIGN
+ * for a buffer that is not 16-byte aligned; QLORA_ERR_SETUP when
+ * format_version != QLORA_FORMAT_VERSION or setup_id !=
+ * qlora_setup_id(dq_format). QLORA_OK otherwise. */
+int qlora_nf4_check(const qlora_nf4* w);
+
 /* Device workspace, in bytes, that qlora_linear_fwd (op = QLORA_OP_FWD),
  * qlora_linear_bwd (op = QLORA_OP_BWD) or qlora_merge_lora (op =
  * QLORA_OP_MERGE, M ignored) needs for these sizes, assuming no saved u. From M = 512 rows on it includes N*K*2 bytes for the dequantized
@@ -155,7 +189,11 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
  *   W        [N,K] row-major, fp32 (w_dtype = QLORA_DTYPE_F32) or bf16
  *            (QLORA_DTYPE_BF16). Values must be finite; a non-finite input
  *            gives unspecified codes (no fault).
- *   codes, absmax_q, absmax_scale  outputs, sizes from qlora_nf4_sizes.
+ *   out      descriptor whose codes, absmax_q and absmax_scale the caller
+ *            has pointed at device buffers of the sizes qlora_nf4_sizes
+ *            gives; the call writes its N, K, dq_format, format_version,
+ *            setup_id and reserved fields (host side, before the launch) and
+ *            the three buffers (on the stream).
  * Per block: c1 = max|w|; x = w / c1 (correctly rounded fp32 division);
  * code = #{i : x > threshold[i]}; an all-zero block gets code 7 (level 0).
  * Per group of 256 blocks: c2 = max c1; s2 = c2 / top (fp32 division; top =
@@ -163,24 +201,25 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
  * (ties to the lower) clamped to [0, top] for the integer formats, or the
  * nearest E4M3 value (ties to even, saturating at 448); 0 for c1 == 0. The
  * NF4 codes use the exact fp32 c1. QLORA_ERR_INVALID_ARG for an unknown
- * dq_format. */
-int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* codes,
-                          int8_t* absmax_q, float* absmax_scale, int dq_format, void* stream);
+ * dq_format or a NULL buffer; the descriptor is left untouched on any
+ * error. */
+int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, int dq_format,
+                          qlora_nf4* out, void* stream);
 
 /* Dequantize to bf16 ([P1] bullets "Compute never happens in 4-bit"; [P3]
  * "How it works": each layer's 4-bit weights are unpacked into 16-bit).
+ *   w       weight descriptor (qlora_nf4_check must pass).
  *   W_out   N*K bf16, w_hat as in the format section, in `layout`
  *           (QLORA_LAYOUT_ROWS or QLORA_LAYOUT_KSLAB32; the K-slab layout
  *           needs N*K/64 < 2^32, else QLORA_ERR_SHAPE).
  * QLORA_ERR_INVALID_ARG for another layout. */
-int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                       int dq_format, int64_t N, int64_t K, uint16_t* W_out, int layout,
-                       void* stream);
+int qlora_dequant_bf16(const qlora_nf4* w, uint16_t* W_out, int layout, void* stream);
 
 /* QLoRA linear forward ([P1] forward equation h = W_hat x + (alpha/r) B(Ax),
  * here in row-major form):
  *   u = x A                     (fp32 [M,r])
  *   y = x W_hat^T + (alpha/r) u B
+ *   w  weight descriptor, W_hat [N,K] (qlora_nf4_check must pass);
  *   x  [M,K] bf16;  A [K,r] bf16;  B [r,N] bf16;  y [M,N] fp32 or bf16
  *      (y_dtype; the bf16 output is the round-to-nearest-even of the fp32
  *      result of the same computation).
@@ -188,8 +227,7 @@ int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float
  *   workspace  device buffer of at least qlora_workspace_bytes(FWD, M,N,K,r).
  * The weight is read through its dequantized bf16 values, products are exact
  * and accumulate in fp32. M == 0 is a successful no-op. r % 16 == 0. */
-int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int dq_format, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M,
                      const uint16_t* A, const uint16_t* B, int r, float alpha, void* y,
                      int y_dtype, float* u_out, void* workspace, size_t workspace_bytes,
                      void* stream);
@@ -206,8 +244,7 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
  *   dX, dA, dB may each be NULL to skip that output (x may then be NULL if
  *   both dA and dB are NULL).
  * The frozen base is never written. M == 0 writes zero dA and dB. */
-int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int dq_format, int64_t N, int64_t K, const uint16_t* x, const uint16_t* dY,
+int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY,
                      int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
                      const float* u_saved, void* dX, int dx_dtype, void* dA, void* dB,
                      int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
@@ -221,15 +258,16 @@ int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
  *   j = 0..r-1 in order, each product rounded to binary32 and then each
  *   addition rounded (nothing fused); then s*d rounds, then the final sum
  *   rounds (nearest-even).
- *   base = w_hat (the dequantized NF4 weight: codes, absmax_q, absmax_scale)
- *          when W is NULL, else the bf16 weight W [N,K].
+ *   base = w_hat (the dequantized NF4 weight of descriptor w, whose N and K
+ *          must equal N and K) when W is NULL, else the bf16 weight W [N,K]
+ *          (w is then ignored and may be NULL).
  *   A [K,r] bf16; B [r,N] bf16; merged fp32 [N,K] (caller-owned output).
  *   workspace  at least qlora_workspace_bytes(QLORA_OP_MERGE, 0, N, K, r).
  * Requantizing the merged weight is qlora_quantize_nf4_dq with
  * QLORA_DTYPE_F32 input. Same shape and rank rules as the linear entry
- * points; QLORA_ERR_INVALID_ARG when neither base is given. */
-int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int dq_format, const uint16_t* W, int64_t N, int64_t K, const uint16_t* A,
+ * points; QLORA_ERR_INVALID_ARG when neither base is given, QLORA_ERR_SHAPE
+ * when w's shape is not [N,K]. */
+int qlora_merge_lora(const qlora_nf4* w, const uint16_t* W, int64_t N, int64_t K, const uint16_t* A,
                      const uint16_t* B, int r, float alpha, float* merged, void* workspace,
                      size_t workspace_bytes, void* stream);
 

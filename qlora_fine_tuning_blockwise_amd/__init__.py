@@ -18,7 +18,7 @@ from . import _lib
 
 __all__ = [
     "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_quotient_thresholds",
-    "qlora_codebook_id", "qlora_setup_id",
+    "qlora_codebook_id", "qlora_setup_id", "qlora_nf4_check",
     "qlora_workspace_bytes", "qlora_quantize_nf4_dq", "qlora_dequant_bf16",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "qlora_merge_lora", "qlora_adamw_step",
     "NF4Weight", "DQ_INT8", "DQ_UINT8", "DQ_E4M3", "LAYOUT_ROWS", "LAYOUT_KSLAB32",
@@ -31,6 +31,23 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("tensors passed to the library must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtypes, device):
+    """Checks one tensor argument before its pointer crosses the C ABI (the
+    library cannot see buffer sizes): shape, dtype, contiguity and device."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
 
 
 def _stream(stream):
@@ -51,16 +68,42 @@ LAYOUT_ROWS, LAYOUT_KSLAB32 = _lib.LAYOUT_ROWS, _lib.LAYOUT_KSLAB32
 
 
 class NF4Weight:
-    """The three device buffers of one quantized [N, K] weight and the
-    second-level format of its absmax codes (DQ_INT8, DQ_UINT8, DQ_E4M3)."""
+    """A quantized [N, K] weight: its three device buffers and the metadata of
+    the C descriptor (struct qlora_nf4): the second-level format of the
+    absmax codes (DQ_INT8, DQ_UINT8, DQ_E4M3), the storage format version and
+    the setup id of the library that quantized it. qlora_quantize_nf4_dq
+    fills the metadata; a weight restored from storage carries the stored
+    values, and the library rejects it if they do not match its own."""
 
-    def __init__(self, codes, absmax_q, absmax_scale, N: int, K: int, dq_format: int = DQ_INT8):
+    def __init__(self, codes, absmax_q, absmax_scale, N: int, K: int, dq_format: int = DQ_INT8,
+                 format_version: int = 0, setup_id: int = 0):
         self.codes, self.absmax_q, self.absmax_scale = codes, absmax_q, absmax_scale
         self.N, self.K = int(N), int(K)
         self.dq_format = int(dq_format)
+        self.format_version = int(format_version)
+        self.setup_id = int(setup_id)
 
     def nbytes(self) -> int:
         return self.codes.numel() + self.absmax_q.numel() + 4 * self.absmax_scale.numel()
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def _check_buffers(self):
+        cb, qb, sb = qlora_nf4_sizes(self.N, self.K)
+        dev = self.codes.device
+        _need(self.codes, "codes", (cb,), torch.uint8, dev)
+        _need(self.absmax_q, "absmax_q", (qb,), torch.int8, dev)
+        _need(self.absmax_scale, "absmax_scale", (sb // 4,), torch.float32, dev)
+
+    def desc(self) -> "ctypes.pointer":
+        """The C descriptor of this weight (buffers checked first)."""
+        self._check_buffers()
+        d = _lib.NF4Desc(self.N, self.K, self.codes.data_ptr(), self.absmax_q.data_ptr(),
+                         self.absmax_scale.data_ptr(), self.dq_format, self.format_version,
+                         self.setup_id, 0)
+        return ctypes.pointer(d)
 
 
 def qlora_strerror(status: int) -> str:
@@ -89,6 +132,11 @@ def qlora_codebook_quotient_thresholds():
     return tq
 
 
+def qlora_nf4_check(w: NF4Weight) -> int:
+    """Status of the library's host check of w's descriptor (0 = usable)."""
+    return int(_lib.load().qlora_nf4_check(w.desc()))
+
+
 def qlora_setup_id(dq_format: int) -> int:
     return int(_lib.load().qlora_setup_id(int(dq_format)))
 
@@ -112,17 +160,24 @@ def qlora_quantize_nf4_dq(W: torch.Tensor, out: NF4Weight | None = None, stream=
                           dq_format: int | None = None) -> NF4Weight:
     """Quantize a [N, K] fp32 or bf16 device tensor to NF4 + double-quantized
     constants in second-level format dq_format (default: out's format, else
-    DQ_INT8)."""
+    DQ_INT8). The returned weight carries the descriptor metadata the library
+    wrote."""
+    if W.dim() != 2:
+        raise ValueError("qlora_quantize_nf4_dq: W must be [N, K]")
     N, K = W.shape
+    _need(W, "W", (N, K), (torch.float32, torch.bfloat16), W.device)
     if dq_format is None:
         dq_format = out.dq_format if out is not None else DQ_INT8
     if out is None:
         out = NF4Weight(*_alloc_nf4(N, K, W.device), N, K, dq_format)
+    if (out.N, out.K) != (N, K):
+        raise ValueError("qlora_quantize_nf4_dq: out has another shape")
     out.dq_format = int(dq_format)
-    st = _lib.load().qlora_quantize_nf4_dq(_ptr(W), _dtype_code(W.dtype), N, K, _ptr(out.codes),
-                                           _ptr(out.absmax_q), _ptr(out.absmax_scale),
-                                           out.dq_format, _stream(stream))
+    d = out.desc()
+    st = _lib.load().qlora_quantize_nf4_dq(_ptr(W), _dtype_code(W.dtype), N, K, out.dq_format, d,
+                                           _stream(stream))
     _lib.check(st, "qlora_quantize_nf4_dq")
+    out.format_version, out.setup_id = int(d.contents.format_version), int(d.contents.setup_id)
     return out
 
 
@@ -131,12 +186,11 @@ def qlora_dequant_bf16(w: NF4Weight, out: torch.Tensor | None = None, stream=Non
     """w_hat as bf16: [N, K] (LAYOUT_ROWS) or [K/32, N, 32] (LAYOUT_KSLAB32)."""
     shape = (w.N, w.K) if layout == LAYOUT_ROWS else (w.K // 32, w.N, 32)
     if out is None:
-        out = torch.empty(shape, dtype=torch.bfloat16, device=w.codes.device)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=w.device)
     if out.numel() != w.N * w.K:
         raise ValueError("qlora_dequant_bf16: out must hold N*K elements")
-    st = _lib.load().qlora_dequant_bf16(_ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale),
-                                        w.dq_format, w.N, w.K, _ptr(out), int(layout),
-                                        _stream(stream))
+    _need(out, "out", tuple(out.shape), torch.bfloat16, w.device)
+    st = _lib.load().qlora_dequant_bf16(w.desc(), _ptr(out), int(layout), _stream(stream))
     _lib.check(st, "qlora_dequant_bf16")
     return out
 
@@ -145,6 +199,9 @@ def _workspace(op, M, N, K, r, device, workspace):
     need = qlora_workspace_bytes(op, M, N, K, r)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous() \
+            or workspace.device != device:
+        raise ValueError("workspace: a contiguous 1-D uint8 tensor on the weight's device")
     return workspace
 
 
@@ -155,14 +212,18 @@ def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, A: torch.Tensor, B: torch.Te
     """y = x W_hat^T + (alpha/r) (x A) B. x [M,K] bf16, A [K,r] bf16, B [r,N] bf16."""
     M = x.shape[0]
     r = A.shape[1]
+    dev = w.device
+    _need(x, "x", (M, w.K), torch.bfloat16, dev)
+    _need(A, "A", (w.K, r), torch.bfloat16, dev)
+    _need(B, "B", (r, w.N), torch.bfloat16, dev)
     if y is None:
-        y = torch.empty((M, w.N), dtype=y_dtype, device=x.device)
-    workspace = _workspace(_lib.OP_FWD, M, w.N, w.K, r, x.device, workspace)
+        y = torch.empty((M, w.N), dtype=y_dtype, device=dev)
+    _need(y, "y", (M, w.N), (torch.float32, torch.bfloat16), dev)
+    _need(u_out, "u_out", (M, r), torch.float32, dev)
+    workspace = _workspace(_lib.OP_FWD, M, w.N, w.K, r, dev, workspace)
     st = _lib.load().qlora_linear_fwd(
-        _ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale), w.dq_format, w.N, w.K, _ptr(x), M,
-        _ptr(A),
-        _ptr(B), r, float(alpha), _ptr(y), _dtype_code(y.dtype), _ptr(u_out), _ptr(workspace),
-        workspace.numel(), _stream(stream))
+        w.desc(), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y), _dtype_code(y.dtype),
+        _ptr(u_out), _ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st, "qlora_linear_fwd")
     return y
 
@@ -175,17 +236,20 @@ def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: 
     """Returns (dX or None, dA or None, dB or None)."""
     M = dY.shape[0]
     r = A.shape[1]
-    dev = dY.device
+    dev = w.device
+    _need(dY, "dY", (M, w.N), torch.bfloat16, dev)
+    _need(x, "x", (M, w.K), torch.bfloat16, dev)
+    _need(A, "A", (w.K, r), torch.bfloat16, dev)
+    _need(B, "B", (r, w.N), torch.bfloat16, dev)
+    _need(u_saved, "u_saved", (M, r), torch.float32, dev)
     dX = torch.empty((M, w.K), dtype=dx_dtype, device=dev) if want_dx else None
     dA = torch.empty((w.K, r), dtype=grad_dtype, device=dev) if want_grads else None
     dB = torch.empty((r, w.N), dtype=grad_dtype, device=dev) if want_grads else None
     workspace = _workspace(_lib.OP_BWD, M, w.N, w.K, r, dev, workspace)
     st = _lib.load().qlora_linear_bwd(
-        _ptr(w.codes), _ptr(w.absmax_q), _ptr(w.absmax_scale), w.dq_format, w.N, w.K, _ptr(x),
-        _ptr(dY), M,
-        _ptr(A), _ptr(B), r, float(alpha), _ptr(u_saved), _ptr(dX), _dtype_code(dx_dtype),
-        _ptr(dA), _ptr(dB), _dtype_code(grad_dtype), _ptr(workspace), workspace.numel(),
-        _stream(stream))
+        w.desc(), _ptr(x), _ptr(dY), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(u_saved),
+        _ptr(dX), _dtype_code(dx_dtype), _ptr(dA), _ptr(dB), _dtype_code(grad_dtype),
+        _ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st, "qlora_linear_bwd")
     return dX, dA, dB
 
@@ -228,9 +292,11 @@ def qlora_merge_lora(A: torch.Tensor, B: torch.Tensor, alpha: float, w: NF4Weigh
     need = qlora_workspace_bytes(_lib.OP_MERGE, 0, N, K, r)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    nf = (w.codes, w.absmax_q, w.absmax_scale) if w is not None else (None, None, None)
-    fmt = w.dq_format if w is not None else DQ_INT8
-    st = _lib.load().qlora_merge_lora(_ptr(nf[0]), _ptr(nf[1]), _ptr(nf[2]), fmt, _ptr(W), N, K,
+    _need(W, "W", (N, K), torch.bfloat16, dev)
+    _need(A, "A", (K, r), torch.bfloat16, dev)
+    _need(B, "B", (r, N), torch.bfloat16, dev)
+    _need(out, "out", (N, K), torch.float32, dev)
+    st = _lib.load().qlora_merge_lora(w.desc() if w is not None else None, _ptr(W), N, K,
                                       _ptr(A), _ptr(B), r, float(alpha), _ptr(out),
                                       _ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st, "qlora_merge_lora")

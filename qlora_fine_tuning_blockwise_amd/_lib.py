@@ -32,6 +32,16 @@ SZ = ctypes.c_size_t
 FLT = ctypes.c_float
 DBL = ctypes.c_double
 
+class NF4Desc(ctypes.Structure):
+    """struct qlora_nf4 of include/qlora_amd.h."""
+    _fields_ = [("N", I64), ("K", I64), ("codes", P), ("absmax_q", P), ("absmax_scale", P),
+                ("dq_format", ctypes.c_int32), ("format_version", ctypes.c_uint32),
+                ("setup_id", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+DESC = ctypes.POINTER(NF4Desc)
+FORMAT_VERSION = 1
+
 SIGNATURES = {
     "qlora_strerror": (ctypes.c_char_p, [INT]),
     "qlora_nf4_sizes": (INT, [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
@@ -40,14 +50,13 @@ SIGNATURES = {
     "qlora_codebook_id": (ctypes.c_uint32, []),
     "qlora_workspace_bytes": (SZ, [INT, I64, I64, I64, INT]),
     "qlora_setup_id": (ctypes.c_uint32, [INT]),
-    "qlora_quantize_nf4_dq": (INT, [P, INT, I64, I64, P, P, P, INT, P]),
-    "qlora_dequant_bf16": (INT, [P, P, P, INT, I64, I64, P, INT, P]),
-    "qlora_linear_fwd": (INT, [P, P, P, INT, I64, I64, P, I64, P, P, INT, FLT, P, INT, P, P, SZ,
-                               P]),
-    "qlora_linear_bwd": (INT, [P, P, P, INT, I64, I64, P, P, I64, P, P, INT, FLT, P, P, INT, P, P,
-                               INT, P, SZ, P]),
+    "qlora_nf4_check": (INT, [DESC]),
+    "qlora_quantize_nf4_dq": (INT, [P, INT, I64, I64, INT, DESC, P]),
+    "qlora_dequant_bf16": (INT, [DESC, P, INT, P]),
+    "qlora_linear_fwd": (INT, [DESC, P, I64, P, P, INT, FLT, P, INT, P, P, SZ, P]),
+    "qlora_linear_bwd": (INT, [DESC, P, P, I64, P, P, INT, FLT, P, P, INT, P, P, INT, P, SZ, P]),
     "qlora_gemm_bf16_nt": (INT, [P, I64, P, I64, INT, P, P, I64, I64, I64, INT, P, INT, P]),
-    "qlora_merge_lora": (INT, [P, P, P, INT, P, I64, I64, P, P, INT, FLT, P, P, SZ, P]),
+    "qlora_merge_lora": (INT, [DESC, P, I64, I64, P, P, INT, FLT, P, P, SZ, P]),
     "qlora_adamw_step": (INT, [P, P, INT, P, P, P, I64, DBL, DBL, DBL, DBL, DBL, I64, P]),
 }
 

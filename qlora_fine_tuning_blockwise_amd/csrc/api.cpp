@@ -115,11 +115,28 @@ T* at(void* base, size_t off) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
 
+bool format_ok(int dq_format) {
+  return dq_format == QLORA_DQ_INT8 || dq_format == QLORA_DQ_UINT8 || dq_format == QLORA_DQ_E4M3;
+}
+
+// Host check of a weight descriptor (the rules of qlora_nf4_check).
+int nf4_check(const qlora_nf4* w) {
+  if (!w || !w->codes || !w->absmax_q || !w->absmax_scale || w->reserved != 0 ||
+      !format_ok(w->dq_format))
+    return QLORA_ERR_INVALID_ARG;
+  if (!shape_ok(w->N, w->K)) return QLORA_ERR_SHAPE;
+  if (!aligned16(w->codes) || !aligned16(w->absmax_q) || !aligned16(w->absmax_scale))
+    return QLORA_ERR_ALIGN;
+  const uint32_t id = setup_id(w->dq_format);
+  if (id == 0) return QLORA_ERR_INTERNAL;
+  if (w->format_version != QLORA_FORMAT_VERSION || w->setup_id != id) return QLORA_ERR_SETUP;
+  return QLORA_OK;
+}
+
 // The codebook as one call's kernels receive it, with that call's
 // second-level format. QLORA_ERR_INVALID_ARG for an unknown format.
 int call_codebook(int dq_format, Codebook* out) {
-  if (dq_format != QLORA_DQ_INT8 && dq_format != QLORA_DQ_UINT8 && dq_format != QLORA_DQ_E4M3)
-    return QLORA_ERR_INVALID_ARG;
+  if (!format_ok(dq_format)) return QLORA_ERR_INVALID_ARG;
   const Codebook* cb = nullptr;
   if (get_codebook(&cb, nullptr) != QLORA_OK) return QLORA_ERR_INTERNAL;
   *out = *cb;
@@ -163,6 +180,9 @@ const char* qlora_strerror(int status) {
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_LAUNCH: return "kernel launch failed";
     case QLORA_ERR_INTERNAL: return "codebook self-check failed";
+    case QLORA_ERR_SETUP:
+      return "weight descriptor does not match this library's format version or quantization "
+             "setup";
     default: return "unknown status";
   }
 }
@@ -202,6 +222,8 @@ uint32_t qlora_codebook_id(void) {
 
 uint32_t qlora_setup_id(int dq_format) { return setup_id(dq_format); }
 
+int qlora_nf4_check(const qlora_nf4* w) { return nf4_check(w); }
+
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
   if (M < 0 || !shape_ok(N, K) || !rank_ok(r)) return 0;
   if (op == QLORA_OP_FWD) return fwd_layout(M, N, K, r, true).total;
@@ -210,52 +232,62 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
   return 0;
 }
 
-int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* codes,
-                          int8_t* absmax_q, float* absmax_scale, int dq_format, void* stream) {
+int qlora_quantize_nf4_dq(const void* W, int w_dtype, int64_t N, int64_t K, int dq_format,
+                          qlora_nf4* out, void* stream) {
   Codebook cb;
   if (const int st = call_codebook(dq_format, &cb)) return st;
-  if (!W || !codes || !absmax_q || !absmax_scale) return QLORA_ERR_INVALID_ARG;
+  if (!W || !out || !out->codes || !out->absmax_q || !out->absmax_scale)
+    return QLORA_ERR_INVALID_ARG;
   if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
   if (w_dtype != QLORA_DTYPE_F32 && w_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
-  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale))
+  if (!aligned16(W) || !aligned16(out->codes) || !aligned16(out->absmax_q) ||
+      !aligned16(out->absmax_scale))
     return QLORA_ERR_ALIGN;
-  return launch_status(launch_quantize(W, w_dtype == QLORA_DTYPE_F32, N * K, codes, absmax_q,
-                                       absmax_scale, cb, static_cast<hipStream_t>(stream)));
+  const uint32_t id = setup_id(dq_format);
+  if (id == 0) return QLORA_ERR_INTERNAL;
+  out->N = N;
+  out->K = K;
+  out->dq_format = dq_format;
+  out->format_version = QLORA_FORMAT_VERSION;
+  out->setup_id = id;
+  out->reserved = 0;
+  return launch_status(launch_quantize(W, w_dtype == QLORA_DTYPE_F32, N * K, out->codes,
+                                       out->absmax_q, out->absmax_scale, cb,
+                                       static_cast<hipStream_t>(stream)));
 }
 
-int qlora_dequant_bf16(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                       int dq_format, int64_t N, int64_t K, uint16_t* W_out, int layout,
-                       void* stream) {
+int qlora_dequant_bf16(const qlora_nf4* w, uint16_t* W_out, int layout, void* stream) {
+  if (const int st = nf4_check(w)) return st;
   Codebook cb;
-  if (const int st = call_codebook(dq_format, &cb)) return st;
-  if (!codes || !absmax_q || !absmax_scale || !W_out) return QLORA_ERR_INVALID_ARG;
+  if (const int st = call_codebook(w->dq_format, &cb)) return st;
+  if (!W_out) return QLORA_ERR_INVALID_ARG;
   if (layout != QLORA_LAYOUT_ROWS && layout != QLORA_LAYOUT_KSLAB32) return QLORA_ERR_INVALID_ARG;
-  if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
+  const int64_t N = w->N, K = w->K;
   if (layout == QLORA_LAYOUT_KSLAB32 && N * (K / kBlock) >= ((int64_t)1 << 32))
     return QLORA_ERR_SHAPE;
-  if (!aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale) || !aligned16(W_out))
-    return QLORA_ERR_ALIGN;
-  return launch_status(launch_dequant(codes, absmax_q, absmax_scale, N * K, W_out,
+  if (!aligned16(W_out)) return QLORA_ERR_ALIGN;
+  return launch_status(launch_dequant(w->codes, w->absmax_q, w->absmax_scale, N * K, W_out,
                                       layout == QLORA_LAYOUT_KSLAB32 ? N : 0, cb,
                                       static_cast<hipStream_t>(stream)));
 }
 
-int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int dq_format, int64_t N, int64_t K, const uint16_t* x, int64_t M,
-                     const uint16_t* A, const uint16_t* B, int r, float alpha, void* y,
-                     int y_dtype, float* u_out, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int r, float alpha, void* y, int y_dtype, float* u_out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (const int st = nf4_check(w)) return st;
   Codebook cb;
-  if (const int st = call_codebook(dq_format, &cb)) return st;
+  if (const int st = call_codebook(w->dq_format, &cb)) return st;
+  const int64_t N = w->N, K = w->K;
+  const uint8_t* codes = w->codes;
+  const int8_t* absmax_q = w->absmax_q;
+  const float* absmax_scale = w->absmax_scale;
   if (M < 0) return QLORA_ERR_INVALID_ARG;
-  if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
   if (y_dtype != QLORA_DTYPE_F32 && y_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
   if (!rank_ok(r)) return QLORA_ERR_RANK;
   if (M == 0) return QLORA_OK;
-  if (!codes || !absmax_q || !absmax_scale || !x || !A || !B || !y) return QLORA_ERR_INVALID_ARG;
-  if (!aligned16(codes) || !aligned16(absmax_q) || !aligned16(absmax_scale) || !aligned16(x) ||
-      !aligned16(A) || !aligned16(B) || !aligned16(y) || (u_out && !aligned16(u_out)) ||
-      (workspace && !aligned16(workspace)))
+  if (!x || !A || !B || !y) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
+      (u_out && !aligned16(u_out)) || (workspace && !aligned16(workspace)))
     return QLORA_ERR_ALIGN;
   const FwdLayout L = fwd_layout(M, N, K, r, u_out == nullptr);
   if (!workspace || workspace_bytes < L.total) return QLORA_ERR_WORKSPACE;
@@ -294,24 +326,26 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* absmax_q, const float* 
   return launch_status(e);
 }
 
-int qlora_linear_bwd(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int dq_format, int64_t N, int64_t K, const uint16_t* x, const uint16_t* dY,
-                     int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
+int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int r, float alpha,
                      const float* u_saved, void* dX, int dx_dtype, void* dA, void* dB,
                      int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (const int st = nf4_check(w)) return st;
   Codebook cb;
-  if (const int st = call_codebook(dq_format, &cb)) return st;
+  if (const int st = call_codebook(w->dq_format, &cb)) return st;
+  const int64_t N = w->N, K = w->K;
+  const uint8_t* codes = w->codes;
+  const int8_t* absmax_q = w->absmax_q;
+  const float* absmax_scale = w->absmax_scale;
   if (M < 0) return QLORA_ERR_INVALID_ARG;
-  if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
   if ((dx_dtype != QLORA_DTYPE_F32 && dx_dtype != QLORA_DTYPE_BF16) ||
       (grad_dtype != QLORA_DTYPE_F32 && grad_dtype != QLORA_DTYPE_BF16))
     return QLORA_ERR_DTYPE;
   if (!rank_ok(r)) return QLORA_ERR_RANK;
   if (!A || !B) return QLORA_ERR_INVALID_ARG;
   if (M > 0 && !dY) return QLORA_ERR_INVALID_ARG;
-  if (dX && (!codes || !absmax_q || !absmax_scale)) return QLORA_ERR_INVALID_ARG;
   if ((dA || dB) && M > 0 && !x) return QLORA_ERR_INVALID_ARG;
-  const void* ptrs[] = {codes, absmax_q, absmax_scale, x, dY, A, B, u_saved, dX, dA, dB, workspace};
+  const void* ptrs[] = {x, dY, A, B, u_saved, dX, dA, dB, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
 
@@ -412,17 +446,22 @@ int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_
                                       static_cast<hipStream_t>(stream)));
 }
 
-int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* absmax_scale,
-                     int dq_format, const uint16_t* W, int64_t N, int64_t K, const uint16_t* A,
-                     const uint16_t* B, int r, float alpha, float* merged, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+int qlora_merge_lora(const qlora_nf4* w, const uint16_t* W, int64_t N, int64_t K,
+                     const uint16_t* A, const uint16_t* B, int r, float alpha, float* merged,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!W && !w) return QLORA_ERR_INVALID_ARG;
+  if (!W)
+    if (const int st = nf4_check(w)) return st;
   Codebook cb;
-  if (const int st = call_codebook(dq_format, &cb)) return st;
+  if (const int st = call_codebook(W ? QLORA_DQ_INT8 : w->dq_format, &cb)) return st;
   if (!shape_ok(N, K)) return QLORA_ERR_SHAPE;
+  if (!W && (w->N != N || w->K != K)) return QLORA_ERR_SHAPE;
   if (!rank_ok(r)) return QLORA_ERR_RANK;
   if (!A || !B || !merged) return QLORA_ERR_INVALID_ARG;
-  if (!W && (!codes || !absmax_q || !absmax_scale)) return QLORA_ERR_INVALID_ARG;
-  const void* ptrs[] = {codes, absmax_q, absmax_scale, W, A, B, merged, workspace};
+  const uint8_t* codes = W ? nullptr : w->codes;
+  const int8_t* absmax_q = W ? nullptr : w->absmax_q;
+  const float* absmax_scale = W ? nullptr : w->absmax_scale;
+  const void* ptrs[] = {W, A, B, merged, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
   const MergeLayout L = merge_layout(N, K, r);
@@ -432,7 +471,7 @@ int qlora_merge_lora(const uint8_t* codes, const int8_t* absmax_q, const float* 
   uint16_t* Bt = at<uint16_t>(workspace, L.Bt);
   hipError_t e = launch_transpose2_bf16(A, K, r, At, B, r, N, Bt, st);  // A^T [r,K], B^T [N,r]
   if (e == hipSuccess)
-    e = launch_merge(W ? nullptr : codes, absmax_q, absmax_scale, W, N, K, At, Bt, r,
+    e = launch_merge(codes, absmax_q, absmax_scale, W, N, K, At, Bt, r,
                      alpha / (float)r, merged, cb, st);
   return launch_status(e);
 }

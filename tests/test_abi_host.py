@@ -52,8 +52,8 @@ def test_sizes_accounting(lib):
 
 
 def test_strerror_covers_codes(lib):
-    texts = {q.qlora_strerror(s) for s in range(9)}
-    assert len(texts) == 9 and q.qlora_strerror(99) == "unknown status"
+    texts = {q.qlora_strerror(s) for s in range(10)}
+    assert len(texts) == 10 and q.qlora_strerror(99) == "unknown status"
 
 
 FAKE = 1 << 20  # an aligned address never dereferenced: validation fails first
@@ -63,22 +63,76 @@ def _p(v):
     return ctypes.c_void_p(v)
 
 
+def _desc(**kw):
+    """A descriptor with aligned fake buffers and this library's metadata."""
+    a = dict(N=64, K=128, codes=FAKE, absmax_q=FAKE, absmax_scale=FAKE, dq_format=0,
+             format_version=_lib.FORMAT_VERSION, setup_id=None, reserved=0)
+    a.update(kw)
+    if a["setup_id"] is None:
+        a["setup_id"] = q.qlora_setup_id(a["dq_format"]) if a["dq_format"] in (0, 1, 2) else 0
+    return ctypes.pointer(_lib.NF4Desc(a["N"], a["K"], a["codes"], a["absmax_q"],
+                                       a["absmax_scale"], a["dq_format"], a["format_version"],
+                                       a["setup_id"], a["reserved"]))
+
+
+def test_descriptor_check(lib):
+    """[P4] "Operational coupling": a weight is only read with the setup it
+    was quantized with. Each mismatch is rejected on the host."""
+    c = lib.qlora_nf4_check
+    assert c(_desc()) == 0
+    for f in (0, 1, 2):
+        assert c(_desc(dq_format=f)) == 0
+    assert c(None) == 1
+    assert c(_desc(codes=None)) == 1
+    assert c(_desc(absmax_q=None)) == 1
+    assert c(_desc(absmax_scale=None)) == 1
+    assert c(_desc(dq_format=3, setup_id=q.qlora_setup_id(0))) == 1   # unknown format
+    assert c(_desc(reserved=1)) == 1
+    assert c(_desc(K=96)) == 2
+    assert c(_desc(N=0)) == 2
+    assert c(_desc(codes=FAKE + 4)) == 3
+    assert c(_desc(absmax_scale=FAKE + 8)) == 3
+    assert c(_desc(format_version=0)) == 9                            # never quantized
+    assert c(_desc(format_version=2)) == 9                            # another layout version
+    assert c(_desc(setup_id=0)) == 9
+    assert c(_desc(setup_id=q.qlora_setup_id(0) ^ 1)) == 9            # another codebook
+    # the format travels with its setup id: relabelling the format alone fails
+    assert c(_desc(dq_format=1, setup_id=q.qlora_setup_id(0))) == 9
+    assert c(_desc(dq_format=0, setup_id=q.qlora_setup_id(2))) == 9
+    # every reading entry point runs the same check first
+    bad = _desc(setup_id=q.qlora_setup_id(1))
+    assert lib.qlora_dequant_bf16(bad, _p(FAKE), 0, None) == 9
+    assert _fwd(lib, w=bad) == 9
+    assert lib.qlora_merge_lora(bad, None, 64, 128, _p(FAKE), _p(FAKE), 16, 32.0, _p(FAKE),
+                                _p(FAKE), 1 << 30, None) == 9
+    args = _bwd_base()
+    args[0] = bad
+    assert lib.qlora_linear_bwd(*args) == 9
+
+
 def test_quantize_validation(lib):
     f = lib.qlora_quantize_nf4_dq
-    assert f(None, 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 1
-    assert f(_p(FAKE), 1, 4, 96, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 2
-    assert f(_p(FAKE), 1, 0, 64, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 2
-    assert f(_p(FAKE), 7, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 4
-    assert f(_p(FAKE + 2), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), 0, None) == 3
-    assert f(_p(FAKE), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), 3, None) == 1   # dq format
-    assert f(_p(FAKE), 1, 4, 64, _p(FAKE), _p(FAKE), _p(FAKE), -1, None) == 1
-    d = lib.qlora_dequant_bf16
-    assert d(_p(FAKE), None, _p(FAKE), 0, 4, 64, _p(FAKE), 0, None) == 1
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 0, 4, 65, _p(FAKE), 0, None) == 2
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE + 4), 0, 4, 64, _p(FAKE), 0, None) == 3
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 9, 4, 64, _p(FAKE), 0, None) == 1     # dq format
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 0, 4, 64, _p(FAKE), 2, None) == 1     # layout
-    assert d(_p(FAKE), _p(FAKE), _p(FAKE), 0, 1 << 22, 1 << 16, _p(FAKE), 1, None) == 2
+    d = _desc(N=0, K=0, format_version=0, setup_id=0)
+    assert f(None, 1, 4, 64, 0, d, None) == 1
+    assert f(_p(FAKE), 1, 4, 64, 0, None, None) == 1
+    assert f(_p(FAKE), 1, 4, 64, 0, _desc(codes=None), None) == 1
+    assert f(_p(FAKE), 1, 4, 96, 0, d, None) == 2
+    assert f(_p(FAKE), 1, 0, 64, 0, d, None) == 2
+    assert f(_p(FAKE), 7, 4, 64, 0, d, None) == 4
+    assert f(_p(FAKE + 2), 1, 4, 64, 0, d, None) == 3
+    assert f(_p(FAKE), 1, 4, 64, 3, d, None) == 1   # dq format
+    assert f(_p(FAKE), 1, 4, 64, -1, d, None) == 1
+    # rejected calls leave the descriptor untouched
+    assert (d.contents.N, d.contents.format_version, d.contents.setup_id) == (0, 0, 0)
+    dq = lib.qlora_dequant_bf16
+    assert dq(_desc(), None, 0, None) == 1
+    assert dq(_desc(absmax_q=None), _p(FAKE), 0, None) == 1
+    assert dq(_desc(K=65), _p(FAKE), 0, None) == 2
+    assert dq(_desc(absmax_scale=FAKE + 4), _p(FAKE), 0, None) == 3
+    assert dq(_desc(), _p(FAKE + 2), 0, None) == 3
+    assert dq(_desc(dq_format=9, setup_id=1), _p(FAKE), 0, None) == 1     # dq format
+    assert dq(_desc(), _p(FAKE), 2, None) == 1     # layout
+    assert dq(_desc(N=1 << 22, K=1 << 16), _p(FAKE), 1, None) == 2
 
 
 def test_setup_ids(lib):
@@ -90,14 +144,14 @@ def test_setup_ids(lib):
 
 
 def _fwd(lib, **kw):
-    a = dict(codes=FAKE, q8=FAKE, s2=FAKE, fmt=0, N=64, K=128, x=FAKE, M=32, A=FAKE, B=FAKE, r=16,
-             alpha=32.0, y=FAKE, ydt=0, u=None, ws=FAKE, wsb=1 << 30)
+    a = dict(w=None, x=FAKE, M=32, A=FAKE, B=FAKE, r=16, alpha=32.0, y=FAKE, ydt=0, u=None, ws=FAKE,
+             wsb=1 << 30)
+    wkw = {k: kw.pop(k) for k in list(kw) if k in ("N", "K", "dq_format", "codes")}
     a.update(kw)
+    w = a["w"] if a["w"] is not None else _desc(**wkw)
     P = lambda v: None if v is None else _p(v)
-    return lib.qlora_linear_fwd(P(a["codes"]), P(a["q8"]), P(a["s2"]), a["fmt"], a["N"], a["K"],
-                                P(a["x"]),
-                                a["M"], P(a["A"]), P(a["B"]), a["r"], a["alpha"], P(a["y"]),
-                                a["ydt"], P(a["u"]), P(a["ws"]), a["wsb"], None)
+    return lib.qlora_linear_fwd(w, P(a["x"]), a["M"], P(a["A"]), P(a["B"]), a["r"], a["alpha"],
+                                P(a["y"]), a["ydt"], P(a["u"]), P(a["ws"]), a["wsb"], None)
 
 
 def test_fwd_validation(lib):
@@ -111,28 +165,33 @@ def test_fwd_validation(lib):
     assert _fwd(lib, B=FAKE + 8) == 3
     assert _fwd(lib, wsb=16) == 6
     assert _fwd(lib, ws=None) == 6
-    assert _fwd(lib, fmt=5) == 1
+    assert _fwd(lib, codes=None) == 1
+    assert lib.qlora_linear_fwd(None, _p(FAKE), 32, _p(FAKE), _p(FAKE), 16, 32.0, _p(FAKE), 0,
+                                None, _p(FAKE), 1 << 30, None) == 1
     assert _fwd(lib, M=0) == 0  # empty batch: a no-op that enqueues nothing
+
+
+def _bwd_base():
+    return [_desc(), _p(FAKE), _p(FAKE), 32, _p(FAKE), _p(FAKE), 16, 32.0, None, _p(FAKE), 0,
+            _p(FAKE), _p(FAKE), 0, _p(FAKE), 1 << 30, None]
 
 
 def test_bwd_validation(lib):
     f = lib.qlora_linear_bwd
-    base = [_p(FAKE)] * 3 + [0, 64, 128, _p(FAKE), _p(FAKE), 32, _p(FAKE), _p(FAKE), 16, 32.0,
-                             None, _p(FAKE), 0, _p(FAKE), _p(FAKE), 0, _p(FAKE), 1 << 30, None]
 
     def call(i, v):
-        a = list(base)
+        a = _bwd_base()
         a[i] = v
         return f(*a)
-    assert call(7, None) == 1          # dY missing
-    assert call(6, None) == 1          # x missing while dA/dB wanted
-    assert call(5, 96) == 2            # K % 64
-    assert call(15, 3) == 4            # dx dtype
-    assert call(18, 9) == 4            # grad dtype
-    assert call(11, 0) == 5            # r
-    assert call(9, _p(FAKE + 1)) == 3  # A misaligned
-    assert call(20, 64) == 6           # workspace too small
-    assert call(3, 7) == 1             # dq format
+    assert call(2, None) == 1          # dY missing
+    assert call(1, None) == 1          # x missing while dA/dB wanted
+    assert call(0, _desc(K=96)) == 2   # K % 64
+    assert call(10, 3) == 4            # dx dtype
+    assert call(13, 9) == 4            # grad dtype
+    assert call(6, 0) == 5             # r
+    assert call(4, _p(FAKE + 1)) == 3  # A misaligned
+    assert call(15, 64) == 6           # workspace too small
+    assert call(0, None) == 1          # no weight
 
 
 def test_gemm_nt_validation(lib):
@@ -163,20 +222,20 @@ def test_gemm_nt_validation(lib):
 
 def test_merge_validation(lib):
     f = lib.qlora_merge_lora
-    base = [_p(FAKE), _p(FAKE), _p(FAKE), 0, None, 64, 128, _p(FAKE), _p(FAKE), 16, 32.0,
-            _p(FAKE), _p(FAKE), 1 << 30, None]
 
     def call(i, v):
-        a = list(base)
+        a = [_desc(), None, 64, 128, _p(FAKE), _p(FAKE), 16, 32.0, _p(FAKE), _p(FAKE), 1 << 30,
+             None]
         a[i] = v
         return f(*a)
-    assert call(6, 100) == 2            # K % 64
-    assert call(9, 8) == 5              # r
-    assert call(11, None) == 1          # merged missing
+    assert call(3, 100) == 2            # K % 64
+    assert call(6, 8) == 5              # r
+    assert call(8, None) == 1           # merged missing
     assert call(0, None) == 1           # neither NF4 base nor bf16 base
-    assert call(7, _p(FAKE + 4)) == 3   # A misaligned
-    assert call(13, 64) == 6            # workspace too small
-    assert call(3, 4) == 1              # dq format
+    assert call(4, _p(FAKE + 4)) == 3   # A misaligned
+    assert call(10, 64) == 6            # workspace too small
+    assert call(0, _desc(dq_format=4, setup_id=1)) == 1  # dq format
+    assert call(2, 32) == 2             # descriptor is [64, 128], not [32, 128]
     assert lib.qlora_workspace_bytes(2, 0, 64, 128, 16) >= 2 * 16 * (64 + 128)
 
 

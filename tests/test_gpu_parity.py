@@ -552,8 +552,7 @@ def _bwd_abi(P, xd, dYd, dA, dB):
     ws = torch.empty(q.qlora_workspace_bytes(1, M, P.w.N, P.w.K, r), dtype=torch.uint8, device=DEV)
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     st = q._lib.load().qlora_linear_bwd(
-        ptr(P.w.codes), ptr(P.w.absmax_q), ptr(P.w.absmax_scale), P.w.dq_format, P.w.N, P.w.K,
-        ptr(xd), ptr(dYd), M, ptr(P.At), ptr(P.Bt), r, float(P.alpha), None, None, 0,
+        P.w.desc(), ptr(xd), ptr(dYd), M, ptr(P.At), ptr(P.Bt), r, float(P.alpha), None, None, 0,
         ptr(dA), ptr(dB), 0, ptr(ws), ws.numel(), None)
     torch.cuda.synchronize()
     assert st == 0, q.qlora_strerror(st)
@@ -679,6 +678,41 @@ def test_layer_70b_fwd_bwd_sampled():
         for g, rr, k in zip(got, ref, ("y", "dX", "dA", "dB")):
             tol_check(g, rr, f"70b {name} {k}")
         say("70b layer ok", name)
+
+
+# ------------------------------------------------------------ descriptor
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_quantize_records_the_setup_and_calls_check_it(fmt):
+    """[P4] "Operational coupling": quantizing records the format version and
+    the setup id in the weight's descriptor; a descriptor relabelled to
+    another second-level format, or carrying another setup id, is refused by
+    every reading call before anything is launched."""
+    N, K, r = 96, 256, 16
+    say("descriptor", fmt)
+    w = quantize_gpu(dev_bf16(syn.normal_bf16((N, K), 0.02, 80 + fmt)), fmt)
+    assert w.format_version == 1 and w.setup_id == q.qlora_setup_id(fmt)
+    assert q.qlora_nf4_check(w) == 0
+    x = dev_bf16(syn.normal_bf16((32, K), 1.0, 83))
+    A = dev_bf16(syn.normal_bf16((K, r), 0.05, 84))
+    B = dev_bf16(syn.normal_bf16((r, N), 0.01, 85))
+    y0 = q.qlora_linear_fwd(w, x, A, B, 32.0)
+    torch.cuda.synchronize()
+    relabelled = q.NF4Weight(w.codes, w.absmax_q, w.absmax_scale, N, K, (fmt + 1) % 3,
+                             w.format_version, w.setup_id)
+    foreign = q.NF4Weight(w.codes, w.absmax_q, w.absmax_scale, N, K, fmt, w.format_version,
+                          w.setup_id ^ 0x5A5A)
+    for bad in (relabelled, foreign):
+        assert q.qlora_nf4_check(bad) == 9
+        y = torch.full((32, N), 7.0, device=DEV)
+        with pytest.raises(RuntimeError, match="setup"):
+            q.qlora_linear_fwd(bad, x, A, B, 32.0, y=y)
+        with pytest.raises(RuntimeError, match="setup"):
+            q.qlora_dequant_bf16(bad)
+        with pytest.raises(RuntimeError, match="setup"):
+            q.qlora_linear_bwd(bad, x, dev_bf16(syn.normal_bf16((32, N), 1.0, 86)), A, B, 32.0)
+        torch.cuda.synchronize()
+        assert torch.all(y == 7.0)  # nothing was launched
+    assert torch.equal(q.qlora_linear_fwd(w, x, A, B, 32.0), y0)
 
 
 # ------------------------------------------------------------------- merge
