@@ -179,8 +179,10 @@ int qlora_nf4_check(const qlora_nf4* w);
 
 /* Device workspace, in bytes, that qlora_linear_fwd (op = QLORA_OP_FWD),
  * qlora_linear_bwd (op = QLORA_OP_BWD) or qlora_merge_lora (op =
- * QLORA_OP_MERGE, M ignored) needs for these sizes, assuming no saved u. From M = 512 rows on it includes N*K*2 bytes for the dequantized
- * weight (see qlora_gemm_bf16_nt). Host only; 0 on invalid sizes. */
+ * QLORA_OP_MERGE, M ignored) needs for these sizes, assuming no saved u. For
+ * the backward from M = 512 rows on it includes N*K*2 bytes for the
+ * transposed dequantized weight (see qlora_gemm_bf16_nt); the forward never
+ * holds a bf16 copy of the weight. Host only; 0 on invalid sizes. */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
 
 /* Quantize once, at load time ([P4] "The mechanism": the pretrained weights
@@ -315,12 +317,13 @@ int qlora_adamw_step(float* param, const void* grad, int grad_dtype, float* exp_
  *      ignored; for instance W_out of qlora_dequant_bf16);  e [M,2r] bf16;
  *   f  [N,r] bf16;  y [M,N] fp32 or bf16 (y_dtype; bf16 is the
  *      round-to-nearest-even of the fp32 result).
- * From M = 512 rows on, qlora_linear_fwd dequantizes the weight once into
- * its workspace (K-slab layout) and runs this stage with a = x, b = w_hat,
- * f = B^T and e the
- * two-term split [hi | lo] of (alpha/r) u (hi = bf16(v), lo = bf16(v - hi)),
- * so that e [f|f]^T adds (hi + lo) B; qlora_linear_bwd does the same for dX
- * with a = dY, b = w_hat^T (K-slab), f = A. Requires K >= 32 and K % 32 ==
+ * From M = 512 rows on, qlora_linear_bwd dequantizes the transposed weight
+ * once into its workspace (K-slab layout) and runs this stage for dX with
+ * a = dY, b = w_hat^T, f = A and e the two-term split [hi | lo] of
+ * (alpha/r) v (hi = bf16(v), lo = bf16(v - hi)), so that e [f|f]^T adds
+ * (hi + lo) A^T. With qlora_dequant_bf16 it also forms the unfused
+ * counterpart of the forward, whose large-batch kernel dequantizes in
+ * registers instead. Requires K >= 32 and K % 32 ==
  * 0, lda a multiple of 8 with 512*lda + 2*K < 2^31 and lda >= K; for
  * QLORA_LAYOUT_ROWS ldb likewise, for QLORA_LAYOUT_KSLAB32 2*N*K < 2^31; r as
  * for the linear entry points (QLORA_ERR_SHAPE / QLORA_ERR_RANK otherwise;

@@ -12,16 +12,16 @@ namespace qlora {
 namespace {
 
 constexpr int64_t kGemvMaxM = 16;  // decode sizes take the GEMV path
-// From this many rows on, the weight is dequantized once into the workspace
-// and the product runs as a plain bf16 GEMM (the dequantization is then a
-// small share of the call); below it the tile kernels dequantize in place.
+// From this many rows on (training batches), the forward runs the fused
+// 256 x 256-tile dequantize-GEMM; below it the 512 x 128-tile kernel.
 constexpr int64_t kPlainMinM = 512;
 
-// The large-M path keeps the dequantized weight in the K-slab layout (whole
-// cache lines per direct-to-LDS load of the GEMM's b operand).
-bool fwd_plain(int64_t M, int64_t N, int64_t K) {
-  return M >= kPlainMinM && gemm_nt_supported(K, K, 0, N, true);
+bool fwd_fused(int64_t M, int64_t N, int64_t K) {
+  return M >= kPlainMinM && gemm_nf4_supported(M, N, K);
 }
+// The backward's dX from 512 rows on: the weight is dequantized once,
+// transposed, into the workspace (K-slab layout: whole cache lines per
+// direct-to-LDS load of the GEMM's b operand), then a plain bf16 GEMM.
 bool bwd_plain(int64_t M, int64_t N, int64_t K) {
   return M >= kPlainMinM && N % 32 == 0 && gemm_nt_supported(N, N, 0, K, true);
 }
@@ -45,8 +45,8 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, W = 0, total = 0;
-  bool gemv_path = false, plain = false;
+  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, total = 0;
+  bool gemv_path = false, fused = false;
 };
 
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
@@ -61,8 +61,7 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
     L.down = c.take((size_t)lora_down_slices(K) * M * r * 4);
     L.Bt = c.take((size_t)N * r * 2);
     L.ulr = c.take((size_t)M * 2 * r * 2);
-    L.plain = fwd_plain(M, N, K);
-    if (L.plain) L.W = c.take((size_t)N * K * 2);
+    L.fused = fwd_fused(M, N, K);
   }
   L.total = c.off;
   return L;
@@ -315,10 +314,9 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
       if (e == hipSuccess)
         e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, u, ulr, nullptr, st);
     }
-    if (e == hipSuccess && L.plain) {
-      uint16_t* W = at<uint16_t>(workspace, L.W);
-      e = launch_dequant(codes, absmax_q, absmax_scale, N * K, W, N, cb, st);  // K-slab
-      if (e == hipSuccess) e = launch_gemm_nt(x, K, W, 0, ulr, Bt, M, N, K, r, y, ybf, true, st);
+    if (e == hipSuccess && L.fused) {
+      e = launch_gemm_nf4_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, cb,
+                              st);
     } else if (e == hipSuccess) {
       e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, cb, st);
     }

@@ -106,6 +106,15 @@ bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb, int64_t N, bool b_k
 hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                           const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t Kr,
                           int r, void* y, bool y_bf16, bool b_kslab, hipStream_t st);
+// Fused large-M forward: y = x W_hat^T + e [f|f]^T with the NF4 weight
+// dequantized in registers right before the MFMAs (no bf16 copy of the
+// weight). e is the two-term split of s*u (launch_lora_down_*), f = B^T.
+bool gemm_nf4_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_nf4_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
+                               const float* s2, const uint16_t* e, const uint16_t* f, int64_t M,
+                               int64_t N, int64_t K, int r, void* y, bool y_bf16,
+                               const Codebook& cb, hipStream_t st);
+
 // out[k][n] = w_hat[n][k] as bf16: [K, N] row-major (the transpose of
 // launch_dequant's output), or in the K-slab layout [N/32][K][32] when kslab
 // (N % 32 == 0).

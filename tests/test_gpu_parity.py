@@ -302,7 +302,12 @@ def test_fwd_decode_llama7b(M, name):
                                      (600, 520, 192, 16), (512, 256, 64, 32), (700, 300, 1024, 64),
                                      # single-pass down projection with two rank tiles
                                      # (M >= 2048, r = 32), ragged last 16-row tile
-                                     (2056, 544, 640, 32)])
+                                     (2056, 544, 640, 32),
+                                     # fused large-M kernel: one-block rows (K = 64), pair
+                                     # counts off the four-pair unroll (5, 7), weight rows
+                                     # that leave waves or whole 32-row halves empty
+                                     (1024, 1000, 64, 16), (520, 100, 320, 16),
+                                     (513, 40, 448, 32), (777, 289, 192, 48)])
 def test_fwd_full_small(M, N, K, r):
     say("fwd small", M, N, K, r)
     P = Problem(N, K, r, 32.0, seed=M + N + K)
