@@ -102,6 +102,7 @@ extern "C" {
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1
 #define QLORA_OP_MERGE 2
+#define QLORA_OP_FWD_LEAN 3 /* the forward without a bf16 copy of the weight */
 
 /* Format version of the storage layout above. */
 #define QLORA_FORMAT_VERSION 1u
@@ -179,10 +180,15 @@ int qlora_nf4_check(const qlora_nf4* w);
 
 /* Device workspace, in bytes, that qlora_linear_fwd (op = QLORA_OP_FWD),
  * qlora_linear_bwd (op = QLORA_OP_BWD) or qlora_merge_lora (op =
- * QLORA_OP_MERGE, M ignored) needs for these sizes, assuming no saved u. For
- * the backward from M = 512 rows on it includes N*K*2 bytes for the
- * transposed dequantized weight (see qlora_gemm_bf16_nt); the forward never
- * holds a bf16 copy of the weight. Host only; 0 on invalid sizes. */
+ * QLORA_OP_MERGE, M ignored) needs for these sizes, assuming no saved u.
+ * From M = 512 rows on, QLORA_OP_FWD and QLORA_OP_BWD include N*K*2 bytes for
+ * one dequantized bf16 copy of the weight (the pages' one layer's worth of
+ * 16-bit weights, [P3] "How it works"): the fast route. QLORA_OP_FWD_LEAN is
+ * the smallest workspace the forward accepts: with less than the QLORA_OP_FWD
+ * size but at least this one, qlora_linear_fwd runs its fused kernel, which
+ * dequantizes each weight tile in registers right before the matrix cores
+ * use it and never holds a bf16 copy ([P4] "The mechanism"). Host only; 0 on
+ * invalid sizes. */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
 
 /* Quantize once, at load time ([P4] "The mechanism": the pretrained weights
@@ -226,7 +232,9 @@ int qlora_dequant_bf16(const qlora_nf4* w, uint16_t* W_out, int layout, void* st
  *      (y_dtype; the bf16 output is the round-to-nearest-even of the fp32
  *      result of the same computation).
  *   u_out      fp32 [M,r] or NULL; when given it receives u (for the backward).
- *   workspace  device buffer of at least qlora_workspace_bytes(FWD, M,N,K,r).
+ *   workspace  device buffer of at least qlora_workspace_bytes(FWD_LEAN,
+ *              M,N,K,r); from M = 512 on, a workspace of the FWD size selects
+ *              the faster route through one bf16 copy of the weight.
  * The weight is read through its dequantized bf16 values, products are exact
  * and accumulate in fp32. M == 0 is a successful no-op. r % 16 == 0. */
 int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M,

@@ -208,8 +208,11 @@ def _workspace(op, M, N, K, r, device, workspace):
 def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                      alpha: float, y: torch.Tensor | None = None, y_dtype=torch.float32,
                      u_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                     stream=None) -> torch.Tensor:
-    """y = x W_hat^T + (alpha/r) (x A) B. x [M,K] bf16, A [K,r] bf16, B [r,N] bf16."""
+                     stream=None, lean: bool = False) -> torch.Tensor:
+    """y = x W_hat^T + (alpha/r) (x A) B. x [M,K] bf16, A [K,r] bf16, B [r,N] bf16.
+    The route follows the workspace size (an allocated one is sized for the
+    fast route, or for the lean route that holds no bf16 copy of the weight
+    when `lean`)."""
     M = x.shape[0]
     r = A.shape[1]
     dev = w.device
@@ -220,7 +223,8 @@ def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, A: torch.Tensor, B: torch.Te
         y = torch.empty((M, w.N), dtype=y_dtype, device=dev)
     _need(y, "y", (M, w.N), (torch.float32, torch.bfloat16), dev)
     _need(u_out, "u_out", (M, r), torch.float32, dev)
-    workspace = _workspace(_lib.OP_FWD, M, w.N, w.K, r, dev, workspace)
+    workspace = _workspace(_lib.OP_FWD_LEAN if lean else _lib.OP_FWD, M, w.N, w.K, r, dev,
+                           workspace)
     st = _lib.load().qlora_linear_fwd(
         w.desc(), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y), _dtype_code(y.dtype),
         _ptr(u_out), _ptr(workspace), workspace.numel(), _stream(stream))

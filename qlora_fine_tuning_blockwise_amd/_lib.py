@@ -24,6 +24,7 @@ DQ_E4M3 = 2
 OP_FWD = 0
 OP_BWD = 1
 OP_MERGE = 2
+OP_FWD_LEAN = 3
 
 P = ctypes.c_void_p
 I64 = ctypes.c_int64

@@ -12,10 +12,20 @@ namespace qlora {
 namespace {
 
 constexpr int64_t kGemvMaxM = 16;  // decode sizes take the GEMV path
-// From this many rows on (training batches), the forward runs the fused
-// 256 x 256-tile dequantize-GEMM; below it the 512 x 128-tile kernel.
+// From this many rows on (training batches) the forward has two routes:
+//  - fast: the weight is dequantized once into the caller's workspace (one
+//    layer's worth of bf16, K-slab layout) and a plain bf16 MFMA GEMM runs on
+//    it; needs N*K*2 bytes more workspace;
+//  - lean: the fused kernel dequantizes each weight tile in registers right
+//    before its MFMAs, so no bf16 copy of the weight ever exists.
+// The call takes the fast route when the workspace holds it, else the lean
+// one (qlora_workspace_bytes with QLORA_OP_FWD or QLORA_OP_FWD_LEAN).
+// Below 512 rows the 512 x 128-tile kernel dequantizes in LDS.
 constexpr int64_t kPlainMinM = 512;
 
+bool fwd_plain(int64_t M, int64_t N, int64_t K) {
+  return M >= kPlainMinM && gemm_nt_supported(K, K, 0, N, true);
+}
 bool fwd_fused(int64_t M, int64_t N, int64_t K) {
   return M >= kPlainMinM && gemm_nf4_supported(M, N, K);
 }
@@ -45,11 +55,12 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, total = 0;
-  bool gemv_path = false, fused = false;
+  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, W = 0, total = 0;
+  bool gemv_path = false, plain = false, fused = false;
 };
 
-FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
+// lean: the layout of the lean route (no bf16 copy of the weight).
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u, bool lean = false) {
   FwdLayout L;
   Carve c;
   L.gemv_path = M <= kGemvMaxM;
@@ -61,7 +72,9 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
     L.down = c.take((size_t)lora_down_slices(K) * M * r * 4);
     L.Bt = c.take((size_t)N * r * 2);
     L.ulr = c.take((size_t)M * 2 * r * 2);
-    L.fused = fwd_fused(M, N, K);
+    L.plain = !lean && fwd_plain(M, N, K);
+    L.fused = !L.plain && fwd_fused(M, N, K);
+    if (L.plain) L.W = c.take((size_t)N * K * 2);
   }
   L.total = c.off;
   return L;
@@ -226,6 +239,7 @@ int qlora_nf4_check(const qlora_nf4* w) { return nf4_check(w); }
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
   if (M < 0 || !shape_ok(N, K) || !rank_ok(r)) return 0;
   if (op == QLORA_OP_FWD) return fwd_layout(M, N, K, r, true).total;
+  if (op == QLORA_OP_FWD_LEAN) return fwd_layout(M, N, K, r, true, true).total;
   if (op == QLORA_OP_BWD) return bwd_layout(M, N, K, r, true).total;
   if (op == QLORA_OP_MERGE) return merge_layout(N, K, r).total;
   return 0;
@@ -288,7 +302,8 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
   if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
       (u_out && !aligned16(u_out)) || (workspace && !aligned16(workspace)))
     return QLORA_ERR_ALIGN;
-  const FwdLayout L = fwd_layout(M, N, K, r, u_out == nullptr);
+  FwdLayout L = fwd_layout(M, N, K, r, u_out == nullptr);
+  if (L.plain && workspace_bytes < L.total) L = fwd_layout(M, N, K, r, u_out == nullptr, true);
   if (!workspace || workspace_bytes < L.total) return QLORA_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -314,7 +329,11 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
       if (e == hipSuccess)
         e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, u, ulr, nullptr, st);
     }
-    if (e == hipSuccess && L.fused) {
+    if (e == hipSuccess && L.plain) {
+      uint16_t* W = at<uint16_t>(workspace, L.W);
+      e = launch_dequant(codes, absmax_q, absmax_scale, N * K, W, N, cb, st);  // K-slab
+      if (e == hipSuccess) e = launch_gemm_nt(x, K, W, 0, ulr, Bt, M, N, K, r, y, ybf, true, st);
+    } else if (e == hipSuccess && L.fused) {
       e = launch_gemm_nf4_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, cb,
                               st);
     } else if (e == hipSuccess) {

@@ -83,13 +83,17 @@ __device__ __forceinline__ void nf4_planes(const Codebook& cb, float ch, uint32_
 // Even and odd nibbles are looked up separately: the low 3 bits of a code
 // select a byte among entries 0..7 and among 8..15, bit 3 picks one of the
 // two, then the low and high bytes are interleaved into bf16 pairs.
+// The two selector constants in VGPRs (kb4 = 0x04040404, kid = 0x03020100):
+// a VOP3 operation on gfx950 reads at most one scalar, so with both in
+// scalars (x & kb4) | kid would take two instructions instead of one
+// v_and_or_b32.
 __device__ __forceinline__ u32x4_t nf4_lut(uint32_t d, const uint32_t (&pl)[4],
-                                           const uint32_t (&ph)[4]) {
+                                           const uint32_t (&ph)[4], uint32_t kb4, uint32_t kid) {
   const uint32_t se = d & 0x07070707u;
   const uint32_t d4 = d >> 4;
   const uint32_t so = d4 & 0x07070707u;
-  const uint32_t ke = ((d >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t ko = ((d4 >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t ke = ((d >> 1) & kb4) | kid;
+  const uint32_t ko = ((d4 >> 1) & kb4) | kid;
   const uint32_t le = perm(perm(pl[3], pl[2], se), perm(pl[1], pl[0], se), ke);
   const uint32_t he = perm(perm(ph[3], ph[2], se), perm(ph[1], ph[0], se), ke);
   const uint32_t lo = perm(perm(pl[3], pl[2], so), perm(pl[1], pl[0], so), ko);
@@ -142,11 +146,32 @@ __device__ __forceinline__ T* pick(T* const (&arr)[N]) {
   return arr[S];
 }
 
-// Codes and block constants of one pair (block) for the lane's two rows.
+// Value of an absmax code byte b (0..255, loaded zero-extended) in format
+// kFmt, exact in fp32. The signed byte is read as (b ^ 0x80) - 128, so that
+// the compiler never turns the byte load into a sign-extending load issued
+// again next to this use.
+template <int kFmt>
+__device__ __forceinline__ float absmax_value(int b) {
+  if constexpr (kFmt == kDqInt8) {
+    return (float)(b ^ 0x80) - 128.0f;
+  } else {
+    return q8_value(b, kFmt);
+  }
+}
+
+// Codes of one pair (block) for the lane's two rows, and the block constants
+// of the row whose table this lane builds (row h; the lane pair (i, 0),
+// (i, 1) builds one table each and they swap).
 struct PairCodes {
   u32x4_t c[2];  // 16 bytes of codes per row: weights 32h .. 32h+31 of the block
-  int q[2];      // absmax code byte
-  float s[2];    // second-level scale of the block's group
+  int q;         // absmax code byte of row h, zero-extended
+  float s;       // second-level scale of row h's block group
+  float ch;      // c1_hat of row h: value(q) * s, formed once the loads have landed
+};
+
+// Dequantization tables of one pair for the lane's two rows (byte planes).
+struct Planes {
+  uint32_t lo[2][4], hi[2][4];
 };
 
 template <int kFmt, bool kOutBf16>
@@ -191,38 +216,51 @@ __global__ __launch_bounds__(256, 1) void gemm_nf4_fwd_kernel(Nf4Args p, Codeboo
   const __amdgpu_buffer_rsrc_t cres = make_rsrc(p.codes + n0 * (K / 2), (N - n0) * (K / 2));
   const __amdgpu_buffer_rsrc_t qres = make_rsrc(p.q8 + n0 * KB, (N - n0) * KB);
   const __amdgpu_buffer_rsrc_t sres = make_rsrc(p.s2, ((N * KB + 255) / 256) * 4);
-  uint32_t coff[2], qoff[2];
-  int64_t bfirst[2];
+  uint32_t coff[2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int row = 64 * w + 32 * nt + i;
-    coff[nt] = (uint32_t)(row * (K / 2) + 16 * h);
-    qoff[nt] = (uint32_t)(row * KB);
-    bfirst[nt] = (n0 + row) * KB;  // global block index of the row's first block
-  }
+  for (int nt = 0; nt < 2; ++nt) coff[nt] = (uint32_t)((64 * w + 32 * nt + i) * (K / 2) + 16 * h);
+  const int trow = 64 * w + 32 * h + i;  // the row whose table this lane builds
+  const uint32_t qoff = (uint32_t)(trow * KB);
+  const uint32_t bfirst = (uint32_t)((n0 + trow) * KB);  // N * K/64 < 2^31 (gemm_nf4_supported)
   auto load_pair = [&](int pair, PairCodes& pc) {
     const int ps = pair < npairs ? pair : npairs - 1;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < 2; ++nt)
       pc.c[nt] = __builtin_bit_cast(
           u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(cres, coff[nt], 32 * ps, 0));
-      pc.q[nt] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(qres, qoff[nt], ps, 0);
-      const int64_t b = bfirst[nt] + ps;
-      pc.s[nt] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(sres, (uint32_t)((b >> 8) * 4), 0, 0));
+    pc.q = (int)__builtin_amdgcn_raw_buffer_load_b8(qres, qoff, ps, 0);
+    pc.s = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(sres, ((bfirst + (uint32_t)ps) >> 8) * 4, 0, 0));
+  };
+  // mbcnt_lo(0, c) is c in every lane, but the compiler treats it as
+  // lane-varying and keeps it in a VGPR.
+  const uint32_t kb4 = __builtin_amdgcn_mbcnt_lo(0u, 0x04040404u);
+  const uint32_t kid = __builtin_amdgcn_mbcnt_lo(0u, 0x03020100u);
+  // Planes of row nt of a pair, and the operand of substep d (dword d of the
+  // row's 16 code bytes) for both rows.
+  // The planes of both rows: this lane builds row h's, then lanes l and
+  // l + 32 swap halves (v_permlane32_swap: the upper 32 lanes of the first
+  // operand trade places with the lower 32 lanes of the second), which
+  // leaves row 0's planes in the first result and row 1's in the second.
+  auto planes = [&](const PairCodes& pc, Planes& pl) {
+    uint32_t lo[4], hi[4];
+    nf4_planes(cb, pc.ch, lo, hi);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const auto xl = __builtin_amdgcn_permlane32_swap(lo[g], lo[g], false, false);
+      const auto xh = __builtin_amdgcn_permlane32_swap(hi[g], hi[g], false, false);
+      pl.lo[0][g] = xl[0];
+      pl.lo[1][g] = xl[1];
+      pl.hi[0][g] = xh[0];
+      pl.hi[1][g] = xh[1];
     }
   };
-  // Dequantize one pair: B operand (nt, t, s) of the pair, t = step, s =
-  // substep, is dword 2t+s of the row's 16 code bytes.
-  auto dequant_pair = [&](const PairCodes& pc, u32x4_t (&bo)[2][4]) {
+  auto operands = [&](const PairCodes& pc, const Planes& pl, int d, u32x4_t (&bo)[2]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      uint32_t pl[4], ph[4];
-      nf4_planes(cb, q8_value(pc.q[nt], kFmt) * pc.s[nt], pl, ph);
-      bo[nt][0] = nf4_lut(pc.c[nt].x, pl, ph);
-      bo[nt][1] = nf4_lut(pc.c[nt].y, pl, ph);
-      bo[nt][2] = nf4_lut(pc.c[nt].z, pl, ph);
-      bo[nt][3] = nf4_lut(pc.c[nt].w, pl, ph);
+      const uint32_t c = d == 0 ? pc.c[nt].x : d == 1 ? pc.c[nt].y : d == 2 ? pc.c[nt].z
+                                                                           : pc.c[nt].w;
+      bo[nt] = nf4_lut(c, pl.lo[nt], pl.hi[nt], kb4, kid);
     }
   };
 
@@ -241,17 +279,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nf4_fwd_kernel(Nf4Args p, Codeboo
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.0f;
 
-  // Prologue: x pairs 0 and 1, codes of pairs 0 and 1; pair 0's operands.
-  PairCodes cA, cB;
+  // Prologue: x pairs 0 and 1, codes of pairs 0 and 1; pair 0's planes and
+  // the operands of its first substep.
+  PairCodes c0, c1, c2;
+  Planes pA, pB;
 #pragma unroll
   for (int q = 0; q < 8; ++q) dma_x(q, 0, sa0);
-  load_pair(0, cA);
+  load_pair(0, c0);
+  load_pair(1, c1);
 #pragma unroll
   for (int q = 0; q < 8; ++q) dma_x(q, 1, sa1);
-  load_pair(1, cB);
-  u32x4_t bA[2][4], bB[2][4];
-  dequant_pair(cA, bA);  // the compiler waits for pair 0's codes
-  wait_vm_lgkm0<14>();   // pair 0's x has landed (pair 1 and its codes may fly)
+  u32x4_t b0[2], b1[2];
+  c0.ch = absmax_value<kFmt>(c0.q) * c0.s;  // the compiler waits for pair 0's codes
+  planes(c0, pA);
+  operands(c0, pA, 0, b0);
+  wait_vm_lgkm0<8>();  // pair 0's x and pair 1's codes have landed (pair 1's x may fly)
+  c1.ch = absmax_value<kFmt>(c1.q) * c1.s;
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   u32x4_t a0[8], a1[8];
@@ -260,48 +303,49 @@ __global__ __launch_bounds__(256, 1) void gemm_nf4_fwd_kernel(Nf4Args p, Codeboo
     a0[mt] = *reinterpret_cast<const u32x4_t*>(&sa0[fa[0] + 2048 * mt]);
 
   // One pair (a 64-weight block): four substeps q = 2t + s. Substep q runs
-  // 16 MFMAs on (a_cur, bc[.][q]) while the fragments of substep q+1 (or of
-  // the next pair's first substep, from the next slot) are read and a
-  // quarter of the next pair's operands is dequantized: in step t the
-  // operands of row nt = t, its table in substep 0, dwords 0-1 in substep 0
-  // and 2-3 in substep 1. Step t issues four x loads of pair + 2; step 0
-  // also issues the code loads of pair + 2. Each step ends with a wait for
-  // all but its own loads and one barrier. The last pair dequantizes a
-  // repeat of itself (codes of pair + 1 are clamped): one basic block per
-  // pair keeps the VALU work interleaved with the MFMAs.
-  auto pair_fn = [&](int pr, auto slotc, u32x4_t (&bc)[2][4], u32x4_t (&bn)[2][4],
-                     PairCodes& cuse, PairCodes& cload) {
+  // 16 MFMAs on (a_cur, b_cur) while the x fragments of substep q+1 (of the
+  // next pair's first substep, from the next slot, when q = 3) are read and
+  // the weight operands of substep q+1 are dequantized: dwords 1..3 of this
+  // pair's codes through its planes, then dword 0 of the next pair's. The
+  // next pair's planes are built in substeps 1 (row 0) and 2 (row 1). Step t
+  // issues four x loads of pair + 2; substep 0 also issues the code loads of
+  // pair + 2. Each step ends with a wait for all but its own loads and one
+  // barrier. The last pair prepares a repeat of itself (the loads clamp to
+  // the last pair), so each pair stays one basic block.
+  auto pair_fn = [&](int pr, auto slotc, const PairCodes& cc, const PairCodes& cn,
+                     PairCodes& cl, const Planes& pc, Planes& pn) {
     constexpr int SL = decltype(slotc)::value;
     uint16_t* const acur = pick<SL>(sa);
     uint16_t* const anxt = pick<(SL + 1) & 3>(sa);
     uint16_t* const ald = pick<(SL + 2) & 3>(sa);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      uint32_t pl[4], ph[4];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int qs = 2 * t + s;
         u32x4_t(&acu)[8] = (qs & 1) ? a1 : a0;
         u32x4_t(&anx)[8] = (qs & 1) ? a0 : a1;
+        u32x4_t(&bcu)[2] = (qs & 1) ? b1 : b0;
+        u32x4_t(&bnx)[2] = (qs & 1) ? b0 : b1;
         uint16_t* const src = qs == 3 ? anxt : acur;
         const int fnext = fa[(qs + 1) & 3];
-        if (qs == 0) load_pair(pr + 2, cload);
-        if (s == 0) nf4_planes(cb, q8_value(cuse.q[t], kFmt) * cuse.s[t], pl, ph);
-        const uint32_t d0 = s ? cuse.c[t].z : cuse.c[t].x;
-        const uint32_t d1 = s ? cuse.c[t].w : cuse.c[t].y;
-        bn[t][2 * s] = nf4_lut(d0, pl, ph);
-        bn[t][2 * s + 1] = nf4_lut(d1, pl, ph);
+        if (qs == 0) load_pair(pr + 2, cl);
+        if (qs == 1) planes(cn, pn);
+        if (qs < 3)
+          operands(cc, pc, qs + 1, bnx);
+        else
+          operands(cn, pn, 0, bnx);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
           const int mt = g >> 1, nt = g & 1;
-          acc[mt][nt] = mfma_32x32x16(acu[mt], bc[nt][qs], acc[mt][nt]);
+          acc[mt][nt] = mfma_32x32x16(acu[mt], bcu[nt], acc[mt][nt]);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
           if (g & 1) {
             anx[g >> 1] = *reinterpret_cast<const u32x4_t*>(&src[fnext + 2048 * (g >> 1)]);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-          if (qs == 0 && g == 2) __builtin_amdgcn_sched_group_barrier(0x020, 6, 0);
+          if (qs == 0 && g == 2) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
           if ((g & 7) == 7) {
             dma_x(4 * t + 2 * s + (g >> 3), pr + 2, ald);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -310,27 +354,37 @@ __global__ __launch_bounds__(256, 1) void gemm_nf4_fwd_kernel(Nf4Args p, Codeboo
         __builtin_amdgcn_sched_barrier(0);
       }
       if (t == 0)
-        wait_vm_lgkm0<10>();  // all but this step's 4 x loads and 6 code loads
+        wait_vm_lgkm0<8>();  // all but this step's 4 x loads and 4 code loads
       else
         wait_vm_lgkm0<4>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
+    // pair + 2's constants have landed: form its c1_hat now, so that no
+    // load result crosses the loop's back edge still pending
+    cl.ch = absmax_value<kFmt>(cl.q) * cl.s;
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   using S3 = std::integral_constant<int, 3>;
+  // Pair p: codes p, p+1 in use, p+2 loading (three sets, rotating); planes
+  // of p in use, p+1 being built (two sets); x slot p % 4.
   int pr = 0;
   for (; pr + 4 <= npairs; pr += 4) {
-    pair_fn(pr + 0, S0(), bA, bB, cB, cA);
-    pair_fn(pr + 1, S1(), bB, bA, cA, cB);
-    pair_fn(pr + 2, S2(), bA, bB, cB, cA);
-    pair_fn(pr + 3, S3(), bB, bA, cA, cB);
+    pair_fn(pr + 0, S0(), c0, c1, c2, pA, pB);
+    pair_fn(pr + 1, S1(), c1, c2, c0, pB, pA);
+    pair_fn(pr + 2, S2(), c2, c0, c1, pA, pB);
+    pair_fn(pr + 3, S3(), c0, c1, c2, pB, pA);
+    // four pairs move the code sets on by one: rename for the next round
+    const PairCodes t0 = c0;
+    c0 = c1;
+    c1 = c2;
+    c2 = t0;
   }
-  if (pr + 0 < npairs) pair_fn(pr + 0, S0(), bA, bB, cB, cA);
-  if (pr + 1 < npairs) pair_fn(pr + 1, S1(), bB, bA, cA, cB);
-  if (pr + 2 < npairs) pair_fn(pr + 2, S2(), bA, bB, cB, cA);
+  if (pr + 0 < npairs) pair_fn(pr + 0, S0(), c0, c1, c2, pA, pB);
+  if (pr + 1 < npairs) pair_fn(pr + 1, S1(), c1, c2, c0, pB, pA);
+  if (pr + 2 < npairs) pair_fn(pr + 2, S2(), c2, c0, c1, pA, pB);
   wait_vm_lgkm0<0>();  // direct-to-LDS loads must land before the workgroup ends
 
   // Adapter term: 2r extra reduction elements, 16 per MFMA; lane half h

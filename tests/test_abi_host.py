@@ -244,15 +244,16 @@ def test_workspace_query(lib):
     assert q.qlora_workspace_bytes(0, 4096, 4096, 4096, 16) > q.qlora_workspace_bytes(0, 1024, 4096, 4096, 16)
     assert q.qlora_workspace_bytes(1, 4096, 11008, 4096, 16) > 0
     assert q.qlora_workspace_bytes(0, 16, 4096, 4000, 16) == 0
-    assert q.qlora_workspace_bytes(3, 16, 4096, 4096, 16) == 0  # no such op
-    # the forward never holds a bf16 copy of the weight (the large-batch
-    # kernel dequantizes in registers); the backward's dX from 512 rows on
-    # keeps the transposed dequantized weight in the workspace
-    big = q.qlora_workspace_bytes(0, 512, 4096, 1024, 16)
-    assert big < 4096 * 1024 * 2 // 8
-    big = q.qlora_workspace_bytes(1, 512, 4096, 1024, 16)
-    small = q.qlora_workspace_bytes(1, 511, 4096, 1024, 16)
-    assert big - small >= 4096 * 1024 * 2
+    assert q.qlora_workspace_bytes(4, 16, 4096, 4096, 16) == 0  # no such op
+    # from 512 rows on the fast routes hold one bf16 copy of the weight; the
+    # forward's lean route (fused in-register dequantization) holds none
+    for op in (0, 1):
+        big = q.qlora_workspace_bytes(op, 512, 4096, 1024, 16)
+        small = q.qlora_workspace_bytes(op, 511, 4096, 1024, 16)
+        assert big - small >= 4096 * 1024 * 2
+    lean = q.qlora_workspace_bytes(3, 512, 4096, 1024, 16)
+    assert 0 < lean < 4096 * 1024 * 2 // 8
+    assert q.qlora_workspace_bytes(3, 16, 4096, 1024, 16) == q.qlora_workspace_bytes(0, 16, 4096, 1024, 16)
 
 
 @pytest.fixture(scope="module")

@@ -312,12 +312,15 @@ def test_fwd_full_small(M, N, K, r):
     say("fwd small", M, N, K, r)
     P = Problem(N, K, r, 32.0, seed=M + N + K)
     x = syn.normal_bf16((M, K), 1.0, 7 + M)
-    y = host(run_fwd(P, x))
     yo, _ = oracle.linear_fwd(x, P.What, P.A, P.B, r, 32.0)
-    tol_check(y, yo, f"y {M}x{N}x{K}")
-    # bf16 output is the RNE rounding of the fp32 output of the same computation
-    yb = run_fwd(P, x, y_dtype=torch.bfloat16)
-    assert torch.equal(yb, torch.from_numpy(y).to(torch.bfloat16).to(DEV))
+    # from 512 rows on both routes: one bf16 copy of the weight in the
+    # workspace (fast) and the fused in-register dequantization (lean)
+    for lean in ((False, True) if M >= 512 else (False,)):
+        y = host(run_fwd(P, x, lean=lean))
+        tol_check(y, yo, f"y {M}x{N}x{K} lean={lean}")
+        # bf16 output is the RNE rounding of the fp32 output of the same computation
+        yb = run_fwd(P, x, y_dtype=torch.bfloat16, lean=lean)
+        assert torch.equal(yb, torch.from_numpy(y).to(torch.bfloat16).to(DEV))
 
 
 def test_fwd_linear_1024_f32_weight():
@@ -345,6 +348,8 @@ def test_fwd_train_llama7b_sampled_rows(name):
     yo, uo = oracle.linear_fwd(x[rows], P.What, P.A, P.B, P.r, P.alpha)
     tol_check(host(y)[rows], yo, f"y train {name}")
     tol_check(host(u)[rows], uo, f"u train {name}")
+    yl = run_fwd(P, x, lean=True)
+    tol_check(host(yl)[rows], yo, f"y train {name} lean")
 
 
 def test_fwd_one_hot_rows_exact_gemm_and_gemv():
@@ -353,13 +358,13 @@ def test_fwd_one_hot_rows_exact_gemm_and_gemv():
     N, K, r = 512, 1024, 16
     P = Problem(N, K, r, 32.0, seed=5)
     P.Bt = torch.zeros_like(P.Bt)
-    for M in (16, 64, 600):
+    for M, lean in ((16, False), (64, False), (600, False), (600, True)):
         ks = np.random.default_rng(M).choice(K, M, replace=False)
         x = np.zeros((M, K), np.uint16)
         x[np.arange(M), ks] = 0x3F80
-        y = host(run_fwd(P, x))
+        y = host(run_fwd(P, x, lean=lean))
         Wf = oracle.bf16_to_f32(P.What)
-        assert np.array_equal(y, Wf[:, ks].T + 0.0), f"one-hot M={M}"
+        assert np.array_equal(y, Wf[:, ks].T + 0.0), f"one-hot M={M} lean={lean}"
 
 
 def test_fwd_lora_only_isolated():
@@ -941,11 +946,12 @@ def test_formats_one_hot_fwd_and_bwd_exact(fmt):
     P = Problem(N, K, r, 32.0, seed=304, fmt=fmt)
     P.Bt = torch.zeros_like(P.Bt)
     Wf = oracle.bf16_to_f32(P.What)
-    for M in (16, 64, 600):
+    for M, lean in ((16, False), (64, False), (600, False), (600, True)):
         ks = np.random.default_rng(M).choice(K, M, replace=False)
         x = np.zeros((M, K), np.uint16)
         x[np.arange(M), ks] = 0x3F80
-        assert np.array_equal(host(run_fwd(P, x)), Wf[:, ks].T + 0.0), f"fwd one-hot M={M}"
+        assert np.array_equal(host(run_fwd(P, x, lean=lean)), Wf[:, ks].T + 0.0), \
+            f"fwd one-hot M={M} lean={lean}"
     for M in (40, 600):
         ns = np.random.default_rng(M + 1).choice(N, M, replace=False)
         dY = np.zeros((M, N), np.uint16)
