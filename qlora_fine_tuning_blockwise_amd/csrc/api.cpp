@@ -69,7 +69,7 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u, bool l
   } else {
     L.At = c.take((size_t)r * K * 2);
     L.u = need_u ? c.take((size_t)M * r * 4) : 0;
-    L.down = c.take((size_t)lora_down_slices(K) * M * r * 4);
+    L.down = c.take((size_t)lora_down_slices(M, K, r) * M * r * 4);
     L.Bt = c.take((size_t)N * r * 2);
     L.ulr = c.take((size_t)M * 2 * r * 2);
     L.plain = !lean && fwd_plain(M, N, K);
@@ -91,9 +91,9 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   // u is recomputed with the kernels of the forward pass for this M, so that
   // it has the same bits as the u the forward pass returns.
   if (need_u && M > kGemvMaxM) L.At = c.take((size_t)r * K * 2);
-  const int64_t T = K > N ? K : N;
-  const int down_slices = lora_down_slices(T) > decode_down_slices(K) ? lora_down_slices(T)
-                                                                      : decode_down_slices(K);
+  int down_slices = decode_down_slices(K);
+  if (lora_down_slices(M, K, r) > down_slices) down_slices = lora_down_slices(M, K, r);
+  if (lora_down_slices(M, N, r) > down_slices) down_slices = lora_down_slices(M, N, r);
   L.down = c.take((size_t)down_slices * M * r * 4);
   L.v = c.take((size_t)M * r * 4);
   L.svlr = c.take((size_t)M * 2 * r * 2);
@@ -327,7 +327,8 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
     } else {
       if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
       if (e == hipSuccess)
-        e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, u, ulr, nullptr, st);
+        e = launch_lora_down_finalize(down, lora_down_slices(M, K, r), M, r, s, u, ulr, nullptr,
+                                      st);
     }
     if (e == hipSuccess && L.plain) {
       uint16_t* W = at<uint16_t>(workspace, L.W);
@@ -394,7 +395,7 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
   } else {
     e = launch_lora_down_parts(dY, B, M, N, r, down, st);
     if (e == hipSuccess)
-      e = launch_lora_down_finalize(down, lora_down_slices(N), M, r, s, v, svlr,
+      e = launch_lora_down_finalize(down, lora_down_slices(M, N, r), M, r, s, v, svlr,
                                     dA ? vT : nullptr, st);
   }
   if (e == hipSuccess && dX && L.plain) {  // dX = dY w_hat through w_hat^T [K,N]
@@ -424,7 +425,8 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
       } else {
         if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
         if (e == hipSuccess)
-          e = launch_lora_down_finalize(down, lora_down_slices(K), M, r, s, nullptr, nullptr, uT,
+          e = launch_lora_down_finalize(down, lora_down_slices(M, K, r), M, r, s, nullptr, nullptr,
+                                        uT,
                                         st);
       }
     } else {

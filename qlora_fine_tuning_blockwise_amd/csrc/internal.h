@@ -60,7 +60,7 @@ hipError_t launch_transpose2_bf16(const uint16_t* in0, int64_t rows0, int64_t co
 // lr[m][0..r) = bf16(s*out), lr[m][r..2r) = bf16(s*out - hi); if lrT != NULL
 // transposed as lrT[j][m] (hi) and lrT[r+j][m] (lo), row stride
 // Mp = round_up(M, 8), zero for m >= M.
-int lora_down_slices(int64_t T);
+int lora_down_slices(int64_t M, int64_t T, int r);
 hipError_t launch_lora_down_parts(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
                                   int r, float* part, hipStream_t st);
 // lora_down and lora_down_finalize in one pass, for large M (see

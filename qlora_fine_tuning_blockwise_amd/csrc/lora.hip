@@ -294,6 +294,99 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
   }
 }
 
+// Tiled form for large M and ranks that are multiples of 32 (from 64 on),
+// where the 16-row kernel above re-reads the whole rank-side operand from L2
+// for every 16 rows (at r = 64 four times the activation bytes): a
+// 256-thread workgroup owns 128 rows x 64 rank columns of one 512-wide slice
+// of T. Its slice of P [64 rows x 512 t] is staged once in LDS and read by
+// all four waves (row stride 520 elements: consecutive rows start 4 banks
+// apart); wave w owns rows 32w .. 32w+31 and loads its activation fragments
+// straight from X (row i, 8 consecutive t per lane: two lanes per row cover
+// 32 bytes per instruction, and the four instructions of each 64-t group
+// cover whole 128-byte lines). v_mfma_f32_32x32x16_bf16, two 32-column
+// tiles; the slice's partial sums go to part[slice][m][j] for the finalize,
+// which adds the slices in order. Requires T % 8 == 0; reads past T are
+// clamped into X and P and multiply zeros.
+constexpr int kTileT = 512;   // t per slice
+constexpr int kTileLd = 520;  // staged P row stride (bf16)
+
+__global__ __launch_bounds__(256) void lora_down_tile_kernel(const uint16_t* __restrict__ X,
+                                                             const uint16_t* __restrict__ P,
+                                                             int64_t M, int64_t T, int r,
+                                                             float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t ps[64 * kTileLd];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 31, h = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.x * 128 + 32 * w;
+  const int j0 = blockIdx.y * 64;
+  const int ncol = min(2, (r - j0) / 32);  // 32-column tiles of this workgroup
+  const int slice = blockIdx.z;
+  const int64_t t0 = (int64_t)slice * kTileT;
+  const int64_t tend = min(T, t0 + kTileT);
+
+  // Stage P rows j0 .. j0+63 (rows past r read row r-1, multiplied by
+  // nothing that is stored) and t0 .. t0+511 (past T: zero).
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = q * 256 + tid;  // 16-byte chunk: row e/64, t 8*(e%64)
+    const int row = e >> 6, tc = 8 * (e & 63);
+    const int64_t prow = min(j0 + row, r - 1);
+    const int64_t t = t0 + tc;
+    const u32x4_t v = t < tend ? *reinterpret_cast<const u32x4_t*>(P + prow * T + t) : zero4();
+    *reinterpret_cast<u32x4_t*>(&ps[row * kTileLd + tc]) = v;
+  }
+
+  // Activation fragments: row m0 + i (clamped to M-1), t = t0 + 16*st + 8h.
+  const int64_t arow = min(m0 + i, M - 1);
+  const uint16_t* xr = X + arow * T;
+  auto xload = [&](int st) {
+    const int64_t t = t0 + 16 * st + 8 * h;
+    return t < tend ? *reinterpret_cast<const u32x4_t*>(xr + t) : zero4();
+  };
+  f32x16_t acc[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
+  u32x4_t xa[8], xb[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) xa[st] = xload(st);
+  __syncthreads();  // P staged
+  // 32 steps of 16 t in four groups of 8; the next group's loads fly while
+  // this one's MFMAs run.
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    u32x4_t(&cur)[8] = (grp & 1) ? xb : xa;
+    u32x4_t(&nxt)[8] = (grp & 1) ? xa : xb;
+    if (grp < 3) {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) nxt[st] = xload(8 * (grp + 1) + st);
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int tt = 16 * (8 * grp + st) + 8 * h;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        if (ct < ncol) {
+          const u32x4_t b = *reinterpret_cast<const u32x4_t*>(&ps[(32 * ct + i) * kTileLd + tt]);
+          acc[ct] = mfma_32x32x16(cur[st], b, acc[ct]);
+        }
+      }
+    }
+  }
+  // element e of tile ct: row 8(e/4) + 4h + e%4 of the wave's 32, column
+  // 32ct + i of the workgroup's 64
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    if (ct < ncol) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) part[((int64_t)slice * M + m) * r + j0 + 32 * ct + i] = acc[ct][e];
+      }
+    }
+  }
+}
+
 // out[m][j] = sum over slices (skipped if out == NULL); with sv = s*out:
 // lr[m][j] = bf16(sv), lr[m][r+j] = bf16(sv - hi) (row-major two-term split),
 // lrT[j][m] = bf16(sv), lrT[r+j][m] = bf16(sv - hi) (transposed, row stride
@@ -530,12 +623,27 @@ hipError_t launch_transpose2_bf16(const uint16_t* in0, int64_t rows0, int64_t co
   return hipGetLastError();
 }
 
-int lora_down_slices(int64_t T) { return (int)((T + kDownTC - 1) / kDownTC); }
+// The tiled down projection serves large M with ranks that are multiples of
+// 32 from 64 on (r = 16 and 32 take the single-pass kernel from M = 2048).
+static bool lora_down_tiled(int64_t M, int64_t T, int r) {
+  return M >= 1024 && r >= 64 && r % 32 == 0 && T % 8 == 0;
+}
+
+int lora_down_slices(int64_t M, int64_t T, int r) {
+  return lora_down_tiled(M, T, r) ? (int)((T + kTileT - 1) / kTileT)
+                                  : (int)((T + kDownTC - 1) / kDownTC);
+}
 
 hipError_t launch_lora_down_parts(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
                                   int r, float* part, hipStream_t st) {
+  if (lora_down_tiled(M, T, r)) {
+    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((r + 63) / 64),
+                    (unsigned)lora_down_slices(M, T, r));
+    hipLaunchKernelGGL(lora_down_tile_kernel, grid, dim3(256), 0, st, X, P, M, T, r, part);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 63) / 64),
-                  (unsigned)lora_down_slices(T));
+                  (unsigned)lora_down_slices(M, T, r));
   hipLaunchKernelGGL(lora_down_kernel, grid, dim3(256), 0, st, X, P, M, T, r, part);
   return hipGetLastError();
 }

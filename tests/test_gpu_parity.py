@@ -307,7 +307,10 @@ def test_fwd_decode_llama7b(M, name):
                                      # counts off the four-pair unroll (5, 7), weight rows
                                      # that leave waves or whole 32-row halves empty
                                      (1024, 1000, 64, 16), (520, 100, 320, 16),
-                                     (513, 40, 448, 32), (777, 289, 192, 48)])
+                                     (513, 40, 448, 32), (777, 289, 192, 48),
+                                     # tiled down projection: 128-row tiles, 512-wide
+                                     # slices with a ragged last one, r = 64 and 96
+                                     (1024, 520, 1088, 64), (1100, 200, 320, 96)])
 def test_fwd_full_small(M, N, K, r):
     say("fwd small", M, N, K, r)
     P = Problem(N, K, r, 32.0, seed=M + N + K)
@@ -521,7 +524,14 @@ def run_bwd(P, x, dY, **kw):
                                      (600, 544, 192, 16), (520, 320, 640, 32),
                                      # single-pass down projections (v over N, the
                                      # recomputed u over K) with r = 32, M >= 2048
-                                     (2056, 544, 640, 32)])
+                                     (2056, 544, 640, 32),
+                                     # tiled down projections (128-row tiles, 512-wide
+                                     # slices, two rank chunks at r = 96), ragged M
+                                     (1100, 200, 1088, 64), (1030, 520, 320, 96),
+                                     # dX from 512 rows with N % 32 != 0: the tile
+                                     # kernel (N % 8 == 0) and the general one
+                                     (600, 1000, 192, 16), (520, 1100, 320, 32),
+                                     (600, 100, 128, 16)])
 def test_bwd_full_small(M, N, K, r):
     say("bwd small", M, N, K, r)
     P = Problem(N, K, r, 24.0, seed=M + 2 * N + K)
@@ -538,11 +548,13 @@ def test_bwd_full_small(M, N, K, r):
     assert torch.equal(dAb, dA.to(torch.bfloat16)) and torch.equal(dBb, dB.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("M,N,K,r", [(5, 520, 1024, 32), (16, 300, 4096, 16)])
+@pytest.mark.parametrize("M,N,K,r", [(5, 520, 1024, 32), (16, 300, 4096, 16),
+                                     (1100, 200, 1088, 64)])
 def test_bwd_decode_recomputed_u_matches_saved(M, N, K, r):
-    """At decode sizes the backward recomputes u with the forward's down
-    projection and slice sum: the same bits as the u the forward returns, so
-    dA and dB agree exactly with u_saved given or not."""
+    """The backward recomputes u with the forward's down projection and slice
+    sum (at decode sizes and through the tiled kernel): the same bits as the u
+    the forward returns, so dA and dB agree exactly with u_saved given or
+    not."""
     P = Problem(N, K, r, 24.0, seed=M + N)
     x = syn.normal_bf16((M, K), 1.0, 40 + M)
     dY = syn.normal_bf16((M, N), 1.0, 41 + M)
@@ -688,6 +700,39 @@ def test_layer_70b_fwd_bwd_sampled():
         for g, rr, k in zip(got, ref, ("y", "dX", "dA", "dB")):
             tol_check(g, rr, f"70b {name} {k}")
         say("70b layer ok", name)
+
+
+# ------------------------------------------------------- beyond 2^31 bytes
+def test_fwd_bwd_weight_past_2gib_of_bf16():
+    """A weight whose bf16 copy is past 2^31 bytes (16448 x 65536, 1.08G
+    weights) at M = 512: the forward takes the fused route (the dense
+    stage's 32-bit offsets cannot hold the copy) and the backward's dX the
+    tile kernel. Sampled rows of y and dX against the oracle, which quantizes
+    the same bf16 weight itself."""
+    N, K, M, r = 16448, 65536, 512, 16
+    say("weight past 2 GiB", N, K)
+    assert 2 * N * K >= 2 ** 31
+    Wb = syn.normal_bf16((N, K), 0.02, 90)
+    w = quantize_gpu(dev_bf16(Wb))
+    codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+    del Wb
+    assert_nf4_equal(w, codes, q8, s2, "weight past 2 GiB")
+    What = oracle.dequant_dq(codes, q8, s2)[1].reshape(N, K)
+    del codes, q8, s2
+    A = syn.normal_bf16((K, r), 1.0 / np.sqrt(K), 91)
+    B = syn.normal_bf16((r, N), 0.01, 92)
+    x = syn.normal_bf16((M, K), 1.0, 93)
+    dY = syn.normal_bf16((M, N), 1.0, 94)
+    At, Bt = dev_bf16(A), dev_bf16(B)
+    assert q.qlora_workspace_bytes(0, M, N, K, r) == q.qlora_workspace_bytes(3, M, N, K, r)
+    y = q.qlora_linear_fwd(w, dev_bf16(x), At, Bt, 32.0)
+    dX, _, _ = q.qlora_linear_bwd(w, None, dev_bf16(dY), At, Bt, 32.0, want_grads=False)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 300, M - 1])
+    yo, _ = oracle.linear_fwd(x[rows], What, A, B, r, 32.0)
+    tol_check(host(y)[rows], yo, "y past 2 GiB")
+    go = oracle.linear_bwd(x[rows], dY[rows], What, A, B, r, 32.0, ("dX",))
+    tol_check(host(dX)[rows], go["dX"], "dX past 2 GiB")
 
 
 # ------------------------------------------------------------ descriptor
