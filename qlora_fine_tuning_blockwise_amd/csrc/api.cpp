@@ -55,8 +55,9 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, W = 0, total = 0;
+  size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, W = 0, part = 0, total = 0;
   bool gemv_path = false, plain = false, fused = false;
+  int splits = 1;  // reduction splits of the dense stage (fp32 partials at `part`)
 };
 
 // lean: the layout of the lean route (no bf16 copy of the weight).
@@ -74,15 +75,20 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u, bool l
     L.ulr = c.take((size_t)M * 2 * r * 2);
     L.plain = !lean && fwd_plain(M, N, K);
     L.fused = !L.plain && fwd_fused(M, N, K);
-    if (L.plain) L.W = c.take((size_t)N * K * 2);
+    if (L.plain) {
+      L.W = c.take((size_t)N * K * 2);
+      L.splits = gemm_nt_splits(M, N, K);
+      if (L.splits > 1) L.part = c.take((size_t)L.splits * M * N * 4);
+    }
   }
   L.total = c.off;
   return L;
 }
 
 struct BwdLayout {
-  size_t At = 0, down = 0, v = 0, svlr = 0, vT = 0, uT = 0, col = 0, Wt = 0, total = 0;
+  size_t At = 0, down = 0, v = 0, svlr = 0, vT = 0, uT = 0, col = 0, Wt = 0, part = 0, total = 0;
   bool plain = false;
+  int splits = 1;  // reduction splits of the dense stage for dX
 };
 
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
@@ -102,7 +108,11 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   L.uT = c.take(2 * (size_t)r * Mp * 2);
   L.col = c.take((size_t)colred_splits(M) * (K + N) * r * 4);  // dA's partials, then dB's
   L.plain = bwd_plain(M, N, K);
-  if (L.plain) L.Wt = c.take((size_t)K * N * 2);
+  if (L.plain) {
+    L.Wt = c.take((size_t)K * N * 2);
+    L.splits = gemm_nt_splits(M, K, N);
+    if (L.splits > 1) L.part = c.take((size_t)L.splits * M * K * 4);
+  }
   L.total = c.off;
   return L;
 }
@@ -333,7 +343,9 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
     if (e == hipSuccess && L.plain) {
       uint16_t* W = at<uint16_t>(workspace, L.W);
       e = launch_dequant(codes, absmax_q, absmax_scale, N * K, W, N, cb, st);  // K-slab
-      if (e == hipSuccess) e = launch_gemm_nt(x, K, W, 0, ulr, Bt, M, N, K, r, y, ybf, true, st);
+      if (e == hipSuccess)
+        e = launch_gemm_nt(x, K, W, 0, ulr, Bt, M, N, K, r, y, ybf, true, st, L.splits,
+                           at<float>(workspace, L.part));
     } else if (e == hipSuccess && L.fused) {
       e = launch_gemm_nf4_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, cb,
                               st);
@@ -403,7 +415,7 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
     e = launch_dequant_t(codes, absmax_q, absmax_scale, N, K, Wt, true, cb, st);  // K-slab
     if (e == hipSuccess)
       e = launch_gemm_nt(dY, N, Wt, 0, svlr, A, M, K, N, r, dX, dx_dtype == QLORA_DTYPE_BF16, true,
-                         st);
+                         st, L.splits, at<float>(workspace, L.part));
   } else if (e == hipSuccess && dX) {
     e = launch_gemm_bwd(dY, codes, absmax_q, absmax_scale, svlr, A, M, N, K, r, dX,
                         dx_dtype == QLORA_DTYPE_BF16, cb, st);

@@ -43,6 +43,12 @@ struct NtArgs {
   int64_t M, N, Kr, lda, ldb;
   int r;
   int tiles_m, tiles_n;
+  // K split: workgroup wg takes tile wg / ksplit and the split wg % ksplit
+  // of the reduction steps; with ksplit > 1 every split stores its fp32 sums
+  // to part + split * M * N (the rank extension rides in split 0) and a
+  // reduce kernel adds the splits in order into y.
+  int ksplit;
+  float* part;
   // b in the K-slab layout [Kr/32][N][32]: the 32 reduction elements of one
   // step of every row are one contiguous 64-byte piece, and a step's rows
   // follow each other, so a direct-to-LDS load of 16 rows reads 1 KB of
@@ -107,7 +113,7 @@ __device__ __forceinline__ T* pick(T* const (&arr)[N]) {
 // overwrites was last read before the previous barrier.
 constexpr int kNtPair = kNtBM * 2 * kNtBK;  // bf16 elements of one a pair slot (32 KB)
 
-template <bool kOutBf16>
+template <bool kOutBf16, bool kSplit>
 __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sa0[kNtPair];
   __shared__ __attribute__((aligned(1024))) uint16_t sa1[kNtPair];
@@ -122,11 +128,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = w >> 1, wn = w & 1;
   int tm, tn;
-  nt_tile((int)blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int split = kSplit ? (int)blockIdx.x % p.ksplit : 0;
+  nt_tile(kSplit ? (int)blockIdx.x / p.ksplit : (int)blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t M = p.M, N = p.N;
   const int64_t m0 = (int64_t)tm * kNtBM, n0 = (int64_t)tn * kNtBN;
-  const int nsteps = (int)(p.Kr / kNtBK);
+  // this split's reduction steps [ks0, ks0 + nsteps)
+  const int steps_all = (int)(p.Kr / kNtBK);
+  const int per_split = kSplit ? (steps_all + p.ksplit - 1) / p.ksplit : steps_all;
+  const int ks0 = split * per_split;
+  const int nsteps = kSplit ? min(per_split, steps_all - ks0) : steps_all;
   const int npairs = (nsteps + 1) / 2;
+  const int64_t k0 = (int64_t)ks0 * kNtBK;  // first reduction element
 
   // Direct-to-LDS roles. a: wave w loads rows 64w + 8q + L/8 (q = 0..7) of
   // each pair, lane L at LDS position L%8 (global chunk (L%8) ^ ((row>>1)&7));
@@ -153,12 +165,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
   // Bytes from the tile's first row to the matrix's last element; a tile's
   // own offsets stay below 2^31 (gemm_nt_supported), so clamping a longer
   // range only matters for tiles that are not the last and read in bounds.
-  const int64_t a_bytes = min(((M - 1 - m0) * p.lda + p.Kr) * 2, (int64_t)0x7FFFFFFF);
+  const int64_t a_bytes = min(((M - 1 - m0) * p.lda + p.Kr - k0) * 2, (int64_t)0x7FFFFFFF);
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(p.a + m0 * p.lda), (short)0, (int)a_bytes, 0x00020000);
+      (void*)uniform_ptr(p.a + m0 * p.lda + k0), (short)0, (int)a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(p.b + n0 * (p.b_kslab ? 32 : p.ldb)), (short)0, (int)0x7FFFFFFF,
-      0x00020000);
+      (void*)uniform_ptr(p.b + (p.b_kslab ? n0 * 32 + k0 * N : n0 * p.ldb + k0)), (short)0,
+      (int)0x7FFFFFFF, 0x00020000);
   const int bstep = p.b_kslab ? (int)(64 * N) : 64;  // bytes from one step to the next
   typedef __attribute__((address_space(3))) void lds_void;
   auto dma_a = [&](int q, int pair, uint16_t* slot) {
@@ -342,12 +354,32 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
   // Direct-to-LDS loads still in flight must land before the workgroup ends.
   wait_vmem_lgkm0<0>();
 
-  // Adapter term as 2r extra reduction elements, 16 per MFMA.
-  ext_mfma(e0, f0);
-  ext_mfma(e1, f1);
-  for (int q = 2; q < r2 / 16; ++q) {
-    ext_load(q, e0, f0);
+  // Adapter term as 2r extra reduction elements, 16 per MFMA (split 0 only).
+  if (!kSplit || split == 0) {
     ext_mfma(e0, f0);
+    ext_mfma(e1, f1);
+    for (int q = 2; q < r2 / 16; ++q) {
+      ext_load(q, e0, f0);
+      ext_mfma(e0, f0);
+    }
+  }
+  if (kSplit) {  // fp32 partial sums of this split
+    float* dst = p.part + (int64_t)split * M * N;
+    const int64_t mw = m0 + 128 * wm + 4 * h, nw = n0 + 128 * wn + i;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int64_t n = nw + 32 * nt;
+      if (n < N) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t m = mw + 32 * mt + 8 * (e >> 2) + (e & 3);
+            if (m < M) dst[m * N + n] = acc[mt][nt][e];
+          }
+      }
+    }
+    return;
   }
 
   // Output. Accumulator element e of (mt, nt) is row 32mt + 8(e/4) + 4h +
@@ -394,7 +426,49 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(NtArgs p) {
   }
 }
 
+// y[i] = sum over splits s = 0, 1, ... of part[s][i], in that order (fp32,
+// or bf16 by round to nearest even of the fp32 sum); four elements a thread.
+template <bool kOutBf16>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           int splits, int64_t n, void* y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  if (i + 4 <= n && (n & 3) == 0) {
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + i);
+    for (int s = 1; s < splits; ++s) {
+      const f32x4_t t = *reinterpret_cast<const f32x4_t*>(part + (int64_t)s * n + i);
+      v = f32x4_t{v[0] + t[0], v[1] + t[1], v[2] + t[2], v[3] + t[3]};
+    }
+    if (kOutBf16)
+      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(y) + i) =
+          u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    else
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(y) + i) = v;
+    return;
+  }
+  for (int64_t j = i; j < i + 4 && j < n; ++j) {
+    float v = part[j];
+    for (int s = 1; s < splits; ++s) v += part[(int64_t)s * n + j];
+    if (kOutBf16)
+      static_cast<uint16_t*>(y)[j] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    else
+      static_cast<float*>(y)[j] = v;
+  }
+}
+
 }  // namespace
+
+int gemm_nt_splits(int64_t M, int64_t N, int64_t Kr) {
+  // Few output tiles (under a quarter of the 256 CUs) and a long reduction:
+  // split the reduction so that the launch fills the GPU, at least 16 steps
+  // of 32 per split.
+  const int64_t tiles = ((M + kNtBM - 1) / kNtBM) * ((N + kNtBN - 1) / kNtBN);
+  if (tiles >= 64) return 1;
+  int s = (int)(256 / tiles);
+  if (s > 8) s = 8;
+  while (s > 1 && Kr / kNtBK / s < 16) --s;
+  return s < 1 ? 1 : s;
+}
 
 bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb, int64_t N, bool b_kslab) {
   // Buffer offsets (tile row offset + step offset) stay below 2^31.
@@ -405,14 +479,32 @@ bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb, int64_t N, bool b_k
 
 hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                           const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t Kr,
-                          int r, void* y, bool y_bf16, bool b_kslab, hipStream_t st) {
+                          int r, void* y, bool y_bf16, bool b_kslab, hipStream_t st,
+                          int ksplit, float* part) {
+  if (ksplit < 1 || !part) ksplit = 1;
+  // every split must hold at least one step
+  const int64_t steps = Kr / kNtBK;
+  while (ksplit > 1 && (ksplit - 1) * ((steps + ksplit - 1) / ksplit) >= steps) --ksplit;
   const int tiles_m = (int)((M + kNtBM - 1) / kNtBM), tiles_n = (int)((N + kNtBN - 1) / kNtBN);
-  const NtArgs args{a, b, e, f, y, M, N, Kr, lda, ldb, r, tiles_m, tiles_n, b_kslab ? 1 : 0};
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
-  if (y_bf16)
-    hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(256), 0, st, args);
+  const NtArgs args{a,       b,       e, f, y, M, N, Kr, lda, ldb, r, tiles_m, tiles_n, ksplit,
+                    part, b_kslab ? 1 : 0};
+  const dim3 grid((unsigned)(tiles_m * tiles_n * ksplit));
+  if (ksplit > 1)
+    hipLaunchKernelGGL((gemm_nt_kernel<false, true>), grid, dim3(256), 0, st, args);
+  else if (y_bf16)
+    hipLaunchKernelGGL((gemm_nt_kernel<true, false>), grid, dim3(256), 0, st, args);
   else
-    hipLaunchKernelGGL(gemm_nt_kernel<false>, grid, dim3(256), 0, st, args);
+    hipLaunchKernelGGL((gemm_nt_kernel<false, false>), grid, dim3(256), 0, st, args);
+  if (ksplit > 1) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t n = M * N;
+    const dim3 rg((unsigned)((n + 1023) / 1024));
+    if (y_bf16)
+      hipLaunchKernelGGL(split_reduce_kernel<true>, rg, dim3(256), 0, st, part, ksplit, n, y);
+    else
+      hipLaunchKernelGGL(split_reduce_kernel<false>, rg, dim3(256), 0, st, part, ksplit, n, y);
+  }
   return hipGetLastError();
 }
 

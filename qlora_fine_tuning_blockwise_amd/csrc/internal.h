@@ -102,10 +102,15 @@ hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_
 // by launch_lora_down_finalize; f [N,r]). gemm_nt_supported says whether the
 // shape fits the kernel (Kr a multiple of 32, 16-byte aligned rows, 32-bit
 // buffer offsets).
+// With few output tiles the reduction is split (gemm_nt_splits > 1): each
+// split writes fp32 sums to part [splits][M][N] and a reduce launch adds
+// them in split order into y.
 bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb, int64_t N, bool b_kslab);
+int gemm_nt_splits(int64_t M, int64_t N, int64_t Kr);
 hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                           const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t Kr,
-                          int r, void* y, bool y_bf16, bool b_kslab, hipStream_t st);
+                          int r, void* y, bool y_bf16, bool b_kslab, hipStream_t st,
+                          int ksplit = 1, float* part = nullptr);
 // Fused large-M forward: y = x W_hat^T + e [f|f]^T with the NF4 weight
 // dequantized in registers right before the MFMAs (no bf16 copy of the
 // weight). e is the two-term split of s*u (launch_lora_down_*), f = B^T.

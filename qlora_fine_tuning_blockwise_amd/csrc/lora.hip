@@ -303,10 +303,11 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
 // apart); wave w owns rows 32w .. 32w+31 and loads its activation fragments
 // straight from X (row i, 8 consecutive t per lane: two lanes per row cover
 // 32 bytes per instruction, and the four instructions of each 64-t group
-// cover whole 128-byte lines). v_mfma_f32_32x32x16_bf16, two 32-column
-// tiles; the slice's partial sums go to part[slice][m][j] for the finalize,
-// which adds the slices in order. Requires T % 8 == 0; reads past T are
-// clamped into X and P and multiply zeros.
+// cover whole 128-byte lines). All of a workgroup's loads are issued before
+// it waits (one round trip to memory). v_mfma_f32_32x32x16_bf16, two
+// 32-column tiles; the slice's partial sums go to part[slice][m][j] for the
+// finalize, which adds the slices in order. Requires T % 8 == 0; reads past
+// T read zeros.
 constexpr int kTileT = 512;   // t per slice
 constexpr int kTileLd = 520;  // staged P row stride (bf16)
 
@@ -323,53 +324,45 @@ __global__ __launch_bounds__(256) void lora_down_tile_kernel(const uint16_t* __r
   const int64_t t0 = (int64_t)slice * kTileT;
   const int64_t tend = min(T, t0 + kTileT);
 
-  // Stage P rows j0 .. j0+63 (rows past r read row r-1, multiplied by
-  // nothing that is stored) and t0 .. t0+511 (past T: zero).
+  // Every load is issued first, so the workgroup waits for memory once:
+  // the P slice (rows j0 .. j0+63; rows past r read row r-1, multiplied by
+  // nothing that is stored; t past T read zero), then the wave's 32
+  // activation fragments (row m0 + i clamped to M-1, t = t0 + 16 st + 8h).
+  u32x4_t pv[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int e = q * 256 + tid;  // 16-byte chunk: row e/64, t 8*(e%64)
-    const int row = e >> 6, tc = 8 * (e & 63);
-    const int64_t prow = min(j0 + row, r - 1);
-    const int64_t t = t0 + tc;
-    const u32x4_t v = t < tend ? *reinterpret_cast<const u32x4_t*>(P + prow * T + t) : zero4();
-    *reinterpret_cast<u32x4_t*>(&ps[row * kTileLd + tc]) = v;
+    const int64_t prow = min(j0 + (e >> 6), r - 1);
+    const int64_t t = t0 + 8 * (e & 63);
+    pv[q] = t < tend ? *reinterpret_cast<const u32x4_t*>(P + prow * T + t) : zero4();
   }
-
-  // Activation fragments: row m0 + i (clamped to M-1), t = t0 + 16*st + 8h.
   const int64_t arow = min(m0 + i, M - 1);
   const uint16_t* xr = X + arow * T;
-  auto xload = [&](int st) {
+  u32x4_t xv[32];
+#pragma unroll
+  for (int st = 0; st < 32; ++st) {
     const int64_t t = t0 + 16 * st + 8 * h;
-    return t < tend ? *reinterpret_cast<const u32x4_t*>(xr + t) : zero4();
-  };
+    xv[st] = t < tend ? *reinterpret_cast<const u32x4_t*>(xr + t) : zero4();
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = q * 256 + tid;
+    *reinterpret_cast<u32x4_t*>(&ps[(e >> 6) * kTileLd + 8 * (e & 63)]) = pv[q];
+  }
   f32x16_t acc[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
-  u32x4_t xa[8], xb[8];
-#pragma unroll
-  for (int st = 0; st < 8; ++st) xa[st] = xload(st);
   __syncthreads();  // P staged
-  // 32 steps of 16 t in four groups of 8; the next group's loads fly while
-  // this one's MFMAs run.
 #pragma unroll
-  for (int grp = 0; grp < 4; ++grp) {
-    u32x4_t(&cur)[8] = (grp & 1) ? xb : xa;
-    u32x4_t(&nxt)[8] = (grp & 1) ? xa : xb;
-    if (grp < 3) {
+  for (int st = 0; st < 32; ++st) {
+    const int tt = 16 * st + 8 * h;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) nxt[st] = xload(8 * (grp + 1) + st);
-    }
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const int tt = 16 * (8 * grp + st) + 8 * h;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        if (ct < ncol) {
-          const u32x4_t b = *reinterpret_cast<const u32x4_t*>(&ps[(32 * ct + i) * kTileLd + tt]);
-          acc[ct] = mfma_32x32x16(cur[st], b, acc[ct]);
-        }
+    for (int ct = 0; ct < 2; ++ct) {
+      if (ct < ncol) {
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(&ps[(32 * ct + i) * kTileLd + tt]);
+        acc[ct] = mfma_32x32x16(xv[st], b, acc[ct]);
       }
     }
   }
@@ -626,7 +619,10 @@ hipError_t launch_transpose2_bf16(const uint16_t* in0, int64_t rows0, int64_t co
 // The tiled down projection serves large M with ranks that are multiples of
 // 32 from 64 on (r = 16 and 32 take the single-pass kernel from M = 2048).
 static bool lora_down_tiled(int64_t M, int64_t T, int r) {
-  return M >= 1024 && r >= 64 && r % 32 == 0 && T % 8 == 0;
+  const int64_t wgs = ((M + 127) / 128) * ((r + 63) / 64) * ((T + kTileT - 1) / kTileT);
+  // measured: 21 vs 23 us at T = 8192, but slower than the 16-row kernel at
+  // T = 28672 (82 vs 75 us) and with few workgroups (T = 1024)
+  return M >= 1024 && r >= 64 && r % 32 == 0 && T % 8 == 0 && wgs >= 128 && T <= 16384;
 }
 
 int lora_down_slices(int64_t M, int64_t T, int r) {

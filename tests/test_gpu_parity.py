@@ -310,7 +310,10 @@ def test_fwd_decode_llama7b(M, name):
                                      (513, 40, 448, 32), (777, 289, 192, 48),
                                      # tiled down projection: 128-row tiles, 512-wide
                                      # slices with a ragged last one, r = 64 and 96
-                                     (1024, 520, 1088, 64), (1100, 200, 320, 96)])
+                                     (1024, 520, 1088, 64), (1100, 200, 320, 96),
+                                     # few output tiles: the dense stage splits the
+                                     # reduction (eight splits of 16 steps)
+                                     (600, 300, 4096, 16), (520, 1024, 8192, 64)])
 def test_fwd_full_small(M, N, K, r):
     say("fwd small", M, N, K, r)
     P = Problem(N, K, r, 32.0, seed=M + N + K)
@@ -531,7 +534,9 @@ def run_bwd(P, x, dY, **kw):
                                      # dX from 512 rows with N % 32 != 0: the tile
                                      # kernel (N % 8 == 0) and the general one
                                      (600, 1000, 192, 16), (520, 1100, 320, 32),
-                                     (600, 100, 128, 16)])
+                                     (600, 100, 128, 16),
+                                     # few dX tiles: the reduction over N is split
+                                     (600, 4096, 512, 16)])
 def test_bwd_full_small(M, N, K, r):
     say("bwd small", M, N, K, r)
     P = Problem(N, K, r, 24.0, seed=M + 2 * N + K)
