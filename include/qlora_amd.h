@@ -77,6 +77,8 @@ extern "C" {
 #define QLORA_ERR_INTERNAL 8    /* codebook construction failed its self-check */
 #define QLORA_ERR_SETUP 9       /* weight descriptor from another format version or
                                    quantization setup than this library's */
+#define QLORA_ERR_TOO_LARGE 10  /* the call needs more workspace than the
+                                   allocation-free entry point holds */
 
 /* Element types. */
 #define QLORA_DTYPE_F32 0
@@ -340,6 +342,28 @@ int qlora_adamw_step(float* param, const void* grad, int grad_dtype, float* exp_
 int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                        int b_layout, const uint16_t* e, const uint16_t* f, int64_t M, int64_t N,
                        int64_t K, int r, void* y, int y_dtype, void* stream);
+
+/* Bytes of the device array that qlora_linear_fwd_noalloc uses as its
+ * workspace (one array per GPU, held until the process ends). */
+#define QLORA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* qlora_linear_fwd for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation. Same arguments and results as qlora_linear_fwd without the
+ * workspace: the call takes its workspace from a file-scope device array of
+ * QLORA_NOALLOC_SCRATCH_BYTES on the current device and allocates nothing
+ * (no hipMalloc, no host allocation). It runs the launches that
+ * qlora_linear_fwd runs with a workspace of exactly
+ * qlora_workspace_bytes(QLORA_OP_FWD_LEAN, M, N, K, r) bytes (from 512 rows
+ * on, the fused route that holds no bf16 copy of the weight), so its
+ * results equal that call's bit for bit. QLORA_ERR_TOO_LARGE when that size
+ * exceeds QLORA_NOALLOC_SCRATCH_BYTES, before anything is enqueued; the
+ * other errors as qlora_linear_fwd. All calls on one GPU share its array:
+ * calls that overlap on one GPU (other streams, other threads) race, and the
+ * caller must order them. */
+int qlora_linear_fwd_noalloc(const qlora_nf4* w, const uint16_t* x, int64_t M,
+                             const uint16_t* A, const uint16_t* B, int r, float alpha, void* y,
+                             int y_dtype, float* u_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ __all__ = [
     "qlora_strerror", "qlora_nf4_sizes", "qlora_codebook", "qlora_codebook_quotient_thresholds",
     "qlora_codebook_id", "qlora_setup_id", "qlora_nf4_check",
     "qlora_workspace_bytes", "qlora_quantize_nf4_dq", "qlora_dequant_bf16",
-    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemm_bf16_nt", "qlora_merge_lora", "qlora_adamw_step",
+    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_fwd_noalloc", "qlora_gemm_bf16_nt", "qlora_merge_lora", "qlora_adamw_step",
     "NF4Weight", "DQ_INT8", "DQ_UINT8", "DQ_E4M3", "LAYOUT_ROWS", "LAYOUT_KSLAB32",
 ]
 
@@ -229,6 +229,26 @@ def qlora_linear_fwd(w: NF4Weight, x: torch.Tensor, A: torch.Tensor, B: torch.Te
         w.desc(), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y), _dtype_code(y.dtype),
         _ptr(u_out), _ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st, "qlora_linear_fwd")
+    return y
+
+
+def qlora_linear_fwd_noalloc(w: NF4Weight, x: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                             alpha: float, y: torch.Tensor, u_out: torch.Tensor | None = None,
+                             stream=None) -> torch.Tensor:
+    """qlora_linear_fwd with the library's own device array as the workspace:
+    the call allocates nothing (y and u_out are the caller's)."""
+    M = x.shape[0]
+    r = A.shape[1]
+    dev = w.device
+    _need(x, "x", (M, w.K), torch.bfloat16, dev)
+    _need(A, "A", (w.K, r), torch.bfloat16, dev)
+    _need(B, "B", (r, w.N), torch.bfloat16, dev)
+    _need(y, "y", (M, w.N), (torch.float32, torch.bfloat16), dev)
+    _need(u_out, "u_out", (M, r), torch.float32, dev)
+    st = _lib.load().qlora_linear_fwd_noalloc(
+        w.desc(), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(y), _dtype_code(y.dtype),
+        _ptr(u_out), _stream(stream))
+    _lib.check(st, "qlora_linear_fwd_noalloc")
     return y
 
 

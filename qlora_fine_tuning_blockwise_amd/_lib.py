@@ -25,6 +25,7 @@ OP_FWD = 0
 OP_BWD = 1
 OP_MERGE = 2
 OP_FWD_LEAN = 3
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 P = ctypes.c_void_p
 I64 = ctypes.c_int64
@@ -56,6 +57,7 @@ SIGNATURES = {
     "qlora_dequant_bf16": (INT, [DESC, P, INT, P]),
     "qlora_linear_fwd": (INT, [DESC, P, I64, P, P, INT, FLT, P, INT, P, P, SZ, P]),
     "qlora_linear_bwd": (INT, [DESC, P, P, I64, P, P, INT, FLT, P, P, INT, P, P, INT, P, SZ, P]),
+    "qlora_linear_fwd_noalloc": (INT, [DESC, P, I64, P, P, INT, FLT, P, INT, P, P]),
     "qlora_gemm_bf16_nt": (INT, [P, I64, P, I64, INT, P, P, I64, I64, I64, INT, P, INT, P]),
     "qlora_merge_lora": (INT, [DESC, P, I64, I64, P, P, INT, FLT, P, P, SZ, P]),
     "qlora_adamw_step": (INT, [P, P, INT, P, P, P, I64, DBL, DBL, DBL, DBL, DBL, I64, P]),

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqlora_amd.so")
 SOURCES = ["codebook.cpp", "api.cpp", "quantize.hip", "gemm.hip", "gemm_nt.hip", "gemm_nf4.hip", "lora.hip", "decode.hip", "merge.hip",
-           "adamw.hip"]
+           "adamw.hip", "noalloc.hip"]
 
 # Bit-exact arithmetic: no fast-math, no FP contraction, IEEE fp32 division,
 # denormals kept. Packed-fp32 VALU forms are switched off for the device.

@@ -202,6 +202,8 @@ const char* qlora_strerror(int status) {
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_LAUNCH: return "kernel launch failed";
     case QLORA_ERR_INTERNAL: return "codebook self-check failed";
+    case QLORA_ERR_TOO_LARGE:
+      return "the call needs more workspace than the allocation-free entry point holds";
     case QLORA_ERR_SETUP:
       return "weight descriptor does not match this library's format version or quantization "
              "setup";

@@ -52,8 +52,8 @@ def test_sizes_accounting(lib):
 
 
 def test_strerror_covers_codes(lib):
-    texts = {q.qlora_strerror(s) for s in range(10)}
-    assert len(texts) == 10 and q.qlora_strerror(99) == "unknown status"
+    texts = {q.qlora_strerror(s) for s in range(11)}
+    assert len(texts) == 11 and q.qlora_strerror(99) == "unknown status"
 
 
 FAKE = 1 << 20  # an aligned address never dereferenced: validation fails first

@@ -1,0 +1,101 @@
+"""GPU test of qlora_linear_fwd_noalloc: the forward that allocates nothing
+(its workspace is the library's own device array). Through the C ABI, its
+outputs equal those of qlora_linear_fwd given a workspace of exactly
+qlora_workspace_bytes(QLORA_OP_FWD_LEAN, ...) bytes, bit for bit, and meet the
+oracle's tolerance, on calls in a row with shrinking inputs (the array keeps
+the previous call's contents); a call that needs more than the array holds is
+refused before anything is launched."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qlora_fine_tuning_blockwise_amd as q
+from qlora_fine_tuning_blockwise_amd import _lib
+from qlora_fine_tuning_blockwise_amd import synthetic as syn
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev_bf16(bits):
+    return syn.bits_to_torch_bf16(bits).to(DEV)
+
+
+def tol_check(got, ref, name):
+    got, ref = got.astype(np.float64), ref.astype(np.float64)
+    rf = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    mx = np.max(np.abs(got - ref))
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert rf <= 2e-3, f"{name}: relative Frobenius error {rf:.3e}"
+    assert mx <= 1e-2 * rms, f"{name}: max error {mx:.3e} vs rms {rms:.3e}"
+
+
+def _case(M, N, K, r, y_dtype, with_u, seed):
+    Wb = syn.normal_bf16((N, K), 0.02, seed)
+    w = q.qlora_quantize_nf4_dq(dev_bf16(Wb))
+    codes, q8, s2 = oracle.quantize_nf4_dq(Wb, "bf16")
+    What = oracle.dequant_dq(codes, q8, s2)[1].reshape(N, K)
+    A = syn.normal_bf16((K, r), 1.0 / np.sqrt(K), seed + 1)
+    B = syn.normal_bf16((r, N), 0.01, seed + 2)
+    x = syn.normal_bf16((M, K), 1.0, seed + 3)
+    return w, What, A, B, x
+
+
+@pytest.mark.parametrize("M,N,K,r,y_dtype,with_u", [
+    (600, 520, 1088, 64, torch.float32, True),    # fused route (from 512 rows)
+    (40, 300, 512, 16, torch.bfloat16, False),    # 512 x 128 tile kernel, smaller
+    (4, 300, 512, 32, torch.float32, True),       # decode GEMV, smaller still
+])
+def test_noalloc_forward_equals_the_workspace_call(M, N, K, r, y_dtype, with_u):
+    say("noalloc", M, N, K, r, y_dtype, with_u)
+    alpha = 32.0
+    w, What, A, B, x = _case(M, N, K, r, y_dtype, with_u, 300 + M)
+    xt, At, Bt = dev_bf16(x), dev_bf16(A), dev_bf16(B)
+    y0 = torch.full((M, N), float("nan"), dtype=y_dtype, device=DEV)
+    u0 = torch.full((M, r), float("nan"), dtype=torch.float32, device=DEV) if with_u else None
+    ws = torch.empty(q.qlora_workspace_bytes(_lib.OP_FWD_LEAN, M, N, K, r), dtype=torch.uint8,
+                     device=DEV)
+    q.qlora_linear_fwd(w, xt, At, Bt, alpha, y=y0, u_out=u0, workspace=ws)
+    # the entry point through the raw C ABI, then through the binding
+    y1 = torch.full((M, N), float("nan"), dtype=y_dtype, device=DEV)
+    u1 = torch.full((M, r), float("nan"), dtype=torch.float32, device=DEV) if with_u else None
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    st = _lib.load().qlora_linear_fwd_noalloc(
+        w.desc(), ptr(xt), M, ptr(At), ptr(Bt), r, alpha, ptr(y1),
+        _lib.DTYPE_F32 if y_dtype == torch.float32 else _lib.DTYPE_BF16, ptr(u1),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, q.qlora_strerror(st)
+    y2 = torch.full((M, N), float("nan"), dtype=y_dtype, device=DEV)
+    q.qlora_linear_fwd_noalloc(w, xt, At, Bt, alpha, y=y2, u_out=u1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y0) and torch.equal(y2, y0), "outputs differ from the workspace call"
+    if with_u:
+        assert torch.equal(u1, u0)
+    yo, _ = oracle.linear_fwd(x, What, A, B, r, alpha)
+    tol_check(y1.float().cpu().numpy(), yo, f"y noalloc M={M}")
+
+
+def test_noalloc_refuses_more_than_its_array():
+    """M = 65536 rows at K = 8192, r = 64 needs far more than the array:
+    QLORA_ERR_TOO_LARGE before anything is launched (the activation and
+    output pointers are never touched)."""
+    N, K, r, M = 128, 8192, 64, 65536
+    w = q.qlora_quantize_nf4_dq(dev_bf16(syn.normal_bf16((N, K), 0.02, 7)))
+    need = q.qlora_workspace_bytes(_lib.OP_FWD_LEAN, M, N, K, r)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    y = torch.full((8, N), 7.0, device=DEV)
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: the size check comes first
+    st = _lib.load().qlora_linear_fwd_noalloc(w.desc(), fake, M, fake, fake, r, 32.0,
+                                              ctypes.c_void_p(y.data_ptr()), _lib.DTYPE_F32,
+                                              None, None)
+    torch.cuda.synchronize()
+    assert st == 10, q.qlora_strerror(st)
+    assert torch.all(y == 7.0)
