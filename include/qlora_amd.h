@@ -68,7 +68,8 @@ extern "C" {
 /* Status codes. */
 #define QLORA_OK 0
 #define QLORA_ERR_INVALID_ARG 1 /* NULL pointer, negative size, bad enum */
-#define QLORA_ERR_SHAPE 2       /* K % 64 != 0, N or K < 1 */
+#define QLORA_ERR_SHAPE 2       /* K % 64 != 0, N or K < 1, or two of M, N, K
+                                   whose product passes 2^40 elements */
 #define QLORA_ERR_ALIGN 3       /* a device pointer is not 16-byte aligned */
 #define QLORA_ERR_DTYPE 4       /* unsupported dtype enum */
 #define QLORA_ERR_RANK 5        /* r not a positive multiple of 16, or r > 256 */
@@ -136,7 +137,8 @@ typedef struct qlora_nf4 {
 const char* qlora_strerror(int status);
 
 /* Byte sizes of the three quantized buffers of an [N,K] weight. Host only.
- * Returns QLORA_ERR_SHAPE unless N >= 1, K >= 64 and K % 64 == 0. */
+ * Returns QLORA_ERR_SHAPE unless N >= 1, K >= 64, K % 64 == 0 and
+ * N*K <= 2^40. */
 int qlora_nf4_sizes(int64_t N, int64_t K, size_t* codes_bytes, size_t* absmax_q_bytes,
                     size_t* absmax_scale_bytes);
 
@@ -174,8 +176,8 @@ uint32_t qlora_setup_id(int dq_format);
 
 /* Checks a weight descriptor on the host: QLORA_ERR_INVALID_ARG for a NULL
  * descriptor or buffer, an unknown dq_format or reserved != 0;
- * QLORA_ERR_SHAPE unless N >= 1, K >= 64 and K % 64 == 0; QLORA_ERR_ALIGN
- * for a buffer that is not 16-byte aligned; QLORA_ERR_SETUP when
+ * QLORA_ERR_SHAPE unless N >= 1, K >= 64, K % 64 == 0 and N*K <= 2^40;
+ * QLORA_ERR_ALIGN for a buffer that is not 16-byte aligned; QLORA_ERR_SETUP when
  * format_version != QLORA_FORMAT_VERSION or setup_id !=
  * qlora_setup_id(dq_format). QLORA_OK otherwise. */
 int qlora_nf4_check(const qlora_nf4* w);
@@ -238,7 +240,8 @@ int qlora_dequant_bf16(const qlora_nf4* w, uint16_t* W_out, int layout, void* st
  *              M,N,K,r); from M = 512 on, a workspace of the FWD size selects
  *              the faster route through one bf16 copy of the weight.
  * The weight is read through its dequantized bf16 values, products are exact
- * and accumulate in fp32. M == 0 is a successful no-op. r % 16 == 0. */
+ * and accumulate in fp32. M == 0 is a successful no-op. r % 16 == 0.
+ * QLORA_ERR_SHAPE when M*N or M*K passes 2^40. */
 int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M,
                      const uint16_t* A, const uint16_t* B, int r, float alpha, void* y,
                      int y_dtype, float* u_out, void* workspace, size_t workspace_bytes,
@@ -255,7 +258,8 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M,
  *   u_saved  fp32 [M,r] from qlora_linear_fwd's u_out, or NULL to recompute.
  *   dX, dA, dB may each be NULL to skip that output (x may then be NULL if
  *   both dA and dB are NULL).
- * The frozen base is never written. M == 0 writes zero dA and dB. */
+ * The frozen base is never written. M == 0 writes zero dA and dB.
+ * QLORA_ERR_SHAPE when M*N or M*K passes 2^40. */
 int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY,
                      int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
                      const float* u_saved, void* dX, int dx_dtype, void* dA, void* dB,

@@ -117,7 +117,7 @@ int oracle_linear_bwd(const uint16_t* x, const uint16_t* dY, int64_t M, int64_t 
 
 /* Merge of the adapter into the base in binary32 (see oracle.c):
  * out = base + s * (A B)^T with the adapter sum taken in order j = 0..r-1,
- * one fused multiply-add per term.
+ * each product rounded to binary32 and then added (nothing fused).
  * base = the dequantized NF4 weight (wbf16 == NULL) or the bf16 weight. */
 int oracle_merge_lora(const uint8_t* codes, const int8_t* q8, const float* s2, int fmt,
                       const uint16_t* wbf16, int64_t N, int64_t K, const uint16_t* A,

@@ -38,7 +38,17 @@ bool bwd_plain(int64_t M, int64_t N, int64_t K) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool shape_ok(int64_t N, int64_t K) { return N >= 1 && K >= 64 && K % 64 == 0; }
+// Every product of two of M, N and K stays at most 2^40 (a bf16 matrix of
+// 2 TiB, far beyond one GPU's memory), so no byte count, workspace size or
+// offset formed from them can overflow 64 bits.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool shape_ok(int64_t N, int64_t K) {
+  return N >= 1 && K >= 64 && K % 64 == 0 && N <= kMaxElems / K;
+}
+
+// M rows against a weight of shape_ok (N, K >= 1); M >= 0 is checked first.
+bool rows_ok(int64_t M, int64_t N, int64_t K) { return M <= kMaxElems / N && M <= kMaxElems / K; }
 
 bool rank_ok(int r) { return r >= 16 && r <= 256 && r % 16 == 0; }
 
@@ -249,7 +259,7 @@ uint32_t qlora_setup_id(int dq_format) { return setup_id(dq_format); }
 int qlora_nf4_check(const qlora_nf4* w) { return nf4_check(w); }
 
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
-  if (M < 0 || !shape_ok(N, K) || !rank_ok(r)) return 0;
+  if (M < 0 || !shape_ok(N, K) || !rows_ok(M, N, K) || !rank_ok(r)) return 0;
   if (op == QLORA_OP_FWD) return fwd_layout(M, N, K, r, true).total;
   if (op == QLORA_OP_FWD_LEAN) return fwd_layout(M, N, K, r, true, true).total;
   if (op == QLORA_OP_BWD) return bwd_layout(M, N, K, r, true).total;
@@ -307,6 +317,7 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
   const int8_t* absmax_q = w->absmax_q;
   const float* absmax_scale = w->absmax_scale;
   if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(M, N, K)) return QLORA_ERR_SHAPE;
   if (y_dtype != QLORA_DTYPE_F32 && y_dtype != QLORA_DTYPE_BF16) return QLORA_ERR_DTYPE;
   if (!rank_ok(r)) return QLORA_ERR_RANK;
   if (M == 0) return QLORA_OK;
@@ -370,6 +381,7 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
   const int8_t* absmax_q = w->absmax_q;
   const float* absmax_scale = w->absmax_scale;
   if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(M, N, K)) return QLORA_ERR_SHAPE;
   if ((dx_dtype != QLORA_DTYPE_F32 && dx_dtype != QLORA_DTYPE_BF16) ||
       (grad_dtype != QLORA_DTYPE_F32 && grad_dtype != QLORA_DTYPE_BF16))
     return QLORA_ERR_DTYPE;
@@ -464,6 +476,7 @@ int qlora_gemm_bf16_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_
                        int b_layout, const uint16_t* e, const uint16_t* f, int64_t M, int64_t N,
                        int64_t K, int r, void* y, int y_dtype, void* stream) {
   if (M < 0 || N < 1 || K < 1) return M < 0 ? QLORA_ERR_INVALID_ARG : QLORA_ERR_SHAPE;
+  if (N > kMaxElems / K || !rows_ok(M, N, K)) return QLORA_ERR_SHAPE;
   if (b_layout != QLORA_LAYOUT_ROWS && b_layout != QLORA_LAYOUT_KSLAB32) return QLORA_ERR_INVALID_ARG;
   const bool kslab = b_layout == QLORA_LAYOUT_KSLAB32;
   if (lda < K || (!kslab && ldb < K) || !gemm_nt_supported(K, lda, ldb, N, kslab))
