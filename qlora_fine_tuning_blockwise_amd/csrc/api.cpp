@@ -336,7 +336,10 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
   hipError_t e = hipSuccess;
   if (L.gemv_path) {
     e = launch_lora_down_decode(x, A, M, K, r, down, st);
-    if (e == hipSuccess)
+    if (e == hipSuccess && decode_tiles_ok(M, N, K, r))
+      e = launch_gemv_tiles(x, codes, absmax_q, absmax_scale, down, decode_down_slices(K), B, M, N,
+                            K, r, s, u_out, y, ybf, cb, st);
+    else if (e == hipSuccess)
       e = launch_gemv(x, codes, absmax_q, absmax_scale, down, decode_down_slices(K), B, M, N, K, r,
                       s, u_out, y, ybf, cb, st);
   } else {

@@ -18,6 +18,8 @@
 // the codes are; the two halves of an entry hold the bf16 values of the
 // lane's two blocks. The lookup address is assembled with one byte permute
 // per code.
+#include <algorithm>
+
 #include "device.h"
 
 namespace qlora {
@@ -322,6 +324,268 @@ __global__ __launch_bounds__(512, 4) void gemv_kernel(GemvArgs p, Codebook cb) {
   }
 }
 
+__device__ __forceinline__ const void* gv_uniform(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+
+// Buffer resource over `bytes` bytes at `base` (uniform): loads past the end
+// return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gv_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)(bytes < (int64_t)0x7FFFFFFF ? (bytes > 0 ? bytes : 0) : 0x7FFFFFFF);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)gv_uniform(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t gv_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+template <int kFmt>
+__device__ __forceinline__ float gv_absmax(int b) {  // b: the byte, zero-extended
+  if constexpr (kFmt == kDqInt8) {
+    return (float)(b ^ 0x80) - 128.0f;
+  } else {
+    return q8_value(b, kFmt);
+  }
+}
+
+
+// ------------------------------------------- one-round-trip GEMV (K <= 4096)
+// Under the full weight stream a memory round trip takes microseconds, so
+// gemv_tiles_kernel makes exactly one: every wave issues all of its loads
+// (its codes, absmax bytes and group scales, its slice of x by
+// direct-to-LDS loads, and in wave 0 the down projection's slices and the B
+// columns of the tile) before its first wait, and a workgroup of four waves
+// covers one 16-row tile, so that the whole weight is requested at once.
+// Per weight a lane does one address permute, one 16-bit LDS lookup and
+// half a packing permute; each pair of blocks costs 32 multiplies and 16
+// conversions for its table. Measured on the 11008 x 4096 weight at M = 1
+// (a ring of 24 weights, each call with the down projection): 14.0 us per
+// call against 15.9 us for gemv_kernel; the same call with the lookups and
+// MFMAs taken out (a timing copy) takes 10.2 us, and the down projection
+// alone 2.2 us, so the stream of codes itself runs at about 4 TB/s here.
+constexpr int kTlMaxR = 32;
+constexpr int kTlMaxM = 2;
+constexpr int kTlUp = 16 * kTlMaxM * kTlMaxR;         // staged slices (16 x M r floats)
+
+struct TilesArgs {
+  const uint16_t* x;      // [M, K] bf16
+  const uint8_t* codes;   // [N, K/2]
+  const int8_t* q8;       // [N*K/64]
+  const float* s2;        // [ceil(N*K/64/256)]
+  const float* upart;     // [slices, M, r] from lora_down_decode
+  const uint16_t* B;      // [r, N] bf16
+  float* u_out;           // [M, r] fp32 or NULL (written by workgroup 0)
+  void* y;                // [M, N] fp32 or bf16
+  int64_t M, N, K;
+  int r, slices;
+  float s;
+};
+
+__device__ __forceinline__ uint32_t tl_lookup(const char* tab, uint32_t addr) {
+  return *reinterpret_cast<const uint16_t*>(tab + addr);
+}
+
+// grid: ceil(N / 16) workgroups of 64 kWaves threads (kWaves = 4, or 8 for
+// weights with under 512 tiles). Workgroup rows n0 .. n0+15 form one 16-row
+// MFMA tile. With bpl = 16 / kWaves, lane (i, g) of wave w owns row n0 + i
+// and the blocks bpl (4 w + g) .. + bpl - 1, two per table; the table
+// (bf16(L[e] c1_hat) for both blocks of a pair, one in each half of an LDS
+// dword) sits in a bank-private column: entry e of lane t at 256 e + 4 t in
+// the wave's 4 KB region. MFMA rows are the tokens; MFMA step s of a block
+// takes, in every lane, the block's weights 8 s .. 8 s + 7, and the x
+// operand of the same k comes from the wave's LDS slice of x (the 256 bpl k
+// its blocks cover, M <= 2; tokens >= M read a zero row).
+template <int kFmt, bool kOutBf16, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Codebook cb) {
+  constexpr int kTlWaves = kWaves;
+  constexpr int kTlBpl = 16 / kWaves;                          // blocks per lane (K <= 4096)
+  constexpr int kSpan = 64 * 4 * kTlBpl;                       // k covered by one wave
+  constexpr int kXw = 2 * kSpan * kTlMaxM;                     // x slice bytes per wave
+  __shared__ __attribute__((aligned(16))) uint32_t tabs[kTlWaves][16][64];
+  __shared__ __attribute__((aligned(16))) unsigned char xs[kTlWaves][kXw + 16];
+  __shared__ __attribute__((aligned(16))) float ups[kTlUp];  // wave 0's staged slices
+  __shared__ __attribute__((aligned(16))) float usm[kTlMaxM * kTlMaxR];  // s*u [M][r]
+  __shared__ __attribute__((aligned(16))) uint16_t bsm[kTlMaxR * 16];  // B tile [r][16]
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int tid = threadIdx.x, lane = tid & 63, i = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int r = p.r;
+  const int mr = (int)M * r;
+  const int64_t KB = K >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int rows = (int)min((int64_t)16, N - n0);
+  const uint32_t nl = (uint32_t)min(i, rows - 1);  // rows past N read row N-1 (never stored)
+  const int64_t b0 = kTlBpl * (4 * w + g);          // the lane's first block
+
+  // 1. x slice of this wave (M <= 2 tokens x kSpan k) by direct-to-LDS
+  //    loads: instruction q covers 512 k (piece q % kXq) of token q / kXq;
+  //    the zero row behind it is written first.
+  unsigned char* xw = xs[w];
+  if (lane < 4) reinterpret_cast<uint32_t*>(xw + kXw)[lane] = 0u;
+  const __amdgpu_buffer_rsrc_t xres = gv_rsrc(p.x, M * K * 2);
+  constexpr int kXq = kSpan / 512;  // 1 KB (512 k) pieces per token
+#pragma unroll
+  for (int q = 0; q < kXq * kTlMaxM; ++q) {
+    const int m = q / kXq, hk = q % kXq;
+    const int64_t k = (int64_t)kSpan * w + 512 * hk + 8 * lane;
+    const uint32_t off = (m < M && k < K) ? (uint32_t)((m * K + k) * 2) : 0x80000000u;
+    if (q < kXq * M)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)(xw + 1024 * q), 16, off, 0, 0, 0);
+  }
+  // 2. codes, absmax bytes and group scales of the lane's four blocks
+  //    (blocks past the row end read the row's last block and get zeros).
+  const uint32_t kb32 = (uint32_t)KB;
+  const __amdgpu_buffer_rsrc_t cres = gv_rsrc(p.codes + n0 * (K >> 1), (int64_t)rows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t qres = gv_rsrc(p.q8 + n0 * KB, (int64_t)rows * KB);
+  //    Every load instruction costs the CU's load pipeline about the same
+  //    whatever its width, so each is as wide as the data allows: the four
+  //    blocks' 128 bytes of codes in eight 16-byte loads, their absmax bytes
+  //    in one dword (K % 256 == 0: the four bytes are aligned), and one
+  //    group scale (four blocks from a multiple of four never straddle a
+  //    256-block group).
+  u32x4_t cw[kTlBpl][2];
+  const uint32_t bq = (uint32_t)min(b0, KB - kTlBpl);  // lanes past the row end: the last blocks
+#pragma unroll
+  for (int h = 0; h < kTlBpl; ++h) {
+    const uint32_t off = nl * (32u * kb32) + 32u * (bq + h);
+    cw[h][0] = gv_load16(cres, off);
+    cw[h][1] = gv_load16(cres, off + 16);
+  }
+  const uint32_t qi = nl * kb32 + bq;
+  uint32_t q4;
+  if constexpr (kTlBpl == 4)
+    q4 = __builtin_amdgcn_raw_buffer_load_b32(qres, (int)qi, 0, 0);
+  else
+    q4 = __builtin_amdgcn_raw_buffer_load_b16(qres, (int)qi, 0, 0);
+  const float sv = (p.s2 + ((n0 * KB) >> 8))[((uint32_t)((n0 * KB) & 255) + qi) >> 8];
+  // 3. wave 0: the down projection's slices (slices x M r floats, 1 KB per
+  //    instruction) and the tile's B columns.
+  const int upb = p.slices * mr * 4;
+  if (w == 0) {
+    const __amdgpu_buffer_rsrc_t ures = gv_rsrc(p.upart, upb);
+    for (int q = 0; q < (upb + 1023) / 1024; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ures, (lds_void*)(ups + 256 * q), 16,
+                                               (uint32_t)(1024 * q + 16 * lane), 0, 0, 0);
+  }
+  uint16_t bv[kTlMaxR / 16];
+#pragma unroll
+  for (int q = 0; q < kTlMaxR / 16; ++q) {  // 16 r values over 256 threads
+    const int idx = tid + 256 * q;
+    const uint32_t bj = (uint32_t)min(idx >> 4, r - 1);
+    const uint32_t bc = (uint32_t)min((int64_t)(idx & 15), N - 1 - n0);
+    if (q == 0 || idx < 16 * r) bv[q] = (p.B + n0)[bj * (uint32_t)N + bc];
+  }
+
+  const uint32_t region = __builtin_amdgcn_mbcnt_lo(0u, 0u) + 0x10101010u * (uint32_t)w;
+  const uint32_t colbase = 4u * (uint32_t)lane;
+  const char* tab = reinterpret_cast<const char*>(&tabs[0][0][0]);
+  // x operand of step s of block h: x[i][64 (b0 + h) + 8 s .. + 8] from the
+  // wave's slice (k within the slice: 256 g + 64 h + 8 s), zeros for i >= M.
+  const bool xok = i < M;
+  const unsigned char* xrow = xok ? xw + 2 * kSpan * i + 2 * (64 * kTlBpl * g) : xw + kXw;
+  const int xstep = xok ? 16 : 0;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  bool first = true;
+#pragma unroll
+  for (int pr = 0; pr < kTlBpl / 2; ++pr) {
+    const int q0 = (int)((q4 >> (16 * pr)) & 0xFFu), q1 = (int)((q4 >> (16 * pr + 8)) & 0xFFu);
+    const float ch0 = b0 + 2 * pr < KB ? gv_absmax<kFmt>(q0) * sv : 0.0f;
+    const float ch1 = b0 + 2 * pr + 1 < KB ? gv_absmax<kFmt>(q1) * sv : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tabs[w][e][lane] = pack_bf16x2(cb.level[e] * ch0, cb.level[e] * ch1);
+    if (first) {  // the x slice (this wave's own loads, issued first)
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): every load of this wave
+      first = false;
+    }
+    const uint32_t dw[16] = {cw[2 * pr][0].x, cw[2 * pr][0].y, cw[2 * pr][0].z, cw[2 * pr][0].w,
+                             cw[2 * pr][1].x, cw[2 * pr][1].y, cw[2 * pr][1].z, cw[2 * pr][1].w,
+                             cw[2 * pr + 1][0].x, cw[2 * pr + 1][0].y, cw[2 * pr + 1][0].z,
+                             cw[2 * pr + 1][0].w, cw[2 * pr + 1][1].x, cw[2 * pr + 1][1].y,
+                             cw[2 * pr + 1][1].z, cw[2 * pr + 1][1].w};
+    uint32_t va[2][8];
+    auto issue = [&](int s, uint32_t (&v)[8]) {  // step s of the pair: block s / 8
+      const uint32_t d = dw[s];
+      const uint32_t lo = (d & 0x0F0F0F0Fu) | region;
+      const uint32_t hi = ((d >> 4) & 0x0F0F0F0Fu) | region;
+      const int hh = s >> 3;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        v[2 * b] = tl_lookup(tab, lut_addr(lo, colbase, b) + 2 * hh);
+        v[2 * b + 1] = tl_lookup(tab, lut_addr(hi, colbase, b) + 2 * hh);
+      }
+    };
+    issue(0, va[0]);
+    issue(1, va[1]);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t (&v)[8] = va[s & 1];
+      const u32x4_t bop{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
+                        __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                        __builtin_amdgcn_perm(v[5], v[4], 0x05040100u),
+                        __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)};
+      const u32x4_t xop = *reinterpret_cast<const u32x4_t*>(
+          xrow + xstep * (8 * (2 * pr + (s >> 3)) + (s & 7)));
+      if (s + 2 < 16) issue(s + 2, v);
+      acc = mfma_16x16x32(xop, bop, acc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // u = sum of the slices in order from +0 (the same bits as the finalize
+  // kernel's sum), s*u for the epilogue; wave 0 staged the slices.
+  if (w == 0)
+    for (int idx = lane; idx < mr; idx += 64) {
+      float t[kDecMaxSlices];
+#pragma unroll
+      for (int k = 0; k < kDecMaxSlices; ++k) t[k] = ups[min(k, p.slices - 1) * mr + idx];
+      float u = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kDecMaxSlices; ++k) u += k < p.slices ? t[k] : 0.0f;
+      usm[idx] = p.s * u;
+      if (p.u_out && blockIdx.x == 0) p.u_out[idx] = u;
+    }
+#pragma unroll
+  for (int q = 0; q < kTlMaxR / 16; ++q)
+    if (tid + 256 * q < 16 * r) bsm[tid + 256 * q] = bv[q];
+  // cross-wave sum (each wave's partial tile in its own table region, which
+  // only it reads), adapter term, store. acc[v]: token 4 g + v, row n0 + i.
+  float* red = reinterpret_cast<float*>(&tabs[w][0][0]);  // [16][17] per wave
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[(4 * g + v) * 17 + i] = acc[v];
+  __syncthreads();
+  {
+    const int m = tid >> 4, c = tid & 15;
+    const int64_t n = n0 + c;
+    if (m < M && n < N) {
+      const int o = m * 17 + c;
+      float v = reinterpret_cast<const float*>(&tabs[0][0][0])[o];
+#pragma unroll
+      for (int ww = 1; ww < kTlWaves; ++ww) v += reinterpret_cast<const float*>(&tabs[ww][0][0])[o];
+      float lo = 0.0f;
+      for (int j0 = 0; j0 < r; j0 += 16) {
+        float uv[16], bw[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          uv[jj] = usm[m * r + j0 + jj];
+          bw[jj] = bf16_lo(bsm[(j0 + jj) * 16 + c]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) lo = __builtin_fmaf(uv[jj], bw[jj], lo);
+      }
+      v += lo;
+      if (kOutBf16)
+        static_cast<uint16_t*>(p.y)[m * N + n] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+      else
+        static_cast<float*>(p.y)[m * N + n] = v;
+    }
+  }
+}
+
 }  // namespace
 
 int decode_down_slices(int64_t K) {
@@ -350,6 +614,41 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const int8_t* q8
     hipLaunchKernelGGL(gemv_kernel<true>, grid, dim3(64 * kGvWaves), dyn, st, a, cb);
   else
     hipLaunchKernelGGL(gemv_kernel<false>, grid, dim3(64 * kGvWaves), dyn, st, a, cb);
+  return hipGetLastError();
+}
+
+
+bool decode_tiles_ok(int64_t M, int64_t N, int64_t K, int r) {
+  (void)N;
+  // x slice in LDS (2 tokens x 1024 k per wave), the down projection's
+  // slices in LDS (16 x M r floats), B tile and s*u in LDS
+  return M >= 1 && M <= kTlMaxM && K <= 4096 && K % 256 == 0 && r <= kTlMaxR &&
+         (int64_t)decode_down_slices(K) * M * r <= kTlUp;
+}
+
+hipError_t launch_gemv_tiles(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
+                             const float* s2, const float* upart, int slices, const uint16_t* B,
+                             int64_t M, int64_t N, int64_t K, int r, float s, float* u_out,
+                             void* y, bool y_bf16, const Codebook& cb, hipStream_t st) {
+  const TilesArgs a{x, codes, q8, s2, upart, B, u_out, y, M, N, K, r, slices, s};
+  const int64_t tiles = (N + 15) / 16;
+  const dim3 grid((unsigned)tiles);
+  // Eight waves per tile when there are few tiles (below 512: under two
+  // workgroups per CU), four otherwise.
+  const bool eight = tiles < 512;
+#define QLORA_TL(F, B16)                                                                     \
+  do {                                                                                       \
+    if (eight)                                                                               \
+      hipLaunchKernelGGL((gemv_tiles_kernel<F, B16, 8>), grid, dim3(512), 0, st, a, cb);    \
+    else                                                                                     \
+      hipLaunchKernelGGL((gemv_tiles_kernel<F, B16, 4>), grid, dim3(256), 0, st, a, cb);    \
+  } while (0)
+  switch (cb.dq_format) {
+    case kDqInt8: if (y_bf16) QLORA_TL(kDqInt8, true); else QLORA_TL(kDqInt8, false); break;
+    case kDqUint8: if (y_bf16) QLORA_TL(kDqUint8, true); else QLORA_TL(kDqUint8, false); break;
+    default: if (y_bf16) QLORA_TL(kDqE4m3, true); else QLORA_TL(kDqE4m3, false); break;
+  }
+#undef QLORA_TL
   return hipGetLastError();
 }
 

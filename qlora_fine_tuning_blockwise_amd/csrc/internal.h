@@ -90,6 +90,15 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const int8_t* q8
                        int64_t M, int64_t N, int64_t K, int r, float s, float* u_out, void* y,
                        bool y_bf16, const Codebook& cb, hipStream_t st);
 
+// The decode GEMV as a persistent grid (decode_tiles_ok: M <= 16, K <= 4096,
+// r <= 64): one 1024-thread workgroup per CU streams a run of 16-row tiles;
+// same arguments and results as launch_gemv.
+bool decode_tiles_ok(int64_t M, int64_t N, int64_t K, int r);
+hipError_t launch_gemv_tiles(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
+                             const float* s2, const float* upart, int slices, const uint16_t* B,
+                             int64_t M, int64_t N, int64_t K, int r, float s, float* u_out,
+                             void* y, bool y_bf16, const Codebook& cb, hipStream_t st);
+
 // dX = dY W_hat + [svlr-extended term with A].
 hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_t* q8,
                            const float* s2, const uint16_t* svlr, const uint16_t* A, int64_t M,

@@ -364,7 +364,7 @@ def test_fwd_one_hot_rows_exact_gemm_and_gemv():
     N, K, r = 512, 1024, 16
     P = Problem(N, K, r, 32.0, seed=5)
     P.Bt = torch.zeros_like(P.Bt)
-    for M, lean in ((16, False), (64, False), (600, False), (600, True)):
+    for M, lean in ((2, False), (16, False), (64, False), (600, False), (600, True)):
         ks = np.random.default_rng(M).choice(K, M, replace=False)
         x = np.zeros((M, K), np.uint16)
         x[np.arange(M), ks] = 0x3F80
@@ -407,7 +407,13 @@ def run_fwd_other_stream(P, x, **kw):
 @pytest.mark.parametrize("M,N,K,r", [(1, 72, 64, 16), (3, 330, 192, 32), (16, 100, 320, 16),
                                      (7, 1000, 1600, 64), (2, 40, 4096, 144),
                                      # four waves per tile (>= 512 tiles), ragged rows
-                                     (16, 8200, 512, 16), (3, 8200, 256, 80)])
+                                     (16, 8200, 512, 16), (3, 8200, 256, 80),
+                                     # one-round-trip kernel (M <= 2, K % 256 == 0,
+                                     # K <= 4096, r <= 32): eight waves per tile
+                                     # with a ragged last tile and lanes past the
+                                     # row end; four waves per tile (>= 512 tiles)
+                                     (1, 100, 256, 16), (2, 300, 4096, 32),
+                                     (2, 8200, 768, 32), (1, 8192, 4096, 16)])
 def test_fwd_decode_ragged(M, N, K, r):
     """Decode (M <= 16): ragged rows, chunks and adapter column groups against
     the oracle; a call on another stream gives the same bits."""
@@ -988,7 +994,7 @@ def test_formats_llama7b_up_bit_exact(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_formats_one_hot_fwd_and_bwd_exact(fmt):
-    """One-hot rows through the GEMV (M = 16), the tile kernels (M = 64, 40)
+    """One-hot rows through both GEMVs (M = 2, 16), the tile kernels (M = 64, 40)
     and the large-M path (M = 600) return the format's dequantized weight
     columns and rows bit for bit: every in-kernel decoding of the absmax
     byte follows the format."""
@@ -996,7 +1002,7 @@ def test_formats_one_hot_fwd_and_bwd_exact(fmt):
     P = Problem(N, K, r, 32.0, seed=304, fmt=fmt)
     P.Bt = torch.zeros_like(P.Bt)
     Wf = oracle.bf16_to_f32(P.What)
-    for M, lean in ((16, False), (64, False), (600, False), (600, True)):
+    for M, lean in ((2, False), (16, False), (64, False), (600, False), (600, True)):
         ks = np.random.default_rng(M).choice(K, M, replace=False)
         x = np.zeros((M, K), np.uint16)
         x[np.arange(M), ks] = 0x3F80
