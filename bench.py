@@ -39,9 +39,12 @@ AdamW step on a Llama-7B adapter arena. `cpu_baseline` times the oracle
 (single-threaded C) per operation on one core and extrapolates the step; an
 all-cores quantize/dequantize run uses P independent oracle processes.
 
-Counter helpers: `--only CALL` runs one call of the step (e.g. fwd_up) for
-the timed iterations; `--copy-calibration BYTES` runs an elementwise copy of
-BYTES bytes (the reference reading for the counter scale).
+Counter helpers: `--only CALL` runs one call of the step (e.g. fwd_up,
+quantize_up) for the timed iterations, or one of the extra calls
+dequant_up (row-major dequantization of the 28672x8192 projection) and
+decode_up7b_m1 (the decode forward, M = 1, r = 16, on one 11008x4096
+weight); `--copy-calibration BYTES` runs an elementwise copy of BYTES bytes
+(the reference reading for the counter scale).
 """
 from __future__ import annotations
 
@@ -68,7 +71,8 @@ ACT_DTYPE_NAME = "bfloat16"  # y and dX: the activations' compute dtype
 # for an elementwise copy of known size. Valid while every listed source
 # hashes to the recorded value; None: not measured for these sources.
 TRAFFIC = {"call": "fwd_up", "sources": ["api.cpp", "quantize.hip", "gemm_nt.hip", "lora.hip"],
-           "src_sha256": None, "fetch_bytes": None, "write_bytes": None}
+           "src_sha256": "6826268cf0165f7f22b3dff00c6bdb7121a01e7ecc2e3e708af21e9d569a7aa2",
+           "fetch_bytes": 1688613216, "write_bytes": 601358387}
 
 
 def log(*a):
@@ -217,6 +221,27 @@ def main():
     step_flops = sum(c[2] for c in calls)
     roof_call = "fwd_up"
 
+    deq = None
+    if args.only == "dequant_up":
+        p = L["up"]
+        deq = torch.empty((p["N"], p["K"]), dtype=torch.bfloat16, device=dev)
+        calls.append(("dequant_up", lambda p=p: q.qlora_dequant_bf16(p["w"], out=deq), 0,
+                      nf4_bytes(p["N"], p["K"]) + 2 * p["N"] * p["K"]))
+    if args.only == "decode_up7b_m1":
+        dc = syn.LLAMA7B_DECODE
+        N7, K7 = dc["weights"]["up"]
+        r7 = dc["r"]
+        w7 = q.qlora_quantize_nf4_dq(syn.torch_normal_bf16((N7, K7), dc["w_std"],
+                                                           syn.seed_of(2, 11), dev))
+        A7 = syn.torch_normal_bf16((K7, r7), 1.0 / K7 ** 0.5, syn.seed_of(2, 30), dev)
+        B7 = syn.torch_normal_bf16((r7, N7), 0.01, syn.seed_of(2, 31), dev)
+        x7 = syn.torch_normal_bf16((1, K7), 1.0, syn.seed_of(2, 41), dev)
+        y7 = torch.empty((1, N7), dtype=torch.float32, device=dev)
+        ws7 = torch.empty(q.qlora_workspace_bytes(0, 1, N7, K7, r7), dtype=torch.uint8,
+                          device=dev)
+        calls.append(("decode_up7b_m1", lambda: q.qlora_linear_fwd(
+            w7, x7, A7, B7, dc["alpha"], y=y7, workspace=ws7), fwd_flops(1, N7, K7, r7),
+            nf4_bytes(N7, K7) + 2 * (K7 * r7 + r7 * N7)))
     if args.only:
         sel = [c for c in calls if c[0] == args.only]
         if not sel:
@@ -302,8 +327,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "call": "qlora_linear_fwd (whole call)", "label": lab,
-                "kernels": ["transpose2_kernel", "lora_down_kernel", "lora_finalize_kernel",
-                            "dequant_kernel (K-slab)", "gemm_nt_kernel"],
+                "kernels": ["transpose_kernel", "lora_down_tile_kernel", "lora_down_finalize_kernel",
+                            "dequant_kernel<true> (K-slab)", "gemm_nt_kernel"],
                 "shape": {"M": M, "N": pu["N"], "K": pu["K"], "r": r},
                 "flops_per_call": rflops, "flops_formula": "2MNK + 2Mr(K+N)",
                 "avg_ms": round(rms, 5)}
