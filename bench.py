@@ -41,7 +41,9 @@ all-cores quantize/dequantize run uses P independent oracle processes.
 
 Counter helpers: `--only CALL` runs one call of the step (e.g. fwd_up,
 quantize_up) for the timed iterations, or one of the extra calls
-dequant_up (row-major dequantization of the 28672x8192 projection) and
+fwd_up_lean (the same forward with the smallest workspace, so the fused
+kernel that keeps no bf16 copy of the weight runs), dequant_up (row-major
+dequantization of the 28672x8192 projection) and
 decode_up7b_m1 (the decode forward, M = 1, r = 16, on one 11008x4096
 weight); `--copy-calibration BYTES` runs an elementwise copy of BYTES bytes
 (the reference reading for the counter scale).
@@ -221,6 +223,13 @@ def main():
     step_flops = sum(c[2] for c in calls)
     roof_call = "fwd_up"
 
+    if args.only == "fwd_up_lean":
+        p = L["up"]
+        ws_lean = torch.empty(q.qlora_workspace_bytes(3, M, p["N"], p["K"], r), dtype=torch.uint8,
+                              device=dev)
+        calls.append(("fwd_up_lean", lambda p=p: q.qlora_linear_fwd(
+            p["w"], p["x"], p["A"], p["B"], alpha, y=p["y"], u_out=p["u"], workspace=ws_lean),
+            fwd_flops(M, p["N"], p["K"], r), 0))
     deq = None
     if args.only == "dequant_up":
         p = L["up"]
