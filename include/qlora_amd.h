@@ -106,6 +106,7 @@ extern "C" {
 #define QLORA_OP_BWD 1
 #define QLORA_OP_MERGE 2
 #define QLORA_OP_FWD_LEAN 3 /* the forward without a bf16 copy of the weight */
+#define QLORA_OP_BWD_LEAN 4 /* the backward without a bf16 copy of the weight */
 
 /* Format version of the storage layout above. */
 #define QLORA_FORMAT_VERSION 1u
@@ -191,8 +192,11 @@ int qlora_nf4_check(const qlora_nf4* w);
  * the smallest workspace the forward accepts: with less than the QLORA_OP_FWD
  * size but at least this one, qlora_linear_fwd runs its fused kernel, which
  * dequantizes each weight tile in registers right before the matrix cores
- * use it and never holds a bf16 copy ([P4] "The mechanism"). Host only; 0 on
- * invalid sizes. */
+ * use it and never holds a bf16 copy ([P4] "The mechanism"). Likewise
+ * QLORA_OP_BWD_LEAN for the backward: with less than the QLORA_OP_BWD size
+ * but at least this one, dX runs through the kernel that dequantizes the
+ * transposed operand in registers ([P2] s3). Host only; 0 on invalid
+ * sizes. */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
 
 /* Quantize once, at load time ([P4] "The mechanism": the pretrained weights
@@ -258,6 +262,10 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M,
  *   u_saved  fp32 [M,r] from qlora_linear_fwd's u_out, or NULL to recompute.
  *   dX, dA, dB may each be NULL to skip that output (x may then be NULL if
  *   both dA and dB are NULL).
+ *   workspace  device buffer of at least qlora_workspace_bytes(BWD_LEAN,
+ *              M,N,K,r); from M = 512 on, a workspace of the BWD size selects
+ *              the faster route through one transposed bf16 copy of the
+ *              weight.
  * The frozen base is never written. M == 0 writes zero dA and dB.
  * QLORA_ERR_SHAPE when M*N or M*K passes 2^40. */
 int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY,

@@ -256,8 +256,10 @@ def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: 
                      B: torch.Tensor, alpha: float, u_saved: torch.Tensor | None = None,
                      want_dx: bool = True, dx_dtype=torch.float32, grad_dtype=torch.float32,
                      want_grads: bool = True, workspace: torch.Tensor | None = None,
-                     stream=None):
-    """Returns (dX or None, dA or None, dB or None)."""
+                     stream=None, lean: bool = False):
+    """Returns (dX or None, dA or None, dB or None). With lean=True (and no
+    workspace given) the call gets the smallest workspace it accepts, so from
+    512 rows on dX is computed without a bf16 copy of the weight."""
     M = dY.shape[0]
     r = A.shape[1]
     dev = w.device
@@ -269,7 +271,8 @@ def qlora_linear_bwd(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: 
     dX = torch.empty((M, w.K), dtype=dx_dtype, device=dev) if want_dx else None
     dA = torch.empty((w.K, r), dtype=grad_dtype, device=dev) if want_grads else None
     dB = torch.empty((r, w.N), dtype=grad_dtype, device=dev) if want_grads else None
-    workspace = _workspace(_lib.OP_BWD, M, w.N, w.K, r, dev, workspace)
+    workspace = _workspace(_lib.OP_BWD_LEAN if lean else _lib.OP_BWD, M, w.N, w.K, r, dev,
+                           workspace)
     st = _lib.load().qlora_linear_bwd(
         w.desc(), _ptr(x), _ptr(dY), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(u_saved),
         _ptr(dX), _dtype_code(dx_dtype), _ptr(dA), _ptr(dB), _dtype_code(grad_dtype),

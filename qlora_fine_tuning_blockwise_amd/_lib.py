@@ -25,6 +25,7 @@ OP_FWD = 0
 OP_BWD = 1
 OP_MERGE = 2
 OP_FWD_LEAN = 3
+OP_BWD_LEAN = 4
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
 P = ctypes.c_void_p

@@ -101,7 +101,9 @@ struct BwdLayout {
   int splits = 1;  // reduction splits of the dense stage for dX
 };
 
-BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
+// lean: the layout of the lean route (dX through the in-register kernel, no
+// bf16 copy of the weight).
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u, bool lean = false) {
   BwdLayout L;
   Carve c;
   // u is recomputed with the kernels of the forward pass for this M, so that
@@ -117,7 +119,7 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u) {
   L.vT = c.take(2 * (size_t)r * Mp * 2);
   L.uT = c.take(2 * (size_t)r * Mp * 2);
   L.col = c.take((size_t)colred_splits(M) * (K + N) * r * 4);  // dA's partials, then dB's
-  L.plain = bwd_plain(M, N, K);
+  L.plain = !lean && bwd_plain(M, N, K);
   if (L.plain) {
     L.Wt = c.take((size_t)K * N * 2);
     L.splits = gemm_nt_splits(M, K, N);
@@ -263,6 +265,7 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
   if (op == QLORA_OP_FWD) return fwd_layout(M, N, K, r, true).total;
   if (op == QLORA_OP_FWD_LEAN) return fwd_layout(M, N, K, r, true, true).total;
   if (op == QLORA_OP_BWD) return bwd_layout(M, N, K, r, true).total;
+  if (op == QLORA_OP_BWD_LEAN) return bwd_layout(M, N, K, r, true, true).total;
   if (op == QLORA_OP_MERGE) return merge_layout(N, K, r).total;
   return 0;
 }
@@ -406,7 +409,8 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
     return launch_status(e);
   }
   const bool need_u = dB && !u_saved;
-  const BwdLayout L = bwd_layout(M, N, K, r, need_u);
+  BwdLayout L = bwd_layout(M, N, K, r, need_u);
+  if (L.plain && workspace_bytes < L.total) L = bwd_layout(M, N, K, r, need_u, true);
   if (!workspace || workspace_bytes < L.total) return QLORA_ERR_WORKSPACE;
 
   const float s = alpha / (float)r;

@@ -76,7 +76,7 @@ static void queries(void) {
     const int64_t NKs[][2] = {{4096, 4096}, {1, 64}, {28672, 8192}, {(int64_t)1 << 40, 1 << 20},
                               {INT64_MAX, 64}, {64, INT64_MAX / 64 * 64}};
     const int rs[] = {0, 16, 24, 64, 256, 272};
-    for (int op = -1; op <= 4; ++op)
+    for (int op = -1; op <= 5; ++op)
         for (size_t i = 0; i < sizeof Ms / sizeof Ms[0]; ++i)
             for (size_t j = 0; j < sizeof NKs / sizeof NKs[0]; ++j)
                 for (size_t k = 0; k < sizeof rs / sizeof rs[0]; ++k)

@@ -244,7 +244,7 @@ def test_workspace_query(lib):
     assert q.qlora_workspace_bytes(0, 4096, 4096, 4096, 16) > q.qlora_workspace_bytes(0, 1024, 4096, 4096, 16)
     assert q.qlora_workspace_bytes(1, 4096, 11008, 4096, 16) > 0
     assert q.qlora_workspace_bytes(0, 16, 4096, 4000, 16) == 0
-    assert q.qlora_workspace_bytes(4, 16, 4096, 4096, 16) == 0  # no such op
+    assert q.qlora_workspace_bytes(5, 16, 4096, 4096, 16) == 0  # no such op
     # from 512 rows on the fast routes hold one bf16 copy of the weight; the
     # forward's lean route (fused in-register dequantization) holds none
     for op in (0, 1):
@@ -254,6 +254,11 @@ def test_workspace_query(lib):
     lean = q.qlora_workspace_bytes(3, 512, 4096, 1024, 16)
     assert 0 < lean < 4096 * 1024 * 2 // 8
     assert q.qlora_workspace_bytes(3, 16, 4096, 1024, 16) == q.qlora_workspace_bytes(0, 16, 4096, 1024, 16)
+    # the backward's lean route holds no transposed copy (nor the dense
+    # stage's split partials) either
+    assert q.qlora_workspace_bytes(1, 512, 4096, 1024, 16) - q.qlora_workspace_bytes(4, 512, 4096, 1024, 16) \
+        >= 4096 * 1024 * 2
+    assert q.qlora_workspace_bytes(4, 511, 4096, 1024, 16) == q.qlora_workspace_bytes(1, 511, 4096, 1024, 16)
 
 
 @pytest.fixture(scope="module")

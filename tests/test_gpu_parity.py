@@ -548,15 +548,19 @@ def test_bwd_full_small(M, N, K, r):
     P = Problem(N, K, r, 24.0, seed=M + 2 * N + K)
     x = syn.normal_bf16((M, K), 1.0, 3 + M)
     dY = syn.normal_bf16((M, N), 1.0, 4 + M)
-    dX, dA, dB = run_bwd(P, x, dY)
     go = oracle.linear_bwd(x, dY, P.What, P.A, P.B, r, 24.0)
-    tol_check(host(dX), go["dX"], "dX")
-    tol_check(host(dA), go["dA"], "dA")
-    tol_check(host(dB), go["dB"], "dB")
-    # bf16 outputs are the RNE of the fp32 ones
-    dXb, dAb, dBb = run_bwd(P, x, dY, dx_dtype=torch.bfloat16, grad_dtype=torch.bfloat16)
-    assert torch.equal(dXb, dX.to(torch.bfloat16))
-    assert torch.equal(dAb, dA.to(torch.bfloat16)) and torch.equal(dBb, dB.to(torch.bfloat16))
+    # from 512 rows on both routes: dX through one transposed bf16 copy of the
+    # weight (fast) and through the in-register kernel (lean)
+    for lean in ((False, True) if M >= 512 else (False,)):
+        dX, dA, dB = run_bwd(P, x, dY, lean=lean)
+        tol_check(host(dX), go["dX"], f"dX lean={lean}")
+        tol_check(host(dA), go["dA"], f"dA lean={lean}")
+        tol_check(host(dB), go["dB"], f"dB lean={lean}")
+        # bf16 outputs are the RNE of the fp32 ones
+        dXb, dAb, dBb = run_bwd(P, x, dY, dx_dtype=torch.bfloat16, grad_dtype=torch.bfloat16,
+                                lean=lean)
+        assert torch.equal(dXb, dX.to(torch.bfloat16))
+        assert torch.equal(dAb, dA.to(torch.bfloat16)) and torch.equal(dBb, dB.to(torch.bfloat16))
 
 
 @pytest.mark.parametrize("M,N,K,r", [(5, 520, 1024, 32), (16, 300, 4096, 16),
@@ -655,9 +659,10 @@ def test_bwd_one_hot_dy_rows_exact(M, N):
     ns = np.random.default_rng(4).choice(N, M, replace=False)
     dY = np.zeros((M, N), np.uint16)
     dY[np.arange(M), ns] = 0x3F80
-    dX, _, _ = run_bwd(P, None, dY, want_grads=False)
     Wf = oracle.bf16_to_f32(P.What)
-    assert np.array_equal(host(dX), Wf[ns] + 0.0)
+    for lean in ((False, True) if M >= 512 else (False,)):
+        dX, _, _ = run_bwd(P, None, dY, want_grads=False, lean=lean)
+        assert np.array_equal(host(dX), Wf[ns] + 0.0), f"lean={lean}"
 
 
 def test_bwd_empty_batch_gives_zero_grads():
