@@ -291,13 +291,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const int64_t b0 = ((int64_t)blockIdx.x * 4 + w) * (8 * kDqPasses) + g;
   uint32_t srow = 0, sblk0 = 0;  // K-slab mode: this group's row, the wave's first block
   if (kKSlab) {
-    // Consecutive waves take consecutive row groups of one block group, so
-    // the eight slabs a block group writes fill sequentially.
+    // Consecutive waves take consecutive block groups of one row group, so
+    // the waves that run together read each row's codes as one contiguous
+    // run. (Row groups first would make them read 128 bytes per row at the
+    // row stride of the codes, K/2 bytes: measured 148 against 122 us on a
+    // 28672 x 8192 weight, although the slabs then fill sequentially.)
     const uint32_t wid = (uint32_t)blockIdx.x * 4 + (uint32_t)__builtin_amdgcn_readfirstlane(w);
-    const uint32_t rgs = (rows + 7) / 8;  // row groups
-    const uint32_t cg = wid / rgs;
-    srow = min(8 * (wid - cg * rgs) + (uint32_t)g, rows - 1);
-    sblk0 = min(cg * kDqPasses, kb - 1);
+    const uint32_t ncg = (kb + kDqPasses - 1) / kDqPasses;  // block groups
+    const uint32_t rg = wid / ncg;
+    srow = min(8 * rg + (uint32_t)g, rows - 1);
+    sblk0 = min((wid - rg * ncg) * kDqPasses, kb - 1);
   }
   int64_t bk[kDqPasses];
   uint32_t cw[kDqPasses];
