@@ -380,6 +380,120 @@ __global__ __launch_bounds__(256) void lora_down_tile_kernel(const uint16_t* __r
   }
 }
 
+// Streaming form for large M and ranks that are multiples of 32: a 256-thread
+// workgroup owns 128 rows x 64 rank columns of one slice of T and walks the
+// slice in 64-wide chunks. Each chunk of X (128 rows) and of P (64 rows) is
+// loaded as whole 128-byte lines (eight lanes a row, one 16-byte piece
+// each), staged in LDS (row stride 144 bytes: the 16 lanes of each phase of
+// a fragment read hit 16 distinct bank groups) and consumed by
+// v_mfma_f32_32x32x16_bf16, wave w taking rows 32w .. 32w+31 and both
+// 32-column tiles. Two LDS buffers alternate, and the loads of the next two
+// chunks are in flight while one chunk is computed, so the workgroup keeps
+// about 48 KB of reads outstanding. Every load is clamped into the matrices
+// and every stage is unconditional: positions past the slice are stored as
+// zeros (a chunk past the end adds +0), so no branch separates a load from
+// its wait. part[slice][m][j] as above. Requires T % 8 == 0 and r % 32 == 0.
+constexpr int kStrT = 64;   // t per chunk
+constexpr int kStrLd = 72;  // staged row stride (bf16)
+
+__global__ __launch_bounds__(256) void lora_down_stream_kernel(const uint16_t* __restrict__ X,
+                                                               const uint16_t* __restrict__ P,
+                                                               int64_t M, int64_t T, int r,
+                                                               int64_t tslice,
+                                                               float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][128 * kStrLd];
+  __shared__ __attribute__((aligned(16))) uint16_t ps[2][64 * kStrLd];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 31, h = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.x * 128;
+  const int j0 = blockIdx.y * 64;
+  const int ncol = min(2, (r - j0) / 32);  // 32-column tiles of this workgroup
+  const int slice = blockIdx.z;
+  const int64_t t0 = (int64_t)slice * tslice;
+  const int64_t t1 = min(T, t0 + tslice);
+  const int npairs = (int)((t1 - t0 + 2 * kStrT - 1) / (2 * kStrT));
+  // Staging roles: rows srow + 32q (X: q < 4, P: q < 2), 8 t at 8*sc.
+  const int srow = tid >> 3, sc = tid & 7;
+  int64_t xoff[4], poff[2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) xoff[q] = min(m0 + srow + 32 * q, M - 1) * T;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) poff[q] = (int64_t)min(j0 + srow + 32 * q, r - 1) * T;
+
+  auto load = [&](int c, u32x4_t (&xv)[4], u32x4_t (&pv)[2]) {
+    const int64_t t = t0 + (int64_t)c * kStrT + 8 * sc;
+    const int64_t tc = t < t1 ? t : t1 - 8;  // t1 - t0 >= 8: T % 8 == 0
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[q] = *reinterpret_cast<const u32x4_t*>(X + xoff[q] + tc);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) pv[q] = *reinterpret_cast<const u32x4_t*>(P + poff[q] + tc);
+  };
+  auto stage = [&](int c, uint16_t* xb, uint16_t* pb, const u32x4_t (&xv)[4],
+                   const u32x4_t (&pv)[2]) {
+    const bool ok = t0 + (int64_t)c * kStrT + 8 * sc < t1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4_t*>(&xb[(srow + 32 * q) * kStrLd + 8 * sc]) = ok ? xv[q] : zero4();
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<u32x4_t*>(&pb[(srow + 32 * q) * kStrLd + 8 * sc]) = ok ? pv[q] : zero4();
+  };
+  f32x16_t acc[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
+  auto compute = [&](const uint16_t* xb, const uint16_t* pb) {
+#pragma unroll
+    for (int st = 0; st < kStrT / 16; ++st) {
+      const int tt = 16 * st + 8 * h;
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xb[(32 * w + i) * kStrLd + tt]);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {  // a second tile past r holds row r-1 of P, not stored
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(&pb[(32 * ct + i) * kStrLd + tt]);
+        acc[ct] = mfma_32x32x16(a, b, acc[ct]);
+      }
+    }
+  };
+
+  u32x4_t xa[4], pa[2], xn[4], pn[2];
+  load(0, xa, pa);
+  load(1, xn, pn);
+  stage(0, xs[0], ps[0], xa, pa);
+  __syncthreads();
+  // The scheduling barriers keep each chunk's loads ahead of the previous
+  // chunk's compute (left alone, the compiler reuses the fragment registers
+  // for them and waits for every load before the next one issues).
+  for (int p = 0; p < npairs; ++p) {
+    const int c = 2 * p;
+    // buffer 0 holds chunk c; chunk c+1 is in flight (xn, pn)
+    load(c + 2, xa, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xs[0], ps[0]);
+    stage(c + 1, xs[1], ps[1], xn, pn);
+    __syncthreads();
+    load(c + 3, xn, pn);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xs[1], ps[1]);
+    stage(c + 2, xs[0], ps[0], xa, pa);
+    __syncthreads();
+  }
+  // the last loads (chunk 2 npairs + 1) land before the workgroup ends
+  stage(2 * npairs + 1, xs[1], ps[1], xn, pn);
+
+  // element e of tile ct: row 8(e/4) + 4h + e%4 of the wave's 32, column
+  // 32ct + i of the workgroup's 64
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    if (ct < ncol) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + 32 * w + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) part[((int64_t)slice * M + m) * r + j0 + 32 * ct + i] = acc[ct][e];
+      }
+    }
+  }
+}
+
 // out[m][j] = sum over slices (skipped if out == NULL); with sv = s*out:
 // lr[m][j] = bf16(sv), lr[m][r+j] = bf16(sv - hi) (row-major two-term split),
 // lrT[j][m] = bf16(sv), lrT[r+j][m] = bf16(sv - hi) (transposed, row stride
@@ -625,13 +739,40 @@ static bool lora_down_tiled(int64_t M, int64_t T, int r) {
   return M >= 1024 && r >= 64 && r % 32 == 0 && T % 8 == 0 && wgs >= 128 && T <= 16384;
 }
 
+// The streaming form: large M, ranks that are multiples of 32, long T.
+static bool lora_down_streamed(int64_t M, int64_t T, int r) {
+  return M >= 512 && r % 32 == 0 && T % 8 == 0 && T >= 4096;
+}
+
+// t per slice of the streaming form: about 512 workgroups (two per CU), at
+// least 8 chunks a slice.
+static int64_t lora_down_tslice(int64_t M, int64_t T, int r) {
+  const int64_t base = ((M + 127) / 128) * ((r + 63) / 64);
+  const int64_t chunks = (T + kStrT - 1) / kStrT;
+  int64_t S = (512 + base - 1) / base;
+  if (S > chunks / 8) S = chunks / 8;
+  if (S < 1) S = 1;
+  return (chunks + S - 1) / S * kStrT;
+}
+
 int lora_down_slices(int64_t M, int64_t T, int r) {
+  if (lora_down_streamed(M, T, r)) {
+    const int64_t ts = lora_down_tslice(M, T, r);
+    return (int)((T + ts - 1) / ts);
+  }
   return lora_down_tiled(M, T, r) ? (int)((T + kTileT - 1) / kTileT)
                                   : (int)((T + kDownTC - 1) / kDownTC);
 }
 
 hipError_t launch_lora_down_parts(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
                                   int r, float* part, hipStream_t st) {
+  if (lora_down_streamed(M, T, r)) {
+    const int64_t ts = lora_down_tslice(M, T, r);
+    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((r + 63) / 64),
+                    (unsigned)((T + ts - 1) / ts));
+    hipLaunchKernelGGL(lora_down_stream_kernel, grid, dim3(256), 0, st, X, P, M, T, r, ts, part);
+    return hipGetLastError();
+  }
   if (lora_down_tiled(M, T, r)) {
     const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((r + 63) / 64),
                     (unsigned)lora_down_slices(M, T, r));

@@ -313,7 +313,10 @@ def test_fwd_decode_llama7b(M, name):
                                      (1024, 520, 1088, 64), (1100, 200, 320, 96),
                                      # few output tiles: the dense stage splits the
                                      # reduction (eight splits of 16 steps)
-                                     (600, 300, 4096, 16), (520, 1024, 8192, 64)])
+                                     (600, 300, 4096, 16), (520, 1024, 8192, 64),
+                                     # streaming down projection: 64-wide chunks, an odd
+                                     # count (65), ragged 128-row blocks, r = 32 and 96
+                                     (600, 520, 4160, 32), (1030, 300, 4096, 96)])
 def test_fwd_full_small(M, N, K, r):
     say("fwd small", M, N, K, r)
     P = Problem(N, K, r, 32.0, seed=M + N + K)
@@ -542,7 +545,10 @@ def run_bwd(P, x, dY, **kw):
                                      (600, 1000, 192, 16), (520, 1100, 320, 32),
                                      (600, 100, 128, 16),
                                      # few dX tiles: the reduction over N is split
-                                     (600, 4096, 512, 16)])
+                                     (600, 4096, 512, 16),
+                                     # streaming down projections: v over N = 4104 (a
+                                     # last chunk of 8), u over K = 4160, r = 32 and 96
+                                     (600, 4104, 320, 32), (1030, 4096, 4160, 96)])
 def test_bwd_full_small(M, N, K, r):
     say("bwd small", M, N, K, r)
     P = Problem(N, K, r, 24.0, seed=M + 2 * N + K)
