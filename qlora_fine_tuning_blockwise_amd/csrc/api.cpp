@@ -466,7 +466,14 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
       e = launch_lora_down_finalize(u_saved, 1, M, r, s, nullptr, nullptr, uT, st);
     }
   }
-  if (e == hipSuccess && (dA || dB)) {
+  // The route depends on the shape alone, so that dA or dB asked for alone
+  // has the bits of the call that asks for both.
+  const int cg = colred_direct_cg(M, K, N, r);
+  if (e == hipSuccess && (dA || dB) && cg) {
+    // One launch writes dA [K, r] and dB [r, N] (transposed) directly.
+    e = launch_colred_direct2(dA ? x : dY, dA ? vT : uT, dA ? K : N, dA ? dA : dB, !dA,
+                              dA && dB ? dY : nullptr, uT, N, dB, true, M, r, cg, gbf, st);
+  } else if (e == hipSuccess && (dA || dB)) {
     // Partial sums: dA's [splits, K, r] at col, dB's [splits, N, r] after it.
     float* colB = col + (size_t)colred_splits(M) * K * r;
     e = launch_colred2(dA ? x : dY, dA ? vT : uT, dA ? K : N, dA ? col : colB,

@@ -173,6 +173,17 @@ hipError_t launch_colred_finalize(const float* part, int splits, int64_t C, int 
 hipError_t launch_colred2(const uint16_t* X0, const uint16_t* PT0, int64_t C0, float* part0,
                           const uint16_t* X1, const uint16_t* PT1, int64_t C1, float* part1,
                           int64_t M, int r, hipStream_t st);
+// Both reductions in one launch written straight to their outputs (no
+// partial sums, no finalize): out = sum_m X[m][c] (PT[j][m] + PT[r+j][m]) as
+// [C, r] or transposed [r, C]. colred_direct_cg(M, K, N, r) decides from the
+// layer's shape alone whether it applies (0: no) and with how many 32-column
+// groups a workgroup (2 or 4; the bits do not depend on it); X1 = NULL: one
+// job.
+int colred_direct_cg(int64_t M, int64_t K, int64_t N, int r);
+hipError_t launch_colred_direct2(const uint16_t* X0, const uint16_t* PT0, int64_t C0,
+                                 void* out0, bool transpose0, const uint16_t* X1,
+                                 const uint16_t* PT1, int64_t C1, void* out1, bool transpose1,
+                                 int64_t M, int r, int cg, bool out_bf16, hipStream_t st);
 hipError_t launch_colred_finalize2(const float* part0, int64_t C0, bool transpose_out0,
                                    void* out0, const float* part1, int64_t C1,
                                    bool transpose_out1, void* out1, int splits, int r, float s,

@@ -669,6 +669,192 @@ __global__ __launch_bounds__(256) void colred_kernel(ColJob j0, ColJob j1, int64
   }
 }
 
+// Direct form for M >= 256 and column counts that are multiples of 8: a
+// workgroup owns 32*kCG columns c of one job and 64 rank columns j, walks the
+// whole of M in 64-row chunks and writes the result itself (no slices, no
+// finalize): out[c][j] = sum_m X[m][c] (PT[j][m] + PT[r+j][m]), stored as
+// [C, r] or transposed [r, C], fp32 or bf16. Chunks of X (64 rows x 32*kCG
+// columns, whole 128-byte lines) and of the split (128 rows: 64 hi, 64 lo,
+// x 64 m) are staged in double-buffered LDS. Wave w takes the 32
+// columns of group w % kCG and, for kCG = 4, both 32-wide rank tiles (for
+// kCG = 2, rank tile w / 2); v_mfma_f32_32x32x16_bf16 with the reduction
+// over m: the x operand reads 8 rows of one column (16-bit LDS reads; the
+// row stride puts the two 8-row halves of a read in distinct banks), the
+// split operand one 16-byte read per lane. The loads run three chunks ahead
+// (the grids are small: about one workgroup per CU for the 70B-shaped
+// projections). Rows past M and past the split's
+// padded length are staged as zeros; rank rows past r are clamped and not
+// stored.
+struct ColOut {
+  const uint16_t* X;
+  const uint16_t* PT;
+  int64_t C;
+  void* out;
+  int transpose_out;
+  unsigned tiles;  // column tiles of 32*kCG
+};
+
+template <int kCG, bool kBf16>
+__global__ __launch_bounds__(256) void colred_direct_kernel(ColOut j0, ColOut j1, int64_t M,
+                                                            int64_t Mp, int r) {
+  constexpr int kCT = 32 * kCG;          // columns per workgroup
+  constexpr int kLdX = kCT + 8;          // staged x row stride (bf16)
+  constexpr int kXP = 64 * kCT / 8 / 256;  // 16-byte x pieces per thread and chunk
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * kLdX];
+  __shared__ __attribute__((aligned(16))) uint16_t ps[2][128 * kStrLd];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 31, h = lane >> 5;
+  const bool second = blockIdx.x >= j0.tiles;
+  const ColOut& J = second ? j1 : j0;
+  const uint16_t* __restrict__ X = J.X;
+  const uint16_t* __restrict__ PT = J.PT;
+  const int64_t C = J.C;
+  const int64_t c0 = (int64_t)(second ? blockIdx.x - j0.tiles : blockIdx.x) * kCT;
+  const int jb = blockIdx.y * 64;
+  const int nquads = (int)((M + 255) / 256);  // four 64-row chunks each
+
+  // Staging roles. x piece e = tid + 256q: row e / (kCT/8), columns
+  // 8 (e % (kCT/8)) (clamped into the matrix). Split piece e = tid + 256q:
+  // tile row e >> 3 (hi rows 0..63, lo rows 64..127), m 8 (e & 7).
+  int64_t xoff[kXP];
+  int xrow[kXP], xcol[kXP];
+#pragma unroll
+  for (int q = 0; q < kXP; ++q) {
+    const int e = tid + 256 * q;
+    xrow[q] = e / (kCT / 8);
+    xcol[q] = 8 * (e % (kCT / 8));
+    xoff[q] = min(c0 + xcol[q], C - 8);
+  }
+  int64_t poff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int pr = (tid >> 3) + 32 * q;
+    const int j = min(jb + (pr & 63), r - 1);
+    poff[q] = (int64_t)(pr < 64 ? j : r + j) * Mp;
+  }
+  const int pm = 8 * (tid & 7);
+
+  auto load = [&](int c, u32x4_t (&xv)[kXP], u32x4_t (&pv)[4]) {
+    const int64_t m = (int64_t)c * 64;
+#pragma unroll
+    for (int q = 0; q < kXP; ++q) {
+      const int64_t row = min(m + xrow[q], M - 1);
+      xv[q] = *reinterpret_cast<const u32x4_t*>(X + row * C + xoff[q]);
+    }
+    const int64_t mm = min(m + pm, Mp - 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pv[q] = *reinterpret_cast<const u32x4_t*>(PT + poff[q] + mm);
+  };
+  auto stage = [&](int c, uint16_t* xb, uint16_t* pb, const u32x4_t (&xv)[kXP],
+                   const u32x4_t (&pv)[4]) {
+    const int64_t m = (int64_t)c * 64;
+#pragma unroll
+    for (int q = 0; q < kXP; ++q)
+      *reinterpret_cast<u32x4_t*>(&xb[xrow[q] * kLdX + xcol[q]]) =
+          m + xrow[q] < M ? xv[q] : zero4();
+    const bool pok = m + pm < Mp;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4_t*>(&pb[((tid >> 3) + 32 * q) * kStrLd + pm]) =
+          pok ? pv[q] : zero4();
+  };
+  constexpr int kJT = kCG == 4 ? 2 : 1;  // rank tiles per wave
+  const int cb = 32 * (w % kCG);
+  const int jt0 = kCG == 4 ? 0 : w / 2;
+  f32x16_t acc[kJT];
+#pragma unroll
+  for (int t = 0; t < kJT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+  auto compute = [&](const uint16_t* xb, const uint16_t* pb) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const uint16_t* xa = &xb[(16 * st + 8 * h) * kLdX + cb + i];
+      u32x4_t a;
+      a.x = (uint32_t)xa[0 * kLdX] | ((uint32_t)xa[1 * kLdX] << 16);
+      a.y = (uint32_t)xa[2 * kLdX] | ((uint32_t)xa[3 * kLdX] << 16);
+      a.z = (uint32_t)xa[4 * kLdX] | ((uint32_t)xa[5 * kLdX] << 16);
+      a.w = (uint32_t)xa[6 * kLdX] | ((uint32_t)xa[7 * kLdX] << 16);
+#pragma unroll
+      for (int t = 0; t < kJT; ++t) {
+        const int tr = 32 * (jt0 + t) + i;
+        const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(&pb[tr * kStrLd + 16 * st + 8 * h]);
+        const u32x4_t bl =
+            *reinterpret_cast<const u32x4_t*>(&pb[(64 + tr) * kStrLd + 16 * st + 8 * h]);
+        acc[t] = mfma_32x32x16(a, bh, acc[t]);
+        acc[t] = mfma_32x32x16(a, bl, acc[t]);
+      }
+    }
+  };
+
+  // Four register slots: while one chunk is computed from LDS, the loads of
+  // the next three are in flight (about 96 KB a workgroup).
+  u32x4_t x0[kXP], p0[4], x1[kXP], p1[4], x2[kXP], p2[4], x3[kXP], p3[4];
+  load(0, x0, p0);
+  load(1, x1, p1);
+  load(2, x2, p2);
+  stage(0, xs[0], ps[0], x0, p0);
+  __syncthreads();
+  for (int qd = 0; qd < nquads; ++qd) {
+    const int c = 4 * qd;
+    load(c + 3, x3, p3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xs[0], ps[0]);
+    stage(c + 1, xs[1], ps[1], x1, p1);
+    __syncthreads();
+    load(c + 4, x0, p0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xs[1], ps[1]);
+    stage(c + 2, xs[0], ps[0], x2, p2);
+    __syncthreads();
+    load(c + 5, x1, p1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xs[0], ps[0]);
+    stage(c + 3, xs[1], ps[1], x3, p3);
+    __syncthreads();
+    load(c + 6, x2, p2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xs[1], ps[1]);
+    stage(c + 4, xs[0], ps[0], x0, p0);
+    __syncthreads();
+  }
+  // the last loads land before the workgroup ends
+  stage(4 * nquads + 1, xs[1], ps[1], x1, p1);
+  stage(4 * nquads + 2, xs[1], ps[1], x2, p2);
+
+  // Element e of tile t: column c0 + cb + 8(e/4) + 4h + e%4, rank
+  // jb + 32(jt0 + t) + i.
+#pragma unroll
+  for (int t = 0; t < kJT; ++t) {
+    const int j = jb + 32 * (jt0 + t) + i;
+    if (j >= r) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t c = c0 + cb + 8 * g + 4 * h;  // four consecutive columns
+      if (c >= C) continue;                       // C % 8 == 0: all four or none
+      const float v0 = acc[t][4 * g], v1 = acc[t][4 * g + 1], v2 = acc[t][4 * g + 2],
+                  v3 = acc[t][4 * g + 3];
+      if (J.transpose_out) {
+        const int64_t o = (int64_t)j * C + c;
+        if (kBf16)
+          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(J.out) + o) =
+              u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        else
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(J.out) + o) = f32x4_t{v0, v1, v2, v3};
+      } else {
+        const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int64_t o = (c + k) * r + j;
+          if (kBf16)
+            static_cast<uint16_t*>(J.out)[o] = (uint16_t)(pack_bf16x2(vv[k], 0.0f) & 0xFFFFu);
+          else
+            static_cast<float*>(J.out)[o] = vv[k];
+        }
+      }
+    }
+  }
+}
+
 // out = s * sum_slice part[slice][c][j], as [C, r] or transposed [r, C];
 // workgroups 0 .. j0.blocks-1 take job j0, the rest job j1.
 struct FinJob {
@@ -839,6 +1025,40 @@ hipError_t launch_colred_finalize(const float* part, int splits, int64_t C, int 
                                   bool transpose_out, void* out, bool out_bf16, hipStream_t st) {
   return launch_colred_finalize2(part, C, transpose_out, out, nullptr, 0, false, nullptr, splits,
                                  r, s, out_bf16, st);
+}
+
+int colred_direct_cg(int64_t M, int64_t K, int64_t N, int r) {
+  if (M < 256 || K % 8 || N % 8) return 0;
+  // measured on the 70B-shaped layer (M = 2048, r = 64): dA and dB of up
+  // and down 75 -> 59 us, of q 36 -> 28 us; with fewer workgroups than CUs
+  // (k and v: 144) the sliced form with its finalize is as fast
+  const int64_t rb = (r + 63) / 64;
+  if (((K + 63) / 64 + (N + 63) / 64) * rb < 256) return 0;
+  return ((K + 127) / 128 + (N + 127) / 128) * rb >= 256 ? 4 : 2;
+}
+
+hipError_t launch_colred_direct2(const uint16_t* X0, const uint16_t* PT0, int64_t C0,
+                                 void* out0, bool transpose0, const uint16_t* X1,
+                                 const uint16_t* PT1, int64_t C1, void* out1, bool transpose1,
+                                 int64_t M, int r, int cg, bool out_bf16, hipStream_t st) {
+  if ((cg != 2 && cg != 4) || M < 256 || C0 % 8 || (X1 && C1 % 8)) return hipErrorInvalidValue;
+  const int64_t Mp = (M + 7) & ~(int64_t)7;
+  const int64_t ct = 32 * cg;
+  const ColOut a{X0, PT0, C0, out0, transpose0 ? 1 : 0, (unsigned)((C0 + ct - 1) / ct)};
+  const ColOut b{X1, PT1, C1, out1, transpose1 ? 1 : 0, X1 ? (unsigned)((C1 + ct - 1) / ct) : 0u};
+  const dim3 grid(a.tiles + b.tiles, (unsigned)((r + 63) / 64));
+  if (cg == 4) {
+    if (out_bf16)
+      hipLaunchKernelGGL((colred_direct_kernel<4, true>), grid, dim3(256), 0, st, a, b, M, Mp, r);
+    else
+      hipLaunchKernelGGL((colred_direct_kernel<4, false>), grid, dim3(256), 0, st, a, b, M, Mp, r);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((colred_direct_kernel<2, true>), grid, dim3(256), 0, st, a, b, M, Mp, r);
+    else
+      hipLaunchKernelGGL((colred_direct_kernel<2, false>), grid, dim3(256), 0, st, a, b, M, Mp, r);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_colred_finalize2(const float* part0, int64_t C0, bool transpose_out0,

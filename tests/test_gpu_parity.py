@@ -619,6 +619,33 @@ def test_bwd_single_adapter_gradient_matches_both(M, N, K, r):
     assert torch.equal(dA1, dA) and torch.equal(dB1, dB)
 
 
+def test_bwd_direct_gradients_single_matches_both():
+    """Shapes whose adapter gradients take the direct reduction (one launch
+    per call, no slices): dA alone and dB alone equal the gradients of the
+    call that asks for both, bit for bit, and a 64-row tail of M pads with
+    zeros. The weight is quantized on the GPU only: both sides are this
+    library."""
+    for M, N, K, r in [(520, 8192, 8192, 16), (300, 24576, 8192, 64)]:
+        say("direct gradients", M, N, K, r)
+        W = syn.torch_normal_bf16((N, K), 0.02, syn.seed_of(9, N), DEV)
+        w = quantize_gpu(W)
+        del W
+        A = dev_bf16(syn.normal_bf16((K, r), 1.0 / np.sqrt(K), 61))
+        B = dev_bf16(syn.normal_bf16((r, N), 0.01, 62))
+        xd = dev_bf16(syn.normal_bf16((M, K), 1.0, 63))
+        dYd = dev_bf16(syn.normal_bf16((M, N), 1.0, 64))
+        P = types.SimpleNamespace(w=w, At=A, Bt=B, alpha=16.0, N=N, K=K, r=r)
+        _, dA, dB = q.qlora_linear_bwd(w, xd, dYd, A, B, 16.0, want_dx=False)
+        torch.cuda.synchronize()
+        dA1 = torch.full_like(dA, float("nan"))
+        dB1 = torch.full_like(dB, float("nan"))
+        _bwd_abi(P, xd, dYd, dA1, None)
+        _bwd_abi(P, xd, dYd, None, dB1)
+        assert torch.equal(dA1, dA) and torch.equal(dB1, dB), (M, N, K, r)
+        del w, xd, dYd
+        torch.cuda.empty_cache()
+
+
 def test_bwd_linear_1024_f32_weight():
     cfg = syn.LINEAR_1024
     N, K = cfg["weights"]["w"]
