@@ -422,14 +422,18 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
   float* col = at<float>(workspace, L.col);
   hipError_t e = hipSuccess;
   // v = dY B^T (B [r,N] is already contiguous along N); the finalize writes
-  // the split of s*v both row-major (dX tiles) and transposed (dA).
+  // the split of s*v both row-major (dX tiles) and transposed (dA). With a
+  // saved u, the transposed split of s u for dB shares that launch.
+  bool uT_done = false;
   if (lora_down_full_ok(M, N, r)) {
     e = launch_lora_down_full(dY, B, M, N, r, s, v, svlr, dA ? vT : nullptr, st);
   } else {
     e = launch_lora_down_parts(dY, B, M, N, r, down, st);
+    uT_done = dB && !need_u;
     if (e == hipSuccess)
-      e = launch_lora_down_finalize(down, lora_down_slices(M, N, r), M, r, s, v, svlr,
-                                    dA ? vT : nullptr, st);
+      e = launch_lora_down_finalize2(down, lora_down_slices(M, N, r), v, svlr, dA ? vT : nullptr,
+                                     uT_done ? u_saved : nullptr, 1, nullptr, nullptr, uT, M, r,
+                                     s, st);
   }
   if (e == hipSuccess && dX && L.plain) {  // dX = dY w_hat through w_hat^T [K,N]
     uint16_t* Wt = at<uint16_t>(workspace, L.Wt);
@@ -462,7 +466,7 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
                                         uT,
                                         st);
       }
-    } else {
+    } else if (!uT_done) {
       e = launch_lora_down_finalize(u_saved, 1, M, r, s, nullptr, nullptr, uT, st);
     }
   }

@@ -71,6 +71,11 @@ hipError_t launch_lora_down_full(const uint16_t* X, const uint16_t* P, int64_t M
                                  hipStream_t st);
 hipError_t launch_lora_down_finalize(const float* part, int slices, int64_t M, int r, float s,
                                      float* out, uint16_t* lr, uint16_t* lrT, hipStream_t st);
+// Two independent finalizes of the same M and r in one launch.
+hipError_t launch_lora_down_finalize2(const float* part0, int slices0, float* out0, uint16_t* lr0,
+                                      uint16_t* lrT0, const float* part1, int slices1,
+                                      float* out1, uint16_t* lr1, uint16_t* lrT1, int64_t M, int r,
+                                      float s, hipStream_t st);
 
 // y = x W_hat^T + [ulr-extended term], M > 16 path (MFMA tiles).
 hipError_t launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,

@@ -497,15 +497,28 @@ __global__ __launch_bounds__(256) void lora_down_stream_kernel(const uint16_t* _
 // out[m][j] = sum over slices (skipped if out == NULL); with sv = s*out:
 // lr[m][j] = bf16(sv), lr[m][r+j] = bf16(sv - hi) (row-major two-term split),
 // lrT[j][m] = bf16(sv), lrT[r+j][m] = bf16(sv - hi) (transposed, row stride
-// Mp, zero for M <= m < Mp). Either split output may be NULL. The grid
-// covers Mp * r elements.
-__global__ __launch_bounds__(256) void lora_down_finalize_kernel(
-    const float* __restrict__ part, int slices, int64_t M, int64_t Mp, int r, float s,
-    float* __restrict__ out, uint16_t* __restrict__ lr, uint16_t* __restrict__ lrT) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Mp, zero for M <= m < Mp). Either split output may be NULL. Two
+// independent jobs of the same M and r share a launch: workgroups 0 ..
+// j0.blocks-1 take job j0 (each job's blocks cover Mp * r elements).
+struct FinJobD {
+  const float* part;
+  int slices;
+  float* out;
+  uint16_t* lr;
+  uint16_t* lrT;
+  unsigned blocks;
+};
+
+__global__ __launch_bounds__(256) void lora_down_finalize_kernel(FinJobD j0, FinJobD j1, int64_t M,
+                                                                 int64_t Mp, int r, float s) {
+  const bool second = blockIdx.x >= j0.blocks;
+  const FinJobD& J = second ? j1 : j0;
+  const int64_t i = (int64_t)(second ? blockIdx.x - j0.blocks : blockIdx.x) * 256 + threadIdx.x;
   if (i >= Mp * r) return;
   const int64_t m = i / r;
   const int j = (int)(i % r);
+  uint16_t* __restrict__ lr = J.lr;
+  uint16_t* __restrict__ lrT = J.lrT;
   if (m >= M) {
     if (lrT) {
       lrT[(int64_t)j * Mp + m] = 0;
@@ -513,8 +526,8 @@ __global__ __launch_bounds__(256) void lora_down_finalize_kernel(
     }
     return;
   }
-  const float v = sum_strided<8>(part + i, M * r, slices);
-  if (out) out[i] = v;
+  const float v = sum_strided<8>(J.part + i, M * r, J.slices);
+  if (J.out) J.out[i] = v;
   const float sv = s * v;
   const uint32_t hi = pack_bf16x2(sv, 0.0f) & 0xFFFFu;
   const float rem = sv - __uint_as_float(hi << 16);
@@ -973,10 +986,20 @@ hipError_t launch_lora_down_parts(const uint16_t* X, const uint16_t* P, int64_t 
 
 hipError_t launch_lora_down_finalize(const float* part, int slices, int64_t M, int r, float s,
                                      float* out, uint16_t* lr, uint16_t* lrT, hipStream_t st) {
+  return launch_lora_down_finalize2(part, slices, out, lr, lrT, nullptr, 0, nullptr, nullptr,
+                                    nullptr, M, r, s, st);
+}
+
+hipError_t launch_lora_down_finalize2(const float* part0, int slices0, float* out0, uint16_t* lr0,
+                                      uint16_t* lrT0, const float* part1, int slices1,
+                                      float* out1, uint16_t* lr1, uint16_t* lrT1, int64_t M, int r,
+                                      float s, hipStream_t st) {
   const int64_t Mp = (M + 7) & ~(int64_t)7;
-  const dim3 grid((unsigned)((Mp * r + 255) / 256));
-  hipLaunchKernelGGL(lora_down_finalize_kernel, grid, dim3(256), 0, st, part, slices, M, Mp, r, s,
-                     out, lr, lrT);
+  const unsigned blocks = (unsigned)((Mp * r + 255) / 256);
+  const FinJobD j0{part0, slices0, out0, lr0, lrT0, blocks};
+  const FinJobD j1{part1, slices1, out1, lr1, lrT1, part1 ? blocks : 0u};
+  hipLaunchKernelGGL(lora_down_finalize_kernel, dim3(j0.blocks + j1.blocks), dim3(256), 0, st, j0,
+                     j1, M, Mp, r, s);
   return hipGetLastError();
 }
 
