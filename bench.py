@@ -73,8 +73,8 @@ ACT_DTYPE_NAME = "bfloat16"  # y and dX: the activations' compute dtype
 # for an elementwise copy of known size. Valid while every listed source
 # hashes to the recorded value; None: not measured for these sources.
 TRAFFIC = {"call": "fwd_up", "sources": ["api.cpp", "quantize.hip", "gemm_nt.hip", "lora.hip"],
-           "src_sha256": "6826268cf0165f7f22b3dff00c6bdb7121a01e7ecc2e3e708af21e9d569a7aa2",
-           "fetch_bytes": 1688613216, "write_bytes": 601358387}
+           "src_sha256": "5c41a644e78230852249b63c7f641a7cae001c03c6470a3f0f8bd0e3567cb779",
+           "fetch_bytes": 1710838366, "write_bytes": 601358336}
 
 
 def log(*a):
@@ -336,7 +336,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "call": "qlora_linear_fwd (whole call)", "label": lab,
-                "kernels": ["transpose_kernel", "lora_down_tile_kernel", "lora_down_finalize_kernel",
+                "kernels": ["transpose_kernel", "lora_down_stream_kernel", "lora_down_finalize_kernel",
                             "dequant_kernel<true> (K-slab)", "gemm_nt_kernel"],
                 "shape": {"M": M, "N": pu["N"], "K": pu["K"], "r": r},
                 "flops_per_call": rflops, "flops_formula": "2MNK + 2Mr(K+N)",
