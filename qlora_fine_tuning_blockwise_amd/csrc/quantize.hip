@@ -23,9 +23,11 @@ namespace qlora {
 namespace {
 
 constexpr int kLut = 128;  // 65 live buckets, padded so a masked index stays in bounds
-// Threads per group: 256 (8 passes) for large tensors; 512 (4 passes) when
-// there are too few groups to fill the GPU with 256-thread workgroups.
-constexpr int kQSmallGroups = 4096;
+// Threads per group: 512 (4 passes). Measured against 256 threads x 8 passes
+// on one GPU: equal or faster for every layer shape (8192 x 8192: 31.3 ->
+// 28.4 us; 8192 x 28672: 115.5 -> 109.8 us; 28672 x 8192: 117.0 -> 115.7
+// us), and it fills the GPU when there are few groups.
+constexpr int kQThreadsUsed = 512;
 static_assert(kGroup == 4 * 64 && 2 * kLut == 256, "");
 
 // Max of a non-negative value over each aligned group of 8 lanes.
@@ -462,21 +464,12 @@ hipError_t launch_quantize(const void* W, bool f32_in, int64_t n, uint8_t* codes
   const int64_t ng = (nb + kGroup - 1) / kGroup;
   if (ng == 0) return hipSuccess;
   const dim3 grid((unsigned)ng);
-  if (ng < kQSmallGroups) {
-    if (f32_in)
-      hipLaunchKernelGGL((quantize_kernel<true, 512>), grid, dim3(512), 0, st, W, nb, codes, q8,
-                         s2, cb);
-    else
-      hipLaunchKernelGGL((quantize_kernel<false, 512>), grid, dim3(512), 0, st, W, nb, codes, q8,
-                         s2, cb);
-  } else {
-    if (f32_in)
-      hipLaunchKernelGGL((quantize_kernel<true, 256>), grid, dim3(256), 0, st, W, nb, codes, q8,
-                         s2, cb);
-    else
-      hipLaunchKernelGGL((quantize_kernel<false, 256>), grid, dim3(256), 0, st, W, nb, codes, q8,
-                         s2, cb);
-  }
+  if (f32_in)
+    hipLaunchKernelGGL((quantize_kernel<true, kQThreadsUsed>), grid, dim3(kQThreadsUsed), 0, st, W,
+                       nb, codes, q8, s2, cb);
+  else
+    hipLaunchKernelGGL((quantize_kernel<false, kQThreadsUsed>), grid, dim3(kQThreadsUsed), 0, st, W,
+                       nb, codes, q8, s2, cb);
   return hipGetLastError();
 }
 
