@@ -97,6 +97,8 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u, bool l
 
 struct BwdLayout {
   size_t At = 0, down = 0, v = 0, svlr = 0, vT = 0, uT = 0, col = 0, Wt = 0, part = 0, total = 0;
+  size_t dxpart = 0;  // split sums of the in-register dX kernel (dxsplit > 1)
+  int dxsplit = 1;
   bool plain = false;
   int splits = 1;  // reduction splits of the dense stage for dX
 };
@@ -124,6 +126,9 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u, bool l
     L.Wt = c.take((size_t)K * N * 2);
     L.splits = gemm_nt_splits(M, K, N);
     if (L.splits > 1) L.part = c.take((size_t)L.splits * M * K * 4);
+  } else if (M > 0) {
+    L.dxsplit = gemm_bwd_splits(M, N, K);
+    if (L.dxsplit > 1) L.dxpart = c.take((size_t)L.dxsplit * M * K * 4);
   }
   L.total = c.off;
   return L;
@@ -443,7 +448,8 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
                          st, L.splits, at<float>(workspace, L.part));
   } else if (e == hipSuccess && dX) {
     e = launch_gemm_bwd(dY, codes, absmax_q, absmax_scale, svlr, A, M, N, K, r, dX,
-                        dx_dtype == QLORA_DTYPE_BF16, cb, st);
+                        dx_dtype == QLORA_DTYPE_BF16, cb, st,
+                        L.dxsplit > 1 ? at<float>(workspace, L.dxpart) : nullptr);
   }
   // The split of s u first (it depends only on x, A or the saved u), so that
   // both reductions over M, dA = x^T (s v) and dB = (s u)^T dY, run as one

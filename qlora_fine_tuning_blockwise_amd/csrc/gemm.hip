@@ -609,6 +609,12 @@ struct BwdArgs {
   void* dX;
   int64_t M, N, K;
   int r;
+  // Reduction split (nsplit > 1): workgroup z takes the z-th range of whole
+  // 64-row steps of N and stores fp32 sums for rows m < M to part + z*M*K
+  // (the adapter term rides in split 0); a reduce launch adds the splits in
+  // order into dX.
+  int nsplit;
+  float* part;
 };
 
 // Tile mapping (v_mfma_f32_32x32x16_bf16). Lane l = 32h + c of wave w:
@@ -646,7 +652,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
   const int64_t m0 = (int64_t)blockIdx.y * kBM;
   const int64_t kt0 = (int64_t)blockIdx.x * kBN;
   const int64_t KB = K / 64;
-  const int64_t NS = (N + 63) / 64;
+  // this workgroup's steps: [nsb, nsb + NS) of the (N + 63) / 64 steps of N
+  const int64_t NS_all = (N + 63) / 64;
+  const int split = (int)blockIdx.z;
+  const int64_t per = (NS_all + p.nsplit - 1) / p.nsplit;
+  const int64_t nsb = split * per;
+  const int64_t NS = per < NS_all - nsb ? per : NS_all - nsb;
   const int64_t kbase = kt0 + 64 * w;
   const bool wave_live = kbase < K;
 
@@ -679,7 +690,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
 
   // 8 vector-memory instructions
   auto issue_y = [&](int64_t ns, uint16_t* ydst) {
-    int64_t ccl = ns * 64 + ychunk * 8;
+    int64_t ccl = (nsb + ns) * 64 + ychunk * 8;
     if (ccl + 8 > N) ccl = N - 8;
     const uint16_t* ysrc = yrow0 + ccl;
 #pragma unroll
@@ -690,7 +701,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
   auto issue_codes = [&](int64_t ns, uint8_t* cdst) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      int64_t row = ns * 64 + crow[j];
+      int64_t row = (nsb + ns) * 64 + crow[j];
       row = row < N ? row : N - 1;
       __builtin_amdgcn_global_load_lds(p.codes + row * (K / 2) + ccol + 16 * chalf[j],
                                        cdst + w * 2048 + 64 * j * 16, 16, 0, 0);
@@ -698,12 +709,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
   };
   // 2 vector-memory instructions (unconditional; masked when the table is built)
   auto load_scale = [&](int64_t ns, int& qv, float& sv) {
-    const int64_t nn = ns * 64 + (tid & 63);
+    const int64_t nn = (nsb + ns) * 64 + (tid & 63);
     const int64_t bi = (nn < N ? nn : N - 1) * KB + (tblk_ok ? tblk : KB - 1);
     qv = (int)p.q8[bi];
     sv = p.s2[bi >> 8];
   };
-  auto scale_ok = [&](int64_t ns) { return ns * 64 + (tid & 63) < N && tblk_ok; };
+  auto scale_ok = [&](int64_t ns) { return (nsb + ns) * 64 + (tid & 63) < N && tblk_ok; };
 
   f32x16_t acc[8][2];
 #pragma unroll
@@ -834,9 +845,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
   if (ns < NS) step(ns, std::integral_constant<int, 0>());
   if (ns + 1 < NS) step(ns + 1, std::integral_constant<int, 1>());
 
-  // Adapter term as 2r extra reduction elements, 16 per MFMA.
+  // Adapter term as 2r extra reduction elements, 16 per MFMA (split 0).
   const int r = p.r, r2 = 2 * r;
-  for (int q = 0; q < r2 / 16; ++q) {
+  for (int q = 0; q < (split == 0 ? r2 / 16 : 0); ++q) {
     const int jj = 16 * q + 8 * h;
     const int jb = jj % r;
     u32x4_t bfr[2];
@@ -855,7 +866,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
   }
 
   const int64_t kcol = kbase + 2 * c;
-  if (wave_live) {
+  if (wave_live && p.nsplit > 1) {  // fp32 partial sums of this split
+    float* dst = p.part + (int64_t)split * M * K;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) store2<false>(dst, K, m, kcol, K, acc[mt][0][e], acc[mt][1][e]);
+      }
+  } else if (wave_live) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -881,18 +901,49 @@ hipError_t launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const int8_t
   return hipGetLastError();
 }
 
+int gemm_bwd_splits(int64_t M, int64_t N, int64_t K) {
+  // Few output tiles (small M): split the reduction over N into ranges of
+  // at least two 64-row steps so that the launch fills the GPU (measured
+  // on the 1024 x 1024 layer at M = 16: 4 workgroups walking all 16 steps
+  // took 45 us). The general kernel (N % 8 != 0) does not split.
+  if (N % 8) return 1;
+  const int64_t tiles = ((K + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
+  if (tiles >= 64) return 1;
+  const int64_t steps = (N + 63) / 64;
+  int64_t s = 256 / tiles;
+  if (s > steps / 2) s = steps / 2;
+  if (s > 64) s = 64;
+  // the fp32 partial sums (s * M * K * 4 bytes) stay within the size of the
+  // NF4 weight (N * K / 2 bytes): small M only
+  if (s > N / (8 * M)) s = N / (8 * M);
+  if (s < 2) return 1;
+  // no empty split: the last range must hold a step
+  while (s > 1 && (s - 1) * ((steps + s - 1) / s) >= steps) --s;
+  return (int)s;
+}
+
 hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_t* q8,
                            const float* s2, const uint16_t* svlr, const uint16_t* A, int64_t M,
                            int64_t N, int64_t K, int r, void* dX, bool dx_bf16,
-                           const Codebook& cb, hipStream_t st) {
-  const dim3 grid((unsigned)((K + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
+                           const Codebook& cb, hipStream_t st, float* part) {
+  const int nsplit = part ? gemm_bwd_splits(M, N, K) : 1;
   if (N % 8 == 0) {
-    const BwdArgs a{dY, codes, q8, s2, svlr, A, dX, M, N, K, r};
+    const dim3 grid((unsigned)((K + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM),
+                    (unsigned)nsplit);
+    const BwdArgs a{dY, codes, q8, s2, svlr, A, dX, M, N, K, r, nsplit, part};
     if (dx_bf16)
       hipLaunchKernelGGL(gemm_bwd_kernel<true>, grid, dim3(256), 0, st, a, cb);
     else
       hipLaunchKernelGGL(gemm_bwd_kernel<false>, grid, dim3(256), 0, st, a, cb);
-  } else if (dx_bf16) {
+    if (nsplit > 1) {
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      return launch_split_reduce(part, nsplit, M * K, dX, dx_bf16, st);
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((K + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
+  if (dx_bf16) {
     hipLaunchKernelGGL(gemm_bwd_general_kernel<true>, grid, dim3(256), 0, st, dY, codes, q8, s2,
                        svlr, A, M, N, K, r, dX, cb);
   } else {

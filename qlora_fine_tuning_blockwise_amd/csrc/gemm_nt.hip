@@ -477,6 +477,16 @@ bool gemm_nt_supported(int64_t Kr, int64_t lda, int64_t ldb, int64_t N, bool b_k
   return Kr >= kNtBK && Kr % kNtBK == 0 && lda % 8 == 0 && 2 * kNtBM * lda + 2 * Kr < lim && b_ok;
 }
 
+hipError_t launch_split_reduce(const float* part, int splits, int64_t n, void* y, bool y_bf16,
+                               hipStream_t st) {
+  const dim3 rg((unsigned)((n + 1023) / 1024));
+  if (y_bf16)
+    hipLaunchKernelGGL(split_reduce_kernel<true>, rg, dim3(256), 0, st, part, splits, n, y);
+  else
+    hipLaunchKernelGGL(split_reduce_kernel<false>, rg, dim3(256), 0, st, part, splits, n, y);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                           const uint16_t* e, const uint16_t* f, int64_t M, int64_t N, int64_t Kr,
                           int r, void* y, bool y_bf16, bool b_kslab, hipStream_t st,
@@ -498,12 +508,7 @@ hipError_t launch_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int
   if (ksplit > 1) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t n = M * N;
-    const dim3 rg((unsigned)((n + 1023) / 1024));
-    if (y_bf16)
-      hipLaunchKernelGGL(split_reduce_kernel<true>, rg, dim3(256), 0, st, part, ksplit, n, y);
-    else
-      hipLaunchKernelGGL(split_reduce_kernel<false>, rg, dim3(256), 0, st, part, ksplit, n, y);
+    return launch_split_reduce(part, ksplit, M * N, y, y_bf16, st);
   }
   return hipGetLastError();
 }

@@ -105,10 +105,18 @@ hipError_t launch_gemv_tiles(const uint16_t* x, const uint8_t* codes, const int8
                              void* y, bool y_bf16, const Codebook& cb, hipStream_t st);
 
 // dX = dY W_hat + [svlr-extended term with A].
+// With a buffer `part` of gemm_bwd_splits(M, N, K) * M * K floats (when that
+// count is above 1) the reduction over N is split across workgroups and the
+// splits are added in order; part = NULL: no split.
+int gemm_bwd_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_t* q8,
                            const float* s2, const uint16_t* svlr, const uint16_t* A, int64_t M,
                            int64_t N, int64_t K, int r, void* dX, bool dx_bf16,
-                           const Codebook& cb, hipStream_t st);
+                           const Codebook& cb, hipStream_t st, float* part = nullptr);
+// y[i] = sum over s of part[s][i] for i < n, in split order (fp32, or bf16 by
+// round to nearest even of the fp32 sum).
+hipError_t launch_split_reduce(const float* part, int splits, int64_t n, void* y, bool y_bf16,
+                               hipStream_t st);
 
 // Large-M path: plain bf16 GEMM y[M,N] = a[M,Kr] b[N,Kr]^T + e[M,2r] [f|f][N,2r]^T
 // (a row-major with row stride lda; b row-major with row stride ldb, or in

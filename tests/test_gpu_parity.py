@@ -548,7 +548,11 @@ def run_bwd(P, x, dY, **kw):
                                      (600, 4096, 512, 16),
                                      # streaming down projections: v over N = 4104 (a
                                      # last chunk of 8), u over K = 4160, r = 32 and 96
-                                     (600, 4104, 320, 32), (1030, 4096, 4160, 96)])
+                                     (600, 4104, 320, 32), (1030, 4096, 4160, 96),
+                                     # small M: dX's reduction over N split into
+                                     # ranges (11 with a last step of 8 rows and a
+                                     # 64-column last tile; 32)
+                                     (3, 2056, 320, 16), (16, 4096, 1024, 64)])
 def test_bwd_full_small(M, N, K, r):
     say("bwd small", M, N, K, r)
     P = Problem(N, K, r, 24.0, seed=M + 2 * N + K)
@@ -684,7 +688,7 @@ def test_bwd_train_llama7b(name):
     tol_check(host(dB), g["dB"], f"dB train {name}")
 
 
-@pytest.mark.parametrize("M,N", [(40, 320), (600, 640)])
+@pytest.mark.parametrize("M,N", [(40, 320), (600, 640), (16, 1024)])
 def test_bwd_one_hot_dy_rows_exact(M, N):
     K, r = 512, 16
     P = Problem(N, K, r, 32.0, seed=11)
