@@ -66,12 +66,16 @@ struct Carve {
 
 struct FwdLayout {
   size_t At = 0, Bt = 0, u = 0, ulr = 0, down = 0, W = 0, part = 0, total = 0;
+  size_t fpart = 0;  // split sums of the tile kernel (fsplit > 1)
+  int fsplit = 1;
   bool gemv_path = false, plain = false, fused = false;
   int splits = 1;  // reduction splits of the dense stage (fp32 partials at `part`)
 };
 
-// lean: the layout of the lean route (no bf16 copy of the weight).
-FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u, bool lean = false) {
+// lean: the layout of the lean route (no bf16 copy of the weight); nosplit:
+// without the tile kernel's split sums (it then walks all of K).
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u, bool lean = false,
+                     bool nosplit = false) {
   FwdLayout L;
   Carve c;
   L.gemv_path = M <= kGemvMaxM;
@@ -89,6 +93,9 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int r, bool need_u, bool l
       L.W = c.take((size_t)N * K * 2);
       L.splits = gemm_nt_splits(M, N, K);
       if (L.splits > 1) L.part = c.take((size_t)L.splits * M * N * 4);
+    } else if (!L.fused && !nosplit) {
+      L.fsplit = gemm_fwd_splits(M, N, K);
+      if (L.fsplit > 1) L.fpart = c.take((size_t)L.fsplit * M * N * 4);
     }
   }
   L.total = c.off;
@@ -202,6 +209,12 @@ void* device_view(void* p) {
 }
 
 }  // namespace
+
+size_t fwd_workspace_nosplit(int64_t M, int64_t N, int64_t K, int r) {
+  if (M < 0 || !shape_ok(N, K) || !rows_ok(M, N, K) || !rank_ok(r)) return 0;
+  return fwd_layout(M, N, K, r, true, true, true).total;
+}
+
 }  // namespace qlora
 
 using namespace qlora;
@@ -335,6 +348,8 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
     return QLORA_ERR_ALIGN;
   FwdLayout L = fwd_layout(M, N, K, r, u_out == nullptr);
   if (L.plain && workspace_bytes < L.total) L = fwd_layout(M, N, K, r, u_out == nullptr, true);
+  if (L.fsplit > 1 && workspace_bytes < L.total)
+    L = fwd_layout(M, N, K, r, u_out == nullptr, true, true);
   if (!workspace || workspace_bytes < L.total) return QLORA_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -374,7 +389,8 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
       e = launch_gemm_nf4_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, cb,
                               st);
     } else if (e == hipSuccess) {
-      e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, cb, st);
+      e = launch_gemm_fwd(x, codes, absmax_q, absmax_scale, ulr, Bt, M, N, K, r, y, ybf, cb, st,
+                          L.fsplit > 1 ? at<float>(workspace, L.fpart) : nullptr);
     }
   }
   return launch_status(e);

@@ -122,6 +122,12 @@ struct FwdArgs {
   void* y;
   int64_t M, N, K;
   int r;
+  // Reduction split (nsplit > 1): workgroup z takes the z-th range of whole
+  // 64-weight blocks of K and stores fp32 sums for rows m < M to
+  // part + z*M*N (the adapter term rides in split 0); a reduce launch adds
+  // the splits in order into y.
+  int nsplit;
+  float* part;
 };
 
 // Write 2 adjacent fp32 (or bf16) outputs of row m starting at column c.
@@ -199,25 +205,39 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m0 = (int64_t)blockIdx.y * kF2BM, n0 = (int64_t)blockIdx.x * kF2BN;
   const int64_t KB = K / 64;
-  const int nsteps = (int)(K / 32);
+  // this workgroup's blocks [kblk0, kblk0 + nsteps/2): whole blocks, so the
+  // local step parity is the global one
+  const int split = (int)blockIdx.z;
+  const int64_t bper = (KB + p.nsplit - 1) / p.nsplit;
+  const int64_t kblk0 = split * bper;
+  const int nsteps = (int)(2 * (bper < KB - kblk0 ? bper : KB - kblk0));
+  const int64_t kstep0 = 2 * kblk0;  // first global step
   if (tid < 16) levels[tid] = cb.level[tid];
   auto clamp = [&](int kb) { return kb < nsteps ? kb : nsteps - 1; };
 
   // x staging role: chunk q = tid + 256 j (j < 8) of the tile -> row q / 4,
-  // 16-byte chunk q % 4; rows past M read row M-1 (never stored).
+  // 16-byte chunk q % 4. Rows past M are not loaded: their LDS rows keep
+  // whatever they held and only feed accumulator rows that are never stored
+  // (at small M this saves all but M of the tile's 512 rows of traffic).
+  // Every step waits for all of its loads, so skipping some costs no wait.
   const uint16_t* xsrc[8];
   int xdst[8];
+  bool xok[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int q = tid + 256 * j, row = q >> 2, c = q & 3;
-    const int64_t grow = m0 + row < M ? m0 + row : M - 1;
+    xok[j] = m0 + row < M;
+    const int64_t grow = xok[j] ? m0 + row : M - 1;
     xsrc[j] = p.x + grow * K + 8 * c;
     xdst[j] = row * 32 + 8 * (c ^ ((row >> 2) & 3));
   }
   u32x4_t xr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) xr[j] = zero4();
   auto load_x = [&](int kb) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xr[j] = *reinterpret_cast<const u32x4_t*>(xsrc[j] + 32 * kb);
+    for (int j = 0; j < 8; ++j)
+      if (xok[j]) xr[j] = *reinterpret_cast<const u32x4_t*>(xsrc[j] + 32 * (kstep0 + kb));
   };
   auto store_x = [&](int tile) {
 #pragma unroll
@@ -245,10 +265,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
   int qv = 0;
   float sv = 0.0f;
   auto load_c = [&](int par, int kb) {
-    cr[par] = *reinterpret_cast<const u32x2_t*>(dcode + 16 * kb);
+    cr[par] = *reinterpret_cast<const u32x2_t*>(dcode + 16 * (kstep0 + kb));
   };
   auto load_s = [&](int kb) {
-    const int64_t bi = dblk + kb / 2;
+    const int64_t bi = dblk + kblk0 + kb / 2;
     qv = (int)p.q8[bi];
     sv = p.s2[bi >> 8];
   };
@@ -420,9 +440,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
   }
 
   // Adapter term as 2r extra reduction elements, 16 per MFMA: lane group h
-  // supplies elements 16q + 8h + (0..7).
+  // supplies elements 16q + 8h + (0..7) (split 0).
   const int r = p.r, r2 = 2 * r;
-  for (int q = 0; q < r2 / 16; ++q) {
+  for (int q = 0; q < (split == 0 ? r2 / 16 : 0); ++q) {
     const int jj = 16 * q + 8 * h;
     const int jb = jj % r;
     u32x4_t bfr[4];
@@ -440,6 +460,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
     }
   }
 
+  float* const dst = p.nsplit > 1 ? p.part + (int64_t)split * M * N : nullptr;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int64_t n = n0 + 32 * nt + i;
@@ -449,7 +470,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdArgs p, Codebook cb
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t m = m0 + 128 * w + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (m < M) {
+          if (m < M && dst) {
+            dst[m * N + n] = acc[mt][nt][e];
+          } else if (m < M) {
             if (kOutBf16)
               static_cast<uint16_t*>(p.y)[m * N + n] =
                   (uint16_t)(pack_bf16x2(acc[mt][nt][e], 0.0f) & 0xFFFFu);
@@ -888,16 +911,52 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
 
 }  // namespace
 
+int gemm_fwd_splits(int64_t M, int64_t N, int64_t K) {
+  // Under half as many output tiles as CUs: split the reduction over K into
+  // ranges of whole 64-weight blocks (at least two a range) so that the
+  // launch fills more of the GPU (one workgroup per CU); the fp32 partial
+  // sums (s * M * N * 4 bytes) stay within 24 MB. The count minimises rounds
+  // of 256 workgroups times (blocks per range + 2, the fixed cost of a
+  // workgroup in blocks). Measured at 16 < M < 512 before: every M took
+  // 155-170 us on 4096-wide weights, each workgroup walking all of K.
+  const int64_t tiles = ((N + kF2BN - 1) / kF2BN) * ((M + kF2BM - 1) / kF2BM);
+  if (tiles >= 128) return 1;
+  const int64_t blocks = K / 64;
+  int64_t smax = blocks / 2;
+  if (smax > 64) smax = 64;
+  const int64_t cap = ((int64_t)24 << 20) / (M * N * 4);
+  if (smax > cap) smax = cap;
+  int best = 1;
+  int64_t best_cost = blocks + 2;  // one range: one round
+  for (int64_t s = 2; s <= smax; ++s) {
+    if ((s - 1) * ((blocks + s - 1) / s) >= blocks) continue;  // an empty range
+    const int64_t rounds = (tiles * s + 255) / 256;
+    const int64_t cost = rounds * ((blocks + s - 1) / s + 2);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = (int)s;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
                            const float* s2, const uint16_t* ulr, const uint16_t* Bt, int64_t M,
                            int64_t N, int64_t K, int r, void* y, bool y_bf16, const Codebook& cb,
-                           hipStream_t st) {
-  const FwdArgs a{x, codes, q8, s2, ulr, Bt, y, M, N, K, r};
-  const dim3 grid((unsigned)((N + kF2BN - 1) / kF2BN), (unsigned)((M + kF2BM - 1) / kF2BM));
+                           hipStream_t st, float* part) {
+  const int nsplit = part ? gemm_fwd_splits(M, N, K) : 1;
+  const FwdArgs a{x, codes, q8, s2, ulr, Bt, y, M, N, K, r, nsplit, part};
+  const dim3 grid((unsigned)((N + kF2BN - 1) / kF2BN), (unsigned)((M + kF2BM - 1) / kF2BM),
+                  (unsigned)nsplit);
   if (y_bf16)
     hipLaunchKernelGGL(gemm_fwd_kernel<true>, grid, dim3(256), 0, st, a, cb);
   else
     hipLaunchKernelGGL(gemm_fwd_kernel<false>, grid, dim3(256), 0, st, a, cb);
+  if (nsplit > 1) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_split_reduce(part, nsplit, M * N, y, y_bf16, st);
+  }
   return hipGetLastError();
 }
 

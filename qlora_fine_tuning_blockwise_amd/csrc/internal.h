@@ -78,10 +78,17 @@ hipError_t launch_lora_down_finalize2(const float* part0, int slices0, float* ou
                                       float s, hipStream_t st);
 
 // y = x W_hat^T + [ulr-extended term], M > 16 path (MFMA tiles).
+// With a buffer `part` of gemm_fwd_splits(M, N, K) * M * N floats (when that
+// count is above 1) the reduction over K is split across workgroups and the
+// splits are added in order; part = NULL: no split.
+int gemm_fwd_splits(int64_t M, int64_t N, int64_t K);
+// The lean forward's workspace without the tile kernel's split sums (the
+// smallest workspace qlora_linear_fwd accepts; 0 for invalid sizes).
+size_t fwd_workspace_nosplit(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_gemm_fwd(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
                            const float* s2, const uint16_t* ulr, const uint16_t* Bt, int64_t M,
                            int64_t N, int64_t K, int r, void* y, bool y_bf16, const Codebook& cb,
-                           hipStream_t st);
+                           hipStream_t st, float* part = nullptr);
 
 // Decode path (M <= 16), two launches: part[slice][m][j] = sum over one of
 // decode_down_slices(K) slices of K of x[m,k] A[k,j] (A [K,r] as given), then the GEMV with

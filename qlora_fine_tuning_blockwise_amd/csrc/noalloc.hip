@@ -54,11 +54,14 @@ extern "C" int qlora_linear_fwd_noalloc(const qlora_nf4* w, const uint16_t* x, i
   if (const int st = qlora_nf4_check(w)) return st;
   if (M < 0) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
-  const size_t need = qlora_workspace_bytes(QLORA_OP_FWD_LEAN, M, w->N, w->K, r);
+  size_t need = qlora_workspace_bytes(QLORA_OP_FWD_LEAN, M, w->N, w->K, r);
   // No size for these arguments: the forward's own checks name the error
   // (they all come before its workspace check, so nothing is enqueued).
   if (need == 0)
     return qlora_linear_fwd(w, x, M, A, B, r, alpha, y, y_dtype, u_out, nullptr, 0, stream);
+  // Too large with the tile kernel's split sums: without them (the kernel
+  // then walks all of K in each workgroup).
+  if (need > QLORA_NOALLOC_SCRATCH_BYTES) need = qlora::fwd_workspace_nosplit(M, w->N, w->K, r);
   if (need > QLORA_NOALLOC_SCRATCH_BYTES) return QLORA_ERR_TOO_LARGE;
   void* ws = qlora::scratch_ptr();
   if (!ws) return QLORA_ERR_LAUNCH;  // the runtime could not give the array's address

@@ -246,11 +246,17 @@ def test_workspace_query(lib):
     assert q.qlora_workspace_bytes(0, 16, 4096, 4000, 16) == 0
     assert q.qlora_workspace_bytes(5, 16, 4096, 4096, 16) == 0  # no such op
     # from 512 rows on the fast routes hold one bf16 copy of the weight; the
-    # forward's lean route (fused in-register dequantization) holds none
-    for op in (0, 1):
-        big = q.qlora_workspace_bytes(op, 512, 4096, 1024, 16)
-        small = q.qlora_workspace_bytes(op, 511, 4096, 1024, 16)
-        assert big - small >= 4096 * 1024 * 2
+    # lean routes (in-register dequantization) hold none
+    for fast, lean_op in ((0, 3), (1, 4)):
+        assert q.qlora_workspace_bytes(fast, 512, 4096, 1024, 16) \
+            - q.qlora_workspace_bytes(lean_op, 512, 4096, 1024, 16) >= 4096 * 1024 * 2
+    assert q.qlora_workspace_bytes(1, 512, 4096, 1024, 16) \
+        - q.qlora_workspace_bytes(1, 511, 4096, 1024, 16) >= 4096 * 1024 * 2
+    # below 512 rows, with few output tiles, the forward's tile kernel splits
+    # its reduction over K and the workspace holds the fp32 partial sums: two
+    # ranges for 511 x 4096 (8.4 MB each), none with plenty of tiles
+    assert q.qlora_workspace_bytes(0, 511, 4096, 1024, 16) >= 2 * 511 * 4096 * 4
+    assert q.qlora_workspace_bytes(0, 511, 32768, 1024, 16) < 511 * 32768 * 4
     lean = q.qlora_workspace_bytes(3, 512, 4096, 1024, 16)
     assert 0 < lean < 4096 * 1024 * 2 // 8
     assert q.qlora_workspace_bytes(3, 16, 4096, 1024, 16) == q.qlora_workspace_bytes(0, 16, 4096, 1024, 16)

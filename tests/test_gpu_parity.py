@@ -316,7 +316,11 @@ def test_fwd_decode_llama7b(M, name):
                                      (600, 300, 4096, 16), (520, 1024, 8192, 64),
                                      # streaming down projection: 64-wide chunks, an odd
                                      # count (65), ragged 128-row blocks, r = 32 and 96
-                                     (600, 520, 4160, 32), (1030, 300, 4096, 96)])
+                                     (600, 520, 4160, 32), (1030, 300, 4096, 96),
+                                     # 16 < M < 512 with few tiles: the reduction over K
+                                     # split into ranges of blocks (22 ranges, the last
+                                     # of two blocks; 8 ranges)
+                                     (64, 1000, 4160, 16), (130, 2048, 1024, 32)])
 def test_fwd_full_small(M, N, K, r):
     say("fwd small", M, N, K, r)
     P = Problem(N, K, r, 32.0, seed=M + N + K)

@@ -99,3 +99,31 @@ def test_noalloc_refuses_more_than_its_array():
     torch.cuda.synchronize()
     assert st == 10, q.qlora_strerror(st)
     assert torch.all(y == 7.0)
+
+
+def test_noalloc_runs_unsplit_when_the_split_sums_do_not_fit():
+    """M = 128, N = 16256, K = 16384, r = 256: with the tile kernel's split
+    sums the lean forward's workspace passes the array, without them it fits.
+    The entry point then runs the tile kernel over all of K, which equals a
+    workspace call given one byte less than the split layout (the call falls
+    back the same way), bit for bit; the split call agrees within rounding."""
+    M, N, K, r, alpha = 128, 16256, 16384, 256, 16.0
+    need = q.qlora_workspace_bytes(_lib.OP_FWD_LEAN, M, N, K, r)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    say("noalloc unsplit", M, N, K, r, need)
+    Wd = syn.torch_normal_bf16((N, K), 0.02, syn.seed_of(9, 501), DEV)
+    w = q.qlora_quantize_nf4_dq(Wd)
+    del Wd
+    At = dev_bf16(syn.normal_bf16((K, r), 1.0 / np.sqrt(K), 502))
+    Bt = dev_bf16(syn.normal_bf16((r, N), 0.01, 503))
+    xt = dev_bf16(syn.normal_bf16((M, K), 1.0, 504))
+    y_unsplit = q.qlora_linear_fwd(w, xt, At, Bt, alpha,
+                                   workspace=torch.empty(need - 1, dtype=torch.uint8, device=DEV))
+    y_noalloc = torch.full_like(y_unsplit, float("nan"))
+    q.qlora_linear_fwd_noalloc(w, xt, At, Bt, alpha, y=y_noalloc)
+    y_split = q.qlora_linear_fwd(w, xt, At, Bt, alpha,
+                                 workspace=torch.empty(need, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y_noalloc, y_unsplit)
+    d = (y_split.double() - y_unsplit.double()).norm() / y_unsplit.double().norm()
+    assert d < 1e-5, f"split against unsplit: {d:.3e}"
