@@ -320,7 +320,10 @@ def test_fwd_decode_llama7b(M, name):
                                      # 16 < M < 512 with few tiles: the reduction over K
                                      # split into ranges of blocks (22 ranges, the last
                                      # of two blocks; 8 ranges)
-                                     (64, 1000, 4160, 16), (130, 2048, 1024, 32)])
+                                     (64, 1000, 4160, 16), (130, 2048, 1024, 32),
+                                     # the tiled down projection (M >= 1024, r >= 64,
+                                     # 2048 <= K < 4096: 128 workgroups)
+                                     (4096, 256, 2048, 64)])
 def test_fwd_full_small(M, N, K, r):
     say("fwd small", M, N, K, r)
     P = Problem(N, K, r, 32.0, seed=M + N + K)
