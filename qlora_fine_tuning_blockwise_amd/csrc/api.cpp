@@ -372,7 +372,7 @@ int qlora_linear_fwd(const qlora_nf4* w, const uint16_t* x, int64_t M, const uin
     uint16_t* ulr = at<uint16_t>(workspace, L.ulr);
     e = launch_transpose2_bf16(A, K, r, At, B, r, N, Bt, st);  // A^T [r,K], B^T [N,r]
     if (e == hipSuccess && lora_down_full_ok(M, K, r)) {
-      e = launch_lora_down_full(x, At, M, K, r, s, u, ulr, nullptr, st);
+      e = launch_lora_down_full(x, At, M, K, r, s, u, ulr, nullptr, nullptr, nullptr, st);
     } else {
       if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
       if (e == hipSuccess)
@@ -447,7 +447,9 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
   // saved u, the transposed split of s u for dB shares that launch.
   bool uT_done = false;
   if (lora_down_full_ok(M, N, r)) {
-    e = launch_lora_down_full(dY, B, M, N, r, s, v, svlr, dA ? vT : nullptr, st);
+    uT_done = dB && !need_u;
+    e = launch_lora_down_full(dY, B, M, N, r, s, v, svlr, dA ? vT : nullptr,
+                              uT_done ? u_saved : nullptr, uT_done ? uT : nullptr, st);
   } else {
     e = launch_lora_down_parts(dY, B, M, N, r, down, st);
     uT_done = dB && !need_u;
@@ -480,7 +482,8 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
       uint16_t* At = at<uint16_t>(workspace, L.At);
       e = launch_transpose_bf16(A, K, r, At, st);
       if (e == hipSuccess && lora_down_full_ok(M, K, r)) {
-        e = launch_lora_down_full(x, At, M, K, r, s, nullptr, nullptr, uT, st);
+        e = launch_lora_down_full(x, At, M, K, r, s, nullptr, nullptr, uT, nullptr, nullptr,
+                                  st);
       } else {
         if (e == hipSuccess) e = launch_lora_down_parts(x, At, M, K, r, down, st);
         if (e == hipSuccess)

@@ -64,11 +64,13 @@ int lora_down_slices(int64_t M, int64_t T, int r);
 hipError_t launch_lora_down_parts(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
                                   int r, float* part, hipStream_t st);
 // lora_down and lora_down_finalize in one pass, for large M (see
-// lora_down_full_ok): out, lr, lrT as lora_down_finalize writes them.
+// lora_down_full_ok): out, lr, lrT as lora_down_finalize writes them; with
+// u2T != NULL also the transposed split of s*u2 (u2 fp32 [M, r]), as a
+// one-slice lora_down_finalize of u2 writes it.
 bool lora_down_full_ok(int64_t M, int64_t T, int r);
 hipError_t launch_lora_down_full(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
                                  int r, float s, float* out, uint16_t* lr, uint16_t* lrT,
-                                 hipStream_t st);
+                                 const float* u2, uint16_t* u2T, hipStream_t st);
 hipError_t launch_lora_down_finalize(const float* part, int slices, int64_t M, int r, float s,
                                      float* out, uint16_t* lr, uint16_t* lrT, hipStream_t st);
 // Two independent finalizes of the same M and r in one launch.

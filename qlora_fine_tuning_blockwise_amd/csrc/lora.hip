@@ -171,7 +171,8 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
 }
 
 // Single-pass form for large M (enough 16-row tiles to fill the GPU) and
-// r = 16 kTiles <= 32: one 8-wave workgroup per 16 rows walks the whole of T,
+// r = 16, 32 or 64: one 8-wave workgroup per 16 rows and 16 kTiles rank
+// columns (blockIdx.y: the 32-wide rank block at r = 64) walks the whole of T,
 // wave w taking the 256-wide chunks w, w+8, .... Each iteration but the
 // wave's last first issues the next chunk's loads, its P fragments (clamped
 // into P: past T the staged X is zero, so they multiply zeros) and its X (two
@@ -180,17 +181,24 @@ __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restri
 // operands stay in flight meanwhile. The eight waves' sums are added in a fixed order in LDS and the
 // workgroup writes the outputs of lora_down_finalize (out, the row-major and
 // transposed two-term splits of s*out, zero rows of lrT for M <= m < Mp)
-// itself. Requires T % 32 == 0.
+// itself. With u2T != NULL the same epilogue also writes the transposed
+// two-term split of s*u2 (an fp32 [M, r] matrix the caller already holds,
+// as lora_down_finalize with one slice would) for its rows and rank
+// columns. Requires T % 32 == 0. At r = 64 the two rank blocks of a row
+// block read the same X rows at about the same time, from the same XCD
+// (their workgroup ids differ by a multiple of 8), so the second read is
+// served by that XCD's L2.
 template <int kTiles>
 __global__ __launch_bounds__(512) void lora_down_full_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ P, int64_t M, int64_t Mp,
     int64_t T, int r, float s, float* __restrict__ out, uint16_t* __restrict__ lr,
-    uint16_t* __restrict__ lrT) {
+    uint16_t* __restrict__ lrT, const float* __restrict__ u2, uint16_t* __restrict__ u2T) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[8][16 * kDownLd];
   float(*red)[16][33] = reinterpret_cast<float(*)[16][33]>(&xs[0][0]);  // reused after the MFMAs
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, g = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
-  constexpr int j0 = 0, ntile = kTiles;
+  const int j0 = 16 * kTiles * (int)blockIdx.y;
+  constexpr int ntile = kTiles;
   const int nchunks = (int)((T + 255) / 256);
   const int half = lane >> 5, ch = lane & 31;
   constexpr int kSteps = 8;
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
     const int64_t tw0 = (int64_t)min(ck, nchunks - 1) * 256;
 #pragma unroll
     for (int jt = 0; jt < kTiles; ++jt) {
-      const int64_t prow = 16 * jt + c;
+      const int64_t prow = j0 + 16 * jt + c;
 #pragma unroll
       for (int it = 0; it < kSteps; ++it) {
         const int64_t t = tw0 + 32 * it;
@@ -274,7 +282,18 @@ __global__ __launch_bounds__(512) void lora_down_full_kernel(
       lrT[(int64_t)jg * Mp + m] = 0;
       lrT[(int64_t)(r + jg) * Mp + m] = 0;
     }
+    if (u2T && m < Mp) {
+      u2T[(int64_t)jg * Mp + m] = 0;
+      u2T[(int64_t)(r + jg) * Mp + m] = 0;
+    }
     return;
+  }
+  if (u2T) {
+    const float su = s * u2[m * r + jg];
+    const uint32_t uh = pack_bf16x2(su, 0.0f) & 0xFFFFu;
+    const uint32_t ul = pack_bf16x2(su - __uint_as_float(uh << 16), 0.0f) & 0xFFFFu;
+    u2T[(int64_t)jg * Mp + m] = (uint16_t)uh;
+    u2T[(int64_t)(r + jg) * Mp + m] = (uint16_t)ul;
   }
   float v = red[0][mm][j];
 #pragma unroll
@@ -1004,22 +1023,27 @@ hipError_t launch_lora_down_finalize2(const float* part0, int slices0, float* ou
 }
 
 bool lora_down_full_ok(int64_t M, int64_t T, int r) {
-  return M >= 2048 && T % 32 == 0 && (r == 16 || r == 32);
+  // r = 64 re-reads 64 x T of the rank-side operand per 16 rows: measured at
+  // M = 2048 it beats the sliced kernels with their finalize at T = 1024
+  // (the 70B k and v backward, 85 -> 77 us per call) but loses to the
+  // streaming form from T = 8192 on (4-40 us per call)
+  return M >= 2048 && T % 32 == 0 && (r == 16 || r == 32 || (r == 64 && T < 4096));
 }
 
 hipError_t launch_lora_down_full(const uint16_t* X, const uint16_t* P, int64_t M, int64_t T,
                                  int r, float s, float* out, uint16_t* lr, uint16_t* lrT,
-                                 hipStream_t st) {
+                                 const float* u2, uint16_t* u2T, hipStream_t st) {
   const int64_t Mp = (M + 7) & ~(int64_t)7;
-  const dim3 grid((unsigned)((M + 15) / 16));
-  if (r == 16)
-    hipLaunchKernelGGL(lora_down_full_kernel<1>, grid, dim3(512), 0, st, X, P, M, Mp, T, r, s, out,
-                       lr, lrT);
-  else if (r == 32)
-    hipLaunchKernelGGL(lora_down_full_kernel<2>, grid, dim3(512), 0, st, X, P, M, Mp, T, r, s, out,
-                       lr, lrT);
-  else
+  if (u2T && !u2) return hipErrorInvalidValue;
+  if (r == 16) {
+    hipLaunchKernelGGL(lora_down_full_kernel<1>, dim3((unsigned)((M + 15) / 16)), dim3(512), 0,
+                       st, X, P, M, Mp, T, r, s, out, lr, lrT, u2, u2T);
+  } else if (r == 32 || r == 64) {
+    hipLaunchKernelGGL(lora_down_full_kernel<2>, dim3((unsigned)((M + 15) / 16), r / 32),
+                       dim3(512), 0, st, X, P, M, Mp, T, r, s, out, lr, lrT, u2, u2T);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -542,8 +542,9 @@ def run_bwd(P, x, dY, **kw):
                                      # large-M path (reduction over N = 544, 320)
                                      (600, 544, 192, 16), (520, 320, 640, 32),
                                      # single-pass down projections (v over N, the
-                                     # recomputed u over K) with r = 32, M >= 2048
-                                     (2056, 544, 640, 32),
+                                     # recomputed u over K) with r = 32, M >= 2048,
+                                     # and r = 64 (two 32-wide rank blocks)
+                                     (2056, 544, 640, 32), (2056, 544, 640, 64),
                                      # tiled down projections (128-row tiles, 512-wide
                                      # slices, two rank chunks at r = 96), ragged M
                                      (1100, 200, 1088, 64), (1030, 520, 320, 96),
@@ -581,12 +582,13 @@ def test_bwd_full_small(M, N, K, r):
 
 
 @pytest.mark.parametrize("M,N,K,r", [(5, 520, 1024, 32), (16, 300, 4096, 16),
-                                     (1100, 200, 1088, 64)])
+                                     (1100, 200, 1088, 64), (2056, 544, 640, 64)])
 def test_bwd_decode_recomputed_u_matches_saved(M, N, K, r):
     """The backward recomputes u with the forward's down projection and slice
-    sum (at decode sizes and through the tiled kernel): the same bits as the u
-    the forward returns, so dA and dB agree exactly with u_saved given or
-    not."""
+    sum (at decode sizes, through the tiled kernel, and through the
+    single-pass kernel, whose launch for v also splits a saved u): the same
+    bits as the u the forward returns, so dA and dB agree exactly with
+    u_saved given or not."""
     P = Problem(N, K, r, 24.0, seed=M + N)
     x = syn.normal_bf16((M, K), 1.0, 40 + M)
     dY = syn.normal_bf16((M, N), 1.0, 41 + M)
