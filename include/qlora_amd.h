@@ -189,10 +189,14 @@ int qlora_nf4_check(const qlora_nf4* w);
  * From M = 512 rows on, QLORA_OP_FWD and QLORA_OP_BWD include N*K*2 bytes for
  * one dequantized bf16 copy of the weight (the pages' one layer's worth of
  * 16-bit weights, [P3] "How it works"): the fast route. QLORA_OP_FWD_LEAN is
- * the smallest workspace the forward accepts: with less than the QLORA_OP_FWD
- * size but at least this one, qlora_linear_fwd runs its fused kernel, which
- * dequantizes each weight tile in registers right before the matrix cores
- * use it and never holds a bf16 copy ([P4] "The mechanism"). Likewise
+ * the forward's workspace without that copy: with less than the QLORA_OP_FWD
+ * size but at least this one, qlora_linear_fwd runs its fused kernels, which
+ * dequantize each weight tile in registers right before the matrix cores
+ * use it and never hold a bf16 copy ([P4] "The mechanism"). For some shapes
+ * below 512 rows this size includes fp32 partial sums that split the
+ * reduction over K across workgroups; a workspace too small for them but
+ * large enough for the rest runs the same kernel unsplit (the same result
+ * within rounding, not bit for bit). Likewise
  * QLORA_OP_BWD_LEAN for the backward: with less than the QLORA_OP_BWD size
  * but at least this one, dX runs through the kernel that dequantizes the
  * transposed operand in registers ([P2] s3). Host only; 0 on invalid
