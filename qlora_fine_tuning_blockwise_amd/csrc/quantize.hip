@@ -125,7 +125,9 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
   // Issue every load of the group up front (kQPasses passes x 8 weights).
   // Blocks past the group's end (last group only) load the group's last
   // block instead: no branch around the loads, so each pass waits only for
-  // its own. Their constants and codes are never stored.
+  // its own. Their constants and codes are never stored. The weight is read
+  // once, so the loads carry the nontemporal hint: on the 8192 x 28672 bf16
+  // tensor 106 -> 90 us (0.70 -> 0.82 of HBM peak), the codes unchanged.
   constexpr int kWords = kF32In ? 8 : 4;  // dwords per 8 weights
   uint32_t raw[kQPasses][kWords];
 #pragma unroll
@@ -134,11 +136,12 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
     const int64_t e0 = (b0 + bl) * kBlock + (tid & 7) * 8;
     if (kF32In) {
       const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(W) + e0);
-      const u32x4_t a = p[0], b = p[1];
+      const u32x4_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
       raw[it][0] = a.x; raw[it][1] = a.y; raw[it][2] = a.z; raw[it][3] = a.w;
       raw[it][4] = b.x; raw[it][5] = b.y; raw[it][6] = b.z; raw[it][7] = b.w;
     } else {
-      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(W) + e0);
+      const u32x4_t a = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(W) + e0));
       raw[it][0] = a.x; raw[it][1] = a.y; raw[it][2] = a.z; raw[it][3] = a.w;
     }
   }
@@ -271,7 +274,10 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
 // lookup address is one v_perm: byte 0 = 32g + 2*code (computed four codes
 // at a time), bytes 1..3 = the region's offset. Each wave runs kDqPasses
 // passes with every load issued first. Lanes past the last block redo the
-// last block (same values to the same place), so no lane branches.
+// last block (same values to the same place), so no lane branches. The bf16
+// output is written with the nontemporal hint (it is not read back by this
+// kernel): on the 8192 x 28672 weight 101 -> 83 us row-major and
+// 120 -> 87 us in the K-slab layout.
 // With kKSlab the output is the K-slab layout [K/32][rows][32] of a weight
 // with `rows` rows of kb blocks, and a wave takes 8 consecutive rows (one per
 // group) by kDqPasses consecutive blocks (one per pass) instead: per pass,
@@ -348,11 +354,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     } else {
       dst = out + bk[p] * 64 + 8 * j;
     }
-    *reinterpret_cast<u32x4_t*>(dst) =
-        u32x4_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
-                __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
-                __builtin_amdgcn_perm(v[5], v[4], 0x05040100u),
-                __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)};
+    __builtin_nontemporal_store(u32x4_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
+                                        __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                                        __builtin_amdgcn_perm(v[5], v[4], 0x05040100u),
+                                        __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)},
+                                reinterpret_cast<u32x4_t*>(dst));
   }
 }
 
@@ -368,7 +374,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 // every aligned group of four dwords together. The workgroup then writes
 // out: in the K-slab layout [N/32][K][32] a wave store covers 16 consecutive
 // k rows of one slab, 1 KB of consecutive bytes; row-major, a wave store
-// covers 8 k rows x 128 bytes.
+// covers 8 k rows x 128 bytes. The stores carry the nontemporal hint, as in
+// dequant_kernel.
 constexpr int kDtRows = 64;    // tile rows (n)
 constexpr int kDtCols = 256;   // tile columns (k)
 
@@ -429,7 +436,7 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
       if (k >= K) break;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
           &tile[kl * 32 + ((16 * sl + 4 * pc) ^ (8 * ((kl >> 5) & 3)))]);
-      *reinterpret_cast<u32x4_t*>(out + (slab * K + k) * 32 + 8 * pc) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (slab * K + k) * 32 + 8 * pc));
     }
     return;
   }
@@ -446,7 +453,7 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
         &tile[kl * 32 + ((4 * pc) ^ (8 * ((kl >> 5) & 3)))]);
     uint16_t* dst = out + k * N + nc;
     if (nc + 8 <= N && (N & 7) == 0) {
-      *reinterpret_cast<u32x4_t*>(dst) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
     } else {
       const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
