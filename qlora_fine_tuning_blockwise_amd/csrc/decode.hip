@@ -633,9 +633,12 @@ hipError_t launch_gemv_tiles(const uint16_t* x, const uint8_t* codes, const int8
   const TilesArgs a{x, codes, q8, s2, upart, B, u_out, y, M, N, K, r, slices, s};
   const int64_t tiles = (N + 15) / 16;
   const dim3 grid((unsigned)tiles);
-  // Eight waves per tile when there are few tiles (below 512: under two
-  // workgroups per CU), four otherwise.
-  const bool eight = tiles < 512;
+  // Eight waves per tile up to 1023 tiles, four beyond. Measured on the
+  // 11008 x 4096 weight at M = 1 (688 tiles, a ring of 24 weights): 10.8 us
+  // per GEMV with eight waves against 11.4 us with four, although only two
+  // eight-wave workgroups fit a CU (two rounds): each wave has half the
+  // chunks, so a wave's compute after its data lands is half as long.
+  const bool eight = tiles < 1024;
 #define QLORA_TL(F, B16)                                                                     \
   do {                                                                                       \
     if (eight)                                                                               \
