@@ -274,10 +274,12 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
 // lookup address is one v_perm: byte 0 = 32g + 2*code (computed four codes
 // at a time), bytes 1..3 = the region's offset. Each wave runs kDqPasses
 // passes with every load issued first. Lanes past the last block redo the
-// last block (same values to the same place), so no lane branches. The bf16
-// output is written with the nontemporal hint (it is not read back by this
-// kernel): on the 8192 x 28672 weight 101 -> 83 us row-major and
-// 120 -> 87 us in the K-slab layout.
+// last block (same values to the same place), so no lane branches. The
+// row-major output (the standalone dequantization) is written with the
+// nontemporal hint: on the 8192 x 28672 weight 101 -> 83 us. The K-slab
+// copy keeps plain stores: the dense GEMM reads it right after, and with
+// the hint the layer's calls measured 0.5-1% slower (one box, alternating
+// runs), although the copy alone was faster (120 -> 87 us).
 // With kKSlab the output is the K-slab layout [K/32][rows][32] of a weight
 // with `rows` rows of kb blocks, and a wave takes 8 consecutive rows (one per
 // group) by kDqPasses consecutive blocks (one per pass) instead: per pass,
@@ -354,11 +356,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     } else {
       dst = out + bk[p] * 64 + 8 * j;
     }
-    __builtin_nontemporal_store(u32x4_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
-                                        __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
-                                        __builtin_amdgcn_perm(v[5], v[4], 0x05040100u),
-                                        __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)},
-                                reinterpret_cast<u32x4_t*>(dst));
+    const u32x4_t ov{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
+                     __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                     __builtin_amdgcn_perm(v[5], v[4], 0x05040100u),
+                     __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)};
+    if (kKSlab)
+      *reinterpret_cast<u32x4_t*>(dst) = ov;
+    else
+      __builtin_nontemporal_store(ov, reinterpret_cast<u32x4_t*>(dst));
   }
 }
 
@@ -374,7 +379,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 // every aligned group of four dwords together. The workgroup then writes
 // out: in the K-slab layout [N/32][K][32] a wave store covers 16 consecutive
 // k rows of one slab, 1 KB of consecutive bytes; row-major, a wave store
-// covers 8 k rows x 128 bytes. The stores carry the nontemporal hint, as in
+// covers 8 k rows x 128 bytes. The row-major stores carry the nontemporal
+// hint, the K-slab ones (read by the dense GEMM next) do not, as in
 // dequant_kernel.
 constexpr int kDtRows = 64;    // tile rows (n)
 constexpr int kDtCols = 256;   // tile columns (k)
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
       if (k >= K) break;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
           &tile[kl * 32 + ((16 * sl + 4 * pc) ^ (8 * ((kl >> 5) & 3)))]);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (slab * K + k) * 32 + 8 * pc));
+      *reinterpret_cast<u32x4_t*>(out + (slab * K + k) * 32 + 8 * pc) = v;
     }
     return;
   }
