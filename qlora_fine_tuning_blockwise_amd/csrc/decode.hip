@@ -367,8 +367,7 @@ __device__ __forceinline__ float gv_absmax(int b) {  // b: the byte, zero-extend
 // MFMAs taken out (a timing copy) takes 10.2 us, and the down projection
 // alone 2.2 us, so the stream of codes itself runs at about 4 TB/s here.
 constexpr int kTlMaxR = 32;
-constexpr int kTlMaxM = 2;
-constexpr int kTlUp = 16 * kTlMaxM * kTlMaxR;         // staged slices (16 x M r floats)
+constexpr int kTlMaxM = 4;  // tokens; a launch is built for at most 2 or at most 4
 
 struct TilesArgs {
   const uint16_t* x;      // [M, K] bf16
@@ -388,8 +387,8 @@ __device__ __forceinline__ uint32_t tl_lookup(const char* tab, uint32_t addr) {
   return *reinterpret_cast<const uint16_t*>(tab + addr);
 }
 
-// grid: ceil(N / 16) workgroups of 64 kWaves threads (kWaves = 4, or 8 for
-// weights with under 512 tiles). Workgroup rows n0 .. n0+15 form one 16-row
+// grid: ceil(N / 16) workgroups of 64 kWaves threads (kWaves = 8 for
+// weights with under 1024 tiles, else 4). Workgroup rows n0 .. n0+15 form one 16-row
 // MFMA tile. With bpl = 16 / kWaves, lane (i, g) of wave w owns row n0 + i
 // and the blocks bpl (4 w + g) .. + bpl - 1, two per table; the table
 // (bf16(L[e] c1_hat) for both blocks of a pair, one in each half of an LDS
@@ -397,17 +396,18 @@ __device__ __forceinline__ uint32_t tl_lookup(const char* tab, uint32_t addr) {
 // the wave's 4 KB region. MFMA rows are the tokens; MFMA step s of a block
 // takes, in every lane, the block's weights 8 s .. 8 s + 7, and the x
 // operand of the same k comes from the wave's LDS slice of x (the 256 bpl k
-// its blocks cover, M <= 2; tokens >= M read a zero row).
-template <int kFmt, bool kOutBf16, int kWaves>
+// its blocks cover, M <= kMaxM; tokens >= M read a zero row).
+template <int kFmt, bool kOutBf16, int kWaves, int kMaxM>
 __global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Codebook cb) {
   constexpr int kTlWaves = kWaves;
+  constexpr int kTlUp = 16 * kMaxM * kTlMaxR;  // staged slices (16 x M r floats)
   constexpr int kTlBpl = 16 / kWaves;                          // blocks per lane (K <= 4096)
   constexpr int kSpan = 64 * 4 * kTlBpl;                       // k covered by one wave
-  constexpr int kXw = 2 * kSpan * kTlMaxM;                     // x slice bytes per wave
+  constexpr int kXw = 2 * kSpan * kMaxM;                       // x slice bytes per wave
   __shared__ __attribute__((aligned(16))) uint32_t tabs[kTlWaves][16][64];
   __shared__ __attribute__((aligned(16))) unsigned char xs[kTlWaves][kXw + 16];
   __shared__ __attribute__((aligned(16))) float ups[kTlUp];  // wave 0's staged slices
-  __shared__ __attribute__((aligned(16))) float usm[kTlMaxM * kTlMaxR];  // s*u [M][r]
+  __shared__ __attribute__((aligned(16))) float usm[kMaxM * kTlMaxR];  // s*u [M][r]
   __shared__ __attribute__((aligned(16))) uint16_t bsm[kTlMaxR * 16];  // B tile [r][16]
   typedef __attribute__((address_space(3))) void lds_void;
   const int tid = threadIdx.x, lane = tid & 63, i = lane & 15, g = lane >> 4;
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Co
   const uint32_t nl = (uint32_t)min(i, rows - 1);  // rows past N read row N-1 (never stored)
   const int64_t b0 = kTlBpl * (4 * w + g);          // the lane's first block
 
-  // 1. x slice of this wave (M <= 2 tokens x kSpan k) by direct-to-LDS
+  // 1. x slice of this wave (M <= kMaxM tokens x kSpan k) by direct-to-LDS
   //    loads: instruction q covers 512 k (piece q % kXq) of token q / kXq;
   //    the zero row behind it is written first.
   unsigned char* xw = xs[w];
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Co
   const __amdgpu_buffer_rsrc_t xres = gv_rsrc(p.x, M * K * 2);
   constexpr int kXq = kSpan / 512;  // 1 KB (512 k) pieces per token
 #pragma unroll
-  for (int q = 0; q < kXq * kTlMaxM; ++q) {
+  for (int q = 0; q < kXq * kMaxM; ++q) {
     const int m = q / kXq, hk = q % kXq;
     const int64_t k = (int64_t)kSpan * w + 512 * hk + 8 * lane;
     const uint32_t off = (m < M && k < K) ? (uint32_t)((m * K + k) * 2) : 0x80000000u;
@@ -620,10 +620,10 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const int8_t* q8
 
 bool decode_tiles_ok(int64_t M, int64_t N, int64_t K, int r) {
   (void)N;
-  // x slice in LDS (2 tokens x 1024 k per wave), the down projection's
+  // x slice in LDS (up to 4 tokens x the wave's k), the down projection's
   // slices in LDS (16 x M r floats), B tile and s*u in LDS
   return M >= 1 && M <= kTlMaxM && K <= 4096 && K % 256 == 0 && r <= kTlMaxR &&
-         (int64_t)decode_down_slices(K) * M * r <= kTlUp;
+         (int64_t)decode_down_slices(K) * M * r <= 16 * kTlMaxM * kTlMaxR;
 }
 
 hipError_t launch_gemv_tiles(const uint16_t* x, const uint8_t* codes, const int8_t* q8,
@@ -639,12 +639,18 @@ hipError_t launch_gemv_tiles(const uint16_t* x, const uint8_t* codes, const int8
   // eight-wave workgroups fit a CU (two rounds): each wave has half the
   // chunks, so a wave's compute after its data lands is half as long.
   const bool eight = tiles < 1024;
-#define QLORA_TL(F, B16)                                                                     \
-  do {                                                                                       \
-    if (eight)                                                                               \
-      hipLaunchKernelGGL((gemv_tiles_kernel<F, B16, 8>), grid, dim3(512), 0, st, a, cb);    \
-    else                                                                                     \
-      hipLaunchKernelGGL((gemv_tiles_kernel<F, B16, 4>), grid, dim3(256), 0, st, a, cb);    \
+  // x slices for at most two tokens, or for three or four (twice the LDS).
+  const bool four = M > 2;
+#define QLORA_TL(F, B16)                                                                      \
+  do {                                                                                        \
+    if (eight && four)                                                                        \
+      hipLaunchKernelGGL((gemv_tiles_kernel<F, B16, 8, 4>), grid, dim3(512), 0, st, a, cb);  \
+    else if (eight)                                                                           \
+      hipLaunchKernelGGL((gemv_tiles_kernel<F, B16, 8, 2>), grid, dim3(512), 0, st, a, cb);  \
+    else if (four)                                                                            \
+      hipLaunchKernelGGL((gemv_tiles_kernel<F, B16, 4, 4>), grid, dim3(256), 0, st, a, cb);  \
+    else                                                                                      \
+      hipLaunchKernelGGL((gemv_tiles_kernel<F, B16, 4, 2>), grid, dim3(256), 0, st, a, cb);  \
   } while (0)
   switch (cb.dq_format) {
     case kDqInt8: if (y_bf16) QLORA_TL(kDqInt8, true); else QLORA_TL(kDqInt8, false); break;

@@ -104,8 +104,8 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const int8_t* q8
                        int64_t M, int64_t N, int64_t K, int r, float s, float* u_out, void* y,
                        bool y_bf16, const Codebook& cb, hipStream_t st);
 
-// The decode GEMV as a persistent grid (decode_tiles_ok: M <= 16, K <= 4096,
-// r <= 64): one 1024-thread workgroup per CU streams a run of 16-row tiles;
+// The decode GEMV with one memory round trip per wave (decode_tiles_ok:
+// M <= 4, K <= 4096, K % 256 == 0, r <= 32): one workgroup per 16-row tile;
 // same arguments and results as launch_gemv.
 bool decode_tiles_ok(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_gemv_tiles(const uint16_t* x, const uint8_t* codes, const int8_t* q8,

@@ -418,12 +418,17 @@ def run_fwd_other_stream(P, x, **kw):
                                      (7, 1000, 1600, 64), (2, 40, 4096, 144),
                                      # four waves per tile (>= 512 tiles), ragged rows
                                      (16, 8200, 512, 16), (3, 8200, 256, 80),
-                                     # one-round-trip kernel (M <= 2, K % 256 == 0,
+                                     # one-round-trip kernel (M <= 4, K % 256 == 0,
                                      # K <= 4096, r <= 32): eight waves per tile
-                                     # with a ragged last tile and lanes past the
-                                     # row end; four waves per tile (>= 512 tiles)
+                                     # (under 1024 tiles) with a ragged last tile
+                                     # and lanes past the row end, x slices for two
+                                     # or for four tokens; four waves per tile
+                                     # (>= 1024 tiles)
                                      (1, 100, 256, 16), (2, 300, 4096, 32),
-                                     (2, 8200, 768, 32), (1, 8192, 4096, 16)])
+                                     (2, 8200, 768, 32), (1, 8192, 4096, 16),
+                                     (3, 100, 256, 16), (4, 520, 4096, 32),
+                                     (1, 16400, 256, 16), (4, 16400, 512, 32),
+                                     (3, 16392, 256, 16)])
 def test_fwd_decode_ragged(M, N, K, r):
     """Decode (M <= 16): ragged rows, chunks and adapter column groups against
     the oracle; a call on another stream gives the same bits."""
