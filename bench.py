@@ -462,7 +462,8 @@ def decode_7b(q, syn, torch, dev, stream):
     down projection and the fused GEMV), weight GB/s (codes + 8-bit scale
     codes + second-level scales + A + B per call) and total GB/s with the
     fractions of HBM peak, tokens/s. Also quantize and dequantize of both
-    weights (GB/s)."""
+    weights (GB/s), each call on another input (rings past the Infinity
+    Cache)."""
     cfg = syn.LLAMA7B_DECODE
     r, alpha = cfg["r"], cfg["alpha"]
     res = {"r": r}
@@ -476,11 +477,25 @@ def decode_7b(q, syn, torch, dev, stream):
         deq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
         sec = {"weight": [N, K], "ring_weights": nw,
                "ring_mb": round(nw * nf4_bytes(N, K) / 1e6, 1)}
-        for label, fn, nb in (("quantize", lambda: q.qlora_quantize_nf4_dq(base, out=ring[0]),
-                               2 * N * K + nf4_bytes(N, K)),
-                              ("dequant", lambda: q.qlora_dequant_bf16(ring[0], out=deq),
-                               nf4_bytes(N, K) + 2 * N * K)):
-            sec[label] = rate(0, nb, event_ms(torch, fn, 20, stream))
+        # Quantize and dequantize read distinct tensors call after call (bf16
+        # inputs: a ring of at least 512 MB, past the Infinity Cache), so the
+        # rates are HBM rates rather than cache rates.
+        nb16 = -(-512 * 10 ** 6 // (2 * N * K))
+        bases = [base] + [base.roll(i, 1) for i in range(1, nb16)]
+        cnt = [0]
+
+        def quant_next():
+            cnt[0] += 1
+            q.qlora_quantize_nf4_dq(bases[cnt[0] % nb16], out=ring[cnt[0] % nw])
+
+        def deq_next():
+            cnt[0] += 1
+            q.qlora_dequant_bf16(ring[cnt[0] % nw], out=deq)
+        for label, fn, nb in (("quantize", quant_next, 2 * N * K + nf4_bytes(N, K)),
+                              ("dequant", deq_next, nf4_bytes(N, K) + 2 * N * K)):
+            sec[label] = rate(0, nb, event_ms(torch, fn, 48, stream))
+        sec["quantize_ring_mb"] = round(nb16 * 2 * N * K / 1e6, 1)
+        del bases
         A = syn.torch_normal_bf16((K, r), 1.0 / K ** 0.5, syn.seed_of(2, 30), dev)
         B = syn.torch_normal_bf16((r, N), 0.01, syn.seed_of(2, 31), dev)
         for Md in cfg["M"]:
