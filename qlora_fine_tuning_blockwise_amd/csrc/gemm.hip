@@ -659,8 +659,12 @@ struct BwdArgs {
 //   end:   wait until only this step's loads are in flight, then barrier.
 // Wave w only reads the code bytes and tables of its own 64 columns, which
 // its own lanes fetch and build, so those need only this wave's waits.
-template <bool kOutBf16>
+// kMT: 32-row MFMA row tiles of the 256-row output tile that carry rows of
+// dY (8; 1 when M <= 32, so that a decode-size call issues one MFMA group
+// per lookup group instead of eight).
+template <bool kOutBf16, int kMT>
 __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb) {
+  static_assert(kMT == 1 || kMT == 8, "row tiles");
   __shared__ __attribute__((aligned(1024))) uint16_t ys0[kTileBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t ys1[kTileBytes / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t ys2[kTileBytes / 2];
@@ -739,9 +743,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
   };
   auto scale_ok = [&](int64_t ns) { return (nsb + ns) * 64 + (tid & 63) < N && tblk_ok; };
 
-  f32x16_t acc[8][2];
+  f32x16_t acc[kMT][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kMT; ++i)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -767,13 +771,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
     const char* tb = reinterpret_cast<const char*>(tarr);
     u32x4_t a[3];
     a[0] = *reinterpret_cast<const u32x4_t*>(ya);
-    a[1] = *reinterpret_cast<const u32x4_t*>(ya + 4096);
+    if (kMT > 1) a[1] = *reinterpret_cast<const u32x4_t*>(ya + 4096);
     uint32_t lo[8], hi[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      if (mt + 2 < 8) a[(mt + 2) % 3] = *reinterpret_cast<const u32x4_t*>(ya + (mt + 2) * 4096);
+      if (mt + 2 < kMT) a[(mt + 2) % 3] = *reinterpret_cast<const u32x4_t*>(ya + (mt + 2) * 4096);
+      if (mt < kMT) {
+        constexpr int kLast = kMT - 1;
+        const int mi = mt < kMT ? mt : kLast;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma_32x32x16(a[mt % 3], bc[nt], acc[mt][nt]);
+        for (int nt = 0; nt < 2; ++nt) acc[mi][nt] = mfma_32x32x16(a[mt % 3], bc[nt], acc[mi][nt]);
+      }
       {
         const int f = mt >> 2, q = mt & 3;
         const uint32_t r0 = t_byte + (uint32_t)(8 * sn + 2 * q) * 32;
@@ -784,10 +792,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
         hi[mt] = *reinterpret_cast<const uint16_t*>(tb + ((r0 + 32) | o1));
       }
       if (mt >= 2) bn[(mt - 2) >> 2][(mt - 2) & 3] = lo[mt - 2] | (hi[mt - 2] << 16);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      if (kMT == 8) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
     }
     bn[1][2] = lo[6] | (hi[6] << 16);
     bn[1][3] = lo[7] | (hi[7] << 16);
@@ -880,7 +890,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
       bfr[nt] = kc < K ? *reinterpret_cast<const u32x4_t*>(p.A + kc * r + jb) : zero4();
     }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
+    for (int mt = 0; mt < kMT; ++mt) {
       const int64_t m = m0 + 32 * mt + c;
       const u32x4_t a = m < M ? *reinterpret_cast<const u32x4_t*>(p.svlr + m * r2 + jj) : zero4();
 #pragma unroll
@@ -892,7 +902,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
   if (wave_live && p.nsplit > 1) {  // fp32 partial sums of this split
     float* dst = p.part + (int64_t)split * M * K;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -900,7 +910,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdArgs p, Codebook cb
       }
   } else if (wave_live) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -990,10 +1000,18 @@ hipError_t launch_gemm_bwd(const uint16_t* dY, const uint8_t* codes, const int8_
     const dim3 grid((unsigned)((K + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM),
                     (unsigned)nsplit);
     const BwdArgs a{dY, codes, q8, s2, svlr, A, dX, M, N, K, r, nsplit, part};
-    if (dx_bf16)
-      hipLaunchKernelGGL(gemm_bwd_kernel<true>, grid, dim3(256), 0, st, a, cb);
-    else
-      hipLaunchKernelGGL(gemm_bwd_kernel<false>, grid, dim3(256), 0, st, a, cb);
+    // one 32-row MFMA row tile when M <= 32 (the other seven would hold only
+    // the padding rows)
+    if (M <= 32) {
+      if (dx_bf16)
+        hipLaunchKernelGGL((gemm_bwd_kernel<true, 1>), grid, dim3(256), 0, st, a, cb);
+      else
+        hipLaunchKernelGGL((gemm_bwd_kernel<false, 1>), grid, dim3(256), 0, st, a, cb);
+    } else if (dx_bf16) {
+      hipLaunchKernelGGL((gemm_bwd_kernel<true, 8>), grid, dim3(256), 0, st, a, cb);
+    } else {
+      hipLaunchKernelGGL((gemm_bwd_kernel<false, 8>), grid, dim3(256), 0, st, a, cb);
+    }
     if (nsplit > 1) {
       const hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;

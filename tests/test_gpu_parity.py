@@ -374,7 +374,7 @@ def test_fwd_one_hot_rows_exact_gemm_and_gemv():
     N, K, r = 512, 1024, 16
     P = Problem(N, K, r, 32.0, seed=5)
     P.Bt = torch.zeros_like(P.Bt)
-    for M, lean in ((2, False), (16, False), (64, False), (600, False), (600, True)):
+    for M, lean in ((2, False), (4, False), (16, False), (64, False), (600, False), (600, True)):
         ks = np.random.default_rng(M).choice(K, M, replace=False)
         x = np.zeros((M, K), np.uint16)
         x[np.arange(M), ks] = 0x3F80
@@ -1050,15 +1050,16 @@ def test_formats_llama7b_up_bit_exact(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_formats_one_hot_fwd_and_bwd_exact(fmt):
-    """One-hot rows through both GEMVs (M = 2, 16), the tile kernels (M = 64, 40)
-    and the large-M path (M = 600) return the format's dequantized weight
+    """One-hot rows through both GEMVs (M = 2 and 4: x slices for two and for
+    four tokens; M = 16), the tile kernels (M = 64, 40) and the large-M path
+    (M = 600) return the format's dequantized weight
     columns and rows bit for bit: every in-kernel decoding of the absmax
     byte follows the format."""
     N, K, r = 640, 1024, 16
     P = Problem(N, K, r, 32.0, seed=304, fmt=fmt)
     P.Bt = torch.zeros_like(P.Bt)
     Wf = oracle.bf16_to_f32(P.What)
-    for M, lean in ((2, False), (16, False), (64, False), (600, False), (600, True)):
+    for M, lean in ((2, False), (4, False), (16, False), (64, False), (600, False), (600, True)):
         ks = np.random.default_rng(M).choice(K, M, replace=False)
         x = np.zeros((M, K), np.uint16)
         x[np.arange(M), ks] = 0x3F80
