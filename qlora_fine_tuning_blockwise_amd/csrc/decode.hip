@@ -421,7 +421,28 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Co
   const uint32_t nl = (uint32_t)min(i, rows - 1);  // rows past N read row N-1 (never stored)
   const int64_t b0 = kTlBpl * (4 * w + g);          // the lane's first block
 
-  // 1. x slice of this wave (M <= kMaxM tokens x kSpan k) by direct-to-LDS
+  // 1. wave 0: the down projection's slices (slices x M r floats, 1 KB per
+  //    instruction) and the tile's B columns, issued first: they are read
+  //    only in the epilogue, so the waits before the first lookups skip
+  //    them.
+  const int upb = p.slices * mr * 4;
+  if (w == 0) {
+    const __amdgpu_buffer_rsrc_t ures = gv_rsrc(p.upart, upb);
+    for (int q = 0; q < (upb + 1023) / 1024; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ures, (lds_void*)(ups + 256 * q), 16,
+                                               (uint32_t)(1024 * q + 16 * lane), 0, 0, 0);
+  }
+  uint16_t bv[kTlMaxR / 16];
+#pragma unroll
+  for (int q = 0; q < kTlMaxR / 16; ++q) {  // 16 r values over 256 threads
+    const int idx = tid + 256 * q;
+    const uint32_t bj = (uint32_t)min(idx >> 4, r - 1);
+    const uint32_t bc = (uint32_t)min((int64_t)(idx & 15), N - 1 - n0);
+    if (q == 0 || idx < 16 * r) bv[q] = (p.B + n0)[bj * (uint32_t)N + bc];
+  }
+
+
+  // 2. x slice of this wave (M <= kMaxM tokens x kSpan k) by direct-to-LDS
   //    loads: instruction q covers 512 k (piece q % kXq) of token q / kXq;
   //    the zero row behind it is written first.
   unsigned char* xw = xs[w];
@@ -436,7 +457,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Co
     if (q < kXq * M)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)(xw + 1024 * q), 16, off, 0, 0, 0);
   }
-  // 2. codes, absmax bytes and group scales of the lane's four blocks
+  // The wait before the first lookups counts the loads issued after the x
+  // slices: none may move above them.
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. codes, absmax bytes and group scales of the lane's four blocks
   //    (blocks past the row end read the row's last block and get zeros).
   const uint32_t kb32 = (uint32_t)KB;
   const __amdgpu_buffer_rsrc_t cres = gv_rsrc(p.codes + n0 * (K >> 1), (int64_t)rows * (K >> 1));
@@ -462,24 +486,6 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Co
   else
     q4 = __builtin_amdgcn_raw_buffer_load_b16(qres, (int)qi, 0, 0);
   const float sv = (p.s2 + ((n0 * KB) >> 8))[((uint32_t)((n0 * KB) & 255) + qi) >> 8];
-  // 3. wave 0: the down projection's slices (slices x M r floats, 1 KB per
-  //    instruction) and the tile's B columns.
-  const int upb = p.slices * mr * 4;
-  if (w == 0) {
-    const __amdgpu_buffer_rsrc_t ures = gv_rsrc(p.upart, upb);
-    for (int q = 0; q < (upb + 1023) / 1024; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ures, (lds_void*)(ups + 256 * q), 16,
-                                               (uint32_t)(1024 * q + 16 * lane), 0, 0, 0);
-  }
-  uint16_t bv[kTlMaxR / 16];
-#pragma unroll
-  for (int q = 0; q < kTlMaxR / 16; ++q) {  // 16 r values over 256 threads
-    const int idx = tid + 256 * q;
-    const uint32_t bj = (uint32_t)min(idx >> 4, r - 1);
-    const uint32_t bc = (uint32_t)min((int64_t)(idx & 15), N - 1 - n0);
-    if (q == 0 || idx < 16 * r) bv[q] = (p.B + n0)[bj * (uint32_t)N + bc];
-  }
-
   const uint32_t region = __builtin_amdgcn_mbcnt_lo(0u, 0u) + 0x10101010u * (uint32_t)w;
   const uint32_t colbase = 4u * (uint32_t)lane;
   const char* tab = reinterpret_cast<const char*>(&tabs[0][0][0]);
@@ -497,8 +503,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Co
     const float ch1 = b0 + 2 * pr + 1 < KB ? gv_absmax<kFmt>(q1) * sv : 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) tabs[w][e][lane] = pack_bf16x2(cb.level[e] * ch0, cb.level[e] * ch1);
-    if (first) {  // the x slice (this wave's own loads, issued first)
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): every load of this wave
+    if (first) {  // the x slice: every load but the codes, q4 and sv has landed
+      constexpr int kYounger = 2 * kTlBpl + 2;
+      __builtin_amdgcn_s_waitcnt((kYounger & 15) | ((kYounger >> 4) << 14) | (0x7 << 4));
       first = false;
     }
     const uint32_t dw[16] = {cw[2 * pr][0].x, cw[2 * pr][0].y, cw[2 * pr][0].z, cw[2 * pr][0].w,
@@ -538,6 +545,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Co
 
   // u = sum of the slices in order from +0 (the same bits as the finalize
   // kernel's sum), s*u for the epilogue; wave 0 staged the slices.
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the staged slices
   if (w == 0)
     for (int idx = lane; idx < mr; idx += 64) {
       float t[kDecMaxSlices];
