@@ -355,17 +355,18 @@ __device__ __forceinline__ float gv_absmax(int b) {  // b: the byte, zero-extend
 // ------------------------------------------- one-round-trip GEMV (K <= 4096)
 // Under the full weight stream a memory round trip takes microseconds, so
 // gemv_tiles_kernel makes exactly one: every wave issues all of its loads
-// (its codes, absmax bytes and group scales, its slice of x by
-// direct-to-LDS loads, and in wave 0 the down projection's slices and the B
-// columns of the tile) before its first wait, and a workgroup of four waves
-// covers one 16-row tile, so that the whole weight is requested at once.
-// Per weight a lane does one address permute, one 16-bit LDS lookup and
-// half a packing permute; each pair of blocks costs 32 multiplies and 16
-// conversions for its table. Measured on the 11008 x 4096 weight at M = 1
-// (a ring of 24 weights, each call with the down projection): 14.0 us per
-// call against 15.9 us for gemv_kernel; the same call with the lookups and
-// MFMAs taken out (a timing copy) takes 10.2 us, and the down projection
-// alone 2.2 us, so the stream of codes itself runs at about 4 TB/s here.
+// (the B columns of the tile and, in wave 0, the down projection's slices,
+// which only the epilogue reads; its slice of x by direct-to-LDS loads; its
+// absmax bytes, group scale and codes) before its first wait, and the
+// workgroups of one launch cover all 16-row tiles, so that the whole weight
+// is requested at once. The first lookups wait only for the x slice and the
+// codes they read. Per weight a lane does one address permute, one 16-bit
+// LDS lookup and half a packing permute; each pair of blocks costs 32
+// multiplies and 16 conversions for its table. Measured on the 11008 x 4096
+// weight at M = 1 (a ring of 24 weights, each call with the down
+// projection): 13.4 us per call against 15.9 us for gemv_kernel; a plain
+// read of the codes and absmax bytes with the same grid and load pattern (a
+// timing probe) takes 6.2 us, an empty launch of the grid 1.9 us.
 constexpr int kTlMaxR = 32;
 constexpr int kTlMaxM = 4;  // tokens; a launch is built for at most 2 or at most 4
 
