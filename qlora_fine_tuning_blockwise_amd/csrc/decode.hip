@@ -357,9 +357,8 @@ __device__ __forceinline__ float gv_absmax(int b) {  // b: the byte, zero-extend
 // gemv_tiles_kernel makes exactly one: every wave issues all of its loads
 // (the B columns of the tile and, in wave 0, the down projection's slices,
 // which only the epilogue reads; its slice of x by direct-to-LDS loads; its
-// absmax bytes, group scale and codes) before its first wait, and the
-// workgroups of one launch cover all 16-row tiles, so that the whole weight
-// is requested at once. The first lookups wait only for the x slice and the
+// absmax bytes, group scale and codes) before its first wait, so that
+// every resident workgroup's share of the weight is requested at once. The first lookups wait only for the x slice and the
 // codes they read. Per weight a lane does one address permute, one 16-bit
 // LDS lookup and half a packing permute; each pair of blocks costs 32
 // multiplies and 16 conversions for its table. Measured on the 11008 x 4096
