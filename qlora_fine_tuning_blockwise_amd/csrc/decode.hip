@@ -400,7 +400,9 @@ __device__ __forceinline__ uint32_t tl_lookup(const char* tab, uint32_t addr) {
 template <int kFmt, bool kOutBf16, int kWaves, int kMaxM>
 __global__ __launch_bounds__(64 * kWaves) void gemv_tiles_kernel(TilesArgs p, Codebook cb) {
   constexpr int kTlWaves = kWaves;
-  constexpr int kTlUp = 16 * kMaxM * kTlMaxR;  // staged slices (16 x M r floats)
+  // Staged slices (at most 16 x M r floats). The two-token build holds 512
+  // (M r <= 32), so that its eight-wave workgroup fits three to a CU.
+  constexpr int kTlUp = kMaxM == 2 ? 512 : 16 * kMaxM * kTlMaxR;
   constexpr int kTlBpl = 16 / kWaves;                          // blocks per lane (K <= 4096)
   constexpr int kSpan = 64 * 4 * kTlBpl;                       // k covered by one wave
   constexpr int kXw = 2 * kSpan * kMaxM;                       // x slice bytes per wave
@@ -643,12 +645,15 @@ hipError_t launch_gemv_tiles(const uint16_t* x, const uint8_t* codes, const int8
   const dim3 grid((unsigned)tiles);
   // Eight waves per tile up to 1023 tiles, four beyond. Measured on the
   // 11008 x 4096 weight at M = 1 (688 tiles, a ring of 24 weights): 10.8 us
-  // per GEMV with eight waves against 11.4 us with four, although only two
-  // eight-wave workgroups fit a CU (two rounds): each wave has half the
-  // chunks, so a wave's compute after its data lands is half as long.
+  // per GEMV with eight waves against 11.4 us with four when two eight-wave
+  // workgroups fit a CU (two rounds): each wave has half the chunks, so a
+  // wave's compute after its data lands is half as long. With the two-token
+  // build's LDS trimmed so that three fit (one round for 688 tiles) the call
+  // went 13.5 -> 12.4-12.7 us.
   const bool eight = tiles < 1024;
-  // x slices for at most two tokens, or for three or four (twice the LDS).
-  const bool four = M > 2;
+  // x slices (and staged slices of u) for at most two tokens (M r <= 32), or
+  // for three or four tokens (twice the LDS).
+  const bool four = M > 2 || (int64_t)slices * M * r > 512;
 #define QLORA_TL(F, B16)                                                                      \
   do {                                                                                        \
     if (eight && four)                                                                        \
