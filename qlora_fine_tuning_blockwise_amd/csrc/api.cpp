@@ -460,7 +460,7 @@ int qlora_linear_bwd(const qlora_nf4* w, const uint16_t* x, const uint16_t* dY, 
   }
   if (e == hipSuccess && dX && L.plain) {  // dX = dY w_hat through w_hat^T [K,N]
     uint16_t* Wt = at<uint16_t>(workspace, L.Wt);
-    e = launch_dequant_t(codes, absmax_q, absmax_scale, N, K, Wt, true, cb, st);  // K-slab
+    e = launch_dequant_t(codes, absmax_q, absmax_scale, N, K, Wt, cb, st);  // K-slab
     if (e == hipSuccess)
       e = launch_gemm_nt(dY, N, Wt, 0, svlr, A, M, K, N, r, dX, dx_dtype == QLORA_DTYPE_BF16, true,
                          st, L.splits, at<float>(workspace, L.part));

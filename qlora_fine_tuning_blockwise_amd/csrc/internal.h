@@ -151,12 +151,10 @@ hipError_t launch_gemm_nf4_fwd(const uint16_t* x, const uint8_t* codes, const in
                                int64_t N, int64_t K, int r, void* y, bool y_bf16,
                                const Codebook& cb, hipStream_t st);
 
-// out[k][n] = w_hat[n][k] as bf16: [K, N] row-major (the transpose of
-// launch_dequant's output), or in the K-slab layout [N/32][K][32] when kslab
-// (N % 32 == 0).
+// w_hat^T as bf16 in the K-slab layout [N/32][K][32]: out[s][k][j] =
+// w_hat[32 s + j][k] (N % 32 == 0, K % 64 == 0, else hipErrorInvalidValue).
 hipError_t launch_dequant_t(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t N,
-                            int64_t K, uint16_t* out, bool kslab, const Codebook& cb,
-                            hipStream_t st);
+                            int64_t K, uint16_t* out, const Codebook& cb, hipStream_t st);
 
 // merged = base + s (A B)^T in binary32 (adapter sum in order j = 0..r-1);
 // base = the dequantized NF4 weight (W == NULL) or the bf16 weight W.

@@ -367,105 +367,65 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   }
 }
 
-// w_hat^T: out[k][n] = bf16(L[code(n,k)] * c1_hat(n, k/64)), c1_hat =
-// fp32(q8 * s2) (the same roundings as the row-major dequantization).
-// Workgroup tile: 64 weight rows x 256 columns. Thread t owns the row pair
-// (n0 + 2p, n0 + 2p + 1), p = t / 8, and the 32 columns [32c, 32c + 32),
-// c = t % 8, of the tile, so eight consecutive lanes read a row's 128 bytes
-// of codes (whole cache lines). It packs the pair of each column into one
-// dword of the transposed LDS tile: row k holds the 32 pair dwords, dword p
-// at position p ^ (8 ((k / 32) % 4)), which puts the 64 lanes of a write
-// (fixed column offset, eight c and eight p) on 32 distinct banks and keeps
-// every aligned group of four dwords together. The workgroup then writes
-// out: in the K-slab layout [N/32][K][32] a wave store covers 16 consecutive
-// k rows of one slab, 1 KB of consecutive bytes; row-major, a wave store
-// covers 8 k rows x 128 bytes. The row-major stores carry the nontemporal
-// hint, the K-slab ones (read by the dense GEMM next) do not, as in
-// dequant_kernel.
-constexpr int kDtRows = 64;    // tile rows (n)
-constexpr int kDtCols = 256;   // tile columns (k)
+// w_hat^T in the K-slab layout [N/32][K][32]: out[s][k][j] =
+// bf16(L[code(32 s + j, k)] * c1_hat(32 s + j, k / 64)), c1_hat = fp32(q8 * s2)
+// (the same roundings as the row-major dequantization). A workgroup owns one
+// slab s and the 256 columns [k0, k0 + 256): its output is one contiguous
+// 16 KB run, and its 16 KB LDS tile leaves room for eight workgroups on a CU.
+// Thread t owns the row pair (32 s + 2p, 32 s + 2p + 1), p = t / 16, and the
+// 16 columns [k0 + 16c, +16), c = t % 16, so sixteen consecutive lanes read a
+// row's 128 bytes of codes. It packs the pair of each column into one dword
+// of the transposed tile (row k: 16 dwords, the slab row's 64 bytes), dword p
+// at position p ^ (4 ((k >> 2) & 3)), which keeps aligned groups of four
+// dwords together for the 16-byte reads. In write step j a lane takes column
+// (j + c) % 16 of its own 16, so the 64 lanes of a write cover every residue
+// of k mod 16 and, with the swizzle, spread over all banks two lanes a bank.
+// The stores carry no nontemporal hint: the dense GEMM reads the copy next.
+constexpr int kDtCols = 256;  // tile columns (k)
 
-template <bool kKSlab>
 __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
                                                         const int8_t* __restrict__ q8,
-                                                        const float* __restrict__ s2, int64_t N,
-                                                        int64_t K, uint16_t* __restrict__ out,
-                                                        Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint32_t tile[kDtCols * 32];
+                                                        const float* __restrict__ s2, int64_t K,
+                                                        uint16_t* __restrict__ out, Codebook cb) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile[kDtCols * 16];
   __shared__ float levels[16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * kDtRows, k0 = (int64_t)blockIdx.y * kDtCols;
-  const int64_t KB = K / 64;
-  const int p = tid >> 3, c = tid & 7;
-  const int64_t na = n0 + 2 * p, nb = na + 1;
-  const int64_t kk = k0 + 32 * c;
-  u32x4_t ca = zero4(), cbv = zero4();
+  const int tid = threadIdx.x;
+  const int64_t KB = K / 64, ktiles = (K + kDtCols - 1) / kDtCols;
+  const int64_t slab = blockIdx.x / ktiles, k0 = (int64_t)(blockIdx.x % ktiles) * kDtCols;
+  const int p = tid >> 4, c = tid & 15;
+  const int64_t na = 32 * slab + 2 * p, nb = na + 1;  // < N: the grid covers whole slabs
+  const int64_t kk = k0 + 16 * c;
+  uint64_t wa = 0, wb = 0;
   float cha = 0.0f, chb = 0.0f;
   if (kk < K) {
     const int64_t blk = kk / 64;
-    if (na < N) {
-      ca = *reinterpret_cast<const u32x4_t*>(codes + na * (K / 2) + kk / 2);
-      cha = q8_value(q8[na * KB + blk], cb.dq_format) * s2[(na * KB + blk) >> 8];
-    }
-    if (nb < N) {
-      cbv = *reinterpret_cast<const u32x4_t*>(codes + nb * (K / 2) + kk / 2);
-      chb = q8_value(q8[nb * KB + blk], cb.dq_format) * s2[(nb * KB + blk) >> 8];
-    }
+    wa = *reinterpret_cast<const uint64_t*>(codes + na * (K / 2) + kk / 2);
+    wb = *reinterpret_cast<const uint64_t*>(codes + nb * (K / 2) + kk / 2);
+    cha = q8_value(q8[na * KB + blk], cb.dq_format) * s2[(na * KB + blk) >> 8];
+    chb = q8_value(q8[nb * KB + blk], cb.dq_format) * s2[(nb * KB + blk) >> 8];
   }
   if (tid < 16) levels[tid] = cb.level[tid];
   __syncthreads();
-  {
-    const uint32_t wa[4] = {ca.x, ca.y, ca.z, ca.w};
-    const uint32_t wb[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
-    uint32_t* trow = tile + (32 * c) * 32 + (p ^ (8 * (c & 3)));
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float va = levels[(wa[d] >> (4 * e)) & 15u] * cha;
-        const float vb = levels[(wb[d] >> (4 * e)) & 15u] * chb;
-        trow[(8 * d + e) * 32] = pack_bf16x2(va, vb);
-      }
+  for (int j = 0; j < 16; ++j) {
+    const int jj = (j + c) & 15;  // weight kk + jj: code nibble jj
+    const int k = 16 * c + jj;
+    const float va = levels[(uint32_t)(wa >> (4 * jj)) & 15u] * cha;
+    const float vb = levels[(uint32_t)(wb >> (4 * jj)) & 15u] * chb;
+    tile[16 * k + (p ^ (4 * ((k >> 2) & 3)))] = pack_bf16x2(va, vb);
   }
   __syncthreads();
-  if (kKSlab) {
-    // Wave w: slab w % 2 of the tile (32 rows, pair dwords 16s .. 16s+15),
-    // columns [128 (w / 2), +128), 16 per store; lane: column l / 4, 16-byte
-    // piece l % 4 of the slab row.
-    const int sl = w & 1, pc = lane & 3;
-    const int64_t slab = n0 / 32 + sl;
-    if (32 * slab >= N) return;  // N % 32 == 0: whole slabs only
+  // Pass i: thread t copies slab row k = 64 i + t / 4, 16-byte piece q = t % 4
+  // (weight rows 8q .. 8q + 7 of the slab); the workgroup writes 4 KB of
+  // consecutive bytes per pass.
+  const int q = tid & 3;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int kl = 128 * (w >> 1) + 16 * it + (lane >> 2);
-      const int64_t k = k0 + kl;
-      if (k >= K) break;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
-          &tile[kl * 32 + ((16 * sl + 4 * pc) ^ (8 * ((kl >> 5) & 3)))]);
-      *reinterpret_cast<u32x4_t*>(out + (slab * K + k) * 32 + 8 * pc) = v;
-    }
-    return;
-  }
-  // Row-major: wave w writes columns [64w, 64w + 64) of the tile, 8 per
-  // store; lane: column l / 8, eight weight rows 8 (l % 8) .. +7.
-  const int pc = lane & 7;
-  const int64_t nc = n0 + 8 * pc;
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int kl = 64 * w + 8 * it + (lane >> 3);
-    const int64_t k = k0 + kl;
-    if (k >= K) break;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
-        &tile[kl * 32 + ((4 * pc) ^ (8 * ((kl >> 5) & 3)))]);
-    uint16_t* dst = out + k * N + nc;
-    if (nc + 8 <= N && (N & 7) == 0) {
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
-    } else {
-      const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        if (nc + t < N) dst[t] = (uint16_t)(vv[t >> 1] >> (16 * (t & 1)));
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int k = 64 * i + (tid >> 2);
+    if (k0 + k >= K) break;
+    const u32x4_t v =
+        *reinterpret_cast<const u32x4_t*>(&tile[16 * k + 4 * (q ^ ((k >> 2) & 3))]);
+    *reinterpret_cast<u32x4_t*>(out + (slab * K + k0 + k) * 32 + 8 * q) = v;
   }
 }
 
@@ -507,16 +467,15 @@ hipError_t launch_dequant(const uint8_t* codes, const int8_t* q8, const float* s
 
 
 hipError_t launch_dequant_t(const uint8_t* codes, const int8_t* q8, const float* s2, int64_t N,
-                            int64_t K, uint16_t* out, bool kslab, const Codebook& cb,
-                            hipStream_t st) {
-  const dim3 grid((unsigned)((N + kDtRows - 1) / kDtRows), (unsigned)((K + kDtCols - 1) / kDtCols));
-  if (kslab) {
-    if (N % 32) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(dequant_t_kernel<true>, grid, dim3(256), 0, st, codes, q8, s2, N, K, out, cb);
-  } else {
-    hipLaunchKernelGGL(dequant_t_kernel<false>, grid, dim3(256), 0, st, codes, q8, s2, N, K, out,
-                       cb);
-  }
+                            int64_t K, uint16_t* out, const Codebook& cb, hipStream_t st) {
+  if (N % 32 || K % 64) return hipErrorInvalidValue;
+  if (N == 0 || K == 0) return hipSuccess;
+  // Tiles along K first: consecutive workgroups read each row's codes as one
+  // run and write each slab in order.
+  const int64_t tiles = N / 32 * ((K + kDtCols - 1) / kDtCols);
+  if (tiles >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dequant_t_kernel, dim3((unsigned)tiles), dim3(256), 0, st, codes, q8, s2, K,
+                     out, cb);
   return hipGetLastError();
 }
 
