@@ -702,9 +702,12 @@ def test_bwd_train_llama7b(name):
     tol_check(host(dB), g["dB"], f"dB train {name}")
 
 
-@pytest.mark.parametrize("M,N", [(40, 320), (600, 640), (16, 1024)])
-def test_bwd_one_hot_dy_rows_exact(M, N):
-    K, r = 512, 16
+@pytest.mark.parametrize("M,N,K", [(40, 320, 512), (600, 640, 512), (16, 1024, 512),
+                                   # from 512 rows, N % 32 == 0: the transposed copy's
+                                   # last column tile is ragged (K % 256 = 64)
+                                   (512, 544, 320), (520, 672, 4160)])
+def test_bwd_one_hot_dy_rows_exact(M, N, K):
+    r = 16
     P = Problem(N, K, r, 32.0, seed=11)
     P.Bt = torch.zeros_like(P.Bt)
     ns = np.random.default_rng(4).choice(N, M, replace=False)
